@@ -1,0 +1,186 @@
+"""CPU oracle for MoE routing layout, dispatch copy and combine.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+benchmark's CPU-baseline leg, never by the product path.  It wraps the plain C
+definitions in ``ep_oracle.c`` (built with gcc, single-threaded) and shares no
+code with the HIP library.  Arrays are numpy, on the host.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ep_oracle.c")
+_LIB = os.path.join(_HERE, "libep_oracle.so")
+
+CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
+          "-fPIC", "-shared", "-Wall", "-Wextra"]
+
+ERR_CAPACITY = 1
+ERR_ARGS = 2
+
+
+def build(src: str = _SRC, out: str = _LIB, extra=()) -> str:
+    """Compile the oracle with gcc (always recompiles)."""
+    tmp = f"{out}.tmp{os.getpid()}"
+    subprocess.run(["gcc", *CFLAGS, *extra, "-o", tmp, src], check=True)
+    os.replace(tmp, out)
+    return out
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int64
+
+
+def _bind(lib):
+    lib.oracle_capacity_bound.restype = _I
+    lib.oracle_capacity_bound.argtypes = [_I, _I, _I, _I]
+    lib.oracle_layout.restype = ctypes.c_int
+    lib.oracle_layout.argtypes = [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P]
+    lib.oracle_dispatch.restype = None
+    lib.oracle_dispatch.argtypes = [_I, _I, _I, _I, _P, _I, _P, _I, _I, _P,
+                                    _P, _P, _P, _P, _P, _I, _I, _P, ctypes.c_int]
+    lib.oracle_combine.restype = None
+    lib.oracle_combine.argtypes = [_I, _I, _I, _P, _P, _P, _P, _P, _P]
+    lib.oracle_combine_f64.restype = None
+    lib.oracle_combine_f64.argtypes = [_I, _I, _I, _P, _P, _P, _P, _P, _P, _P]
+    return lib
+
+
+_lib = None
+
+
+def load(path: Optional[str] = None):
+    """Load the built oracle (building it first if it is absent)."""
+    global _lib
+    if path is not None:
+        return _bind(ctypes.CDLL(path))
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        _lib = _bind(ctypes.CDLL(_LIB))
+    return _lib
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+class Layout:
+    """Result of :func:`layout`; arrays are numpy int32, scalars Python ints."""
+
+    def __init__(self, status, counts, psum, dst, src_meta, num_recv_tokens,
+                 invalid_count, num_expanded):
+        self.status = status
+        self.counts = counts
+        self.psum = psum
+        self.dst = dst
+        self.src_meta = src_meta
+        self.num_recv_tokens = num_recv_tokens
+        self.invalid_count = invalid_count
+        self.num_expanded = num_expanded
+
+
+def capacity_bound(T, K, E, A, lib=None) -> int:
+    return int((lib or load()).oracle_capacity_bound(T, K, E, A))
+
+
+def layout(topk_idx, num_experts: int, alignment: int, capacity: int,
+           lib=None) -> Layout:
+    """topk_idx: integer [T, K] (int32 is widened to int64)."""
+    lib = lib or load()
+    idx = _c(topk_idx, np.int64)
+    T, K = idx.shape
+    counts = np.zeros(num_experts, np.int32)
+    psum = np.zeros(num_experts + 1, np.int32)
+    dst = np.full(T * K, -7, np.int32)
+    src = np.full(max(capacity, 1), -7, np.int32)
+    sc = np.zeros(3, np.int64)
+    st = lib.oracle_layout(T, K, num_experts, alignment, capacity, _ptr(idx),
+                           _ptr(counts), _ptr(psum), _ptr(dst), _ptr(src),
+                           _ptr(sc))
+    return Layout(int(st), counts, psum, dst.reshape(T, K), src[:capacity],
+                  int(sc[0]), int(sc[1]), int(sc[2]))
+
+
+def dispatch(x_bytes: np.ndarray, lay: Layout, capacity: int,
+             sf: Optional[np.ndarray] = None, sf_strides=None,
+             weights: Optional[np.ndarray] = None, want_w: bool = False,
+             zero_padding: bool = False, out_x=None, out_sf=None,
+             out_sf_strides=None, out_w=None, lib=None):
+    """x_bytes: uint8 [T, row_bytes] (the raw row bytes of bf16 or FP8 x).
+
+    Outputs may be passed in (pre-filled, e.g. with a poison pattern) to show
+    which rows are left untouched; otherwise they are zero-initialised.
+    ``sf`` is float32 and addressed with (token, hidden) element strides.
+    """
+    lib = lib or load()
+    x = np.ascontiguousarray(x_bytes, dtype=np.uint8)
+    T, row_bytes = x.shape
+    K = lay.dst.shape[1]
+    E = lay.counts.shape[0]
+    if out_x is None:
+        out_x = np.zeros((capacity, row_bytes), np.uint8)
+    num_sf = 0
+    ts = hs = ots = ohs = 0
+    sf_arr = None
+    if sf is not None:
+        sf_arr = np.asarray(sf)
+        assert sf_arr.dtype == np.float32
+        ts, hs = sf_strides if sf_strides is not None else (sf_arr.shape[1], 1)
+        num_sf = row_bytes // 128
+        if out_sf is None:
+            out_sf = np.zeros((capacity, num_sf), np.float32)
+        ots, ohs = out_sf_strides if out_sf_strides is not None else (num_sf, 1)
+    if want_w and out_w is None:
+        out_w = np.zeros(capacity, np.float32)
+    w = None if weights is None else _c(weights, np.float32)
+    lib.oracle_dispatch(T, K, E, row_bytes, _ptr(x), num_sf, _ptr(sf_arr),
+                        ts, hs, _ptr(w), _ptr(lay.counts), _ptr(lay.psum),
+                        _ptr(_c(lay.dst, np.int32)), _ptr(out_x),
+                        _ptr(out_sf), ots, ohs, _ptr(out_w),
+                        1 if zero_padding else 0)
+    return out_x, out_sf, out_w
+
+
+def combine(y_bits: np.ndarray, topk_idx, dst, weights=None, bias_bits=None,
+            lib=None) -> np.ndarray:
+    """y_bits: uint16 [rows, H] bf16 bit patterns; returns uint16 [T, H]."""
+    lib = lib or load()
+    y = _c(y_bits, np.uint16)
+    idx = _c(topk_idx, np.int64)
+    d = _c(dst, np.int32)
+    T, K = idx.shape
+    H = y.shape[1]
+    out = np.zeros((T, H), np.uint16)
+    w = None if weights is None else _c(weights, np.float32)
+    b = None if bias_bits is None else _c(bias_bits, np.uint16)
+    lib.oracle_combine(T, K, H, _ptr(y), _ptr(w), _ptr(b), _ptr(idx), _ptr(d),
+                       _ptr(out))
+    return out
+
+
+def combine_f64(y_bits, topk_idx, dst, weights=None, bias_bits=None, lib=None):
+    """binary64 weighted sums and sums of |term|, both float64 [T, H]."""
+    lib = lib or load()
+    y = _c(y_bits, np.uint16)
+    idx = _c(topk_idx, np.int64)
+    d = _c(dst, np.int32)
+    T, K = idx.shape
+    H = y.shape[1]
+    out = np.zeros((T, H), np.float64)
+    mag = np.zeros((T, H), np.float64)
+    w = None if weights is None else _c(weights, np.float32)
+    b = None if bias_bits is None else _c(bias_bits, np.uint16)
+    lib.oracle_combine_f64(T, K, H, _ptr(y), _ptr(w), _ptr(b), _ptr(idx),
+                           _ptr(d), _ptr(out), _ptr(mag))
+    return out, mag

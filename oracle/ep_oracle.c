@@ -1,0 +1,287 @@
+/*
+ * ep_oracle.c - CPU oracle for MoE routing layout, dispatch copy and combine.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the plain, slow, obviously correct
+ * statement of what the GPU path computes.  Only the test suite, the smoke
+ * check and the benchmark's CPU-baseline leg load it; the product path never
+ * does.  It shares no code, header, table or helper with the HIP library.
+ *
+ * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -shared -fPIC
+ * (x86-64 SSE arithmetic: every float operation below is one IEEE-754
+ * binary32 operation rounded to nearest even; nothing is fused or reassociated).
+ *
+ * Sources (web pages; each function cites the section it follows):
+ *   [Ch7]    DeepEP source notes, chapter 7 "V2: how dispatch builds expert
+ *            inputs" (bowenzhou.top/repos/deepep/07-v2-dispatch)
+ *   [Ch8]    DeepEP source notes, chapter 8 "V2: combine, handle and async
+ *            overlap" (bowenzhou.top/repos/deepep/08-v2-combine-events)
+ *   [vLLM]   digest of vLLM pull request 52781, "DeepEP v2 combine made
+ *            asynchronous" (prhub.com.cn/vllm-project/vllm/pull/52781)
+ *   [README] DeepEP README, Chinese rendering (gittoolsai.com)
+ *
+ * Readings where the pages leave a step open (plainest reading consistent
+ * with the rest; the same list is kept with the design notes):
+ *   R1  rows inside an expert segment are ordered by ascending flattened slot
+ *       index i = t*K + k (a stable counting sort); one rank means one source.
+ *   R2  an expert with no routed slot gets an empty segment.
+ *   R3  psum is exclusive with E+1 entries over aligned counts; counts are the
+ *       unaligned per-expert counts.
+ *   R4  source metadata is one int32 per expanded row holding t*K + k, and -1
+ *       on alignment-gap rows; rows at or past psum[E] are not written.
+ *   R5  ids outside [-1, E) are treated as empty slots and counted as invalid.
+ *   R6  duplicate experts inside one token are not merged; each slot gets its
+ *       own row, ordered by k.
+ *   R7  a token whose slots are all empty combines to +0.0 and does not count
+ *       towards num_recv_tokens.
+ *   R8  zero padding clears gap rows only (x bytes, scale entries, weight).
+ *   R9  bias is the expert's output bias [E, H], added to the expert row
+ *       before the weight is applied: out = sum_k w_k * (y_k + b[e_k]).
+ *   R10 missing top-k weights mean weight 1 (the product is skipped).
+ *   R11 combine accumulates in binary32, in slot order k = 0..K-1, starting at
+ *       +0.0, with separately rounded multiply and add; the result is rounded
+ *       to bf16 to nearest even (NaN becomes the quiet NaN 0x7FC0).
+ *   R12 num_recv_tokens is the number of tokens with at least one valid slot.
+ *
+ * Where no reading is needed the definition is the pages' own.
+ */
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* Error codes returned by oracle_layout. */
+#define ORACLE_OK 0
+#define ORACLE_ERR_CAPACITY 1
+#define ORACLE_ERR_ARGS 2
+
+/*
+ * Worst-case number of expanded rows at one rank when the receive counts are
+ * not read back by the CPU [Ch7 §7.2, the no-CPU-sync sizing]: each token can
+ * land on at most min(K, E) local experts, each expert segment can waste up to
+ * A-1 rows of alignment, and the total is rounded up to a multiple of A.
+ */
+int64_t oracle_capacity_bound(int64_t T, int64_t K, int64_t E, int64_t A)
+{
+    int64_t per_token = K < E ? K : E;
+    int64_t n = T * per_token + (A - 1) * E;
+    return (n + A - 1) / A * A;
+}
+
+/*
+ * Routing layout [Ch7 §7.1 (input contract, -1 means no selection),
+ * §7.2 (counts, source metadata and slot index built with the dispatch),
+ * §7.3 (expert-expanded layout, expert_alignment), §7.5 (handle fields:
+ * unaligned counts, per-expert prefix sums, destination slots, source
+ * metadata)].
+ *
+ * topk_idx [T*K] row-major int64.  Outputs:
+ *   counts[E]          unaligned per-expert counts
+ *   psum[E+1]          exclusive scan of counts aligned up to A (R3)
+ *   dst[T*K]           expanded row of slot i, -1 for empty slots
+ *   src_meta[capacity] slot index of each filled row, -1 on gap rows (R4)
+ *   scalars[3]         {num_recv_tokens, invalid_count, num_expanded}
+ * On capacity overflow only counts, psum and scalars are written.
+ */
+int oracle_layout(int64_t T, int64_t K, int64_t E, int64_t A, int64_t capacity,
+                  const int64_t *topk_idx, int32_t *counts, int32_t *psum,
+                  int32_t *dst, int32_t *src_meta, int64_t *scalars)
+{
+    if (T < 0 || K <= 0 || E <= 0 || A <= 0 || capacity < 0)
+        return ORACLE_ERR_ARGS;
+
+    int64_t invalid = 0, num_recv = 0;
+    for (int64_t e = 0; e < E; ++e)
+        counts[e] = 0;
+
+    /* Count valid slots per expert and tokens with any valid slot. */
+    for (int64_t t = 0; t < T; ++t) {
+        int any = 0;
+        for (int64_t k = 0; k < K; ++k) {
+            int64_t e = topk_idx[t * K + k];
+            if (e == -1)
+                continue;
+            if (e < 0 || e >= E) {          /* R5 */
+                ++invalid;
+                continue;
+            }
+            counts[e] += 1;
+            any = 1;
+        }
+        num_recv += any;                    /* R12 */
+    }
+
+    /* Aligned exclusive prefix sum over experts (R2, R3). */
+    int64_t run = 0;
+    psum[0] = 0;
+    for (int64_t e = 0; e < E; ++e) {
+        int64_t aligned = (counts[e] + A - 1) / A * A;
+        run += aligned;
+        if (run > INT32_MAX)
+            return ORACLE_ERR_ARGS;
+        psum[e + 1] = (int32_t)run;
+    }
+    scalars[0] = num_recv;
+    scalars[1] = invalid;
+    scalars[2] = run;
+    if (run > capacity)
+        return ORACLE_ERR_CAPACITY;
+
+    /* Place slots in ascending slot order (R1): the next free row of the
+     * expert's segment. */
+    int32_t *fill = (int32_t *)calloc((size_t)E, sizeof(int32_t));
+    if (!fill)
+        return ORACLE_ERR_ARGS;
+    for (int64_t i = 0; i < T * K; ++i) {
+        int64_t e = topk_idx[i];
+        if (e < 0 || e >= E) {
+            dst[i] = -1;
+            continue;
+        }
+        int32_t row = psum[e] + fill[e];
+        fill[e] += 1;
+        dst[i] = row;
+        src_meta[row] = (int32_t)i;
+    }
+    free(fill);
+
+    /* Alignment gaps: rows [psum[e] + counts[e], psum[e+1]) hold no token. */
+    for (int64_t e = 0; e < E; ++e)
+        for (int64_t r = (int64_t)psum[e] + counts[e]; r < psum[e + 1]; ++r)
+            src_meta[r] = -1;
+    return ORACLE_OK;
+}
+
+/*
+ * Dispatch copy epilogue into the expert-expanded layout [Ch7 §7.1 (x is a
+ * bf16 matrix or FP8 data plus scale factors; weights optional), §7.3 (copy
+ * epilogue writes received rows, scale factors with their own token/hidden
+ * strides and per-row top-k weights; zero padding clears alignment gaps),
+ * §7.4 (each expert owns one contiguous, aligned range)].
+ *
+ * x          [T, row_bytes] raw bytes (bf16: 2H bytes, FP8: H bytes)
+ * sf         FP8 scale factors, element (t, j) at sf[t*sf_ts + j*sf_hs],
+ *            j < num_sf; NULL when num_sf == 0
+ * w          [T*K] top-k weights or NULL (R10: weight 1)
+ * out_x      [capacity, row_bytes]
+ * out_sf     element (r, j) at out_sf[r*o_ts + j*o_hs]; NULL if num_sf == 0
+ * out_w      [capacity] per-row weight or NULL
+ * Rows that are neither routed nor (with zero padding) gap rows are left as
+ * they were.
+ */
+void oracle_dispatch(int64_t T, int64_t K, int64_t E, int64_t row_bytes,
+                     const uint8_t *x, int64_t num_sf, const float *sf,
+                     int64_t sf_ts, int64_t sf_hs, const float *w,
+                     const int32_t *counts, const int32_t *psum,
+                     const int32_t *dst, uint8_t *out_x, float *out_sf,
+                     int64_t o_ts, int64_t o_hs, float *out_w, int zero_padding)
+{
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t k = 0; k < K; ++k) {
+            int64_t r = dst[t * K + k];
+            if (r < 0)
+                continue;
+            memcpy(out_x + r * row_bytes, x + t * row_bytes, (size_t)row_bytes);
+            for (int64_t j = 0; j < num_sf; ++j)
+                out_sf[r * o_ts + j * o_hs] = sf[t * sf_ts + j * sf_hs];
+            if (out_w)
+                out_w[r] = w ? w[t * K + k] : 1.0f;
+        }
+    }
+    if (!zero_padding)
+        return;
+    for (int64_t e = 0; e < E; ++e) {
+        for (int64_t r = (int64_t)psum[e] + counts[e]; r < psum[e + 1]; ++r) {
+            memset(out_x + r * row_bytes, 0, (size_t)row_bytes);
+            for (int64_t j = 0; j < num_sf; ++j)
+                out_sf[r * o_ts + j * o_hs] = 0.0f;
+            if (out_w)
+                out_w[r] = 0.0f;
+        }
+    }
+}
+
+/* bf16 bit pattern -> binary32: the bf16 bits are the high half (exact). */
+static float bf16_to_f32(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* binary32 -> bf16 by round to nearest, ties to even (R11). */
+static uint16_t f32_to_bf16(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu))
+        return 0x7FC0;
+    uint32_t lsb = (u >> 16) & 1u;
+    u += 0x7FFFu + lsb;
+    return (uint16_t)(u >> 16);
+}
+
+/*
+ * Combine: follow the handle back to token order and reduce the expert
+ * outputs [Ch8 §8.1 (combine reads the handle's source metadata and
+ * reduces back to the source; bias and gate-weight reduction can be fused;
+ * the kernel takes bf16 x and fp32 top-k weights), vLLM digest "Implementation
+ * breakdown" (combine input must be bf16; top-k weights may be passed as
+ * None)].  Readings R7, R9, R10, R11.
+ *
+ * y    [rows, H] bf16 bits, row r at y + r*H
+ * w    [T*K] fp32 or NULL; bias [E, H] bf16 bits or NULL
+ * out  [T, H] bf16 bits
+ */
+void oracle_combine(int64_t T, int64_t K, int64_t H, const uint16_t *y,
+                    const float *w, const uint16_t *bias,
+                    const int64_t *topk_idx, const int32_t *dst, uint16_t *out)
+{
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t h = 0; h < H; ++h) {
+            float acc = 0.0f;
+            for (int64_t k = 0; k < K; ++k) {
+                int64_t r = dst[t * K + k];
+                if (r < 0)
+                    continue;
+                float v = bf16_to_f32(y[r * H + h]);
+                if (bias) {
+                    int64_t e = topk_idx[t * K + k];
+                    v = v + bf16_to_f32(bias[e * H + h]);
+                }
+                float p = w ? w[t * K + k] * v : v;
+                acc = acc + p;
+            }
+            out[t * H + h] = f32_to_bf16(acc);
+        }
+    }
+}
+
+/*
+ * The same weighted sum in binary64, without the final rounding to bf16.
+ * Used only to bound the binary32 result of oracle_combine in the tests; it
+ * is not a parity target.  Terms are the binary64 values of the same inputs.
+ */
+void oracle_combine_f64(int64_t T, int64_t K, int64_t H, const uint16_t *y,
+                        const float *w, const uint16_t *bias,
+                        const int64_t *topk_idx, const int32_t *dst,
+                        double *out, double *abs_terms)
+{
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t h = 0; h < H; ++h) {
+            double acc = 0.0, mag = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                int64_t r = dst[t * K + k];
+                if (r < 0)
+                    continue;
+                double v = (double)bf16_to_f32(y[r * H + h]);
+                if (bias)
+                    v += (double)bf16_to_f32(bias[topk_idx[t * K + k] * H + h]);
+                double p = w ? (double)w[t * K + k] * v : v;
+                acc += p;
+                mag += p < 0 ? -p : p;
+            }
+            out[t * H + h] = acc;
+            abs_terms[t * H + h] = mag;
+        }
+    }
+}

@@ -1,0 +1,382 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each ``pin_*`` function takes a loaded oracle library (``oracle.load()`` or a
+deliberately broken build of it) and raises AssertionError on disagreement.
+The pins are: hand-worked golden fixtures (``tests/golden``), brute force on
+tiny inputs (``bruteforce.py``), a special case that reduces to numpy's stable
+argsort, closed forms (identity expert, exact gather) and invariants.
+
+Run as ``python -m tests.pins <oracle.so>`` to get a one-line verdict per pin;
+the mutation test uses that to show every planted mistake is caught.
+"""
+from __future__ import annotations
+
+import json
+import os
+import sys
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, os.path.dirname(_HERE))
+
+import oracle  # noqa: E402
+import ep_workloads as W  # noqa: E402
+
+try:
+    from . import bruteforce as BF  # noqa: E402
+except ImportError:  # run as a script
+    import bruteforce as BF  # type: ignore  # noqa: E402
+
+GOLDEN = os.path.join(_HERE, "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _bf16_bits(vals) -> np.ndarray:
+    a = np.asarray(vals, np.float32)
+    return (a.view(np.uint32) >> 16).astype(np.uint16)   # exact for these values
+
+
+def _bits_to_float(bits) -> np.ndarray:
+    return BF.bf16_bits_to_f32(bits)
+
+
+# ----------------------------------------------------------------------------
+# layout
+
+
+def pin_capacity_golden(lib):
+    g = _golden("capacity_bound.json")
+    for c in g["cases"]:
+        got = oracle.capacity_bound(c["T"], c["K"], c["E"], c["A"], lib=lib)
+        assert got == c["bound"], (c, got)
+
+
+def pin_layout_golden(lib):
+    g = _golden("layout_hand.json")
+    cap = g["capacity_bound"]
+    assert oracle.capacity_bound(3, 2, 3, 2, lib=lib) == cap
+    lay = oracle.layout(np.array(g["topk_idx"]), g["num_experts"], g["alignment"],
+                        cap, lib=lib)
+    assert lay.status == 0
+    assert lay.counts.tolist() == g["counts"]
+    assert lay.psum.tolist() == g["psum"]
+    assert lay.dst.tolist() == g["dst"]
+    assert lay.src_meta[:g["num_expanded"]].tolist() == g["src_meta"]
+    assert lay.num_recv_tokens == g["num_recv_tokens"]
+    assert lay.invalid_count == g["invalid_count"]
+    assert lay.num_expanded == g["num_expanded"]
+
+
+def _random_cases(n=300, seed=7):
+    rng = np.random.default_rng(seed)
+    for c in range(n):
+        T = int(rng.integers(0, 40))
+        K = int(rng.integers(1, 9))
+        E = int(rng.integers(1, 33))
+        A = int(rng.choice([1, 2, 3, 4, 8, 64, 128]))
+        mode = c % 5
+        if mode == 0:      # distinct experts when possible
+            idx = np.stack([rng.permutation(max(E, K))[:K] for _ in range(T)]) \
+                if T else np.zeros((0, K), np.int64)
+            idx = np.where(idx < E, idx, -1)
+        elif mode == 1:    # duplicates allowed
+            idx = rng.integers(0, E, size=(T, K))
+        elif mode == 2:    # invalid ids mixed in
+            idx = rng.integers(-3, E + 3, size=(T, K))
+        elif mode == 3:    # mostly empty
+            idx = np.where(rng.random((T, K)) < 0.8, -1, rng.integers(0, E, size=(T, K)))
+        else:              # all empty
+            idx = np.full((T, K), -1)
+        empty = rng.random((T, K)) < rng.choice([0.0, 0.1, 0.5])
+        idx = np.where(empty, -1, idx).astype(np.int64).reshape(T, K)
+        yield T, K, E, A, idx
+
+
+def _check_layout_vs_sorted(lay, idx, E, A):
+    counts, psum, dst, src, num_recv, invalid = BF.layout_sorted(idx, E, A)
+    assert lay.status == 0
+    np.testing.assert_array_equal(lay.counts, counts)
+    np.testing.assert_array_equal(lay.psum, psum)
+    np.testing.assert_array_equal(lay.dst, dst)
+    np.testing.assert_array_equal(lay.src_meta[:psum[-1]], src)
+    assert lay.num_recv_tokens == num_recv
+    assert lay.invalid_count == invalid
+    assert lay.num_expanded == psum[-1]
+
+
+def pin_layout_bruteforce(lib):
+    for T, K, E, A, idx in _random_cases():
+        cap = T * K + (A - 1) * E + A          # room even with duplicates
+        lay = oracle.layout(idx, E, A, cap, lib=lib)
+        _check_layout_vs_sorted(lay, idx, E, A)
+
+
+def pin_layout_argsort_alignment1(lib):
+    rng = np.random.default_rng(11)
+    for _ in range(40):
+        T, K, E = int(rng.integers(1, 200)), int(rng.integers(1, 9)), int(rng.integers(1, 64))
+        idx = rng.integers(-1, E, size=(T, K))
+        lay = oracle.layout(idx, E, 1, T * K, lib=lib)
+        counts, psum, dst, order = BF.layout_argsort_a1(idx, E)
+        np.testing.assert_array_equal(lay.counts, counts)
+        np.testing.assert_array_equal(lay.psum, psum)
+        np.testing.assert_array_equal(lay.dst, dst)
+        np.testing.assert_array_equal(lay.src_meta[:order.size], order)
+
+
+def check_layout_invariants(lay, idx, E, A, capacity):
+    """Invariants any correct layout satisfies (also used on GPU results)."""
+    idx = np.asarray(idx, np.int64)
+    T, K = idx.shape
+    flat = idx.reshape(-1)
+    ok = (flat >= 0) & (flat < E)
+    counts = lay.counts.astype(np.int64)
+    psum = lay.psum.astype(np.int64)
+    assert counts.sum() == ok.sum()
+    np.testing.assert_array_equal(counts, np.bincount(flat[ok], minlength=E))
+    assert psum[0] == 0 and np.all(psum % A == 0)
+    np.testing.assert_array_equal(np.diff(psum), -(-counts // A) * A)
+    assert psum[-1] <= capacity
+    dst = lay.dst.reshape(-1).astype(np.int64)
+    assert np.all(dst[~ok] == -1)
+    d = dst[ok]
+    assert np.unique(d).size == d.size                       # injective
+    e = flat[ok]
+    assert np.all(d >= psum[e]) and np.all(d < psum[e] + counts[e])
+    src = lay.src_meta.astype(np.int64)
+    np.testing.assert_array_equal(src[d], np.nonzero(ok)[0])
+    gap = np.ones(psum[-1], bool)
+    gap[d] = False
+    assert np.all(src[:psum[-1]][gap] == -1)
+    for ee in range(E):                                       # stability
+        seg = src[psum[ee]:psum[ee] + counts[ee]]
+        assert np.all(np.diff(seg) > 0)
+    assert lay.num_recv_tokens == int(ok.reshape(T, K).any(axis=1).sum())
+
+
+def pin_layout_invariants_configs(lib):
+    for name, cfg in W.CONFIGS.items():
+        idx, _ = W.routing(cfg)
+        cap = oracle.capacity_bound(cfg.tokens, cfg.topk, cfg.experts, cfg.alignment, lib=lib)
+        lay = oracle.layout(idx, cfg.experts, cfg.alignment, cap, lib=lib)
+        assert lay.status == 0, name
+        check_layout_invariants(lay, idx, cfg.experts, cfg.alignment, cap)
+
+
+def pin_layout_capacity_error(lib):
+    idx = np.array([[0, 1], [1, 2], [2, 0]])
+    lay = oracle.layout(idx, 3, 4, 11, lib=lib)      # needs 12 rows
+    assert lay.status == oracle.ERR_CAPACITY
+    assert lay.num_expanded == 12
+    lay = oracle.layout(idx, 3, 4, 12, lib=lib)
+    assert lay.status == 0
+
+
+# ----------------------------------------------------------------------------
+# dispatch
+
+
+def pin_dispatch_golden(lib):
+    g = _golden("layout_hand.json")
+    d = g["dispatch"]
+    cap = g["capacity_bound"]
+    lay = oracle.layout(np.array(g["topk_idx"]), g["num_experts"], g["alignment"], cap, lib=lib)
+    out_x = np.full((cap, 4), 0xA5, np.uint8)
+    out_w = np.full(cap, -9.0, np.float32)
+    ox, _, ow = oracle.dispatch(np.array(d["x"], np.uint8), lay, cap,
+                                weights=np.array(d["weights"], np.float32),
+                                want_w=True, zero_padding=True, out_x=out_x,
+                                out_w=out_w, lib=lib)
+    assert ox[:8].tolist() == d["out_x"]
+    assert np.all(ox[8:] == 0xA5)
+    assert ow[:8].tolist() == d["out_w"]
+    assert np.all(ow[8:] == -9.0)
+
+
+def _dispatch_case(lib, T, K, E, A, row_bytes, fp8, zero_padding, with_w,
+                   rng, sf_layout="row"):
+    idx = rng.integers(-1, E, size=(T, K))
+    cap = T * K + (A - 1) * E + 2 * A
+    lay = oracle.layout(idx, E, A, cap, lib=lib)
+    x = rng.integers(0, 256, size=(T, row_bytes), dtype=np.uint8)
+    w = rng.random((T, K), dtype=np.float32) if with_w else None
+    sf = sf_strides = out_sf = out_sf_strides = None
+    nsf = row_bytes // 128 if fp8 else 0
+    if fp8:
+        sf = rng.random((T, nsf), dtype=np.float32) + 0.5
+        sf_strides = (nsf, 1)
+        if sf_layout == "col":        # source scales stored [nsf, T]
+            sf = np.ascontiguousarray(sf.T)
+            sf_strides = (1, T)
+        out_sf = np.full((cap, nsf), np.frombuffer(b"\xa5" * 4, np.float32)[0], np.float32)
+        out_sf_strides = (nsf, 1)
+    out_x = np.full((cap, row_bytes), 0xA5, np.uint8)
+    out_w = np.full(cap, np.frombuffer(b"\xa5" * 4, np.float32)[0], np.float32)
+    ox, osf, ow = oracle.dispatch(x, lay, cap, sf=sf, sf_strides=sf_strides,
+                                  weights=w, want_w=True,
+                                  zero_padding=zero_padding, out_x=out_x,
+                                  out_sf=out_sf, out_sf_strides=out_sf_strides,
+                                  out_w=out_w, lib=lib)
+    sf_rows = None
+    if fp8:
+        sf_rows = sf if sf_layout == "row" else np.ascontiguousarray(sf.T)
+    ex, esf, ew = BF.dispatch_expected(x, lay.dst, lay.counts, lay.psum, cap,
+                                       sf=sf_rows, weights=w,
+                                       zero_padding=zero_padding)
+    np.testing.assert_array_equal(ox, ex)
+    np.testing.assert_array_equal(ow.view(np.uint32), ew.view(np.uint32))
+    if fp8:
+        np.testing.assert_array_equal(osf.view(np.uint32), esf.view(np.uint32))
+
+
+def pin_dispatch_closed_form(lib):
+    rng = np.random.default_rng(3)
+    for fp8 in (False, True):
+        for zp in (False, True):
+            for with_w in (False, True):
+                for sf_layout in (("row", "col") if fp8 else ("row",)):
+                    _dispatch_case(lib, int(rng.integers(1, 50)), int(rng.integers(1, 9)),
+                                   int(rng.integers(1, 20)), int(rng.choice([1, 4, 16])),
+                                   256 if fp8 else 2 * 24, fp8, zp, with_w, rng,
+                                   sf_layout)
+
+
+# ----------------------------------------------------------------------------
+# combine
+
+
+def pin_combine_golden(lib):
+    g = _golden("combine_hand.json")
+    idx = np.array(g["topk_idx"])
+    lay = oracle.layout(idx, g["num_experts"], g["alignment"], 8, lib=lib)
+    assert lay.dst.tolist() == g["dst"]
+    y = _bf16_bits(g["y"])
+    out = oracle.combine(y, idx, lay.dst, np.array(g["weights"], np.float32),
+                         _bf16_bits(g["bias"]), lib=lib)
+    assert _bits_to_float(out).tolist() == g["expected_with_bias"]
+    out = oracle.combine(y, idx, lay.dst, lib=lib)
+    assert _bits_to_float(out).tolist() == g["no_bias_no_weights"]["expected"]
+    t = g["ties"]
+    out = oracle.combine(_bf16_bits(t["y"]), np.array(t["topk_idx"]),
+                         np.array(t["dst"]), lib=lib)
+    assert out.tolist() == t["expected_bits"]
+    o = g["order"]
+    out = oracle.combine(_bf16_bits(o["y"]), np.array(o["topk_idx"]),
+                         np.array(o["dst"]), np.array(o["weights"], np.float32),
+                         lib=lib)
+    assert out.tolist() == o["expected_bits"]
+
+
+def _bf16_from_normal(rng, shape, scale=1.0):
+    return BF.f32_to_bf16_bits_torch(rng.standard_normal(shape, dtype=np.float32) * scale)
+
+
+def _combine_inputs(rng, T, K, E, H, empty=0.2, bias=True, weights=True):
+    """Random routing (layout by brute force, not by the oracle), bf16 expert
+    rows, signed weights and an optional [E, H] bias.  Token 0 has no slot."""
+    idx = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int64)
+    idx = np.where(rng.random((T, K)) < empty, -1, idx)
+    idx[0] = -1
+    dst = BF.layout_sorted(idx, E, 4)[2]
+    rows = T * K + 4 * E
+    y = _bf16_from_normal(rng, (rows, H), 3.0)
+    w = (rng.random((T, K), dtype=np.float32) * 2 - 0.5) if weights else None
+    b = _bf16_from_normal(rng, (E, H), 0.5) if bias else None
+    return idx, dst, y, w, b
+
+
+def pin_combine_numpy_f32(lib):
+    rng = np.random.default_rng(5)
+    for bias in (False, True):
+        for weights in (False, True):
+            for (T, K, E, H) in ((37, 8, 16, 64), (20, 3, 5, 40), (9, 1, 2, 8)):
+                idx, dst, y, w, b = _combine_inputs(rng, T, K, E, H, bias=bias,
+                                                    weights=weights)
+                got = oracle.combine(y, idx, dst, w, b, lib=lib)
+                exp = BF.combine_f32(y, idx, dst, w, b)
+                np.testing.assert_array_equal(got, exp)
+                assert np.all(got[0] == 0)             # empty token -> +0.0
+
+
+def pin_combine_f64_bound(lib):
+    """The bf16 result is within the binary32 error bound of the binary64 sum:
+    |got - exact| <= 2^-8 |result| (final bf16 rounding, unit roundoff 2^-8)
+    + (K + 2) 2^-24 sum_k |term_k| (bias add, multiply and K - 1 adds in
+    binary32, first order).  The oracle's own binary64 path must agree with
+    the independent binary64 sum."""
+    rng = np.random.default_rng(9)
+    for bias in (False, True):
+        idx, dst, y, w, b = _combine_inputs(rng, 50, 8, 16, 96, bias=bias)
+        got = _bits_to_float(oracle.combine(y, idx, dst, w, b, lib=lib)).astype(np.float64)
+        exact, mag = BF.combine_exact_sum(y, idx, dst, w, b)
+        K = idx.shape[1]
+        bound = 2.0 ** -8 * np.maximum(np.abs(got), np.abs(exact)) \
+            + (K + 2) * 2.0 ** -24 * mag * 1.01
+        assert np.all(np.abs(got - exact) <= bound)
+        o64, omag = oracle.combine_f64(y, idx, dst, w, b, lib=lib)
+        np.testing.assert_allclose(o64, exact, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(omag, mag, rtol=1e-12, atol=1e-12)
+
+
+def pin_combine_identity_expert(lib):
+    """y = dispatch(x) (identity expert), weights None: out[t] = bf16(c_t*x[t])
+    exactly, where c_t is the number of valid slots of token t (the sum of c_t
+    copies of one bf16 value needs at most 8 + log2(K) significant bits)."""
+    import torch
+    cfg = W.CONFIGS["tiny"]
+    wl = W.make(cfg)
+    idx = wl.topk_idx.copy()
+    idx[-1] = -1
+    cap = oracle.capacity_bound(cfg.tokens, cfg.topk, cfg.experts, cfg.alignment, lib=lib)
+    lay = oracle.layout(idx, cfg.experts, cfg.alignment, cap, lib=lib)
+    x_bits = wl.x.contiguous().view(torch.int16).numpy().view(np.uint16)
+    y_bytes, _, _ = oracle.dispatch(x_bits.view(np.uint8), lay, cap, lib=lib)
+    out = oracle.combine(y_bytes.view(np.uint16), idx, lay.dst, lib=lib)
+    c = (idx >= 0).sum(axis=1).astype(np.float32)
+    prod = c[:, None] * _bits_to_float(x_bits)
+    prod = np.where(prod == 0, np.float32(0), prod)     # the sum starts at +0.0
+    exp = BF.f32_to_bf16_bits_torch(prod)
+    np.testing.assert_array_equal(out, exp)
+    assert np.all(out[-1] == 0)
+
+
+def pin_combine_single_slot_gather(lib):
+    """One valid slot per token and no weights: the output row is the expert
+    row itself, except that -0.0 becomes +0.0 (the sum starts at +0.0)."""
+    rng = np.random.default_rng(21)
+    T, K, E, H = 30, 6, 12, 16
+    idx = np.full((T, K), -1, np.int64)
+    idx[np.arange(T), rng.integers(0, K, T)] = rng.integers(0, E, T)
+    dst = BF.layout_sorted(idx, E, 2)[2]
+    y = _bf16_from_normal(rng, (T * K + 2 * E, H))
+    y[:, 3] = 0x8000                                   # -0.0 entries
+    out = oracle.combine(y, idx, dst, lib=lib)
+    exp = y[dst.max(axis=1)]
+    exp = np.where(exp == 0x8000, 0, exp)
+    np.testing.assert_array_equal(out, exp)
+
+
+PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
+
+
+def run_all(lib):
+    """Return {pin name: None or failure text}."""
+    res = {}
+    for p in PINS:
+        try:
+            p(lib)
+            res[p.__name__] = None
+        except Exception as e:  # noqa: BLE001 - report every failing pin
+            res[p.__name__] = f"{type(e).__name__}: {str(e)[:200]}"
+    return res
+
+
+if __name__ == "__main__":
+    lib = oracle.load(sys.argv[1]) if len(sys.argv) > 1 else oracle.load()
+    out = run_all(lib)
+    print(json.dumps(out))
