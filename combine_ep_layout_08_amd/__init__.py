@@ -1,0 +1,367 @@
+"""MI355X (gfx950) MoE routing layout, dispatch copy and combine.
+
+A thin ctypes binding of the C ABI declared in ``include/ep.h`` and built into
+``libep.so`` next to this file (``python -m combine_ep_layout_08_amd.build``).
+Every step of the computation runs in the library's HIP kernels; this module
+only marshals arguments.  PyTorch supplies device memory and the current
+stream.  There is no fallback: without the built library, every entry point
+raises.
+
+Low-level functions carry the C names (``ep_layout``, ``ep_dispatch``, ...)
+and take raw pointers.  :class:`Handle` wraps them for torch tensors.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch  # noqa: F401  (loaded first so libep.so binds torch's HIP runtime)
+
+__all__ = [
+    "EP_OK", "EP_ERR_NULL", "EP_ERR_SHAPE", "EP_ERR_DTYPE", "EP_ERR_UNSUPPORTED",
+    "EP_ERR_MISALIGNED", "EP_ERR_WORKSPACE", "EP_ERR_NOT_LAID_OUT", "EP_ERR_CAPACITY",
+    "EP_ERR_INVALID_ID", "EP_ERR_HIP", "EP_ERR_TIMEOUT", "EP_BF16", "EP_FP8_E4M3", "EP_F32", "EP_I32",
+    "EP_I64", "EpError", "ep_handle", "lib", "Handle", "ep_capacity_bound",
+    "ep_workspace_bytes", "ep_handle_init", "ep_layout", "ep_handle_read_counts",
+    "ep_handle_import", "ep_dispatch", "ep_combine", "ep_status_str", "ep_handle_sizeof",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libep.so")
+
+(EP_OK, EP_ERR_NULL, EP_ERR_SHAPE, EP_ERR_DTYPE, EP_ERR_UNSUPPORTED, EP_ERR_MISALIGNED,
+ EP_ERR_WORKSPACE, EP_ERR_NOT_LAID_OUT, EP_ERR_CAPACITY, EP_ERR_INVALID_ID,
+ EP_ERR_HIP, EP_ERR_TIMEOUT) = range(12)
+EP_BF16, EP_FP8_E4M3, EP_F32, EP_I32, EP_I64 = range(5)
+EP_ERRBIT_CAPACITY = 1
+EP_ERRBIT_INVALID_ID = 2
+EP_ERRBIT_SCAN_TIMEOUT = 4
+
+
+class ep_handle(ctypes.Structure):
+    """Mirror of ``struct ep_handle`` (checked against ep_handle_sizeof)."""
+    _fields_ = [
+        ("max_tokens", ctypes.c_int32),
+        ("num_tokens", ctypes.c_int32),
+        ("num_topk", ctypes.c_int32),
+        ("num_experts", ctypes.c_int32),
+        ("expert_alignment", ctypes.c_int32),
+        ("laid_out", ctypes.c_int32),
+        ("capacity", ctypes.c_int64),
+        ("counts", ctypes.c_void_p),
+        ("psum", ctypes.c_void_p),
+        ("dst_slot", ctypes.c_void_p),
+        ("src_meta", ctypes.c_void_p),
+        ("scalars", ctypes.c_void_p),
+        ("tile_status", ctypes.c_void_p),
+        ("topk_idx", ctypes.c_void_p),
+        ("topk_idx_dtype", ctypes.c_int32),
+        ("status_tiles", ctypes.c_int32),
+    ]
+
+
+class EpError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        super().__init__(f"{what}: {ep_status_str(status)}" if what else ep_status_str(status))
+
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_HP = ctypes.POINTER(ep_handle)
+
+_SIGNATURES = {
+    "ep_handle_sizeof": (ctypes.c_size_t, []),
+    "ep_capacity_bound": (_I64, [_I32, _I32, _I32, _I32]),
+    "ep_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32, _I32, _I64]),
+    "ep_handle_init": (ctypes.c_int, [_HP, _I32, _I32, _I32, _I32, _I64, _P, ctypes.c_size_t, _P]),
+    "ep_layout": (ctypes.c_int, [_HP, _P, ctypes.c_int, _I32, _P, _P]),
+    "ep_handle_read_counts": (ctypes.c_int, [_HP, _P, _P, _P, _P, _P, _P, _P]),
+    "ep_handle_import": (ctypes.c_int, [_HP, _P, ctypes.c_int, _I32, _P, _P, _P, _P, _I32, _P]),
+    "ep_dispatch": (ctypes.c_int, [_HP, _P, ctypes.c_int, _I32, _P, _I64, _I64, _P, _P, _P,
+                                   _I64, _I64, _P, _I32, _P]),
+    "ep_combine": (ctypes.c_int, [_HP, _P, ctypes.c_int, _I32, _P, _P, _P, _P]),
+    "ep_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+}
+
+_lib = None
+
+
+def lib():
+    """The loaded ``libep.so`` (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m combine_ep_layout_08_amd.build` (there is no fallback path)")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        if handle.ep_handle_sizeof() != ctypes.sizeof(ep_handle):
+            raise RuntimeError("ep_handle layout mismatch between libep.so and the binding")
+        _lib = handle
+    return _lib
+
+
+# ---------------------------------------------------------------- C-named calls
+
+def ep_handle_sizeof() -> int:
+    return int(lib().ep_handle_sizeof())
+
+
+def ep_capacity_bound(num_tokens: int, num_topk: int, num_experts: int,
+                      expert_alignment: int) -> int:
+    return int(lib().ep_capacity_bound(num_tokens, num_topk, num_experts, expert_alignment))
+
+
+def ep_workspace_bytes(max_tokens: int, num_topk: int, num_experts: int,
+                       expert_alignment: int, capacity: int) -> int:
+    return int(lib().ep_workspace_bytes(max_tokens, num_topk, num_experts,
+                                        expert_alignment, capacity))
+
+
+def ep_handle_init(h: ep_handle, max_tokens, num_topk, num_experts, expert_alignment,
+                   capacity, workspace_ptr, ws_bytes, stream) -> int:
+    return lib().ep_handle_init(ctypes.byref(h), max_tokens, num_topk, num_experts,
+                                expert_alignment, capacity, workspace_ptr, ws_bytes, stream)
+
+
+def ep_layout(h: ep_handle, topk_idx_ptr, idx_dtype, num_tokens, stats_ptr, stream) -> int:
+    return lib().ep_layout(ctypes.byref(h), topk_idx_ptr, idx_dtype, num_tokens, stats_ptr,
+                           stream)
+
+
+def ep_handle_read_counts(h: ep_handle, counts_ptr, psum_ptr, num_expanded_ptr,
+                          num_recv_ptr, error_bits_ptr, invalid_ptr, stream) -> int:
+    return lib().ep_handle_read_counts(ctypes.byref(h), counts_ptr, psum_ptr,
+                                       num_expanded_ptr, num_recv_ptr, error_bits_ptr,
+                                       invalid_ptr, stream)
+
+
+def ep_handle_import(h: ep_handle, topk_idx_ptr, idx_dtype, num_tokens, counts_ptr, psum_ptr,
+                     dst_ptr, src_meta_ptr, num_recv_tokens, stream) -> int:
+    return lib().ep_handle_import(ctypes.byref(h), topk_idx_ptr, idx_dtype, num_tokens,
+                                  counts_ptr, psum_ptr, dst_ptr, src_meta_ptr,
+                                  num_recv_tokens, stream)
+
+
+def ep_dispatch(h: ep_handle, x_ptr, x_dtype, hidden, sf_ptr, sf_ts, sf_hs, w_ptr, out_x_ptr,
+                out_sf_ptr, out_ts, out_hs, out_w_ptr, zero_padding, stream) -> int:
+    return lib().ep_dispatch(ctypes.byref(h), x_ptr, x_dtype, hidden, sf_ptr, sf_ts, sf_hs,
+                             w_ptr, out_x_ptr, out_sf_ptr, out_ts, out_hs, out_w_ptr,
+                             zero_padding, stream)
+
+
+def ep_combine(h: ep_handle, y_ptr, y_dtype, hidden, w_ptr, bias_ptr, out_ptr, stream) -> int:
+    return lib().ep_combine(ctypes.byref(h), y_ptr, y_dtype, hidden, w_ptr, bias_ptr, out_ptr,
+                            stream)
+
+
+def ep_status_str(status: int) -> str:
+    return lib().ep_status_str(status).decode()
+
+
+# ---------------------------------------------------------------- torch wrapper
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _check(status: int, what: str):
+    if status != EP_OK:
+        raise EpError(status, what)
+
+
+def _need(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _dev(t: torch.Tensor, name: str):
+    _need(t.is_cuda, f"{name} must be a device tensor")
+    _need(t.is_contiguous(), f"{name} must be contiguous")
+
+
+class Handle:
+    """Routing state in a torch-allocated workspace, with layout, dispatch and
+    combine on torch tensors.  ``capacity`` defaults to the worst-case bound,
+    so no count needs to be read back before dispatch."""
+
+    def __init__(self, max_tokens: int, num_topk: int, num_experts: int,
+                 expert_alignment: int = 1, capacity: Optional[int] = None,
+                 device="cuda"):
+        if capacity is None:
+            capacity = ep_capacity_bound(max_tokens, num_topk, num_experts, expert_alignment)
+            _need(capacity >= 0, "invalid sizes")
+        nbytes = ep_workspace_bytes(max_tokens, num_topk, num_experts, expert_alignment,
+                                    capacity)
+        _need(nbytes > 0, "sizes outside the library's limits")
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.h = ep_handle()
+        _check(ep_handle_init(self.h, max_tokens, num_topk, num_experts, expert_alignment,
+                              capacity, self.workspace.data_ptr(), nbytes, _stream()),
+               "ep_handle_init")
+        self.capacity = capacity
+        self.topk_idx = None      # kept alive: the handle borrows it
+
+    # -- views of the handle's device arrays
+    def _view(self, ptr: int, n: int) -> torch.Tensor:
+        off = ptr - self.workspace.data_ptr()
+        return self.workspace[off:off + 4 * n].view(torch.int32)
+
+    @property
+    def num_tokens(self) -> int:
+        return self.h.num_tokens
+
+    @property
+    def counts(self) -> torch.Tensor:
+        return self._view(self.h.counts, self.h.num_experts)
+
+    @property
+    def psum(self) -> torch.Tensor:
+        return self._view(self.h.psum, self.h.num_experts + 1)
+
+    @property
+    def dst_slot(self) -> torch.Tensor:
+        return self._view(self.h.dst_slot, self.h.num_tokens * self.h.num_topk).view(
+            self.h.num_tokens, self.h.num_topk)
+
+    @property
+    def src_meta(self) -> torch.Tensor:
+        return self._view(self.h.src_meta, self.capacity)
+
+    @property
+    def scalars(self) -> torch.Tensor:
+        return self._view(self.h.scalars, 8)
+
+    def layout(self, topk_idx: torch.Tensor,
+               cumulative_stats: Optional[torch.Tensor] = None) -> "Handle":
+        _dev(topk_idx, "topk_idx")
+        _need(topk_idx.dim() == 2 and topk_idx.shape[1] == self.h.num_topk,
+              "topk_idx must be [num_tokens, num_topk]")
+        _need(topk_idx.dtype in (torch.int64, torch.int32), "topk_idx must be int64 or int32")
+        if cumulative_stats is not None:
+            _dev(cumulative_stats, "cumulative_stats")
+            _need(cumulative_stats.dtype == torch.int32 and
+                  cumulative_stats.numel() == self.h.num_experts,
+                  "cumulative_stats must be int32 [num_experts]")
+        dt = EP_I64 if topk_idx.dtype == torch.int64 else EP_I32
+        _check(ep_layout(self.h, _ptr(topk_idx), dt, topk_idx.shape[0],
+                         _ptr(cumulative_stats), _stream()), "ep_layout")
+        self.topk_idx = topk_idx
+        return self
+
+    def import_layout(self, topk_idx: torch.Tensor, counts, psum, dst_slot, src_meta,
+                      num_recv_tokens: int) -> "Handle":
+        """Install a host-computed layout (numpy int32 arrays)."""
+        import numpy as np
+        _dev(topk_idx, "topk_idx")
+        c = np.ascontiguousarray(counts, np.int32)
+        p = np.ascontiguousarray(psum, np.int32)
+        d = np.ascontiguousarray(dst_slot, np.int32)
+        s = np.ascontiguousarray(src_meta, np.int32)
+        dt = EP_I64 if topk_idx.dtype == torch.int64 else EP_I32
+        _check(ep_handle_import(self.h, _ptr(topk_idx), dt, topk_idx.shape[0], c.ctypes.data,
+                                p.ctypes.data, d.ctypes.data, s.ctypes.data if s.size else None,
+                                num_recv_tokens, _stream()), "ep_handle_import")
+        self.topk_idx = topk_idx
+        return self
+
+    def read_counts(self, check: bool = True) -> dict:
+        """Blocking: wait for the stream and read counts, psum and scalars."""
+        import numpy as np
+        E = self.h.num_experts
+        counts = np.zeros(E, np.int32)
+        psum = np.zeros(E + 1, np.int32)
+        ne = ctypes.c_int64(0)
+        nr = ctypes.c_int32(0)
+        eb = ctypes.c_uint32(0)
+        inv = ctypes.c_int32(0)
+        st = ep_handle_read_counts(self.h, counts.ctypes.data, psum.ctypes.data,
+                                   ctypes.addressof(ne), ctypes.addressof(nr),
+                                   ctypes.addressof(eb), ctypes.addressof(inv), _stream())
+        if check and st not in (EP_OK,):
+            raise EpError(st, "ep_handle_read_counts")
+        return dict(status=st, counts=counts, psum=psum, num_expanded=ne.value,
+                    num_recv_tokens=nr.value, error_bits=eb.value, invalid_count=inv.value)
+
+    def dispatch(self, x: torch.Tensor, sf: Optional[torch.Tensor] = None,
+                 topk_weights: Optional[torch.Tensor] = None, zero_padding: bool = False,
+                 out_x: Optional[torch.Tensor] = None, out_sf: Optional[torch.Tensor] = None,
+                 out_w: Optional[torch.Tensor] = None, want_weights: bool = False):
+        """x: bf16 [T, H], or FP8 (float8_e4m3fn or uint8 codes) [T, H] with fp32
+        scales ``sf`` [T, H/128] (any strides).  Returns (out_x, out_sf, out_w);
+        outputs are allocated with ``capacity`` rows unless given."""
+        T = self.h.num_tokens
+        _dev(x, "x")
+        _need(x.dim() == 2 and x.shape[0] == T, "x must be [num_tokens, hidden]")
+        H = x.shape[1]
+        fp8 = x.dtype in (torch.float8_e4m3fn, torch.uint8)
+        _need(fp8 or x.dtype == torch.bfloat16, "x must be bf16 or FP8 e4m3")
+        cap = self.capacity
+        if out_x is None:
+            out_x = torch.empty((cap, H), dtype=x.dtype, device=x.device)
+        _dev(out_x, "out_x")
+        _need(out_x.shape == (cap, H) and out_x.dtype == x.dtype, "out_x must be [capacity, H]")
+        sf_ts = sf_hs = o_ts = o_hs = 0
+        if fp8:
+            _need(sf is not None, "FP8 dispatch needs scale factors")
+            _need(sf.is_cuda and sf.dtype == torch.float32 and sf.dim() == 2 and
+                  tuple(sf.shape) == (T, H // 128), "sf must be fp32 [T, H/128]")
+            sf_ts, sf_hs = sf.stride()
+            if out_sf is None:
+                out_sf = torch.empty((cap, H // 128), dtype=torch.float32, device=x.device)
+            _need(out_sf.is_cuda and out_sf.dtype == torch.float32 and
+                  tuple(out_sf.shape) == (cap, H // 128), "out_sf must be fp32 [capacity, H/128]")
+            o_ts, o_hs = out_sf.stride()
+        else:
+            _need(sf is None, "scale factors are for FP8 only")
+        if topk_weights is not None:
+            _dev(topk_weights, "topk_weights")
+            _need(topk_weights.dtype == torch.float32 and
+                  tuple(topk_weights.shape) == (T, self.h.num_topk),
+                  "topk_weights must be fp32 [T, K]")
+        if want_weights and out_w is None:
+            out_w = torch.empty(cap, dtype=torch.float32, device=x.device)
+        if out_w is not None:
+            _dev(out_w, "out_w")
+            _need(out_w.dtype == torch.float32 and out_w.numel() == cap, "out_w: fp32 [capacity]")
+        _check(ep_dispatch(self.h, _ptr(x), EP_FP8_E4M3 if fp8 else EP_BF16, H, _ptr(sf),
+                           sf_ts, sf_hs, _ptr(topk_weights), _ptr(out_x), _ptr(out_sf),
+                           o_ts, o_hs, _ptr(out_w), 1 if zero_padding else 0, _stream()),
+               "ep_dispatch")
+        return out_x, out_sf, out_w
+
+    def combine(self, y: torch.Tensor, topk_weights: Optional[torch.Tensor] = None,
+                bias: Optional[torch.Tensor] = None,
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """y: bf16 [capacity, H] expert outputs; returns bf16 [T, H]."""
+        T = self.h.num_tokens
+        _dev(y, "y")
+        _need(y.dtype == torch.bfloat16, "combine input must be bf16")
+        _need(y.dim() == 2 and y.shape[0] == self.capacity, "y must be [capacity, H]")
+        H = y.shape[1]
+        if topk_weights is not None:
+            _dev(topk_weights, "topk_weights")
+            _need(topk_weights.dtype == torch.float32 and
+                  tuple(topk_weights.shape) == (T, self.h.num_topk),
+                  "topk_weights must be fp32 [T, K]")
+        if bias is not None:
+            _dev(bias, "bias")
+            _need(bias.dtype == torch.bfloat16 and tuple(bias.shape) == (self.h.num_experts, H),
+                  "bias must be bf16 [E, H]")
+        if out is None:
+            out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
+        _dev(out, "out")
+        _need(tuple(out.shape) == (T, H) and out.dtype == torch.bfloat16, "out must be bf16 [T, H]")
+        _check(ep_combine(self.h, _ptr(y), EP_BF16, H, _ptr(topk_weights), _ptr(bias), _ptr(out),
+                          _stream()), "ep_combine")
+        return out

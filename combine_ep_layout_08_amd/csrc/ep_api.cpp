@@ -1,0 +1,321 @@
+// C ABI of the layout / dispatch / combine library: argument validation,
+// workspace carving and kernel launches.  The semantics of each entry point
+// are documented in include/ep.h.  Nothing here allocates device memory or
+// synchronises, except ep_handle_read_counts and ep_handle_import.
+#include "../../include/ep.h"
+
+#include <cstring>
+
+#include "ep_internal.h"
+
+namespace {
+
+constexpr size_t kCarveAlign = 256;
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Carve {
+    size_t counts, psum, dst, src_meta, scalars, status, total;
+    int64_t tiles;
+};
+
+bool sizes_ok(int32_t max_tokens, int32_t K, int32_t E, int32_t A, int64_t capacity) {
+    return max_tokens >= 0 && K >= 1 && E >= 1 && A >= 1 && capacity >= 0;
+}
+
+ep_status limits(int32_t max_tokens, int32_t K, int32_t E, int64_t capacity) {
+    if (K > ep::kMaxTopk || E > ep::kMaxExperts) return EP_ERR_UNSUPPORTED;
+    if (static_cast<int64_t>(max_tokens) * K > INT32_MAX) return EP_ERR_UNSUPPORTED;
+    if (capacity > INT32_MAX) return EP_ERR_UNSUPPORTED;
+    return EP_OK;
+}
+
+Carve carve(int32_t max_tokens, int32_t K, int32_t E, int64_t capacity) {
+    Carve c{};
+    const int64_t slots = static_cast<int64_t>(max_tokens) * K;
+    c.tiles = ep::layout_tiles(slots);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off = round_up(off + (bytes ? bytes : 4), kCarveAlign);
+        return at;
+    };
+    c.counts = take(sizeof(int32_t) * static_cast<size_t>(E));
+    c.psum = take(sizeof(int32_t) * static_cast<size_t>(E + 1));
+    c.dst = take(sizeof(int32_t) * static_cast<size_t>(slots));
+    c.src_meta = take(sizeof(int32_t) * static_cast<size_t>(capacity));
+    c.scalars = take(sizeof(int32_t) * EP_NUM_SCALARS);
+    c.status = take(sizeof(uint64_t) * static_cast<size_t>(c.tiles) * static_cast<size_t>(E + 1));
+    c.total = off;
+    return c;
+}
+
+ep_status hip_status(hipError_t e) { return e == hipSuccess ? EP_OK : EP_ERR_HIP; }
+
+bool handle_ready(const ep_handle *h) {
+    return h && h->counts && h->psum && h->dst_slot && h->src_meta && h->scalars &&
+           h->tile_status;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ep_handle_sizeof(void) { return sizeof(ep_handle); }
+
+int64_t ep_capacity_bound(int32_t T, int32_t K, int32_t E, int32_t A) {
+    if (T < 0 || K <= 0 || E <= 0 || A <= 0) return -1;
+    const int64_t per_token = K < E ? K : E;
+    const int64_t n = static_cast<int64_t>(T) * per_token + static_cast<int64_t>(A - 1) * E;
+    return (n + A - 1) / A * A;
+}
+
+size_t ep_workspace_bytes(int32_t max_tokens, int32_t K, int32_t E, int32_t A, int64_t capacity) {
+    if (!sizes_ok(max_tokens, K, E, A, capacity)) return 0;
+    if (limits(max_tokens, K, E, capacity) != EP_OK) return 0;
+    return carve(max_tokens, K, E, capacity).total;
+}
+
+ep_status ep_handle_init(ep_handle *h, int32_t max_tokens, int32_t K, int32_t E, int32_t A,
+                         int64_t capacity, void *ws, size_t ws_bytes, hipStream_t stream) {
+    if (!h || !ws) return h ? EP_ERR_WORKSPACE : EP_ERR_NULL;
+    if (!sizes_ok(max_tokens, K, E, A, capacity)) return EP_ERR_SHAPE;
+    const ep_status lim = limits(max_tokens, K, E, capacity);
+    if (lim != EP_OK) return lim;
+    if (!aligned(ws, kCarveAlign)) return EP_ERR_MISALIGNED;
+    const Carve c = carve(max_tokens, K, E, capacity);
+    if (ws_bytes < c.total) return EP_ERR_WORKSPACE;
+    char *base = static_cast<char *>(ws);
+    ep_handle n{};
+    n.max_tokens = max_tokens;
+    n.num_tokens = 0;
+    n.num_topk = K;
+    n.num_experts = E;
+    n.expert_alignment = A;
+    n.laid_out = 0;
+    n.capacity = capacity;
+    n.counts = reinterpret_cast<int32_t *>(base + c.counts);
+    n.psum = reinterpret_cast<int32_t *>(base + c.psum);
+    n.dst_slot = reinterpret_cast<int32_t *>(base + c.dst);
+    n.src_meta = reinterpret_cast<int32_t *>(base + c.src_meta);
+    n.scalars = reinterpret_cast<int32_t *>(base + c.scalars);
+    n.tile_status = reinterpret_cast<uint64_t *>(base + c.status);
+    n.topk_idx = nullptr;
+    n.topk_idx_dtype = EP_I64;
+    n.status_tiles = static_cast<int32_t>(c.tiles);
+    const hipError_t e = ep::launch_handle_clear(n.scalars, n.tile_status,
+                                                 c.tiles * static_cast<int64_t>(E + 1), stream);
+    if (e != hipSuccess) return EP_ERR_HIP;
+    *h = n;
+    return EP_OK;
+}
+
+ep_status ep_layout(ep_handle *h, const void *topk_idx, ep_dtype idx_dtype, int32_t num_tokens,
+                    int32_t *cumulative_stats, hipStream_t stream) {
+    if (!h) return EP_ERR_NULL;
+    if (!handle_ready(h)) return EP_ERR_WORKSPACE;
+    if (idx_dtype != EP_I64 && idx_dtype != EP_I32) return EP_ERR_DTYPE;
+    if (num_tokens < 0 || num_tokens > h->max_tokens) return EP_ERR_SHAPE;
+    if (num_tokens > 0 && !topk_idx) return EP_ERR_NULL;
+    if (!aligned(topk_idx, idx_dtype == EP_I64 ? 8 : 4)) return EP_ERR_MISALIGNED;
+    if (!aligned(cumulative_stats, 4)) return EP_ERR_MISALIGNED;
+    ep::LayoutArgs a{};
+    a.topk_idx = topk_idx;
+    a.idx_is_i64 = idx_dtype == EP_I64;
+    a.num_tokens = num_tokens;
+    a.num_topk = h->num_topk;
+    a.num_experts = h->num_experts;
+    a.alignment = h->expert_alignment;
+    a.capacity = h->capacity;
+    a.counts = h->counts;
+    a.psum = h->psum;
+    a.dst = h->dst_slot;
+    a.src_meta = h->src_meta;
+    a.scalars = h->scalars;
+    a.tile_status = h->tile_status;
+    a.cumulative_stats = cumulative_stats;
+    const hipError_t e = ep::launch_layout(a, stream);
+    if (e != hipSuccess) return EP_ERR_HIP;
+    h->num_tokens = num_tokens;
+    h->topk_idx = topk_idx;
+    h->topk_idx_dtype = idx_dtype;
+    h->laid_out = 1;
+    return EP_OK;
+}
+
+ep_status ep_handle_read_counts(const ep_handle *h, int32_t *counts, int32_t *psum,
+                                int64_t *num_expanded, int32_t *num_recv_tokens,
+                                uint32_t *error_bits, int32_t *invalid_count,
+                                hipStream_t stream) {
+    if (!h) return EP_ERR_NULL;
+    if (!handle_ready(h)) return EP_ERR_WORKSPACE;
+    if (!h->laid_out) return EP_ERR_NOT_LAID_OUT;
+    int32_t sc[EP_NUM_SCALARS];
+    hipError_t e = hipStreamSynchronize(stream);
+    if (e == hipSuccess)
+        e = hipMemcpy(sc, h->scalars, sizeof(sc), hipMemcpyDeviceToHost);
+    if (e == hipSuccess && counts)
+        e = hipMemcpy(counts, h->counts, sizeof(int32_t) * h->num_experts, hipMemcpyDeviceToHost);
+    if (e == hipSuccess && psum)
+        e = hipMemcpy(psum, h->psum, sizeof(int32_t) * (h->num_experts + 1),
+                      hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return EP_ERR_HIP;
+    if (num_expanded) *num_expanded = sc[EP_SCALAR_NUM_EXPANDED];
+    if (num_recv_tokens) *num_recv_tokens = sc[EP_SCALAR_NUM_RECV_TOKENS];
+    if (error_bits) *error_bits = static_cast<uint32_t>(sc[EP_SCALAR_ERROR_BITS]);
+    if (invalid_count) *invalid_count = sc[EP_SCALAR_INVALID_COUNT];
+    const uint32_t bits = static_cast<uint32_t>(sc[EP_SCALAR_ERROR_BITS]);
+    if (bits & EP_ERRBIT_SCAN_TIMEOUT) return EP_ERR_TIMEOUT;
+    if (bits & EP_ERRBIT_CAPACITY) return EP_ERR_CAPACITY;
+    if (bits & EP_ERRBIT_INVALID_ID) return EP_ERR_INVALID_ID;
+    return EP_OK;
+}
+
+ep_status ep_handle_import(ep_handle *h, const void *topk_idx, ep_dtype idx_dtype,
+                           int32_t num_tokens, const int32_t *counts, const int32_t *psum,
+                           const int32_t *dst_slot, const int32_t *src_meta,
+                           int32_t num_recv_tokens, hipStream_t stream) {
+    if (!h || !counts || !psum) return EP_ERR_NULL;
+    if (!handle_ready(h)) return EP_ERR_WORKSPACE;
+    if (idx_dtype != EP_I64 && idx_dtype != EP_I32) return EP_ERR_DTYPE;
+    if (num_tokens < 0 || num_tokens > h->max_tokens) return EP_ERR_SHAPE;
+    if (num_tokens > 0 && (!topk_idx || !dst_slot)) return EP_ERR_NULL;
+    const int32_t E = h->num_experts;
+    const int64_t expanded = psum[E];
+    if (expanded < 0 || expanded > h->capacity) return EP_ERR_CAPACITY;
+    if (expanded > 0 && !src_meta) return EP_ERR_NULL;
+    const int64_t slots = static_cast<int64_t>(num_tokens) * h->num_topk;
+    // Every row the kernels will touch must lie inside [0, psum[E]).
+    if (psum[0] != 0) return EP_ERR_SHAPE;
+    for (int32_t e = 0; e < E; ++e)
+        if (counts[e] < 0 || static_cast<int64_t>(psum[e]) + counts[e] > psum[e + 1])
+            return EP_ERR_SHAPE;
+    for (int64_t i = 0; i < slots; ++i)
+        if (dst_slot[i] < -1 || dst_slot[i] >= expanded) return EP_ERR_SHAPE;
+    int32_t sc[3] = {num_recv_tokens, 0, 0};
+    const int32_t exp32 = static_cast<int32_t>(expanded);
+    hipError_t e = hipStreamSynchronize(stream);
+    if (e == hipSuccess)
+        e = hipMemcpy(h->counts, counts, sizeof(int32_t) * E, hipMemcpyHostToDevice);
+    if (e == hipSuccess)
+        e = hipMemcpy(h->psum, psum, sizeof(int32_t) * (E + 1), hipMemcpyHostToDevice);
+    if (e == hipSuccess && slots)
+        e = hipMemcpy(h->dst_slot, dst_slot, sizeof(int32_t) * slots, hipMemcpyHostToDevice);
+    if (e == hipSuccess && expanded)
+        e = hipMemcpy(h->src_meta, src_meta, sizeof(int32_t) * expanded, hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMemcpy(h->scalars, sc, sizeof(sc), hipMemcpyHostToDevice);
+    if (e == hipSuccess)
+        e = hipMemcpy(h->scalars + EP_SCALAR_NUM_EXPANDED, &exp32, sizeof(exp32),
+                      hipMemcpyHostToDevice);
+    if (e != hipSuccess) return EP_ERR_HIP;
+    h->num_tokens = num_tokens;
+    h->topk_idx = topk_idx;
+    h->topk_idx_dtype = idx_dtype;
+    h->laid_out = 1;
+    return EP_OK;
+}
+
+ep_status ep_dispatch(const ep_handle *h, const void *x, ep_dtype x_dtype, int32_t hidden,
+                      const float *sf, int64_t sf_token_stride, int64_t sf_hidden_stride,
+                      const float *topk_weights, void *out_x, float *out_sf,
+                      int64_t out_sf_token_stride, int64_t out_sf_hidden_stride, float *out_w,
+                      int32_t zero_padding, hipStream_t stream) {
+    if (!h) return EP_ERR_NULL;
+    if (!handle_ready(h)) return EP_ERR_WORKSPACE;
+    if (!h->laid_out) return EP_ERR_NOT_LAID_OUT;
+    if (x_dtype != EP_BF16 && x_dtype != EP_FP8_E4M3) return EP_ERR_DTYPE;
+    if (hidden <= 0) return EP_ERR_SHAPE;
+    const bool fp8 = x_dtype == EP_FP8_E4M3;
+    if (fp8 ? (hidden % 128) != 0 : (hidden % 8) != 0) return EP_ERR_MISALIGNED;
+    if (fp8 && hidden / 128 > 64 * ep::kMaxSfPerLane) return EP_ERR_UNSUPPORTED;
+    if (!fp8 && (sf || out_sf)) return EP_ERR_DTYPE;
+    if (fp8 && (!out_sf || (h->num_tokens > 0 && !sf))) return EP_ERR_NULL;
+    if (sf_token_stride < 0 || sf_hidden_stride < 0 || out_sf_token_stride < 0 ||
+        out_sf_hidden_stride < 0)
+        return EP_ERR_SHAPE;
+    if (!out_x || (h->num_tokens > 0 && !x)) return EP_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(out_x, 16)) return EP_ERR_MISALIGNED;
+    if (!aligned(sf, 4) || !aligned(out_sf, 4) || !aligned(topk_weights, 4) ||
+        !aligned(out_w, 4))
+        return EP_ERR_MISALIGNED;
+    const int64_t row_bytes = fp8 ? hidden : 2 * static_cast<int64_t>(hidden);
+    ep::DispatchArgs a{};
+    a.x = x;
+    a.row_vecs = row_bytes / 16;
+    a.num_tokens = h->num_tokens;
+    a.num_topk = h->num_topk;
+    a.num_experts = h->num_experts;
+    a.alignment = h->expert_alignment;
+    a.capacity = h->capacity;
+    a.dst = h->dst_slot;
+    a.counts = h->counts;
+    a.psum = h->psum;
+    a.scalars = h->scalars;
+    a.w = topk_weights;
+    a.out_x = out_x;
+    a.sf = sf;
+    a.sf_ts = sf_token_stride;
+    a.sf_hs = sf_hidden_stride;
+    a.num_sf = fp8 ? hidden / 128 : 0;
+    a.out_sf = out_sf;
+    a.out_ts = out_sf_token_stride;
+    a.out_hs = out_sf_hidden_stride;
+    a.out_w = out_w;
+    a.zero_padding = zero_padding != 0;
+    return hip_status(ep::launch_dispatch(a, stream));
+}
+
+ep_status ep_combine(const ep_handle *h, const void *y, ep_dtype y_dtype, int32_t hidden,
+                     const float *topk_weights, const void *bias, void *out,
+                     hipStream_t stream) {
+    if (!h) return EP_ERR_NULL;
+    if (!handle_ready(h)) return EP_ERR_WORKSPACE;
+    if (!h->laid_out) return EP_ERR_NOT_LAID_OUT;
+    if (y_dtype != EP_BF16) return EP_ERR_DTYPE;
+    if (hidden <= 0) return EP_ERR_SHAPE;
+    if (hidden % 8 != 0) return EP_ERR_MISALIGNED;
+    if (h->num_tokens > 0 && (!y || !out)) return EP_ERR_NULL;
+    if (bias && h->num_tokens > 0 && !h->topk_idx) return EP_ERR_NULL;
+    if (!aligned(y, 16) || !aligned(out, 16) || !aligned(bias, 16)) return EP_ERR_MISALIGNED;
+    if (!aligned(topk_weights, 4)) return EP_ERR_MISALIGNED;
+    ep::CombineArgs a{};
+    a.y = y;
+    a.row_vecs = hidden / 8;
+    a.num_tokens = h->num_tokens;
+    a.num_topk = h->num_topk;
+    a.num_experts = h->num_experts;
+    a.capacity = h->capacity;
+    a.dst = h->dst_slot;
+    a.scalars = h->scalars;
+    a.w = topk_weights;
+    a.bias = bias;
+    a.topk_idx = h->topk_idx;
+    a.idx_is_i64 = h->topk_idx_dtype == EP_I64;
+    a.out = out;
+    return hip_status(ep::launch_combine(a, stream));
+}
+
+const char *ep_status_str(ep_status s) {
+    switch (s) {
+    case EP_OK: return "EP_OK: success";
+    case EP_ERR_NULL: return "EP_ERR_NULL: a required pointer is NULL";
+    case EP_ERR_SHAPE: return "EP_ERR_SHAPE: a size is out of range or inconsistent";
+    case EP_ERR_DTYPE: return "EP_ERR_DTYPE: element type not accepted by this call";
+    case EP_ERR_UNSUPPORTED:
+        return "EP_ERR_UNSUPPORTED: beyond the library's limits (K <= 64, E <= 1024, "
+               "capacity and T*K < 2^31)";
+    case EP_ERR_MISALIGNED: return "EP_ERR_MISALIGNED: pointer or row size not aligned";
+    case EP_ERR_WORKSPACE: return "EP_ERR_WORKSPACE: workspace missing or too small";
+    case EP_ERR_NOT_LAID_OUT: return "EP_ERR_NOT_LAID_OUT: no layout on this handle yet";
+    case EP_ERR_CAPACITY: return "EP_ERR_CAPACITY: expanded rows exceed the capacity";
+    case EP_ERR_INVALID_ID: return "EP_ERR_INVALID_ID: an expert id outside [-1, E) was seen";
+    case EP_ERR_HIP: return "EP_ERR_HIP: a HIP call or kernel launch failed";
+    case EP_ERR_TIMEOUT:
+        return "EP_ERR_TIMEOUT: the layout scan's bounded wait gave up; the layout is void";
+    }
+    return "unknown ep_status";
+}
+
+}  // extern "C"

@@ -1,0 +1,125 @@
+// Dispatch copy epilogue into the expert-expanded layout on gfx950.
+//
+// What is computed follows DeepEP notes ch.7 "V2: how dispatch builds expert
+// inputs": s7.1 (x is a bf16 matrix or FP8 bytes plus fp32 scale factors;
+// top-k weights optional), s7.3 (the copy epilogue writes each received row
+// into its expert's aligned range, copies scale factors with their own token
+// and hidden strides and the received weights, and optionally zero-fills the
+// alignment gaps), s7.4 (contiguous aligned expert ranges for grouped GEMM).
+//
+// On one GPU the whole epilogue is HBM traffic: read every token row once and
+// write it to each of its slots' rows.  Token blocks: one wave per token; the
+// wave loads the row into registers as 16-byte vectors (64 lanes x VPL vectors
+// per chunk) and stores the chunk once for every valid slot, so x is read
+// from HBM exactly once.  The K destination rows are wave-uniform (readlane
+// into scalar registers).  Gap blocks, when zero padding is on: one block per
+// (expert, 4-row chunk of the gap), one wave per gap row.
+#include "ep_internal.h"
+#include "../../include/ep.h"
+
+namespace ep {
+namespace {
+
+constexpr int kDispatchThreads = 256;
+constexpr int kTokensPerBlock = kDispatchThreads / 64;
+constexpr int kGapRowsPerBlock = kDispatchThreads / 64;
+
+template <int VPL>
+__global__ __launch_bounds__(kDispatchThreads) void dispatch_kernel(DispatchArgs a,
+                                                                   int token_blocks,
+                                                                   int gap_chunks) {
+    if (a.scalars[EP_SCALAR_ERROR_BITS] & EP_ERRBIT_FATAL) return;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t V = a.row_vecs;
+    u32x4 *out = static_cast<u32x4 *>(a.out_x);
+
+    if (static_cast<int>(blockIdx.x) < token_blocks) {
+        const int64_t t = static_cast<int64_t>(blockIdx.x) * kTokensPerBlock + wave;
+        if (t >= a.num_tokens) return;
+        const int K = a.num_topk;
+        // Rows outside [0, capacity) are skipped, so no layout content can
+        // send a store out of the output buffers.
+        int32_t my_dst = lane < K ? a.dst[t * K + lane] : -1;
+        if (my_dst >= a.capacity) my_dst = -1;
+        if (a.out_w && my_dst >= 0) a.out_w[my_dst] = a.w ? a.w[t * K + lane] : 1.0f;
+        if (a.num_sf) {
+            // A token's scale factors (at most 64 * kMaxSfPerLane) go to
+            // registers once and are stored for every valid slot.
+            float sfv[kMaxSfPerLane];
+#pragma unroll
+            for (int q = 0; q < kMaxSfPerLane; ++q) {
+                const int j = lane + 64 * q;
+                sfv[q] = j < a.num_sf ? a.sf[t * a.sf_ts + j * a.sf_hs] : 0.0f;
+            }
+            for (int k = 0; k < K; ++k) {
+                const int32_t r = __builtin_amdgcn_readlane(my_dst, k);
+                if (r < 0) continue;
+#pragma unroll
+                for (int q = 0; q < kMaxSfPerLane; ++q) {
+                    const int j = lane + 64 * q;
+                    if (j < a.num_sf) a.out_sf[r * a.out_ts + j * a.out_hs] = sfv[q];
+                }
+            }
+        }
+        const u32x4 *src = static_cast<const u32x4 *>(a.x) + t * V;
+        for (int64_t c0 = 0; c0 < V; c0 += 64 * VPL) {
+            u32x4 v[VPL];
+#pragma unroll
+            for (int q = 0; q < VPL; ++q) {
+                const int64_t c = c0 + q * 64 + lane;
+                if (c < V) v[q] = src[c];
+            }
+            for (int k = 0; k < K; ++k) {
+                const int32_t r = __builtin_amdgcn_readlane(my_dst, k);
+                if (r < 0) continue;
+                u32x4 *d = out + static_cast<int64_t>(r) * V;
+#pragma unroll
+                for (int q = 0; q < VPL; ++q) {
+                    const int64_t c = c0 + q * 64 + lane;
+                    if (c < V) __builtin_nontemporal_store(v[q], d + c);
+                }
+            }
+        }
+        return;
+    }
+
+    // Zero padding of alignment gaps: rows [psum[e] + counts[e], psum[e+1]).
+    const int g = static_cast<int>(blockIdx.x) - token_blocks;
+    const int e = g / gap_chunks, chunk = g % gap_chunks;
+    const int64_t r = static_cast<int64_t>(a.psum[e]) + a.counts[e] +
+                      static_cast<int64_t>(chunk) * kGapRowsPerBlock + wave;
+    if (r >= a.psum[e + 1] || r >= a.capacity) return;
+    const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
+    u32x4 *d = out + r * V;
+    for (int64_t c = lane; c < V; c += 64) __builtin_nontemporal_store(zero, d + c);
+    for (int j = lane; j < a.num_sf; j += 64) a.out_sf[r * a.out_ts + j * a.out_hs] = 0.0f;
+    if (a.out_w && lane == 0) a.out_w[r] = 0.0f;
+}
+
+template <int VPL>
+hipError_t launch_vpl(const DispatchArgs &a, hipStream_t stream) {
+    const int token_blocks = (a.num_tokens + kTokensPerBlock - 1) / kTokensPerBlock;
+    int gap_chunks = 0;
+    if (a.zero_padding && a.alignment > 1)
+        gap_chunks = (a.alignment - 1 + kGapRowsPerBlock - 1) / kGapRowsPerBlock;
+    const int64_t blocks = static_cast<int64_t>(token_blocks) +
+                           static_cast<int64_t>(gap_chunks) * a.num_experts;
+    if (blocks == 0) return hipSuccess;
+    if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
+    dispatch_kernel<VPL><<<static_cast<unsigned>(blocks), kDispatchThreads, 0, stream>>>(
+        a, token_blocks, gap_chunks > 0 ? gap_chunks : 1);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t stream) {
+    const int64_t per_lane = (a.row_vecs + 63) / 64;
+    if (per_lane <= 1) return launch_vpl<1>(a, stream);
+    if (per_lane <= 2) return launch_vpl<2>(a, stream);
+    if (per_lane <= 4) return launch_vpl<4>(a, stream);
+    if (per_lane <= 8) return launch_vpl<8>(a, stream);
+    return launch_vpl<16>(a, stream);
+}
+
+}  // namespace ep

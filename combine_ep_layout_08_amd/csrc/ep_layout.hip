@@ -1,0 +1,327 @@
+// Routing layout on gfx950: per-expert counts, aligned exclusive prefix sums,
+// the expanded row of every slot and the source slot of every expanded row.
+//
+// What is computed follows DeepEP notes ch.7 "V2: how dispatch builds expert
+// inputs" (s7.1 input contract, -1 = empty slot; s7.2 counts / source metadata
+// / slot index produced with dispatch; s7.3 expanded layout with per-expert
+// alignment; s7.5 handle fields).  Inside an expert's segment rows follow the
+// ascending slot index t*K+k (a stable counting sort).
+//
+// Two kernels:
+//  1. layout_scan: one 256-thread block per tile of 2048 consecutive slots.
+//     Each wave takes 64 slots per round; lanes holding the same bucket find
+//     each other with one ballot per bucket-id bit (match-any), the group's
+//     rank is a popcount below the lane, and the group leader bumps the wave's
+//     LDS counter.  An LDS pass over the 4 waves turns per-wave counts into
+//     in-tile offsets and the tile histogram.  A decoupled lookback over
+//     earlier tiles (one 64-bit status word per tile and bucket holding epoch,
+//     aggregate/prefix flag and count, read and written with agent-scope
+//     atomics so every XCD sees them) gives each bucket's exclusive offset.
+//     Each valid slot gets its position inside its expert's run.  The tile
+//     with the last ticket holds the inclusive totals: it writes counts, runs
+//     the aligned block scan over experts into psum and sets the error word.
+//     Bucket E collects ids outside [-1, E) so that their count needs no extra
+//     pass.  Tiles take their index from an atomic ticket, so every tile a
+//     block waits on has already started; waits always end.
+//  2. layout_finalize: adds psum[e] to each position, scatters source
+//     metadata, marks alignment gaps with -1, counts tokens with a valid slot,
+//     bumps the epoch and resets the ticket for the next call.
+#include "ep_internal.h"
+#include "../../include/ep.h"
+
+namespace ep {
+namespace {
+
+constexpr uint64_t kFlagAggregate = 1;
+constexpr uint64_t kFlagPrefix = 2;
+constexpr uint32_t kMaxSpins = 1u << 21;
+constexpr int kBucketsPerThread = (kMaxBuckets + kLayoutThreads - 1) / kLayoutThreads;
+
+__device__ inline uint64_t pack_status(uint32_t epoch, uint64_t flag, uint32_t value) {
+    return (static_cast<uint64_t>(epoch) << 34) | (flag << 32) | value;
+}
+
+__device__ inline void store_status(uint64_t *p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ inline uint64_t load_status(const uint64_t *p) {
+    return __hip_atomic_load(const_cast<uint64_t *>(p), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ inline int64_t align_up(int64_t c, int64_t a) { return (c + a - 1) / a * a; }
+
+// Exclusive scan of one int64 per thread over a 256-thread block.
+__device__ int64_t block_exclusive_scan(int64_t v, int64_t *s_wave, int64_t *total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int64_t x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int64_t y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    if (lane == 63) s_wave[wave] = x;
+    __syncthreads();
+    int64_t base = 0, sum = 0;
+#pragma unroll
+    for (int w = 0; w < kLayoutWaves; ++w) {
+        const int64_t s = s_wave[w];
+        if (w < wave) base += s;
+        sum += s;
+    }
+    *total = sum;
+    return base + x - v;
+}
+
+template <typename IdxT>
+__global__ __launch_bounds__(kLayoutThreads) void layout_scan_kernel(LayoutArgs a,
+                                                                    int64_t num_slots,
+                                                                    int num_tiles) {
+    __shared__ int32_t s_hist[kLayoutWaves][kMaxBuckets];
+    __shared__ int32_t s_excl[kMaxBuckets];
+    __shared__ int32_t s_total[kMaxBuckets];
+    __shared__ int64_t s_wave[kLayoutWaves];
+    __shared__ int32_t s_tile;
+    __shared__ uint32_t s_epoch;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int E = a.num_experts, NB = E + 1;
+    if (tid == 0) {
+        s_tile = __hip_atomic_fetch_add(&a.scalars[EP_SCALAR_TICKET], 1, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
+        s_epoch = static_cast<uint32_t>(a.scalars[EP_SCALAR_EPOCH]);
+    }
+    for (int w = 0; w < kLayoutWaves; ++w)
+        for (int b = tid; b < NB; b += kLayoutThreads) s_hist[w][b] = 0;
+    __syncthreads();
+    const int tile = s_tile;
+    const uint32_t epoch = s_epoch;
+
+    // 1. In-wave match-any over bucket ids, per-wave running counts in LDS.
+    const int nbits = 32 - __builtin_clz(static_cast<unsigned>(E));   // bits of 0..E
+    const IdxT *idx = static_cast<const IdxT *>(a.topk_idx);
+    const int64_t wave_base = static_cast<int64_t>(tile) * kTileSlots +
+                              static_cast<int64_t>(wave) * (kLayoutRounds * 64);
+    const uint64_t below = (1ull << lane) - 1ull;
+    int bucket[kLayoutRounds];
+    int rank[kLayoutRounds];
+#pragma unroll
+    for (int j = 0; j < kLayoutRounds; ++j) {
+        const int64_t i = wave_base + j * 64 + lane;
+        int b = -1;
+        if (i < num_slots) {
+            const int64_t e = static_cast<int64_t>(idx[i]);
+            b = (e >= 0 && e < E) ? static_cast<int>(e) : (e == -1 ? -1 : E);
+        }
+        uint64_t match = __ballot(b >= 0);
+        for (int bit = 0; bit < nbits; ++bit) {
+            const bool one = (b >> bit) & 1;
+            const uint64_t bal = __ballot(one);
+            match &= one ? bal : ~bal;
+        }
+        int r = 0;
+        if (b >= 0) {
+            const int before = __popcll(match & below);
+            const int old = s_hist[wave][b];
+            if (before == 0) s_hist[wave][b] = old + __popcll(match);
+            r = old + before;
+        }
+        bucket[j] = b;
+        rank[j] = r;
+    }
+    __syncthreads();
+
+    // 2. Per-wave counts -> in-tile offsets; tile aggregate per bucket.
+    int32_t agg[kBucketsPerThread];
+#pragma unroll
+    for (int q = 0; q < kBucketsPerThread; ++q) {
+        const int b = tid + q * kLayoutThreads;
+        agg[q] = 0;
+        if (b < NB) {
+            int32_t run = 0;
+#pragma unroll
+            for (int w = 0; w < kLayoutWaves; ++w) {
+                const int32_t c = s_hist[w][b];
+                s_hist[w][b] = run;
+                run += c;
+            }
+            agg[q] = run;
+        }
+    }
+
+    // 3. Decoupled lookback across tiles, one bucket per thread and pass.
+    uint64_t *my_status = a.tile_status + static_cast<int64_t>(tile) * NB;
+#pragma unroll
+    for (int q = 0; q < kBucketsPerThread; ++q) {
+        const int b = tid + q * kLayoutThreads;
+        if (b < NB)
+            store_status(&my_status[b],
+                         pack_status(epoch, tile == 0 ? kFlagPrefix : kFlagAggregate,
+                                     static_cast<uint32_t>(agg[q])));
+    }
+#pragma unroll
+    for (int q = 0; q < kBucketsPerThread; ++q) {
+        const int b = tid + q * kLayoutThreads;
+        if (b >= NB) continue;
+        uint32_t excl = 0;
+        if (tile > 0) {
+            int j = tile - 1;
+            uint32_t spins = 0;
+            while (true) {
+                const uint64_t s = load_status(&a.tile_status[static_cast<int64_t>(j) * NB + b]);
+                const uint32_t s_epoch_tag = static_cast<uint32_t>(s >> 34);
+                const uint32_t flag = static_cast<uint32_t>(s >> 32) & 3u;
+                if (s_epoch_tag != epoch || flag == 0) {
+                    // A predecessor has always started (ticket order), so the
+                    // wait ends; the bound turns a broken invariant into an
+                    // error word instead of a hung kernel.
+                    if (++spins > kMaxSpins) {
+                        atomicOr(reinterpret_cast<unsigned *>(&a.scalars[EP_SCALAR_ERROR_BITS]),
+                                 EP_ERRBIT_SCAN_TIMEOUT);
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
+                    continue;
+                }
+                excl += static_cast<uint32_t>(s);
+                if (flag == kFlagPrefix || j == 0) break;
+                --j;
+            }
+            store_status(&my_status[b],
+                         pack_status(epoch, kFlagPrefix, excl + static_cast<uint32_t>(agg[q])));
+        }
+        s_excl[b] = static_cast<int32_t>(excl);
+    }
+    __syncthreads();
+
+    // 4. Position of every valid slot inside its expert's run.
+#pragma unroll
+    for (int j = 0; j < kLayoutRounds; ++j) {
+        const int64_t i = wave_base + j * 64 + lane;
+        if (i < num_slots) {
+            const int b = bucket[j];
+            a.dst[i] = (b >= 0 && b < E) ? s_excl[b] + s_hist[wave][b] + rank[j] : -1;
+        }
+    }
+
+    // 5. The last tile owns the totals: counts, aligned scan, error word.
+    if (tile != num_tiles - 1) return;
+#pragma unroll
+    for (int q = 0; q < kBucketsPerThread; ++q) {
+        const int b = tid + q * kLayoutThreads;
+        if (b < NB) {
+            const int32_t tot = s_excl[b] + agg[q];
+            s_total[b] = tot;
+            if (b < E) {
+                a.counts[b] = tot;
+                if (a.cumulative_stats) a.cumulative_stats[b] += tot;
+            }
+        }
+    }
+    __syncthreads();
+    const int per = (E + kLayoutThreads - 1) / kLayoutThreads;
+    const int b0 = tid * per;
+    const int b1 = min(b0 + per, E);
+    int64_t local = 0;
+    for (int b = b0; b < b1; ++b) local += align_up(s_total[b], a.alignment);
+    int64_t total = 0;
+    int64_t run = block_exclusive_scan(local, s_wave, &total);
+    for (int b = b0; b < b1; ++b) {
+        a.psum[b] = static_cast<int32_t>(min(run, static_cast<int64_t>(INT32_MAX)));
+        run += align_up(s_total[b], a.alignment);
+    }
+    if (tid == 0) {
+        const int32_t expanded = static_cast<int32_t>(min(total, static_cast<int64_t>(INT32_MAX)));
+        const int32_t invalid = s_total[E];
+        a.psum[E] = expanded;
+        uint32_t err = static_cast<uint32_t>(a.scalars[EP_SCALAR_ERROR_BITS]) &
+                       EP_ERRBIT_SCAN_TIMEOUT;
+        if (total > a.capacity) err |= EP_ERRBIT_CAPACITY;
+        if (invalid > 0) err |= EP_ERRBIT_INVALID_ID;
+        a.scalars[EP_SCALAR_NUM_EXPANDED] = expanded;
+        a.scalars[EP_SCALAR_INVALID_COUNT] = invalid;
+        a.scalars[EP_SCALAR_ERROR_BITS] = static_cast<int32_t>(err);
+        a.scalars[EP_SCALAR_NUM_RECV_TOKENS] = 0;
+    }
+}
+
+template <typename IdxT>
+__global__ __launch_bounds__(256) void layout_finalize_kernel(LayoutArgs a, int token_blocks) {
+    __shared__ int32_t s_red[4];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (blockIdx.x == 0 && tid == 0) {
+        a.scalars[EP_SCALAR_TICKET] = 0;
+        uint32_t next = static_cast<uint32_t>(a.scalars[EP_SCALAR_EPOCH]) + 1u;
+        if (next >= (1u << 30)) next = 1u;
+        a.scalars[EP_SCALAR_EPOCH] = static_cast<int32_t>(next);
+    }
+    if (a.scalars[EP_SCALAR_ERROR_BITS] & EP_ERRBIT_FATAL) return;
+    const int K = a.num_topk, E = a.num_experts;
+    if (static_cast<int>(blockIdx.x) < token_blocks) {
+        const IdxT *idx = static_cast<const IdxT *>(a.topk_idx);
+        const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + tid;
+        int any = 0;
+        if (t < a.num_tokens) {
+            for (int k = 0; k < K; ++k) {
+                const int64_t i = t * K + k;
+                const int64_t e = static_cast<int64_t>(idx[i]);
+                if (e >= 0 && e < E) {
+                    const int32_t r = a.psum[e] + a.dst[i];
+                    a.dst[i] = r;
+                    if (r < a.capacity) a.src_meta[r] = static_cast<int32_t>(i);
+                    any = 1;
+                }
+            }
+        }
+        const int c = __popcll(__ballot(any));
+        if (lane == 0) s_red[wave] = c;
+        __syncthreads();
+        if (tid == 0) {
+            const int sum = s_red[0] + s_red[1] + s_red[2] + s_red[3];
+            if (sum) atomicAdd(&a.scalars[EP_SCALAR_NUM_RECV_TOKENS], sum);
+        }
+    } else {
+        const int e = static_cast<int>(blockIdx.x) - token_blocks;
+        const int32_t g1 = a.psum[e + 1];
+        const int64_t end = g1 < a.capacity ? g1 : a.capacity;
+        for (int64_t r = static_cast<int64_t>(a.psum[e]) + a.counts[e] + tid; r < end; r += 256)
+            a.src_meta[r] = -1;
+    }
+}
+
+__global__ void handle_clear_kernel(int32_t *scalars, uint64_t *status, int64_t n) {
+    const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (int64_t i = gid; i < n; i += stride) status[i] = 0;
+    if (gid < EP_NUM_SCALARS) scalars[gid] = (gid == EP_SCALAR_EPOCH) ? 1 : 0;
+}
+
+}  // namespace
+
+hipError_t launch_handle_clear(int32_t *scalars, uint64_t *tile_status, int64_t status_words,
+                               hipStream_t stream) {
+    int64_t blocks = (status_words + 255) / 256;
+    if (blocks < 1) blocks = 1;
+    if (blocks > 1024) blocks = 1024;
+    handle_clear_kernel<<<static_cast<unsigned>(blocks), 256, 0, stream>>>(scalars, tile_status,
+                                                                           status_words);
+    return hipGetLastError();
+}
+
+hipError_t launch_layout(const LayoutArgs &a, hipStream_t stream) {
+    const int64_t num_slots = static_cast<int64_t>(a.num_tokens) * a.num_topk;
+    const int tiles = static_cast<int>(layout_tiles(num_slots));
+    const int token_blocks = (a.num_tokens + 255) / 256;
+    const unsigned fin_blocks = static_cast<unsigned>(token_blocks + a.num_experts);
+    if (a.idx_is_i64) {
+        layout_scan_kernel<int64_t><<<tiles, kLayoutThreads, 0, stream>>>(a, num_slots, tiles);
+        layout_finalize_kernel<int64_t><<<fin_blocks, 256, 0, stream>>>(a, token_blocks);
+    } else {
+        layout_scan_kernel<int32_t><<<tiles, kLayoutThreads, 0, stream>>>(a, num_slots, tiles);
+        layout_finalize_kernel<int32_t><<<fin_blocks, 256, 0, stream>>>(a, token_blocks);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace ep

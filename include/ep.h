@@ -1,0 +1,251 @@
+/*
+ * ep.h - C ABI of the one-GPU MoE routing layout, dispatch and combine
+ * library for AMD Instinct MI355X (gfx950).
+ *
+ * Sources: the DeepEP notes, chapter 7 "V2: how dispatch builds expert
+ * inputs" [Ch7] and chapter 8 "V2: combine, handle and async overlap" [Ch8]
+ * (bowenzhou.top/repos/deepep), the digest of vLLM pull request 52781
+ * "DeepEP v2 combine made asynchronous" [vLLM], and the DeepEP README [README].
+ *
+ * What is computed, for one GPU's share of an expert-parallel MoE layer:
+ *   layout   - from topk_idx [T, K] (-1 = empty slot), per-expert counts,
+ *              the exclusive prefix sums of the counts aligned up to
+ *              expert_alignment, the expanded row of every slot and the
+ *              source slot of every expanded row.
+ *   dispatch - copy every token row (bf16, or FP8 bytes plus fp32 scale
+ *              factors) into the expanded row of each of its slots; each
+ *              expert owns one contiguous range whose start is a multiple
+ *              of expert_alignment; alignment gaps can be zero-filled.
+ *   combine  - for every token, sum its expert rows in slot order k = 0..K-1
+ *              in fp32 as w[t,k] * (y[row] + bias[e]) and round to bf16.
+ *
+ * Memory ownership: the library never allocates, frees or keeps memory.  All
+ * device buffers (workspace, inputs, outputs) belong to the caller and must
+ * outlive the stream work that uses them.  The handle is a plain struct owned
+ * by the caller; its device arrays point into the caller's workspace.
+ *
+ * Streams: every call except ep_handle_read_counts and ep_handle_import
+ * only enqueues work on the given stream (0 = the null stream) and returns.
+ * Ordering against other streams is the caller's job (events), which covers
+ * the previous-event / compute-stream controls of [Ch8 §8.2].  Because only
+ * those two calls synchronise, layout, dispatch and combine can be captured
+ * in a HIP graph.
+ *
+ * Errors: a call returns a status.  Problems visible on the host (null
+ * pointers, sizes, dtypes, alignment, workspace size) are reported before
+ * anything is launched.  Problems only the device can see (capacity exceeded,
+ * expert ids outside [-1, E)) set bits in the handle's device error word,
+ * which ep_handle_read_counts turns into EP_ERR_CAPACITY / EP_ERR_INVALID_ID
+ * (or EP_ERR_TIMEOUT if the layout scan's bounded wait ever gave up).  After
+ * a capacity or timeout error, dispatch and combine on that handle write
+ * nothing.  Calls on one handle must be ordered on one stream; overlapping
+ * calls on the same handle race.
+ */
+#ifndef EP_H
+#define EP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ep_status {
+    EP_OK = 0,
+    EP_ERR_NULL = 1,          /* a required pointer is NULL                    */
+    EP_ERR_SHAPE = 2,         /* a size is out of range or inconsistent        */
+    EP_ERR_DTYPE = 3,         /* element type not accepted by this call        */
+    EP_ERR_UNSUPPORTED = 4,   /* valid for the method, beyond this library's   */
+                              /* limits (K > 64, E > 1024, capacity >= 2^31, */
+                              /* FP8 hidden > 32768)                           */
+    EP_ERR_MISALIGNED = 5,    /* pointer or row size not 16-byte aligned       */
+    EP_ERR_WORKSPACE = 6,     /* workspace NULL or smaller than required       */
+    EP_ERR_NOT_LAID_OUT = 7,  /* dispatch / combine before a layout            */
+    EP_ERR_CAPACITY = 8,      /* device: psum[E] > capacity                    */
+    EP_ERR_INVALID_ID = 9,    /* device: an id outside [-1, E) was seen        */
+    EP_ERR_HIP = 10,          /* a HIP runtime call or launch failed           */
+    EP_ERR_TIMEOUT = 11       /* device: the layout scan's bounded wait ended  */
+                              /* without its predecessor's count (layout void) */
+} ep_status;
+
+typedef enum ep_dtype {
+    EP_BF16 = 0,
+    EP_FP8_E4M3 = 1,          /* OCP E4M3FN bytes; copied, never interpreted   */
+    EP_F32 = 2,
+    EP_I32 = 3,
+    EP_I64 = 4
+} ep_dtype;
+
+/* Device error word bits (scalars[EP_SCALAR_ERROR_BITS]). */
+#define EP_ERRBIT_CAPACITY 1u
+#define EP_ERRBIT_INVALID_ID 2u
+#define EP_ERRBIT_SCAN_TIMEOUT 4u
+/* Bits after which dispatch and combine on the handle write nothing. */
+#define EP_ERRBIT_FATAL (EP_ERRBIT_CAPACITY | EP_ERRBIT_SCAN_TIMEOUT)
+
+/* Indices into the handle's device scalars array. */
+#define EP_SCALAR_NUM_RECV_TOKENS 0   /* tokens with >= 1 valid slot          */
+#define EP_SCALAR_ERROR_BITS 1
+#define EP_SCALAR_INVALID_COUNT 2     /* slots with an id outside [-1, E)     */
+#define EP_SCALAR_EPOCH 3             /* internal: layout call tag            */
+#define EP_SCALAR_TICKET 4            /* internal: tile ticket counter        */
+#define EP_SCALAR_NUM_EXPANDED 5      /* psum[E]                              */
+#define EP_NUM_SCALARS 8
+
+/*
+ * Routing state that combine and cached re-dispatch reuse [Ch7 §7.5: the
+ * handle keeps counts, prefix sums, alignment, destination slots and source
+ * metadata; a re-dispatch with an old handle takes no topk_idx and must keep
+ * expert count, alignment and capacity].  Plain data: the caller may copy
+ * it; every copy refers to the same workspace.  Fields are set by
+ * ep_handle_init / ep_layout and must not be edited by the caller.
+ */
+typedef struct ep_handle {
+    int32_t max_tokens;         /* T bound fixed at init                        */
+    int32_t num_tokens;         /* T of the last layout                         */
+    int32_t num_topk;           /* K                                            */
+    int32_t num_experts;        /* E                                            */
+    int32_t expert_alignment;   /* A                                            */
+    int32_t laid_out;           /* 1 after ep_layout / ep_handle_import         */
+    int64_t capacity;           /* rows of every expanded buffer                */
+    int32_t *counts;            /* device [E] unaligned per-expert counts       */
+    int32_t *psum;              /* device [E+1] exclusive scan of aligned counts*/
+    int32_t *dst_slot;          /* device [max_tokens*K] row of slot t*K+k, -1  */
+    int32_t *src_meta;          /* device [capacity] slot t*K+k of a row, -1 on */
+                                /* gap rows, unspecified at or past psum[E]     */
+    int32_t *scalars;           /* device [EP_NUM_SCALARS]                      */
+    uint64_t *tile_status;      /* device scratch of the layout scan            */
+    const void *topk_idx;       /* BORROWED device [T, K] ids of the last layout*/
+    int32_t topk_idx_dtype;     /* EP_I32 or EP_I64                             */
+    int32_t status_tiles;       /* tiles the scratch is sized for               */
+} ep_handle;
+
+/* Size of ep_handle in bytes, so bindings can check their struct layout. */
+size_t ep_handle_sizeof(void);
+
+/*
+ * Worst-case expanded rows at one rank when counts are not read back
+ * [Ch7 §7.2, allocation without CPU sync]: T*min(K,E) + (A-1)*E rounded up
+ * to a multiple of A.  Returns -1 if an argument is <= 0 (T may be 0).
+ * With duplicate experts inside a token and K > E, size by T*K + (A-1)*E.
+ */
+int64_t ep_capacity_bound(int32_t num_tokens, int32_t num_topk,
+                          int32_t num_experts, int32_t expert_alignment);
+
+/* Bytes of device workspace a handle with these sizes needs (0 if invalid). */
+size_t ep_workspace_bytes(int32_t max_tokens, int32_t num_topk,
+                          int32_t num_experts, int32_t expert_alignment,
+                          int64_t capacity);
+
+/*
+ * Set up a handle in a caller-owned device workspace of ws_bytes bytes
+ * (256-byte aligned, at least ep_workspace_bytes).  Clears the layout scan's
+ * scratch with one small kernel on `stream`.  1 <= K <= 64,
+ * 1 <= E <= 1024, A >= 1, 0 <= max_tokens, max_tokens*K < 2^31,
+ * 0 <= capacity < 2^31.
+ */
+ep_status ep_handle_init(ep_handle *h, int32_t max_tokens, int32_t num_topk,
+                         int32_t num_experts, int32_t expert_alignment,
+                         int64_t capacity, void *workspace, size_t ws_bytes,
+                         hipStream_t stream);
+
+/*
+ * Routing layout [Ch7 §7.1 input contract; §7.2 counts, source metadata and
+ * slot index come out of dispatch; §7.3 expanded layout aligned per expert].
+ *   topk_idx  device [num_tokens, K], EP_I64 or EP_I32, -1 = empty slot.
+ *             Borrowed by the handle: it must stay alive and unmodified
+ *             while the handle is used with a bias (combine reads expert ids).
+ *   num_tokens  <= max_tokens.
+ *   cumulative_stats  NULL or device int32 [E]; counts are added to it
+ *             (the per-expert receive statistics of [Ch7 §7.2]).
+ * Order inside an expert segment: ascending slot index t*K+k.  Ids outside
+ * [-1, E) are treated as empty and flagged.  Writes counts, psum, dst_slot,
+ * src_meta (gap rows -1) and the scalars; all on `stream`.
+ */
+ep_status ep_layout(ep_handle *h, const void *topk_idx, ep_dtype idx_dtype,
+                    int32_t num_tokens, int32_t *cumulative_stats,
+                    hipStream_t stream);
+
+/*
+ * The only blocking call besides import [Ch7 §7.2: with CPU sync the host
+ * waits for the receive counts and then sizes outputs exactly].  Waits for
+ * `stream`, then copies to any non-NULL host pointer: counts [E], psum [E+1],
+ * num_expanded (= psum[E]), num_recv_tokens, error_bits, invalid_count.
+ * Returns EP_ERR_TIMEOUT, EP_ERR_CAPACITY or EP_ERR_INVALID_ID (in that order
+ * of precedence) when the device set the bit (outputs are still filled),
+ * else EP_OK.
+ */
+ep_status ep_handle_read_counts(const ep_handle *h, int32_t *counts,
+                                int32_t *psum, int64_t *num_expanded,
+                                int32_t *num_recv_tokens, uint32_t *error_bits,
+                                int32_t *invalid_count, hipStream_t stream);
+
+/*
+ * Install a layout computed elsewhere (host arrays: counts [E], psum [E+1],
+ * dst_slot [num_tokens*K], src_meta [psum[E]]) and the device topk_idx it
+ * belongs to.  Synchronous (host buffers may be reused on return).  Meant
+ * for interop and for checking dispatch/combine against a reference layout.
+ */
+ep_status ep_handle_import(ep_handle *h, const void *topk_idx, ep_dtype idx_dtype,
+                           int32_t num_tokens, const int32_t *counts,
+                           const int32_t *psum, const int32_t *dst_slot,
+                           const int32_t *src_meta, int32_t num_recv_tokens,
+                           hipStream_t stream);
+
+/*
+ * Dispatch copy epilogue into the expert-expanded layout [Ch7 §7.1 (bf16 x,
+ * or FP8 data plus scale factors; top-k weights optional), §7.3 (copy
+ * epilogue with per-expert alignment, optional zero padding of the gaps,
+ * scale factors with their own token and hidden strides, received weights),
+ * §7.4 (contiguous aligned expert ranges for a grouped GEMM)].
+ *   x        device [num_tokens, hidden]: bf16 (hidden % 8 == 0) or FP8
+ *            bytes (hidden % 128 == 0); 16-byte aligned.
+ *   sf       FP8 only (NULL for bf16): fp32 element (t, j), j < hidden/128,
+ *            at sf[t*sf_token_stride + j*sf_hidden_stride].
+ *   topk_weights  NULL or device fp32 [num_tokens, K].
+ *   out_x    device [capacity, hidden] of x's type, 16-byte aligned.
+ *   out_sf   FP8 only: element (r, j) at out_sf[r*out_sf_token_stride +
+ *            j*out_sf_hidden_stride].
+ *   out_w    NULL or device fp32 [capacity]: weight of the row's slot
+ *            (1.0 when topk_weights is NULL).
+ *   zero_padding  nonzero: gap rows get zero bytes, zero scales, weight 0.
+ * Rows at or past psum[E], and gap rows without zero padding, are not
+ * written.  Reuses the handle, so a cached re-dispatch is just another call.
+ */
+ep_status ep_dispatch(const ep_handle *h, const void *x, ep_dtype x_dtype,
+                      int32_t hidden, const float *sf, int64_t sf_token_stride,
+                      int64_t sf_hidden_stride, const float *topk_weights,
+                      void *out_x, float *out_sf, int64_t out_sf_token_stride,
+                      int64_t out_sf_hidden_stride, float *out_w,
+                      int32_t zero_padding, hipStream_t stream);
+
+/*
+ * Combine [Ch8 §8.1: reduce along the handle back to the source, with
+ * optional fused bias and gate-weight reduction; bf16 x and fp32 weights],
+ * [vLLM implementation breakdown: the combine input must be bf16 and the
+ * weights may be None].
+ *   y        device bf16 [capacity, hidden], hidden % 8 == 0, 16-byte
+ *            aligned; only rows that hold a slot are read.
+ *   topk_weights  NULL (weight 1) or device fp32 [num_tokens, K].
+ *   bias     NULL or device bf16 [E, hidden]: expert e's output bias, added
+ *            to the expert row before weighting.
+ *   out      device bf16 [num_tokens, hidden].
+ * out[t][h] = bf16_rne(sum over valid k in order of w[t,k]*(y[r][h]+b[e][h]))
+ * in fp32 from +0.0 with separately rounded multiply and add; a token with
+ * no valid slot gets +0.0.
+ */
+ep_status ep_combine(const ep_handle *h, const void *y, ep_dtype y_dtype,
+                     int32_t hidden, const float *topk_weights,
+                     const void *bias, void *out, hipStream_t stream);
+
+/* Static text for a status code. */
+const char *ep_status_str(ep_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EP_H */

@@ -1,0 +1,191 @@
+"""The C-ABI library on the CPU: it loads, exports every function that
+include/ep.h declares, and its host-side logic (capacity bound, workspace
+size, argument validation) behaves as documented.  No call here reaches a HIP
+runtime function, so nothing needs a GPU."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+import combine_ep_layout_08_amd as ep
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ep.h")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built():
+    if not os.path.exists(ep.LIB_PATH):
+        from combine_ep_layout_08_amd import build
+        build.build()
+    return ep.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ep_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_function_is_exported():
+    names = declared_functions()
+    assert len(names) == 10, names
+    for n in names:
+        assert hasattr(ep.lib(), n), n
+        assert n in ep._SIGNATURES, f"binding lacks {n}"
+
+
+def test_handle_struct_layout_matches():
+    assert ep.ep_handle_sizeof() == ctypes.sizeof(ep.ep_handle) == 96
+
+
+def test_capacity_bound_golden():
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "capacity_bound.json")))
+    for c in g["cases"]:
+        assert ep.ep_capacity_bound(c["T"], c["K"], c["E"], c["A"]) == c["bound"], c
+
+
+def test_capacity_bound_rejects_bad_sizes():
+    assert ep.ep_capacity_bound(-1, 8, 256, 128) == -1
+    assert ep.ep_capacity_bound(4, 0, 256, 128) == -1
+    assert ep.ep_capacity_bound(4, 8, 0, 128) == -1
+    assert ep.ep_capacity_bound(4, 8, 256, 0) == -1
+
+
+def test_workspace_bytes():
+    small = ep.ep_workspace_bytes(64, 4, 16, 1, 256)
+    big = ep.ep_workspace_bytes(4096, 8, 256, 128, 65280)
+    assert 0 < small < big
+    assert big % 256 == 0
+    # counts + psum + dst + src_meta + scalars + one 64-bit status word per
+    # (tile of 2048 slots, expert + 1)
+    need = 4 * 256 + 4 * 257 + 4 * 4096 * 8 + 4 * 65280 + 32 + 8 * 16 * 257
+    assert need <= big <= need + 6 * 256
+    assert ep.ep_workspace_bytes(64, 65, 16, 1, 256) == 0       # K > 64
+    assert ep.ep_workspace_bytes(64, 4, 1025, 1, 256) == 0      # E > 1024
+    assert ep.ep_workspace_bytes(64, 4, 16, 1, 1 << 31) == 0    # capacity >= 2^31
+    assert ep.ep_workspace_bytes(-1, 4, 16, 1, 256) == 0
+
+
+def test_status_strings():
+    for s in range(12):
+        assert ep.ep_status_str(s).startswith("EP_")
+    assert "unknown" in ep.ep_status_str(99)
+
+
+def test_init_validation_before_any_launch():
+    h = ep.ep_handle()
+    fake = ctypes.c_void_p(0x10000)
+    assert ep.lib().ep_handle_init(None, 4, 2, 4, 1, 16, fake, 1 << 20, None) == ep.EP_ERR_NULL
+    assert ep.ep_handle_init(h, 4, 2, 4, 1, 16, None, 1 << 20, None) == ep.EP_ERR_WORKSPACE
+    assert ep.ep_handle_init(h, 4, 0, 4, 1, 16, fake, 1 << 20, None) == ep.EP_ERR_SHAPE
+    assert ep.ep_handle_init(h, 4, 2, 4, 0, 16, fake, 1 << 20, None) == ep.EP_ERR_SHAPE
+    assert ep.ep_handle_init(h, 4, 2, 4, 1, -1, fake, 1 << 20, None) == ep.EP_ERR_SHAPE
+    assert ep.ep_handle_init(h, 4, 65, 4, 1, 16, fake, 1 << 20, None) == ep.EP_ERR_UNSUPPORTED
+    assert ep.ep_handle_init(h, 4, 2, 2000, 1, 16, fake, 1 << 20, None) == ep.EP_ERR_UNSUPPORTED
+    assert ep.ep_handle_init(h, 4, 2, 4, 1, 16, ctypes.c_void_p(0x10010), 1 << 20,
+                             None) == ep.EP_ERR_MISALIGNED
+    need = ep.ep_workspace_bytes(4, 2, 4, 1, 16)
+    assert ep.ep_handle_init(h, 4, 2, 4, 1, 16, fake, need - 1, None) == ep.EP_ERR_WORKSPACE
+    assert h.counts is None                       # untouched on failure
+
+
+def _fake_handle(laid_out=1):
+    h = ep.ep_handle()
+    h.max_tokens, h.num_tokens, h.num_topk, h.num_experts = 8, 8, 2, 4
+    h.expert_alignment, h.laid_out, h.capacity = 1, laid_out, 16
+    for i, f in enumerate(("counts", "psum", "dst_slot", "src_meta", "scalars", "tile_status")):
+        setattr(h, f, 0x100000 + 0x1000 * i)
+    h.topk_idx = 0x200000
+    h.topk_idx_dtype = ep.EP_I64
+    h.status_tiles = 1
+    return h
+
+
+A16 = 0x300000          # 16-byte aligned fake device addresses; never dereferenced
+
+
+def test_layout_validation():
+    h = _fake_handle()
+    assert ep.ep_layout(h, A16, ep.EP_F32, 8, None, None) == ep.EP_ERR_DTYPE
+    assert ep.ep_layout(h, A16, ep.EP_I64, 9, None, None) == ep.EP_ERR_SHAPE
+    assert ep.ep_layout(h, A16, ep.EP_I64, -1, None, None) == ep.EP_ERR_SHAPE
+    assert ep.ep_layout(h, None, ep.EP_I64, 8, None, None) == ep.EP_ERR_NULL
+    assert ep.ep_layout(h, A16 + 4, ep.EP_I64, 8, None, None) == ep.EP_ERR_MISALIGNED
+    empty = ep.ep_handle()
+    assert ep.ep_layout(empty, A16, ep.EP_I64, 0, None, None) == ep.EP_ERR_WORKSPACE
+
+
+def test_dispatch_validation():
+    h = _fake_handle()
+    args = dict(x=A16, dt=ep.EP_BF16, H=64, sf=None, w=None, out=A16, osf=None, ow=None)
+
+    def call(hh=h, **kw):
+        a = dict(args, **kw)
+        return ep.ep_dispatch(hh, a["x"], a["dt"], a["H"], a["sf"], 0, 0, a["w"], a["out"],
+                              a["osf"], 0, 0, a["ow"], 0, None)
+
+    assert call(hh=_fake_handle(laid_out=0)) == ep.EP_ERR_NOT_LAID_OUT
+    assert call(dt=ep.EP_F32) == ep.EP_ERR_DTYPE
+    assert call(H=0) == ep.EP_ERR_SHAPE
+    assert call(H=60) == ep.EP_ERR_MISALIGNED                # bf16 rows of 120 bytes
+    assert call(sf=A16) == ep.EP_ERR_DTYPE                   # scales with bf16
+    assert call(dt=ep.EP_FP8_E4M3, H=7168) == ep.EP_ERR_NULL  # FP8 without scales
+    assert call(dt=ep.EP_FP8_E4M3, H=7000, sf=A16, osf=A16) == ep.EP_ERR_MISALIGNED
+    assert call(dt=ep.EP_FP8_E4M3, H=32768 + 128, sf=A16, osf=A16) == ep.EP_ERR_UNSUPPORTED
+    assert call(x=None) == ep.EP_ERR_NULL
+    assert call(out=None) == ep.EP_ERR_NULL
+    assert call(x=A16 + 8) == ep.EP_ERR_MISALIGNED
+    assert call(w=A16 + 2) == ep.EP_ERR_MISALIGNED
+    assert ep.ep_dispatch(h, A16, ep.EP_BF16, 64, None, -1, 0, None, A16, None, 0, 0, None, 0,
+                          None) == ep.EP_ERR_SHAPE
+
+
+def test_combine_validation():
+    h = _fake_handle()
+
+    def call(hh=h, y=A16, dt=ep.EP_BF16, H=64, w=None, b=None, out=A16):
+        return ep.ep_combine(hh, y, dt, H, w, b, out, None)
+
+    assert call(hh=_fake_handle(laid_out=0)) == ep.EP_ERR_NOT_LAID_OUT
+    assert call(dt=ep.EP_F32) == ep.EP_ERR_DTYPE             # combine input must be bf16
+    assert call(dt=ep.EP_FP8_E4M3) == ep.EP_ERR_DTYPE
+    assert call(H=-8) == ep.EP_ERR_SHAPE
+    assert call(H=12) == ep.EP_ERR_MISALIGNED
+    assert call(y=None) == ep.EP_ERR_NULL
+    assert call(out=None) == ep.EP_ERR_NULL
+    assert call(b=A16 + 2) == ep.EP_ERR_MISALIGNED
+    assert call(w=A16 + 1) == ep.EP_ERR_MISALIGNED
+    nob = _fake_handle()
+    nob.topk_idx = None
+    assert call(hh=nob, b=A16) == ep.EP_ERR_NULL
+
+
+def test_import_validation_rejects_rows_out_of_range():
+    import numpy as np
+    h = _fake_handle()
+    counts = np.array([1, 0, 0, 0], np.int32)
+    psum = np.array([0, 1, 1, 1, 1], np.int32)
+    src = np.array([0], np.int32)
+    bad_dst = np.full(16, -1, np.int32)
+    bad_dst[3] = 1                                          # >= psum[E]
+    assert ep.ep_handle_import(h, A16, ep.EP_I64, 8, counts.ctypes.data, psum.ctypes.data,
+                               bad_dst.ctypes.data, src.ctypes.data, 1,
+                               None) == ep.EP_ERR_SHAPE
+    big = np.array([0, 17, 17, 17, 17], np.int32)          # psum[E] > capacity 16
+    assert ep.ep_handle_import(h, A16, ep.EP_I64, 8, counts.ctypes.data, big.ctypes.data,
+                               bad_dst.ctypes.data, src.ctypes.data, 1,
+                               None) == ep.EP_ERR_CAPACITY
+    gap_bad = np.array([0, 0, 1, 1, 1], np.int32)          # counts[0]=1 > segment 0
+    assert ep.ep_handle_import(h, A16, ep.EP_I64, 8, counts.ctypes.data, gap_bad.ctypes.data,
+                               bad_dst.ctypes.data, src.ctypes.data, 1,
+                               None) == ep.EP_ERR_SHAPE
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(ep, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(ep, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        ep.lib()

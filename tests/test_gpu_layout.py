@@ -1,0 +1,134 @@
+"""Routing layout on the GPU against the CPU oracle, bit-exact: counts, psum,
+slot index, source metadata, received-token count, invalid-id count and error
+bits.  Covers the five workloads at full size, tile boundaries, ragged and
+empty inputs, invalid ids, duplicates, K > E, the limits (E = 1024, K = 64),
+int32 ids, capacity errors, handle reuse and determinism."""
+import numpy as np
+import pytest
+import torch
+
+import combine_ep_layout_08_amd as ep
+import ep_workloads as W
+import oracle
+from tests import pins
+from tests.gpu_util import assert_layout_equal, gpu_layout, needs_gpu, say
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+
+def _check(idx, E, A, capacity, **kw):
+    lay = oracle.layout(idx, E, A, capacity)
+    h, rc, dst, src = gpu_layout(idx, E, A, capacity, **kw)
+    assert_layout_equal(rc, dst, src, lay)
+    return h, lay
+
+
+@pytest.mark.parametrize("name", list(W.CONFIGS))
+def test_layout_configs(name):
+    cfg = W.CONFIGS[name]
+    idx, _ = W.routing(cfg)
+    cap = ep.ep_capacity_bound(cfg.tokens, cfg.topk, cfg.experts, cfg.alignment)
+    say("layout", name, idx.shape, cfg.experts, cfg.alignment, cap)
+    _, lay = _check(idx, cfg.experts, cfg.alignment, cap)
+    pins.check_layout_invariants(lay, idx, cfg.experts, cfg.alignment, cap)
+
+
+def test_layout_random_small_cases():
+    for n, (T, K, E, A, idx) in enumerate(pins._random_cases(n=200, seed=17)):
+        cap = T * K + (A - 1) * E + A
+        say("layout random", n, T, K, E, A)
+        _check(idx, E, A, cap)
+
+
+@pytest.mark.parametrize("slots", [1, 63, 64, 65, 2047, 2048, 2049, 4096, 4097, 2048 * 7 + 5])
+@pytest.mark.parametrize("K,E", [(8, 256), (1, 1024), (4, 1), (3, 5)])
+def test_layout_tile_boundaries(slots, K, E):
+    T = max(1, slots // K)
+    rng = np.random.default_rng(slots * 31 + K)
+    idx = rng.integers(-1, E, size=(T, K))
+    say("layout tiles", T, K, E)
+    _check(idx, E, 4, T * K + 4 * E)
+
+
+def test_layout_limits_and_skew():
+    rng = np.random.default_rng(5)
+    T, K, E = 3000, 64, 1024
+    idx = rng.integers(-1, E, size=(T, K))
+    say("layout E=1024 K=64")
+    _check(idx, E, 16, T * K + 16 * E)
+    idx = np.zeros((5000, 8), np.int64)          # every slot on expert 0
+    say("layout one hot expert")
+    _check(idx, 256, 128, 5000 * 8 + 128 * 256)
+
+
+def test_layout_special_inputs():
+    say("layout T=0")
+    _check(np.zeros((0, 8), np.int64), 16, 4, 64)
+    say("layout all empty")
+    _check(np.full((300, 8), -1), 16, 4, 64)
+    rng = np.random.default_rng(8)
+    idx = rng.integers(-5, 40, size=(700, 6))    # ids beyond E and below -1
+    say("layout invalid ids")
+    _, lay = _check(idx, 32, 8, 700 * 6 + 8 * 32)
+    assert lay.invalid_count > 0
+    say("layout K > E duplicates")
+    _check(rng.integers(0, 3, size=(333, 7)), 3, 2, 333 * 7 + 6)
+    say("layout int32 ids")
+    _check(rng.integers(-1, 64, size=(999, 8)), 64, 32, 999 * 8 + 32 * 64,
+           idx_dtype=torch.int32)
+
+
+def test_layout_golden_hand_example():
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "layout_hand.json")))
+    idx = np.array(g["topk_idx"])
+    say("layout golden")
+    h, rc, dst, src = gpu_layout(idx, g["num_experts"], g["alignment"], g["capacity_bound"])
+    assert rc["counts"].tolist() == g["counts"]
+    assert rc["psum"].tolist() == g["psum"]
+    assert dst.tolist() == g["dst"]
+    assert src[:g["num_expanded"]].tolist() == g["src_meta"]
+    assert rc["num_recv_tokens"] == g["num_recv_tokens"]
+
+
+def test_layout_capacity_error():
+    idx = np.array([[0, 1], [1, 2], [2, 0]])
+    say("layout capacity error")
+    _check(idx, 3, 4, 11)                        # needs 12 rows
+    _check(idx, 3, 4, 12)
+
+
+def test_layout_handle_reuse_and_determinism():
+    cfg = W.CONFIGS["prefill"]
+    cap = ep.ep_capacity_bound(cfg.tokens, cfg.topk, cfg.experts, cfg.alignment)
+    h = ep.Handle(cfg.tokens, cfg.topk, cfg.experts, cfg.alignment, cap)
+    first = None
+    for rep in range(12):
+        seed = 1003 if rep % 2 == 0 else 2000 + rep
+        idx, _ = W.routing(cfg, seed)
+        ntok = cfg.tokens if rep % 3 else cfg.tokens - 7 * rep   # fewer tokens than max
+        idx = idx[:ntok]
+        say("layout reuse", rep, seed, ntok)
+        lay = oracle.layout(idx, cfg.experts, cfg.alignment, cap)
+        _, rc, dst, src = gpu_layout(idx, cfg.experts, cfg.alignment, cap, handle=h)
+        assert_layout_equal(rc, dst, src, lay)
+        if seed == 1003 and ntok == cfg.tokens:
+            if first is None:
+                first = dst.copy()
+            np.testing.assert_array_equal(dst, first)
+
+
+def test_layout_cumulative_stats():
+    rng = np.random.default_rng(12)
+    E = 40
+    h = ep.Handle(500, 4, E, 8)
+    stats = torch.zeros(E, dtype=torch.int32, device="cuda")
+    total = np.zeros(E, np.int64)
+    for rep in range(3):
+        idx = rng.integers(-1, E, size=(500, 4))
+        say("layout stats", rep)
+        h.layout(torch.from_numpy(idx).cuda(), cumulative_stats=stats)
+        total += oracle.layout(idx, E, 8, h.capacity).counts
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(stats.cpu().numpy(), total)
