@@ -1,0 +1,274 @@
+"""Benchmark: MoE routing layout + dispatch + combine on one MI355X.
+
+One step is one pass of the whole hot path over one batch: ep_layout on
+topk_idx, ep_dispatch of the FP8 token rows (+ fp32 scales) into the
+expert-expanded layout, ep_combine of bf16 expert outputs back to token order
+with fp32 weights.  Default workload: prefill, 4096 tokens x hidden 7168,
+256 experts in 8 groups (group-limited top-4 groups, top-8 experts),
+expert_alignment 128, buffers sized at the worst-case bound (65280 rows).
+Inputs are seeded synthetic data, resident in HBM before timing starts.
+
+Prints one JSON line.  ``value`` is whole-step algorithmic HBM throughput
+(GB/s); per-kernel microseconds, GB/s and fractions of the 8 TB/s HBM peak
+are reported beside it, with the roofline of the dominant kernel (combine)
+and the CPU oracle's throughput on the host as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, AMD published peak
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "combine_prefill_counters.json")
+COMBINE_SRC = os.path.join(ROOT, "combine_ep_layout_08_amd", "csrc", "ep_combine.hip")
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--config", default="prefill", help="workload name (default prefill)")
+    p.add_argument("--no-cpu-baseline", action="store_true",
+                   help="skip the oracle timing (for profiler runs)")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="minimum oracle time for the CPU baseline")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 1 GiB device copy (profiler calibration)")
+    return p.parse_args()
+
+
+def algorithmic_bytes(cfg, V: int, G: int, expanded: int, idx_bytes: int = 8) -> dict:
+    """Bytes the method must move per call (read each input once, write each
+    output once).  V = routed slots, G = alignment-gap rows."""
+    T, K, H, E = cfg.tokens, cfg.topk, cfg.hidden, cfg.experts
+    R = H if cfg.fp8 else 2 * H                 # row bytes of x
+    S = 4 * (H // 128) if cfg.fp8 else 0        # scale bytes per row
+    dispatch = T * (R + S) + V * (R + S) + 4 * T * K
+    if cfg.zero_padding:
+        dispatch += G * (R + S)
+    combine = V * 2 * H + T * 2 * H + 4 * T * K + 4 * T * K
+    if cfg.bias:
+        combine += 2 * E * H + idx_bytes * T * K
+    layout = idx_bytes * T * K + 4 * T * K + 4 * expanded + 4 * (2 * E + 1)
+    return {"layout": layout, "dispatch": dispatch, "combine": combine}
+
+
+def kernel_source_hash() -> str:
+    with open(COMBINE_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per combine launch from committed rocprofv3 counters, if they
+    were taken on the current kernel source; else None."""
+    if not os.path.exists(PROFILE_COUNTERS):
+        return None
+    with open(PROFILE_COUNTERS) as f:
+        c = json.load(f)
+    if c.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return c.get("hbm_bytes_per_launch")
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
+
+
+def ceilings(torch, nbytes=1 << 30, reps=5):
+    """Measured device ceilings: 1 GiB device-to-device copy and fill."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    a.fill_(3)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    out = {}
+    for name, fn, moved in (("copy", lambda: b.copy_(a), 2 * nbytes),
+                            ("fill", lambda: b.fill_(7), nbytes)):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e) / reps
+        out[name + "_GBps"] = round(moved / ms / 1e6, 1)
+    del a, b
+    return out
+
+
+def cpu_baseline(cfg, wl, y_host, min_seconds: float):
+    """Time the CPU oracle (single thread, as it stands) on the same workload:
+    full layout + dispatch + combine of the whole batch, repeated until
+    ``min_seconds`` have passed; median step time."""
+    import numpy as np
+    import oracle
+    import torch
+    cap = oracle.capacity_bound(cfg.tokens, cfg.topk, cfg.experts, cfg.alignment)
+    x_bytes = wl.x.contiguous().view(torch.uint8).cpu().numpy()
+    sf = wl.sf.cpu().numpy() if wl.sf is not None else None
+    out_x = np.empty((cap, x_bytes.shape[1]), np.uint8)
+    out_sf = np.empty((cap, sf.shape[1]), np.float32) if sf is not None else None
+    times = []
+    lay = None
+    t_end = time.perf_counter() + min_seconds
+    while True:
+        t0 = time.perf_counter()
+        lay = oracle.layout(wl.topk_idx, cfg.experts, cfg.alignment, cap)
+        oracle.dispatch(x_bytes, lay, cap, sf=sf, zero_padding=cfg.zero_padding,
+                        out_x=out_x, out_sf=out_sf)
+        oracle.combine(y_host, wl.topk_idx, lay.dst, wl.topk_weights)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() >= t_end and len(times) >= 1:
+            break
+    return statistics.median(times), len(times), lay
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no "
+              "multi-GPU path: the data-parallel share per GPU is the one-GPU workload.",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import combine_ep_layout_08_amd as ep
+    import ep_workloads as W
+
+    cfg = W.CONFIGS[args.config]
+    cap = ep.ep_capacity_bound(cfg.tokens, cfg.topk, cfg.experts, cfg.alignment)
+    wl = W.make(cfg, device="cuda", y_rows=cap)
+    idx = torch.from_numpy(wl.topk_idx).cuda()
+    w = torch.from_numpy(wl.topk_weights).cuda()
+    h = ep.Handle(cfg.tokens, cfg.topk, cfg.experts, cfg.alignment, cap)
+    out_x = torch.empty((cap, cfg.hidden), dtype=wl.x.dtype, device="cuda")
+    out_sf = (torch.empty((cap, cfg.hidden // 128), dtype=torch.float32, device="cuda")
+              if cfg.fp8 else None)
+    out = torch.empty((cfg.tokens, cfg.hidden), dtype=torch.bfloat16, device="cuda")
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        h.layout(idx)
+        if ev is not None:
+            ev[1].record()
+        h.dispatch(wl.x, sf=wl.sf, zero_padding=cfg.zero_padding, out_x=out_x, out_sf=out_sf)
+        if ev is not None:
+            ev[2].record()
+        h.combine(wl.y, topk_weights=w, bias=wl.bias, out=out)
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    rc = h.read_counts()                        # raises on any device error
+    V = int((wl.topk_idx >= 0).sum())
+    G = int(rc["num_expanded"]) - V
+    nbytes = algorithmic_bytes(cfg, V, G, int(rc["num_expanded"]))
+
+    # Timed region: exactly `steps` steps, synchronised on both sides.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {"layout": [], "dispatch": [], "combine": []}
+    for e in evs:
+        per["layout"].append(e[0].elapsed_time(e[1]) * 1e3)
+        per["dispatch"].append(e[1].elapsed_time(e[2]) * 1e3)
+        per["combine"].append(e[2].elapsed_time(e[3]) * 1e3)
+    step_gpu_ms = sum(e[0].elapsed_time(e[3]) for e in evs) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+    kernels = {}
+    for k, v in per.items():
+        us = statistics.mean(v)
+        gbps = nbytes[k] / (us * 1e-6) / 1e9
+        kernels[k] = {"us_mean": round(us, 2), "us_median": round(statistics.median(v), 2),
+                      "us_p10": round(float(np.percentile(v, 10)), 2),
+                      "us_p90": round(float(np.percentile(v, 90)), 2),
+                      "bytes": nbytes[k], "GBps": round(gbps, 1),
+                      "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+    total_bytes = sum(nbytes.values())
+    value = total_bytes / (ms_per_step * 1e-3) / 1e9
+    dc_us = kernels["dispatch"]["us_mean"] + kernels["combine"]["us_mean"]
+    comb = kernels["combine"]
+    roofline = {"bound": "hbm", "achieved": comb["GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(comb["GBps"] / HBM_PEAK_GBPS, 4),
+                "traffic": measured_traffic(), "kernel": "combine",
+                "bytes_per_launch": nbytes["combine"]}
+    ceil = ceilings(torch)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        y_host = wl.y.view(torch.int16).cpu().numpy().view(np.uint16)
+        wl_host = W.Workload(cfg, wl.topk_idx, wl.topk_weights, wl.x.cpu(),
+                             None if wl.sf is None else wl.sf.cpu(), None, None)
+        med, reps, _ = cpu_baseline(cfg, wl_host, y_host, args.cpu_seconds)
+        cpu = {"value": round(total_bytes / med / 1e9, 3), "unit": "GB/s", "cores": 1,
+               "kind": "oracle",
+               "sample": f"whole {cfg.name} batch ({cfg.tokens} tokens): layout + dispatch + "
+                         f"combine, {reps} repetitions, median {med:.3f} s per step, "
+                         "single-threaded C oracle",
+               "ms_per_step": round(med * 1e3, 1)}
+
+    line = {
+        "metric": "dispatch+combine µs/call and HBM GB/s (% of peak) at 4096×7168 top-8",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {cfg.tokens} tokens x hidden {cfg.hidden}, "
+                               f"{cfg.experts} experts, top-{cfg.topk}, "
+                               f"{'FP8 e4m3 + fp32 scales' if cfg.fp8 else 'bf16'} dispatch, "
+                               f"bf16 combine with fp32 weights, alignment {cfg.alignment}",
+                   "tokens": cfg.tokens, "hidden": cfg.hidden, "experts": cfg.experts,
+                   "topk": cfg.topk, "expert_alignment": cfg.alignment, "capacity": cap,
+                   "zero_padding": cfg.zero_padding, "routed_slots": V, "gap_rows": G,
+                   "seed": cfg.seed},
+        "dispatch_plus_combine_us": round(dc_us, 2),
+        "dispatch_plus_combine_GBps": round((nbytes["dispatch"] + nbytes["combine"]) /
+                                            (dc_us * 1e-6) / 1e9, 1),
+        "step_gpu_ms": round(step_gpu_ms, 4),
+        "kernels": kernels,
+        "roofline": roofline,
+        "ceilings": ceil,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
