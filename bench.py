@@ -11,7 +11,9 @@ Inputs are seeded synthetic data, resident in HBM before timing starts.
 Prints one JSON line.  ``value`` is whole-step algorithmic HBM throughput
 (GB/s); per-kernel microseconds, GB/s and fractions of the 8 TB/s HBM peak
 are reported beside it, with the roofline of the dominant kernel (combine)
-and the CPU oracle's throughput on the host as a baseline.
+and the CPU oracle's throughput on the host as a baseline.  Per-call times
+come from HIP events that the library attaches to the calls' own kernel
+dispatches (ep_time_next_call), on the stream the kernels run on.
 """
 from __future__ import annotations
 
@@ -27,8 +29,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, AMD published peak
-PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "combine_prefill_counters.json")
-COMBINE_SRC = os.path.join(ROOT, "combine_ep_layout_08_amd", "csrc", "ep_combine.hip")
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "prefill_hbm_counters.json")
+CSRC = os.path.join(ROOT, "combine_ep_layout_08_amd", "csrc")
+KERNEL_SOURCES = {"combine": ["ep_combine.hip", "ep_internal.h"],
+                  "dispatch": ["ep_dispatch.hip", "ep_internal.h"]}
 
 
 def parse():
@@ -62,21 +66,25 @@ def algorithmic_bytes(cfg, V: int, G: int, expanded: int, idx_bytes: int = 8) ->
     return {"layout": layout, "dispatch": dispatch, "combine": combine}
 
 
-def kernel_source_hash() -> str:
-    with open(COMBINE_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def kernel_source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per combine launch from committed rocprofv3 counters, if they
-    were taken on the current kernel source; else None."""
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counters
+    (FETCH_SIZE + WRITE_SIZE, calibrated on a plain copy), if they were taken
+    on the kernel's current source; else None."""
     if not os.path.exists(PROFILE_COUNTERS):
         return None
     with open(PROFILE_COUNTERS) as f:
-        c = json.load(f)
-    if c.get("kernel_source_sha256_16") != kernel_source_hash():
+        k = json.load(f).get("kernels", {}).get(kernel)
+    if not k or k.get("source_sha256_16") != kernel_source_hash(kernel):
         return None
-    return c.get("hbm_bytes_per_launch")
+    return k.get("hbm_bytes_per_launch")
 
 
 def copy_calibration():
@@ -93,15 +101,18 @@ def copy_calibration():
 
 
 def ceilings(torch, nbytes=1 << 30, reps=5):
-    """Measured device ceilings: 1 GiB device-to-device copy and fill."""
+    """Measured device ceilings: 1 GiB device-to-device copy, fill and a
+    read-only reduction (torch kernels)."""
     a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     b = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     a.fill_(3)
     b.copy_(a)
     torch.cuda.synchronize()
     out = {}
+    a32 = a.view(torch.int32)
     for name, fn, moved in (("copy", lambda: b.copy_(a), 2 * nbytes),
-                            ("fill", lambda: b.fill_(7), nbytes)):
+                            ("fill", lambda: b.fill_(7), nbytes),
+                            ("read", lambda: a32.sum(), nbytes)):
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         s.record()
         for _ in range(reps):
@@ -170,17 +181,16 @@ def main():
     out = torch.empty((cfg.tokens, cfg.hidden), dtype=torch.bfloat16, device="cuda")
 
     def step(ev=None):
+        # ev: six events; each pair is stamped on the kernels of one call.
         if ev is not None:
-            ev[0].record()
+            ep.time_next_call(ev[0], ev[1])
         h.layout(idx)
         if ev is not None:
-            ev[1].record()
+            ep.time_next_call(ev[2], ev[3])
         h.dispatch(wl.x, sf=wl.sf, zero_padding=cfg.zero_padding, out_x=out_x, out_sf=out_sf)
         if ev is not None:
-            ev[2].record()
+            ep.time_next_call(ev[4], ev[5])
         h.combine(wl.y, topk_weights=w, bias=wl.bias, out=out)
-        if ev is not None:
-            ev[3].record()
 
     for _ in range(args.warmup):
         step()
@@ -190,8 +200,12 @@ def main():
     G = int(rc["num_expanded"]) - V
     nbytes = algorithmic_bytes(cfg, V, G, int(rc["num_expanded"]))
 
-    # Timed region: exactly `steps` steps, synchronised on both sides.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # Timed region: exactly `steps` steps, synchronised on both sides.  The
+    # per-call events are created (first record) before the region starts.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    for e6 in evs:
+        for e in e6:
+            e.record()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -201,9 +215,9 @@ def main():
     per = {"layout": [], "dispatch": [], "combine": []}
     for e in evs:
         per["layout"].append(e[0].elapsed_time(e[1]) * 1e3)
-        per["dispatch"].append(e[1].elapsed_time(e[2]) * 1e3)
-        per["combine"].append(e[2].elapsed_time(e[3]) * 1e3)
-    step_gpu_ms = sum(e[0].elapsed_time(e[3]) for e in evs) / args.steps
+        per["dispatch"].append(e[2].elapsed_time(e[3]) * 1e3)
+        per["combine"].append(e[4].elapsed_time(e[5]) * 1e3)
+    step_gpu_ms = sum(e[0].elapsed_time(e[5]) for e in evs) / args.steps
     ms_per_step = wall * 1e3 / args.steps
     kernels = {}
     for k, v in per.items():
@@ -214,13 +228,15 @@ def main():
                       "us_p90": round(float(np.percentile(v, 90)), 2),
                       "bytes": nbytes[k], "GBps": round(gbps, 1),
                       "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+        if k in KERNEL_SOURCES:
+            kernels[k]["traffic"] = measured_traffic(k)
     total_bytes = sum(nbytes.values())
     value = total_bytes / (ms_per_step * 1e-3) / 1e9
     dc_us = kernels["dispatch"]["us_mean"] + kernels["combine"]["us_mean"]
     comb = kernels["combine"]
     roofline = {"bound": "hbm", "achieved": comb["GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(comb["GBps"] / HBM_PEAK_GBPS, 4),
-                "traffic": measured_traffic(), "kernel": "combine",
+                "traffic": measured_traffic("combine"), "kernel": "combine",
                 "bytes_per_launch": nbytes["combine"]}
     ceil = ceilings(torch)
 

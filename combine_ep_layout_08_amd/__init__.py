@@ -25,6 +25,7 @@ __all__ = [
     "EP_I64", "EpError", "ep_handle", "lib", "Handle", "ep_capacity_bound",
     "ep_workspace_bytes", "ep_handle_init", "ep_layout", "ep_handle_read_counts",
     "ep_handle_import", "ep_dispatch", "ep_combine", "ep_status_str", "ep_handle_sizeof",
+    "ep_time_next_call", "time_next_call",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libep.so")
@@ -83,6 +84,7 @@ _SIGNATURES = {
                                    _I64, _I64, _P, _I32, _P]),
     "ep_combine": (ctypes.c_int, [_HP, _P, ctypes.c_int, _I32, _P, _P, _P, _P]),
     "ep_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "ep_time_next_call": (ctypes.c_int, [_P, _P]),
 }
 
 _lib = None
@@ -163,6 +165,20 @@ def ep_combine(h: ep_handle, y_ptr, y_dtype, hidden, w_ptr, bias_ptr, out_ptr, s
 
 def ep_status_str(status: int) -> str:
     return lib().ep_status_str(status).decode()
+
+
+def ep_time_next_call(start_event, stop_event) -> int:
+    """Attach raw HIP events (handles) to the next layout/dispatch/combine."""
+    return lib().ep_time_next_call(start_event, stop_event)
+
+
+def time_next_call(start: "torch.cuda.Event", stop: "torch.cuda.Event") -> None:
+    """Stamp two torch events with the first kernel start and last kernel end
+    of the next layout/dispatch/combine call on this thread."""
+    for e in (start, stop):
+        if e.cuda_event == 0:           # torch creates events lazily on first record
+            e.record()
+    _check(ep_time_next_call(start.cuda_event, stop.cuda_event), "ep_time_next_call")
 
 
 # ---------------------------------------------------------------- torch wrapper

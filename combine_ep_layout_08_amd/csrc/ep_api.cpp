@@ -54,6 +54,15 @@ Carve carve(int32_t max_tokens, int32_t K, int32_t E, int64_t capacity) {
 
 ep_status hip_status(hipError_t e) { return e == hipSuccess ? EP_OK : EP_ERR_HIP; }
 
+// Events for the next layout / dispatch / combine call on this host thread.
+thread_local ep::CallEvents g_next_events;
+
+ep::CallEvents take_events() {
+    const ep::CallEvents ev = g_next_events;
+    g_next_events = ep::CallEvents{};
+    return ev;
+}
+
 bool handle_ready(const ep_handle *h) {
     return h && h->counts && h->psum && h->dst_slot && h->src_meta && h->scalars &&
            h->tile_status;
@@ -112,8 +121,15 @@ ep_status ep_handle_init(ep_handle *h, int32_t max_tokens, int32_t K, int32_t E,
     return EP_OK;
 }
 
+ep_status ep_time_next_call(hipEvent_t start, hipEvent_t stop) {
+    g_next_events.start = start;
+    g_next_events.stop = stop;
+    return EP_OK;
+}
+
 ep_status ep_layout(ep_handle *h, const void *topk_idx, ep_dtype idx_dtype, int32_t num_tokens,
                     int32_t *cumulative_stats, hipStream_t stream) {
+    const ep::CallEvents ev = take_events();
     if (!h) return EP_ERR_NULL;
     if (!handle_ready(h)) return EP_ERR_WORKSPACE;
     if (idx_dtype != EP_I64 && idx_dtype != EP_I32) return EP_ERR_DTYPE;
@@ -136,7 +152,7 @@ ep_status ep_layout(ep_handle *h, const void *topk_idx, ep_dtype idx_dtype, int3
     a.scalars = h->scalars;
     a.tile_status = h->tile_status;
     a.cumulative_stats = cumulative_stats;
-    const hipError_t e = ep::launch_layout(a, stream);
+    const hipError_t e = ep::launch_layout(a, stream, ev);
     if (e != hipSuccess) return EP_ERR_HIP;
     h->num_tokens = num_tokens;
     h->topk_idx = topk_idx;
@@ -222,6 +238,7 @@ ep_status ep_dispatch(const ep_handle *h, const void *x, ep_dtype x_dtype, int32
                       const float *topk_weights, void *out_x, float *out_sf,
                       int64_t out_sf_token_stride, int64_t out_sf_hidden_stride, float *out_w,
                       int32_t zero_padding, hipStream_t stream) {
+    const ep::CallEvents ev = take_events();
     if (!h) return EP_ERR_NULL;
     if (!handle_ready(h)) return EP_ERR_WORKSPACE;
     if (!h->laid_out) return EP_ERR_NOT_LAID_OUT;
@@ -264,12 +281,13 @@ ep_status ep_dispatch(const ep_handle *h, const void *x, ep_dtype x_dtype, int32
     a.out_hs = out_sf_hidden_stride;
     a.out_w = out_w;
     a.zero_padding = zero_padding != 0;
-    return hip_status(ep::launch_dispatch(a, stream));
+    return hip_status(ep::launch_dispatch(a, stream, ev));
 }
 
 ep_status ep_combine(const ep_handle *h, const void *y, ep_dtype y_dtype, int32_t hidden,
                      const float *topk_weights, const void *bias, void *out,
                      hipStream_t stream) {
+    const ep::CallEvents ev = take_events();
     if (!h) return EP_ERR_NULL;
     if (!handle_ready(h)) return EP_ERR_WORKSPACE;
     if (!h->laid_out) return EP_ERR_NOT_LAID_OUT;
@@ -294,7 +312,7 @@ ep_status ep_combine(const ep_handle *h, const void *y, ep_dtype y_dtype, int32_
     a.topk_idx = h->topk_idx;
     a.idx_is_i64 = h->topk_idx_dtype == EP_I64;
     a.out = out;
-    return hip_status(ep::launch_combine(a, stream));
+    return hip_status(ep::launch_combine(a, stream, ev));
 }
 
 const char *ep_status_str(ep_status s) {

@@ -45,12 +45,25 @@ __device__ inline uint32_t bf16_rne(float f) {
 
 // Buffer resource word 3 for gfx9-family raw buffers (32-bit data format).
 constexpr int kRsrcWord3 = 0x00020000;
-// Cache policy bits of gfx94x/gfx950 buffer instructions: bit 1 = NT (stream).
-constexpr int kStreamLoad = 2;
+
+// Launch shape.  Each thread owns kVecsPerThread 16-byte output vectors of one
+// token's row, strided by the block size, so a thread keeps
+// kVecsPerThread * kSlotChunk row loads in flight.
+#ifndef EP_COMBINE_VECS_PER_THREAD
+#define EP_COMBINE_VECS_PER_THREAD 1
+#endif
+// Cache policy of the expert-row loads (gfx94x/gfx950 bits: 0 = sc0, 1 = nt,
+// 4 = sc1); rows are read once, so they stream.
+#ifndef EP_COMBINE_LOAD_POLICY
+#define EP_COMBINE_LOAD_POLICY 2
+#endif
+constexpr int kVecsPerThread = EP_COMBINE_VECS_PER_THREAD;
+constexpr int kLoadPolicy = EP_COMBINE_LOAD_POLICY;
 
 // Range-checked row view: a load at a byte offset >= `bytes` returns zero and
 // touches no memory.  Empty slots get bytes = 0, so their loads are free and
-// every slot of a chunk can be loaded without a branch.
+// every slot of a chunk can be loaded without a branch; the same check makes
+// the columns past the row's end safe to load.
 __device__ inline __amdgpu_buffer_rsrc_t row_rsrc(const void *base, int64_t row, int32_t bytes,
                                                   bool valid) {
     const char *p = static_cast<const char *>(base) + (valid ? row * bytes : 0);
@@ -63,21 +76,27 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int blocks_
 #pragma clang fp contract(off)
     if (a.scalars[EP_SCALAR_ERROR_BITS] & EP_ERRBIT_FATAL) return;
     const int64_t t = blockIdx.x / blocks_per_token;
-    const int64_t v = static_cast<int64_t>(blockIdx.x % blocks_per_token) * blockDim.x + threadIdx.x;
-    if (v >= a.row_vecs) return;
+    const int64_t v0 = static_cast<int64_t>(blockIdx.x % blocks_per_token) * blockDim.x *
+                           kVecsPerThread + threadIdx.x;
+    if (v0 >= a.row_vecs) return;
     const int K = a.num_topk;
     const int32_t row_bytes = static_cast<int32_t>(a.row_vecs * 16);
-    const int32_t col = static_cast<int32_t>(v * 16);
+    int32_t col[kVecsPerThread];
+#pragma unroll
+    for (int u = 0; u < kVecsPerThread; ++u)
+        col[u] = static_cast<int32_t>((v0 + static_cast<int64_t>(u) * blockDim.x) * 16);
     const IdxT *idx = static_cast<const IdxT *>(a.topk_idx);
     const int32_t *dst = a.dst + t * K;
 
-    float acc[8];
+    float acc[kVecsPerThread][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+    for (int u = 0; u < kVecsPerThread; ++u)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[u][i] = 0.0f;
 
     for (int k0 = 0; k0 < K; k0 += kSlotChunk) {
         int32_t r[kSlotChunk];
-        u32x4 d[kSlotChunk], bb[kSlotChunk];
+        u32x4 d[kSlotChunk][kVecsPerThread], bb[kSlotChunk][kVecsPerThread];
 #pragma unroll
         for (int j = 0; j < kSlotChunk; ++j) {
             r[j] = (k0 + j < K) ? dst[k0 + j] : -1;
@@ -87,76 +106,90 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int blocks_
 #pragma unroll
         for (int j = 0; j < kSlotChunk; ++j) {
             const bool ok = r[j] >= 0;
-            d[j] = __builtin_amdgcn_raw_buffer_load_b128(row_rsrc(a.y, r[j], row_bytes, ok), col,
-                                                         0, kStreamLoad);
+            const __amdgpu_buffer_rsrc_t ry = row_rsrc(a.y, r[j], row_bytes, ok);
+#pragma unroll
+            for (int u = 0; u < kVecsPerThread; ++u)
+                d[j][u] = __builtin_amdgcn_raw_buffer_load_b128(ry, col[u], 0, kLoadPolicy);
             if (HAS_BIAS) {
                 const int64_t e = ok ? static_cast<int64_t>(idx[t * K + k0 + j]) : 0;
                 const bool e_ok = ok && e >= 0 && e < a.num_experts;
-                bb[j] = __builtin_amdgcn_raw_buffer_load_b128(
-                    row_rsrc(a.bias, e, row_bytes, e_ok), col, 0, 0);
+                const __amdgpu_buffer_rsrc_t rb = row_rsrc(a.bias, e, row_bytes, e_ok);
+#pragma unroll
+                for (int u = 0; u < kVecsPerThread; ++u)
+                    bb[j][u] = __builtin_amdgcn_raw_buffer_load_b128(rb, col[u], 0, 0);
             }
         }
         // Accumulate in slot order.
 #pragma unroll
         for (int j = 0; j < kSlotChunk; ++j) {
             if (r[j] < 0) continue;
-            float f[8];
-            unpack_bf16x8(d[j], f);
-            if (HAS_BIAS) {
-                float b[8];
-                unpack_bf16x8(bb[j], b);
+            const float wk = HAS_W ? a.w[t * K + k0 + j] : 1.0f;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) f[i] = f[i] + b[i];
+            for (int u = 0; u < kVecsPerThread; ++u) {
+                float f[8];
+                unpack_bf16x8(d[j][u], f);
+                if (HAS_BIAS) {
+                    float b[8];
+                    unpack_bf16x8(bb[j][u], b);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) f[i] = f[i] + b[i];
+                }
+                if (HAS_W) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) f[i] = wk * f[i];
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[u][i] = acc[u][i] + f[i];
             }
-            if (HAS_W) {
-                const float wk = a.w[t * K + k0 + j];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) f[i] = wk * f[i];
-            }
-#pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i] = acc[i] + f[i];
         }
     }
-    u32x4 o;
-    o.x = bf16_rne(acc[0]) | (bf16_rne(acc[1]) << 16);
-    o.y = bf16_rne(acc[2]) | (bf16_rne(acc[3]) << 16);
-    o.z = bf16_rne(acc[4]) | (bf16_rne(acc[5]) << 16);
-    o.w = bf16_rne(acc[6]) | (bf16_rne(acc[7]) << 16);
-    __builtin_nontemporal_store(o, static_cast<u32x4 *>(a.out) + t * a.row_vecs + v);
+    u32x4 *out = static_cast<u32x4 *>(a.out) + t * a.row_vecs;
+#pragma unroll
+    for (int u = 0; u < kVecsPerThread; ++u) {
+        const int64_t v = v0 + static_cast<int64_t>(u) * blockDim.x;
+        if (v >= a.row_vecs) break;
+        u32x4 o;
+        o.x = bf16_rne(acc[u][0]) | (bf16_rne(acc[u][1]) << 16);
+        o.y = bf16_rne(acc[u][2]) | (bf16_rne(acc[u][3]) << 16);
+        o.z = bf16_rne(acc[u][4]) | (bf16_rne(acc[u][5]) << 16);
+        o.w = bf16_rne(acc[u][6]) | (bf16_rne(acc[u][7]) << 16);
+        __builtin_nontemporal_store(o, out + v);
+    }
 }
 
 template <bool HAS_BIAS, bool HAS_W>
-hipError_t launch_bw(const CombineArgs &a, hipStream_t stream) {
+hipError_t launch_bw(const CombineArgs &a, hipStream_t stream, CallEvents ev) {
     // Block size among 256 / 128 / 64 threads that wastes the fewest lanes
     // on the row's vector count (ties go to the larger block).
     int threads = 256;
     int64_t best = -1;
     for (int b : {256, 128, 64}) {
-        const int64_t waste = (a.row_vecs + b - 1) / b * b - a.row_vecs;
+        const int64_t span = static_cast<int64_t>(b) * kVecsPerThread;
+        const int64_t waste = (a.row_vecs + span - 1) / span * span - a.row_vecs;
         if (best < 0 || waste < best) {
             best = waste;
             threads = b;
         }
     }
-    const int bpt = static_cast<int>((a.row_vecs + threads - 1) / threads);
+    const int64_t span = static_cast<int64_t>(threads) * kVecsPerThread;
+    const int bpt = static_cast<int>((a.row_vecs + span - 1) / span);
     const int64_t blocks = static_cast<int64_t>(a.num_tokens) * bpt;
     if (blocks == 0) return hipSuccess;
     if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
+    const dim3 grid(static_cast<unsigned>(blocks)), block(threads);
     if (a.idx_is_i64)
-        combine_kernel<HAS_BIAS, HAS_W, int64_t>
-            <<<static_cast<unsigned>(blocks), threads, 0, stream>>>(a, bpt);
-    else
-        combine_kernel<HAS_BIAS, HAS_W, int32_t>
-            <<<static_cast<unsigned>(blocks), threads, 0, stream>>>(a, bpt);
-    return hipGetLastError();
+        return launch_kernel(combine_kernel<HAS_BIAS, HAS_W, int64_t>, grid, block, stream,
+                             ev.start, ev.stop, a, bpt);
+    return launch_kernel(combine_kernel<HAS_BIAS, HAS_W, int32_t>, grid, block, stream,
+                         ev.start, ev.stop, a, bpt);
 }
 
 }  // namespace
 
-hipError_t launch_combine(const CombineArgs &a, hipStream_t stream) {
+hipError_t launch_combine(const CombineArgs &a, hipStream_t stream, CallEvents ev) {
     if (a.bias)
-        return a.w ? launch_bw<true, true>(a, stream) : launch_bw<true, false>(a, stream);
-    return a.w ? launch_bw<false, true>(a, stream) : launch_bw<false, false>(a, stream);
+        return a.w ? launch_bw<true, true>(a, stream, ev) : launch_bw<true, false>(a, stream, ev);
+    return a.w ? launch_bw<false, true>(a, stream, ev) : launch_bw<false, false>(a, stream, ev);
 }
 
 }  // namespace ep

@@ -21,8 +21,28 @@ namespace ep {
 namespace {
 
 constexpr int kDispatchThreads = 256;
-constexpr int kTokensPerBlock = kDispatchThreads / 64;
-constexpr int kGapRowsPerBlock = kDispatchThreads / 64;
+constexpr int kWavesPerBlock = kDispatchThreads / 64;
+constexpr int kGapRowsPerBlock = kWavesPerBlock;
+
+// Launch shape: waves that share one token's row (each copies a contiguous
+// part of it), and whether row stores are non-temporal (streamed past the
+// caches).
+#ifndef EP_DISPATCH_WAVES_PER_TOKEN
+#define EP_DISPATCH_WAVES_PER_TOKEN 1
+#endif
+#ifndef EP_DISPATCH_NT_STORE
+#define EP_DISPATCH_NT_STORE 0
+#endif
+constexpr int kWavesPerToken = EP_DISPATCH_WAVES_PER_TOKEN;
+constexpr int kTokensPerBlock = kWavesPerBlock / kWavesPerToken;
+static_assert(kWavesPerBlock % kWavesPerToken == 0, "waves per token must divide 4");
+
+__device__ inline void store_row_vec(u32x4 *p, u32x4 v) {
+    if (EP_DISPATCH_NT_STORE)
+        __builtin_nontemporal_store(v, p);
+    else
+        *p = v;
+}
 
 template <int VPL>
 __global__ __launch_bounds__(kDispatchThreads) void dispatch_kernel(DispatchArgs a,
@@ -34,40 +54,47 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_kernel(DispatchArgs
     u32x4 *out = static_cast<u32x4 *>(a.out_x);
 
     if (static_cast<int>(blockIdx.x) < token_blocks) {
-        const int64_t t = static_cast<int64_t>(blockIdx.x) * kTokensPerBlock + wave;
+        const int64_t t = static_cast<int64_t>(blockIdx.x) * kTokensPerBlock +
+                          wave / kWavesPerToken;
+        const int part = wave % kWavesPerToken;
         if (t >= a.num_tokens) return;
         const int K = a.num_topk;
         // Rows outside [0, capacity) are skipped, so no layout content can
         // send a store out of the output buffers.
         int32_t my_dst = lane < K ? a.dst[t * K + lane] : -1;
         if (my_dst >= a.capacity) my_dst = -1;
-        if (a.out_w && my_dst >= 0) a.out_w[my_dst] = a.w ? a.w[t * K + lane] : 1.0f;
-        if (a.num_sf) {
-            // A token's scale factors (at most 64 * kMaxSfPerLane) go to
-            // registers once and are stored for every valid slot.
-            float sfv[kMaxSfPerLane];
-#pragma unroll
-            for (int q = 0; q < kMaxSfPerLane; ++q) {
-                const int j = lane + 64 * q;
-                sfv[q] = j < a.num_sf ? a.sf[t * a.sf_ts + j * a.sf_hs] : 0.0f;
-            }
-            for (int k = 0; k < K; ++k) {
-                const int32_t r = __builtin_amdgcn_readlane(my_dst, k);
-                if (r < 0) continue;
+        if (part == 0) {
+            if (a.out_w && my_dst >= 0) a.out_w[my_dst] = a.w ? a.w[t * K + lane] : 1.0f;
+            if (a.num_sf) {
+                // A token's scale factors (at most 64 * kMaxSfPerLane) go to
+                // registers once and are stored for every valid slot.
+                float sfv[kMaxSfPerLane];
 #pragma unroll
                 for (int q = 0; q < kMaxSfPerLane; ++q) {
                     const int j = lane + 64 * q;
-                    if (j < a.num_sf) a.out_sf[r * a.out_ts + j * a.out_hs] = sfv[q];
+                    sfv[q] = j < a.num_sf ? a.sf[t * a.sf_ts + j * a.sf_hs] : 0.0f;
+                }
+                for (int k = 0; k < K; ++k) {
+                    const int32_t r = __builtin_amdgcn_readlane(my_dst, k);
+                    if (r < 0) continue;
+#pragma unroll
+                    for (int q = 0; q < kMaxSfPerLane; ++q) {
+                        const int j = lane + 64 * q;
+                        if (j < a.num_sf) a.out_sf[r * a.out_ts + j * a.out_hs] = sfv[q];
+                    }
                 }
             }
         }
+        const int64_t per_part = (V + kWavesPerToken - 1) / kWavesPerToken;
+        const int64_t p0 = part * per_part;
+        const int64_t p1 = p0 + per_part < V ? p0 + per_part : V;
         const u32x4 *src = static_cast<const u32x4 *>(a.x) + t * V;
-        for (int64_t c0 = 0; c0 < V; c0 += 64 * VPL) {
+        for (int64_t c0 = p0; c0 < p1; c0 += 64 * VPL) {
             u32x4 v[VPL];
 #pragma unroll
             for (int q = 0; q < VPL; ++q) {
                 const int64_t c = c0 + q * 64 + lane;
-                if (c < V) v[q] = src[c];
+                if (c < p1) v[q] = src[c];
             }
             for (int k = 0; k < K; ++k) {
                 const int32_t r = __builtin_amdgcn_readlane(my_dst, k);
@@ -76,7 +103,7 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_kernel(DispatchArgs
 #pragma unroll
                 for (int q = 0; q < VPL; ++q) {
                     const int64_t c = c0 + q * 64 + lane;
-                    if (c < V) __builtin_nontemporal_store(v[q], d + c);
+                    if (c < p1) store_row_vec(d + c, v[q]);
                 }
             }
         }
@@ -91,13 +118,13 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_kernel(DispatchArgs
     if (r >= a.psum[e + 1] || r >= a.capacity) return;
     const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
     u32x4 *d = out + r * V;
-    for (int64_t c = lane; c < V; c += 64) __builtin_nontemporal_store(zero, d + c);
+    for (int64_t c = lane; c < V; c += 64) store_row_vec(d + c, zero);
     for (int j = lane; j < a.num_sf; j += 64) a.out_sf[r * a.out_ts + j * a.out_hs] = 0.0f;
     if (a.out_w && lane == 0) a.out_w[r] = 0.0f;
 }
 
 template <int VPL>
-hipError_t launch_vpl(const DispatchArgs &a, hipStream_t stream) {
+hipError_t launch_vpl(const DispatchArgs &a, hipStream_t stream, CallEvents ev) {
     const int token_blocks = (a.num_tokens + kTokensPerBlock - 1) / kTokensPerBlock;
     int gap_chunks = 0;
     if (a.zero_padding && a.alignment > 1)
@@ -106,20 +133,21 @@ hipError_t launch_vpl(const DispatchArgs &a, hipStream_t stream) {
                            static_cast<int64_t>(gap_chunks) * a.num_experts;
     if (blocks == 0) return hipSuccess;
     if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
-    dispatch_kernel<VPL><<<static_cast<unsigned>(blocks), kDispatchThreads, 0, stream>>>(
-        a, token_blocks, gap_chunks > 0 ? gap_chunks : 1);
-    return hipGetLastError();
+    return launch_kernel(dispatch_kernel<VPL>, dim3(static_cast<unsigned>(blocks)),
+                         dim3(kDispatchThreads), stream, ev.start, ev.stop, a, token_blocks,
+                         gap_chunks > 0 ? gap_chunks : 1);
 }
 
 }  // namespace
 
-hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t stream) {
-    const int64_t per_lane = (a.row_vecs + 63) / 64;
-    if (per_lane <= 1) return launch_vpl<1>(a, stream);
-    if (per_lane <= 2) return launch_vpl<2>(a, stream);
-    if (per_lane <= 4) return launch_vpl<4>(a, stream);
-    if (per_lane <= 8) return launch_vpl<8>(a, stream);
-    return launch_vpl<16>(a, stream);
+hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t stream, CallEvents ev) {
+    const int64_t per_wave = (a.row_vecs + kWavesPerToken - 1) / kWavesPerToken;
+    const int64_t per_lane = (per_wave + 63) / 64;
+    if (per_lane <= 1) return launch_vpl<1>(a, stream, ev);
+    if (per_lane <= 2) return launch_vpl<2>(a, stream, ev);
+    if (per_lane <= 4) return launch_vpl<4>(a, stream, ev);
+    if (per_lane <= 8) return launch_vpl<8>(a, stream, ev);
+    return launch_vpl<16>(a, stream, ev);
 }
 
 }  // namespace ep

@@ -2,6 +2,7 @@
 // Not installed; the public interface is include/ep.h.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -26,6 +27,25 @@ inline int64_t layout_tiles(int64_t num_slots) {
     int64_t t = (num_slots + kTileSlots - 1) / kTileSlots;
     return t < 1 ? 1 : t;
 }
+
+// Launch with optional events attached to the kernel dispatch itself
+// (AMD's hipExtLaunchKernel): `start` is stamped when the kernel begins and
+// `stop` when it ends, so a timed interval holds kernel execution only.
+template <typename... KArgs, typename... Args>
+hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t stream,
+                         hipEvent_t start, hipEvent_t stop, Args... args) {
+    if (start || stop)
+        hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, start, stop, 0u, args...);
+    else
+        kernel<<<grid, block, 0, stream>>>(args...);
+    return hipGetLastError();
+}
+
+// Events handed to the next entry point by ep_time_next_call (null = none).
+struct CallEvents {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
 
 struct LayoutArgs {
     const void *topk_idx;
@@ -69,8 +89,8 @@ struct CombineArgs {
 
 hipError_t launch_handle_clear(int32_t *scalars, uint64_t *tile_status,
                                int64_t status_words, hipStream_t stream);
-hipError_t launch_layout(const LayoutArgs &a, hipStream_t stream);
-hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t stream);
-hipError_t launch_combine(const CombineArgs &a, hipStream_t stream);
+hipError_t launch_layout(const LayoutArgs &a, hipStream_t stream, CallEvents ev);
+hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t stream, CallEvents ev);
+hipError_t launch_combine(const CombineArgs &a, hipStream_t stream, CallEvents ev);
 
 }  // namespace ep

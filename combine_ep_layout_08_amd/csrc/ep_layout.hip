@@ -309,19 +309,26 @@ hipError_t launch_handle_clear(int32_t *scalars, uint64_t *tile_status, int64_t 
     return hipGetLastError();
 }
 
-hipError_t launch_layout(const LayoutArgs &a, hipStream_t stream) {
+hipError_t launch_layout(const LayoutArgs &a, hipStream_t stream, CallEvents ev) {
     const int64_t num_slots = static_cast<int64_t>(a.num_tokens) * a.num_topk;
     const int tiles = static_cast<int>(layout_tiles(num_slots));
     const int token_blocks = (a.num_tokens + 255) / 256;
-    const unsigned fin_blocks = static_cast<unsigned>(token_blocks + a.num_experts);
+    const dim3 fin_blocks(static_cast<unsigned>(token_blocks + a.num_experts));
+    hipError_t e;
     if (a.idx_is_i64) {
-        layout_scan_kernel<int64_t><<<tiles, kLayoutThreads, 0, stream>>>(a, num_slots, tiles);
-        layout_finalize_kernel<int64_t><<<fin_blocks, 256, 0, stream>>>(a, token_blocks);
+        e = launch_kernel(layout_scan_kernel<int64_t>, dim3(tiles), dim3(kLayoutThreads), stream,
+                          ev.start, nullptr, a, num_slots, tiles);
+        if (e == hipSuccess)
+            e = launch_kernel(layout_finalize_kernel<int64_t>, fin_blocks, dim3(256), stream,
+                              nullptr, ev.stop, a, token_blocks);
     } else {
-        layout_scan_kernel<int32_t><<<tiles, kLayoutThreads, 0, stream>>>(a, num_slots, tiles);
-        layout_finalize_kernel<int32_t><<<fin_blocks, 256, 0, stream>>>(a, token_blocks);
+        e = launch_kernel(layout_scan_kernel<int32_t>, dim3(tiles), dim3(kLayoutThreads), stream,
+                          ev.start, nullptr, a, num_slots, tiles);
+        if (e == hipSuccess)
+            e = launch_kernel(layout_finalize_kernel<int32_t>, fin_blocks, dim3(256), stream,
+                              nullptr, ev.stop, a, token_blocks);
     }
-    return hipGetLastError();
+    return e;
 }
 
 }  // namespace ep

@@ -241,6 +241,19 @@ ep_status ep_combine(const ep_handle *h, const void *y, ep_dtype y_dtype,
                      int32_t hidden, const float *topk_weights,
                      const void *bias, void *out, hipStream_t stream);
 
+/*
+ * Profiling hook (the tracing the pages leave to CUDA events, [Ch8 §8.2]):
+ * the next ep_layout, ep_dispatch or ep_combine call made on this host
+ * thread stamps `start` when its first kernel begins and `stop` when its
+ * last kernel ends.  The events ride on the kernel dispatches themselves
+ * (AMD's hipExtLaunchKernel), so the interval holds kernel execution only,
+ * not queueing or launch latency.  Either may be NULL; both must have been
+ * created by the caller on the current device.  The hook applies to exactly
+ * one call (consumed even if that call fails validation); a call that
+ * launches nothing stamps nothing.
+ */
+ep_status ep_time_next_call(hipEvent_t start, hipEvent_t stop);
+
 /* Static text for a status code. */
 const char *ep_status_str(ep_status s);
 
