@@ -45,6 +45,11 @@ def parse():
                    help="skip the oracle timing (for profiler runs)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="minimum oracle time for the CPU baseline")
+    p.add_argument("--cold-reps", type=int, default=30,
+                   help="calls per kernel in the cold-cache phase after the timed steps (0 = skip)")
+    p.add_argument("--flush", action="store_true",
+                   help="read a 1 GiB scratch buffer before every call (outside the per-call "
+                        "events) so each kernel starts with cold L2 and MALL")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device copy (profiler calibration)")
     return p.parse_args()
@@ -180,14 +185,25 @@ def main():
               if cfg.fp8 else None)
     out = torch.empty((cfg.tokens, cfg.hidden), dtype=torch.bfloat16, device="cuda")
 
+    # Cache flush by reading 1 GiB (four times the 256 MB MALL): the caches
+    # end up full of clean lines, so the next kernel pays no write-back.
+    scratch = (torch.ones(1 << 28, dtype=torch.int32, device="cuda") if args.flush else None)
+
+    def flush():
+        if scratch is not None:
+            scratch.sum()
+
     def step(ev=None):
         # ev: six events; each pair is stamped on the kernels of one call.
+        flush()
         if ev is not None:
             ep.time_next_call(ev[0], ev[1])
         h.layout(idx)
+        flush()
         if ev is not None:
             ep.time_next_call(ev[2], ev[3])
         h.dispatch(wl.x, sf=wl.sf, zero_padding=cfg.zero_padding, out_x=out_x, out_sf=out_sf)
+        flush()
         if ev is not None:
             ep.time_next_call(ev[4], ev[5])
         h.combine(wl.y, topk_weights=w, bias=wl.bias, out=out)
@@ -230,7 +246,38 @@ def main():
                       "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
         if k in KERNEL_SOURCES:
             kernels[k]["traffic"] = measured_traffic(k)
+    # Cold-cache phase (after the timed region): each call runs right after a
+    # 1 GiB read that leaves L2 and the MALL full of unrelated clean lines, so
+    # its inputs come from HBM; timed by the events on its own kernels.
+    kernels_cold = None
+    if args.cold_reps > 0:
+        big = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
+        calls = {"layout": lambda: h.layout(idx),
+                 "dispatch": lambda: h.dispatch(wl.x, sf=wl.sf, zero_padding=cfg.zero_padding,
+                                                out_x=out_x, out_sf=out_sf),
+                 "combine": lambda: h.combine(wl.y, topk_weights=w, bias=wl.bias, out=out)}
+        kernels_cold = {}
+        for name, fn in calls.items():
+            pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                     for _ in range(args.cold_reps)]
+            for e0, e1 in pairs:
+                e0.record()
+                e1.record()
+            for e0, e1 in pairs:
+                big.sum()
+                ep.time_next_call(e0, e1)
+                fn()
+            torch.cuda.synchronize()
+            us = statistics.mean(e0.elapsed_time(e1) * 1e3 for e0, e1 in pairs)
+            gbps = nbytes[name] / (us * 1e-6) / 1e9
+            kernels_cold[name] = {"us_mean": round(us, 2), "GBps": round(gbps, 1),
+                                  "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+        del big
+
     total_bytes = sum(nbytes.values())
+    if args.flush:
+        # The wall time also holds the cache flushes; use the calls' own time.
+        ms_per_step = sum(kernels[k]["us_mean"] for k in kernels) / 1e3
     value = total_bytes / (ms_per_step * 1e-3) / 1e9
     dc_us = kernels["dispatch"]["us_mean"] + kernels["combine"]["us_mean"]
     comb = kernels["combine"]
@@ -238,6 +285,9 @@ def main():
                 "frac": round(comb["GBps"] / HBM_PEAK_GBPS, 4),
                 "traffic": measured_traffic("combine"), "kernel": "combine",
                 "bytes_per_launch": nbytes["combine"]}
+    if kernels_cold:
+        roofline["achieved_cold_cache"] = kernels_cold["combine"]["GBps"]
+        roofline["frac_cold_cache"] = kernels_cold["combine"]["frac_hbm_peak"]
     ceil = ceilings(torch)
 
     cpu = None
@@ -278,7 +328,9 @@ def main():
         "dispatch_plus_combine_GBps": round((nbytes["dispatch"] + nbytes["combine"]) /
                                             (dc_us * 1e-6) / 1e9, 1),
         "step_gpu_ms": round(step_gpu_ms, 4),
+        "cache_flush_between_calls": bool(args.flush),
         "kernels": kernels,
+        "kernels_cold_cache": kernels_cold,
         "roofline": roofline,
         "ceilings": ceil,
         "cpu_baseline": cpu,

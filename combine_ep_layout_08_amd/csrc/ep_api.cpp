@@ -35,7 +35,7 @@ ep_status limits(int32_t max_tokens, int32_t K, int32_t E, int64_t capacity) {
 Carve carve(int32_t max_tokens, int32_t K, int32_t E, int64_t capacity) {
     Carve c{};
     const int64_t slots = static_cast<int64_t>(max_tokens) * K;
-    c.tiles = ep::layout_tiles(slots);
+    c.tiles = ep::layout_tiles(max_tokens, K);
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t at = off;
@@ -47,7 +47,7 @@ Carve carve(int32_t max_tokens, int32_t K, int32_t E, int64_t capacity) {
     c.dst = take(sizeof(int32_t) * static_cast<size_t>(slots));
     c.src_meta = take(sizeof(int32_t) * static_cast<size_t>(capacity));
     c.scalars = take(sizeof(int32_t) * EP_NUM_SCALARS);
-    c.status = take(sizeof(uint64_t) * static_cast<size_t>(c.tiles) * static_cast<size_t>(E + 1));
+    c.status = take(sizeof(uint64_t) * static_cast<size_t>(c.tiles) * static_cast<size_t>(E + 2));
     c.total = off;
     return c;
 }
@@ -115,7 +115,7 @@ ep_status ep_handle_init(ep_handle *h, int32_t max_tokens, int32_t K, int32_t E,
     n.topk_idx_dtype = EP_I64;
     n.status_tiles = static_cast<int32_t>(c.tiles);
     const hipError_t e = ep::launch_handle_clear(n.scalars, n.tile_status,
-                                                 c.tiles * static_cast<int64_t>(E + 1), stream);
+                                                 c.tiles * static_cast<int64_t>(E + 2), stream);
     if (e != hipSuccess) return EP_ERR_HIP;
     *h = n;
     return EP_OK;

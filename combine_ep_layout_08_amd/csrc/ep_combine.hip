@@ -12,11 +12,11 @@
 // in binary32 from +0.0, every add and multiply rounded separately (no
 // contraction), a missing weight meaning the product is skipped.
 //
-// Each thread owns one 16-byte column vector (8 bf16) of one token's output
-// row.  The token's destination rows are block-uniform (scalar loads).  For
-// each chunk of up to 8 slots, all rows' vectors are loaded before any is
-// accumulated, so a thread keeps 8 x 16 bytes in flight; the accumulation
-// itself runs in slot order.
+// A block owns whole tokens; each thread owns 16-byte column vectors (8 bf16)
+// of the token's output row.  The token's destination rows are block-uniform
+// (scalar loads).  For each chunk of up to 8 slots, all rows' vectors are
+// loaded before any is accumulated; the accumulation itself runs in slot
+// order.
 #include "ep_internal.h"
 #include "../../include/ep.h"
 
@@ -46,9 +46,16 @@ __device__ inline uint32_t bf16_rne(float f) {
 // Buffer resource word 3 for gfx9-family raw buffers (32-bit data format).
 constexpr int kRsrcWord3 = 0x00020000;
 
-// Launch shape.  Each thread owns kVecsPerThread 16-byte output vectors of one
-// token's row, strided by the block size, so a thread keeps
-// kVecsPerThread * kSlotChunk row loads in flight.
+// Launch shape.  A work unit is one group of a token's columns: blockDim *
+// kVecsPerThread 16-byte vectors of its output row, one block per unit, the
+// block size (256, 128 or 64 threads) picked to tile the row with the fewest
+// idle lanes.  Each thread keeps kVecsPerThread * kSlotChunk row loads in
+// flight.  Measured on MI355X, many short blocks beat a persistent grid that
+// walks whole rows (89 us vs 102-120 us on the prefill workload), so the
+// persistent form is off by default (EP_COMBINE_BLOCKS_PER_CU > 0 enables it).
+#ifndef EP_COMBINE_BLOCKS_PER_CU
+#define EP_COMBINE_BLOCKS_PER_CU 0
+#endif
 #ifndef EP_COMBINE_VECS_PER_THREAD
 #define EP_COMBINE_VECS_PER_THREAD 1
 #endif
@@ -57,6 +64,16 @@ constexpr int kRsrcWord3 = 0x00020000;
 #ifndef EP_COMBINE_LOAD_POLICY
 #define EP_COMBINE_LOAD_POLICY 2
 #endif
+// Output stores are non-temporal unless this is 0.
+#ifndef EP_COMBINE_NT_STORE
+#define EP_COMBINE_NT_STORE 1
+#endif
+// Block size: 0 = pick 256 / 128 / 64 to tile the row, else this many threads.
+#ifndef EP_COMBINE_THREADS
+#define EP_COMBINE_THREADS 0
+#endif
+constexpr int kMaxCombineThreads = 256;
+constexpr int kBlocksPerCu = EP_COMBINE_BLOCKS_PER_CU;
 constexpr int kVecsPerThread = EP_COMBINE_VECS_PER_THREAD;
 constexpr int kLoadPolicy = EP_COMBINE_LOAD_POLICY;
 
@@ -71,14 +88,11 @@ __device__ inline __amdgpu_buffer_rsrc_t row_rsrc(const void *base, int64_t row,
                                              kRsrcWord3);
 }
 
+// One group of columns of one token: loads of every slot first, then the
+// slot-order binary32 accumulation, then the bf16 store.
 template <bool HAS_BIAS, bool HAS_W, typename IdxT>
-__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int blocks_per_token) {
+__device__ inline void combine_columns(const CombineArgs &a, int64_t t, int64_t v0) {
 #pragma clang fp contract(off)
-    if (a.scalars[EP_SCALAR_ERROR_BITS] & EP_ERRBIT_FATAL) return;
-    const int64_t t = blockIdx.x / blocks_per_token;
-    const int64_t v0 = static_cast<int64_t>(blockIdx.x % blocks_per_token) * blockDim.x *
-                           kVecsPerThread + threadIdx.x;
-    if (v0 >= a.row_vecs) return;
     const int K = a.num_topk;
     const int32_t row_bytes = static_cast<int32_t>(a.row_vecs * 16);
     int32_t col[kVecsPerThread];
@@ -153,7 +167,30 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a, int blocks_
         o.y = bf16_rne(acc[u][2]) | (bf16_rne(acc[u][3]) << 16);
         o.z = bf16_rne(acc[u][4]) | (bf16_rne(acc[u][5]) << 16);
         o.w = bf16_rne(acc[u][6]) | (bf16_rne(acc[u][7]) << 16);
-        __builtin_nontemporal_store(o, out + v);
+        if (EP_COMBINE_NT_STORE)
+            __builtin_nontemporal_store(o, out + v);
+        else
+            out[v] = o;
+    }
+}
+
+template <bool HAS_BIAS, bool HAS_W, typename IdxT>
+__global__ __launch_bounds__(kMaxCombineThreads) void combine_kernel(CombineArgs a,
+                                                                    int groups_per_token) {
+    if (a.scalars[EP_SCALAR_ERROR_BITS] & EP_ERRBIT_FATAL) return;
+    const int64_t group = static_cast<int64_t>(blockDim.x) * kVecsPerThread;
+    if (kBlocksPerCu == 0) {
+        // One unit per block, straight-line (measurably faster than the loop).
+        const int64_t t = blockIdx.x / groups_per_token;
+        const int64_t v0 = (blockIdx.x % groups_per_token) * group + threadIdx.x;
+        if (v0 < a.row_vecs) combine_columns<HAS_BIAS, HAS_W, IdxT>(a, t, v0);
+        return;
+    }
+    const int64_t units = static_cast<int64_t>(a.num_tokens) * groups_per_token;
+    for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
+        const int64_t t = u / groups_per_token;
+        const int64_t v0 = (u % groups_per_token) * group + threadIdx.x;
+        if (v0 < a.row_vecs) combine_columns<HAS_BIAS, HAS_W, IdxT>(a, t, v0);
     }
 }
 
@@ -161,7 +198,7 @@ template <bool HAS_BIAS, bool HAS_W>
 hipError_t launch_bw(const CombineArgs &a, hipStream_t stream, CallEvents ev) {
     // Block size among 256 / 128 / 64 threads that wastes the fewest lanes
     // on the row's vector count (ties go to the larger block).
-    int threads = 256;
+    int threads = kMaxCombineThreads;
     int64_t best = -1;
     for (int b : {256, 128, 64}) {
         const int64_t span = static_cast<int64_t>(b) * kVecsPerThread;
@@ -171,17 +208,18 @@ hipError_t launch_bw(const CombineArgs &a, hipStream_t stream, CallEvents ev) {
             threads = b;
         }
     }
+    if (EP_COMBINE_THREADS > 0) threads = EP_COMBINE_THREADS;
     const int64_t span = static_cast<int64_t>(threads) * kVecsPerThread;
-    const int bpt = static_cast<int>((a.row_vecs + span - 1) / span);
-    const int64_t blocks = static_cast<int64_t>(a.num_tokens) * bpt;
+    const int gpt = static_cast<int>((a.row_vecs + span - 1) / span);
+    const int64_t blocks = persistent_grid(static_cast<int64_t>(a.num_tokens) * gpt, kBlocksPerCu);
     if (blocks == 0) return hipSuccess;
     if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
     const dim3 grid(static_cast<unsigned>(blocks)), block(threads);
     if (a.idx_is_i64)
         return launch_kernel(combine_kernel<HAS_BIAS, HAS_W, int64_t>, grid, block, stream,
-                             ev.start, ev.stop, a, bpt);
+                             ev.start, ev.stop, a, gpt);
     return launch_kernel(combine_kernel<HAS_BIAS, HAS_W, int32_t>, grid, block, stream,
-                         ev.start, ev.stop, a, bpt);
+                         ev.start, ev.stop, a, gpt);
 }
 
 }  // namespace

@@ -12,19 +12,31 @@ namespace ep {
 // load/store builtins, which lower to global_load/store_dwordx4 ... nt).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// Layout scan: one tile is kLayoutThreads threads x kLayoutRounds rounds of
-// 64 consecutive slots per wave.
+// Layout scan: a tile is at most kTileSlots slots (kLayoutThreads threads x
+// kLayoutRounds rounds of 64 consecutive slots per wave) and always holds
+// whole tokens.
+#ifndef EP_LAYOUT_ROUNDS
+#define EP_LAYOUT_ROUNDS 8
+#endif
 constexpr int kLayoutThreads = 256;
 constexpr int kLayoutWaves = kLayoutThreads / 64;
-constexpr int kLayoutRounds = 8;
-constexpr int kTileSlots = kLayoutThreads * kLayoutRounds;   // 2048
+constexpr int kLayoutRounds = EP_LAYOUT_ROUNDS;
+constexpr int kTileSlots = kLayoutThreads * kLayoutRounds;
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopk = 64;
-constexpr int kMaxBuckets = kMaxExperts + 1;                 // + invalid-id bucket
+static_assert(kTileSlots >= kMaxTopk, "a tile must hold at least one token");
+// Buckets of the scan: experts, then ids outside [-1, E), then received tokens.
+constexpr int kMaxBuckets = kMaxExperts + 2;
 constexpr int kMaxSfPerLane = 4;                             // FP8 hidden <= 32768
 
-inline int64_t layout_tiles(int64_t num_slots) {
-    int64_t t = (num_slots + kTileSlots - 1) / kTileSlots;
+inline int layout_tokens_per_tile(int num_topk) {
+    const int t = kTileSlots / num_topk;
+    return t < 1 ? 1 : t;
+}
+
+inline int64_t layout_tiles(int64_t num_tokens, int num_topk) {
+    const int64_t tpt = layout_tokens_per_tile(num_topk);
+    const int64_t t = (num_tokens + tpt - 1) / tpt;
     return t < 1 ? 1 : t;
 }
 
@@ -39,6 +51,29 @@ hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStr
     else
         kernel<<<grid, block, 0, stream>>>(args...);
     return hipGetLastError();
+}
+
+// Compute units of the current device (cached per device; 256 on MI355X).
+inline int device_cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+// Grid of a persistent kernel: `units` work items, at most blocks_per_cu
+// resident blocks per compute unit (0 = one block per unit).
+inline int64_t persistent_grid(int64_t units, int blocks_per_cu) {
+    if (blocks_per_cu <= 0) return units;
+    const int64_t cap = static_cast<int64_t>(device_cu_count()) * blocks_per_cu;
+    return units < cap ? units : cap;
 }
 
 // Events handed to the next entry point by ep_time_next_call (null = none).

@@ -8,24 +8,28 @@
 // ascending slot index t*K+k (a stable counting sort).
 //
 // Two kernels:
-//  1. layout_scan: one 256-thread block per tile of 2048 consecutive slots.
-//     Each wave takes 64 slots per round; lanes holding the same bucket find
-//     each other with one ballot per bucket-id bit (match-any), the group's
-//     rank is a popcount below the lane, and the group leader bumps the wave's
-//     LDS counter.  An LDS pass over the 4 waves turns per-wave counts into
-//     in-tile offsets and the tile histogram.  A decoupled lookback over
-//     earlier tiles (one 64-bit status word per tile and bucket holding epoch,
-//     aggregate/prefix flag and count, read and written with agent-scope
-//     atomics so every XCD sees them) gives each bucket's exclusive offset.
-//     Each valid slot gets its position inside its expert's run.  The tile
-//     with the last ticket holds the inclusive totals: it writes counts, runs
-//     the aligned block scan over experts into psum and sets the error word.
-//     Bucket E collects ids outside [-1, E) so that their count needs no extra
-//     pass.  Tiles take their index from an atomic ticket, so every tile a
-//     block waits on has already started; waits always end.
-//  2. layout_finalize: adds psum[e] to each position, scatters source
-//     metadata, marks alignment gaps with -1, counts tokens with a valid slot,
-//     bumps the epoch and resets the ticket for the next call.
+//  1. layout_scan: one 256-thread block per tile of whole tokens (at most
+//     kTileSlots slots).  The block first loads all of its ids (every load in
+//     flight at once), then each wave takes 64 slots per round: lanes holding
+//     the same bucket find each other with one ballot per bucket-id bit
+//     (match-any), a lane's rank is the popcount of matching lower lanes, and
+//     the group leader bumps the wave's LDS counter.  An LDS pass over the 4
+//     waves turns per-wave counts into in-tile offsets and the tile histogram.
+//     Buckets: 0..E-1 the experts, E the ids outside [-1, E), E+1 the tokens
+//     with a valid slot (a tile holds whole tokens, so it can count them).
+//     A decoupled lookback over earlier tiles - one 64-bit status word per
+//     (tile, bucket) holding epoch, aggregate/prefix flag and count, read and
+//     written with agent-scope atomics so every XCD sees them - gives each
+//     bucket's exclusive offset; each thread reads a window of 8 predecessors
+//     per round trip.  Each valid slot gets its position inside its expert's
+//     run.  The tile with the last ticket owns the inclusive totals: it writes
+//     counts, runs the aligned block scan over experts into psum and sets the
+//     scalars.  Tiles take their index from an atomic ticket, so every tile a
+//     block waits on has already started and waits end; a spin bound turns a
+//     broken invariant into an error bit instead of a hang.
+//  2. layout_finalize: thread per slot adds psum[e] to the position and
+//     scatters the source metadata; one block per expert marks its alignment
+//     gap with -1; block 0 bumps the epoch and resets the ticket.
 #include "ep_internal.h"
 #include "../../include/ep.h"
 
@@ -35,6 +39,7 @@ namespace {
 constexpr uint64_t kFlagAggregate = 1;
 constexpr uint64_t kFlagPrefix = 2;
 constexpr uint32_t kMaxSpins = 1u << 21;
+constexpr int kLookbackWindow = 8;
 constexpr int kBucketsPerThread = (kMaxBuckets + kLayoutThreads - 1) / kLayoutThreads;
 
 __device__ inline uint64_t pack_status(uint32_t epoch, uint64_t flag, uint32_t value) {
@@ -74,19 +79,65 @@ __device__ int64_t block_exclusive_scan(int64_t v, int64_t *s_wave, int64_t *tot
     return base + x - v;
 }
 
+// Sum of the counts of tiles [0, tile) for one bucket, by decoupled lookback:
+// each round trip reads up to kLookbackWindow predecessors at once and adds
+// published aggregates up to the first prefix (done) or the first tile that
+// has not published yet (poll it again).  Returns false if the spin bound
+// was hit.
+__device__ bool lookback(const uint64_t *status, int NB, int tile, int b, uint32_t epoch,
+                         uint32_t *excl_out) {
+    uint32_t excl = 0, spins = 0;
+    int j = tile - 1;
+    bool done = false;
+    while (!done && j >= 0) {
+        uint64_t s[kLookbackWindow];
+#pragma unroll
+        for (int w = 0; w < kLookbackWindow; ++w)
+            s[w] = j - w >= 0 ? load_status(&status[static_cast<int64_t>(j - w) * NB + b]) : 0;
+        int used = 0;
+        bool blocked = false;
+#pragma unroll
+        for (int w = 0; w < kLookbackWindow; ++w) {
+            if (done || blocked || j - w < 0) continue;
+            const uint32_t tag = static_cast<uint32_t>(s[w] >> 34);
+            const uint32_t flag = static_cast<uint32_t>(s[w] >> 32) & 3u;
+            if (tag != epoch || flag == 0) {             // not published yet
+                blocked = true;
+                continue;
+            }
+            excl += static_cast<uint32_t>(s[w]);
+            used = w + 1;
+            if (flag == kFlagPrefix) done = true;
+        }
+        if (done) break;
+        if (used == 0) {
+            if (++spins > kMaxSpins) {
+                *excl_out = excl;
+                return false;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        j -= used;
+    }
+    *excl_out = excl;
+    return true;
+}
+
 template <typename IdxT>
 __global__ __launch_bounds__(kLayoutThreads) void layout_scan_kernel(LayoutArgs a,
-                                                                    int64_t num_slots,
+                                                                    int tokens_per_tile,
                                                                     int num_tiles) {
     __shared__ int32_t s_hist[kLayoutWaves][kMaxBuckets];
     __shared__ int32_t s_excl[kMaxBuckets];
     __shared__ int32_t s_total[kMaxBuckets];
+    __shared__ uint8_t s_tok[kTileSlots];
     __shared__ int64_t s_wave[kLayoutWaves];
     __shared__ int32_t s_tile;
     __shared__ uint32_t s_epoch;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int E = a.num_experts, NB = E + 1;
+    const int E = a.num_experts, NB = E + 2, K = a.num_topk;
+    const int B_INVALID = E, B_RECV = E + 1;
     if (tid == 0) {
         s_tile = __hip_atomic_fetch_add(&a.scalars[EP_SCALAR_TICKET], 1, __ATOMIC_RELAXED,
                                         __HIP_MEMORY_SCOPE_AGENT);
@@ -94,26 +145,33 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_scan_kernel(LayoutArgs 
     }
     for (int w = 0; w < kLayoutWaves; ++w)
         for (int b = tid; b < NB; b += kLayoutThreads) s_hist[w][b] = 0;
+    for (int i = tid; i < kTileSlots; i += kLayoutThreads) s_tok[i] = 0;
     __syncthreads();
     const int tile = s_tile;
     const uint32_t epoch = s_epoch;
 
-    // 1. In-wave match-any over bucket ids, per-wave running counts in LDS.
-    const int nbits = 32 - __builtin_clz(static_cast<unsigned>(E));   // bits of 0..E
+    const int64_t num_slots = static_cast<int64_t>(a.num_tokens) * K;
+    const int64_t tile_base = static_cast<int64_t>(tile) * tokens_per_tile * K;
+    const int64_t tile_end_full = tile_base + static_cast<int64_t>(tokens_per_tile) * K;
+    const int64_t tile_end = tile_end_full < num_slots ? tile_end_full : num_slots;
+    const int64_t wave_base = tile_base + static_cast<int64_t>(wave) * (kLayoutRounds * 64);
+
+    // 1. Load every id of the tile first (all loads in flight), then match.
     const IdxT *idx = static_cast<const IdxT *>(a.topk_idx);
-    const int64_t wave_base = static_cast<int64_t>(tile) * kTileSlots +
-                              static_cast<int64_t>(wave) * (kLayoutRounds * 64);
+    int64_t ids[kLayoutRounds];
+#pragma unroll
+    for (int j = 0; j < kLayoutRounds; ++j) {
+        const int64_t i = wave_base + j * 64 + lane;
+        ids[j] = i < tile_end ? static_cast<int64_t>(idx[i]) : -1;
+    }
+    const int nbits = 32 - __builtin_clz(static_cast<unsigned>(E));   // bits of 0..E
     const uint64_t below = (1ull << lane) - 1ull;
     int bucket[kLayoutRounds];
     int rank[kLayoutRounds];
 #pragma unroll
     for (int j = 0; j < kLayoutRounds; ++j) {
-        const int64_t i = wave_base + j * 64 + lane;
-        int b = -1;
-        if (i < num_slots) {
-            const int64_t e = static_cast<int64_t>(idx[i]);
-            b = (e >= 0 && e < E) ? static_cast<int>(e) : (e == -1 ? -1 : E);
-        }
+        const int64_t e = ids[j];
+        const int b = (e >= 0 && e < E) ? static_cast<int>(e) : (e == -1 ? -1 : B_INVALID);
         uint64_t match = __ballot(b >= 0);
         for (int bit = 0; bit < nbits; ++bit) {
             const bool one = (b >> bit) & 1;
@@ -126,9 +184,23 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_scan_kernel(LayoutArgs 
             const int old = s_hist[wave][b];
             if (before == 0) s_hist[wave][b] = old + __popcll(match);
             r = old + before;
+            if (b < E) {
+                const int64_t i = wave_base + j * 64 + lane;
+                s_tok[(i - tile_base) / K] = 1;        // this token has a valid slot
+            }
         }
         bucket[j] = b;
         rank[j] = r;
+    }
+    __syncthreads();
+
+    // Received tokens of the tile go into bucket E+1 (one partial per wave).
+    {
+        int c = 0;
+        for (int i = tid; i < tokens_per_tile; i += kLayoutThreads) c += s_tok[i];
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off, 64);
+        if (lane == 0) s_hist[wave][B_RECV] = c;
     }
     __syncthreads();
 
@@ -150,7 +222,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_scan_kernel(LayoutArgs 
         }
     }
 
-    // 3. Decoupled lookback across tiles, one bucket per thread and pass.
+    // 3. Decoupled lookback across tiles.
     uint64_t *my_status = a.tile_status + static_cast<int64_t>(tile) * NB;
 #pragma unroll
     for (int q = 0; q < kBucketsPerThread; ++q) {
@@ -166,28 +238,9 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_scan_kernel(LayoutArgs 
         if (b >= NB) continue;
         uint32_t excl = 0;
         if (tile > 0) {
-            int j = tile - 1;
-            uint32_t spins = 0;
-            while (true) {
-                const uint64_t s = load_status(&a.tile_status[static_cast<int64_t>(j) * NB + b]);
-                const uint32_t s_epoch_tag = static_cast<uint32_t>(s >> 34);
-                const uint32_t flag = static_cast<uint32_t>(s >> 32) & 3u;
-                if (s_epoch_tag != epoch || flag == 0) {
-                    // A predecessor has always started (ticket order), so the
-                    // wait ends; the bound turns a broken invariant into an
-                    // error word instead of a hung kernel.
-                    if (++spins > kMaxSpins) {
-                        atomicOr(reinterpret_cast<unsigned *>(&a.scalars[EP_SCALAR_ERROR_BITS]),
-                                 EP_ERRBIT_SCAN_TIMEOUT);
-                        break;
-                    }
-                    __builtin_amdgcn_s_sleep(1);
-                    continue;
-                }
-                excl += static_cast<uint32_t>(s);
-                if (flag == kFlagPrefix || j == 0) break;
-                --j;
-            }
+            if (!lookback(a.tile_status, NB, tile, b, epoch, &excl))
+                atomicOr(reinterpret_cast<unsigned *>(&a.scalars[EP_SCALAR_ERROR_BITS]),
+                         EP_ERRBIT_SCAN_TIMEOUT);
             store_status(&my_status[b],
                          pack_status(epoch, kFlagPrefix, excl + static_cast<uint32_t>(agg[q])));
         }
@@ -195,17 +248,17 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_scan_kernel(LayoutArgs 
     }
     __syncthreads();
 
-    // 4. Position of every valid slot inside its expert's run.
+    // 4. Position of every valid slot inside its expert's run (-1 if empty).
 #pragma unroll
     for (int j = 0; j < kLayoutRounds; ++j) {
         const int64_t i = wave_base + j * 64 + lane;
-        if (i < num_slots) {
+        if (i < tile_end) {
             const int b = bucket[j];
             a.dst[i] = (b >= 0 && b < E) ? s_excl[b] + s_hist[wave][b] + rank[j] : -1;
         }
     }
 
-    // 5. The last tile owns the totals: counts, aligned scan, error word.
+    // 5. The last tile owns the totals: counts, aligned scan, scalars.
     if (tile != num_tiles - 1) return;
 #pragma unroll
     for (int q = 0; q < kBucketsPerThread; ++q) {
@@ -233,7 +286,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_scan_kernel(LayoutArgs 
     }
     if (tid == 0) {
         const int32_t expanded = static_cast<int32_t>(min(total, static_cast<int64_t>(INT32_MAX)));
-        const int32_t invalid = s_total[E];
+        const int32_t invalid = s_total[B_INVALID];
         a.psum[E] = expanded;
         uint32_t err = static_cast<uint32_t>(a.scalars[EP_SCALAR_ERROR_BITS]) &
                        EP_ERRBIT_SCAN_TIMEOUT;
@@ -241,15 +294,14 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_scan_kernel(LayoutArgs 
         if (invalid > 0) err |= EP_ERRBIT_INVALID_ID;
         a.scalars[EP_SCALAR_NUM_EXPANDED] = expanded;
         a.scalars[EP_SCALAR_INVALID_COUNT] = invalid;
+        a.scalars[EP_SCALAR_NUM_RECV_TOKENS] = s_total[B_RECV];
         a.scalars[EP_SCALAR_ERROR_BITS] = static_cast<int32_t>(err);
-        a.scalars[EP_SCALAR_NUM_RECV_TOKENS] = 0;
     }
 }
 
 template <typename IdxT>
-__global__ __launch_bounds__(256) void layout_finalize_kernel(LayoutArgs a, int token_blocks) {
-    __shared__ int32_t s_red[4];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+__global__ __launch_bounds__(256) void layout_finalize_kernel(LayoutArgs a, int slot_blocks) {
+    const int tid = threadIdx.x;
     if (blockIdx.x == 0 && tid == 0) {
         a.scalars[EP_SCALAR_TICKET] = 0;
         uint32_t next = static_cast<uint32_t>(a.scalars[EP_SCALAR_EPOCH]) + 1u;
@@ -257,37 +309,25 @@ __global__ __launch_bounds__(256) void layout_finalize_kernel(LayoutArgs a, int 
         a.scalars[EP_SCALAR_EPOCH] = static_cast<int32_t>(next);
     }
     if (a.scalars[EP_SCALAR_ERROR_BITS] & EP_ERRBIT_FATAL) return;
-    const int K = a.num_topk, E = a.num_experts;
-    if (static_cast<int>(blockIdx.x) < token_blocks) {
+    const int E = a.num_experts;
+    if (static_cast<int>(blockIdx.x) < slot_blocks) {
+        const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + tid;
+        if (i >= static_cast<int64_t>(a.num_tokens) * a.num_topk) return;
         const IdxT *idx = static_cast<const IdxT *>(a.topk_idx);
-        const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + tid;
-        int any = 0;
-        if (t < a.num_tokens) {
-            for (int k = 0; k < K; ++k) {
-                const int64_t i = t * K + k;
-                const int64_t e = static_cast<int64_t>(idx[i]);
-                if (e >= 0 && e < E) {
-                    const int32_t r = a.psum[e] + a.dst[i];
-                    a.dst[i] = r;
-                    if (r < a.capacity) a.src_meta[r] = static_cast<int32_t>(i);
-                    any = 1;
-                }
-            }
+        const int64_t e = static_cast<int64_t>(idx[i]);
+        const int32_t pos = a.dst[i];
+        if (e >= 0 && e < E) {
+            const int32_t r = a.psum[e] + pos;
+            a.dst[i] = r;
+            if (r < a.capacity) a.src_meta[r] = static_cast<int32_t>(i);
         }
-        const int c = __popcll(__ballot(any));
-        if (lane == 0) s_red[wave] = c;
-        __syncthreads();
-        if (tid == 0) {
-            const int sum = s_red[0] + s_red[1] + s_red[2] + s_red[3];
-            if (sum) atomicAdd(&a.scalars[EP_SCALAR_NUM_RECV_TOKENS], sum);
-        }
-    } else {
-        const int e = static_cast<int>(blockIdx.x) - token_blocks;
-        const int32_t g1 = a.psum[e + 1];
-        const int64_t end = g1 < a.capacity ? g1 : a.capacity;
-        for (int64_t r = static_cast<int64_t>(a.psum[e]) + a.counts[e] + tid; r < end; r += 256)
-            a.src_meta[r] = -1;
+        return;
     }
+    const int e = static_cast<int>(blockIdx.x) - slot_blocks;
+    const int32_t g1 = a.psum[e + 1];
+    const int64_t end = g1 < a.capacity ? g1 : a.capacity;
+    for (int64_t r = static_cast<int64_t>(a.psum[e]) + a.counts[e] + tid; r < end; r += 256)
+        a.src_meta[r] = -1;
 }
 
 __global__ void handle_clear_kernel(int32_t *scalars, uint64_t *status, int64_t n) {
@@ -310,23 +350,24 @@ hipError_t launch_handle_clear(int32_t *scalars, uint64_t *tile_status, int64_t 
 }
 
 hipError_t launch_layout(const LayoutArgs &a, hipStream_t stream, CallEvents ev) {
-    const int64_t num_slots = static_cast<int64_t>(a.num_tokens) * a.num_topk;
-    const int tiles = static_cast<int>(layout_tiles(num_slots));
-    const int token_blocks = (a.num_tokens + 255) / 256;
-    const dim3 fin_blocks(static_cast<unsigned>(token_blocks + a.num_experts));
+    const int tpt = layout_tokens_per_tile(a.num_topk);
+    const int tiles = static_cast<int>(layout_tiles(a.num_tokens, a.num_topk));
+    const int64_t slots = static_cast<int64_t>(a.num_tokens) * a.num_topk;
+    const int slot_blocks = static_cast<int>((slots + 255) / 256);
+    const dim3 fin_blocks(static_cast<unsigned>(slot_blocks + a.num_experts));
     hipError_t e;
     if (a.idx_is_i64) {
         e = launch_kernel(layout_scan_kernel<int64_t>, dim3(tiles), dim3(kLayoutThreads), stream,
-                          ev.start, nullptr, a, num_slots, tiles);
+                          ev.start, nullptr, a, tpt, tiles);
         if (e == hipSuccess)
             e = launch_kernel(layout_finalize_kernel<int64_t>, fin_blocks, dim3(256), stream,
-                              nullptr, ev.stop, a, token_blocks);
+                              nullptr, ev.stop, a, slot_blocks);
     } else {
         e = launch_kernel(layout_scan_kernel<int32_t>, dim3(tiles), dim3(kLayoutThreads), stream,
-                          ev.start, nullptr, a, num_slots, tiles);
+                          ev.start, nullptr, a, tpt, tiles);
         if (e == hipSuccess)
             e = launch_kernel(layout_finalize_kernel<int32_t>, fin_blocks, dim3(256), stream,
-                              nullptr, ev.stop, a, token_blocks);
+                              nullptr, ev.stop, a, slot_blocks);
     }
     return e;
 }

@@ -60,8 +60,8 @@ def test_workspace_bytes():
     assert 0 < small < big
     assert big % 256 == 0
     # counts + psum + dst + src_meta + scalars + one 64-bit status word per
-    # (tile of 2048 slots, expert + 1)
-    need = 4 * 256 + 4 * 257 + 4 * 4096 * 8 + 4 * 65280 + 32 + 8 * 16 * 257
+    # (tile of 2048 slots, expert + 2 buckets)
+    need = 4 * 256 + 4 * 257 + 4 * 4096 * 8 + 4 * 65280 + 32 + 8 * 16 * 258
     assert need <= big <= need + 6 * 256
     assert ep.ep_workspace_bytes(64, 65, 16, 1, 256) == 0       # K > 64
     assert ep.ep_workspace_bytes(64, 4, 1025, 1, 256) == 0      # E > 1024
