@@ -106,18 +106,16 @@ def copy_calibration():
 
 
 def ceilings(torch, nbytes=1 << 30, reps=5):
-    """Measured device ceilings: 1 GiB device-to-device copy, fill and a
-    read-only reduction (torch kernels)."""
+    """Measured device ceilings: 1 GiB device-to-device copy and fill (torch
+    kernels)."""
     a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     b = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     a.fill_(3)
     b.copy_(a)
     torch.cuda.synchronize()
     out = {}
-    a32 = a.view(torch.int32)
     for name, fn, moved in (("copy", lambda: b.copy_(a), 2 * nbytes),
-                            ("fill", lambda: b.fill_(7), nbytes),
-                            ("read", lambda: a32.sum(), nbytes)):
+                            ("fill", lambda: b.fill_(7), nbytes)):
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         s.record()
         for _ in range(reps):
