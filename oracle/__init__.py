@@ -49,6 +49,11 @@ def _bind(lib):
     lib.oracle_combine.argtypes = [_I, _I, _I, _P, _P, _P, _P, _P, _P]
     lib.oracle_combine_f64.restype = None
     lib.oracle_combine_f64.argtypes = [_I, _I, _I, _P, _P, _P, _P, _P, _P, _P]
+    lib.oracle_combine_backward.restype = None
+    lib.oracle_combine_backward.argtypes = [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P,
+                                            _P, _P, _P, _P]
+    lib.oracle_dispatch_backward.restype = None
+    lib.oracle_dispatch_backward.argtypes = [_I, _I, _I, _P, _P, _P, _P, _P, _P]
     return lib
 
 
@@ -184,3 +189,50 @@ def combine_f64(y_bits, topk_idx, dst, weights=None, bias_bits=None, lib=None):
     lib.oracle_combine_f64(T, K, H, _ptr(y), _ptr(w), _ptr(b), _ptr(idx),
                            _ptr(d), _ptr(out), _ptr(mag))
     return out, mag
+
+
+def combine_backward(g_bits, lay: Layout, topk_idx, weights=None, y_bits=None, bias_bits=None,
+                     capacity=None, want_grad_y=True, want_grad_w=True, want_grad_bias=False,
+                     grad_y=None, lib=None):
+    """Backward of combine.  g_bits: uint16 [T, H] (bf16 gradient of out).
+    Returns (grad_y uint16 [capacity, H] or None, grad_w float64 [T, K] or
+    None, grad_bias float32 [E, H] or None).  grad_y may be passed pre-filled
+    (rows without a slot keep their content)."""
+    lib = lib or load()
+    g = _c(g_bits, np.uint16)
+    idx = _c(topk_idx, np.int64)
+    T, K = idx.shape
+    H = g.shape[1]
+    E = lay.counts.shape[0]
+    w = None if weights is None else _c(weights, np.float32)
+    y = None if y_bits is None else _c(y_bits, np.uint16)
+    b = None if bias_bits is None else _c(bias_bits, np.uint16)
+    gy = None
+    if want_grad_y:
+        gy = grad_y if grad_y is not None else np.zeros((capacity, H), np.uint16)
+    gw = np.zeros((T, K), np.float64) if want_grad_w else None
+    gb = np.zeros((E, H), np.float32) if want_grad_bias else None
+    if want_grad_w:
+        assert y is not None, "grad_w needs the expert outputs y"
+    src = _c(lay.src_meta, np.int32)
+    lib.oracle_combine_backward(T, K, E, H, _ptr(g), _ptr(w), _ptr(y), _ptr(b), _ptr(idx),
+                                _ptr(_c(lay.dst, np.int32)), _ptr(lay.counts), _ptr(lay.psum),
+                                _ptr(src), _ptr(gy), _ptr(gw), _ptr(gb))
+    return gy, gw, gb
+
+
+def dispatch_backward(go_bits, topk_idx, dst, gw=None, lib=None):
+    """Backward of dispatch.  go_bits: uint16 [capacity, H]; gw: float32
+    [capacity] or None.  Returns (grad_x uint16 [T, H], grad_w float32 [T, K])."""
+    lib = lib or load()
+    go = _c(go_bits, np.uint16)
+    idx = _c(topk_idx, np.int64)
+    d = _c(dst, np.int32)
+    T, K = idx.shape
+    H = go.shape[1]
+    gx = np.zeros((T, H), np.uint16)
+    gwo = np.zeros((T, K), np.float32)
+    g = None if gw is None else _c(gw, np.float32)
+    lib.oracle_dispatch_backward(T, K, H, _ptr(go), _ptr(g), _ptr(idx), _ptr(d), _ptr(gx),
+                                 _ptr(gwo))
+    return gx, gwo

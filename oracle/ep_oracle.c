@@ -285,3 +285,90 @@ void oracle_combine_f64(int64_t T, int64_t K, int64_t H, const uint16_t *y,
         }
     }
 }
+
+/*
+ * Backward of combine [README, training example: the backward of combine is
+ * a dispatch of the gradient and the combined top-k weights carry the
+ * weights' gradient; the forward is the combine above].  With
+ * out[t] = sum_k w[t,k] * (y[r] + b[e]) (r = dst[t,k], e = topk_idx[t,k]) and
+ * g = d loss / d out (bf16 [T, H]):
+ *   grad_y[r][h]    = bf16(fl32(w[t,k] * g[t][h]))     (g itself if w is NULL)
+ *   grad_w[t,k]     = sum_h g[t][h] * (y[r][h] + b[e][h])   (binary64, no
+ *                     rounding of the terms: the reference value), 0 for an
+ *                     empty slot
+ *   grad_bias[e][h] = sum over the rows of expert e in row order of
+ *                     fl32(w * g[t][h]), binary32 from +0.0
+ * Any output pointer may be NULL.  Rows of grad_y that hold no slot are not
+ * written.
+ */
+void oracle_combine_backward(int64_t T, int64_t K, int64_t E, int64_t H,
+                             const uint16_t *g, const float *w,
+                             const uint16_t *y, const uint16_t *bias,
+                             const int64_t *topk_idx, const int32_t *dst,
+                             const int32_t *counts, const int32_t *psum,
+                             const int32_t *src_meta, uint16_t *grad_y,
+                             double *grad_w, float *grad_bias)
+{
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t k = 0; k < K; ++k) {
+            int64_t r = dst[t * K + k];
+            if (grad_w)
+                grad_w[t * K + k] = 0.0;
+            if (r < 0)
+                continue;
+            int64_t e = topk_idx[t * K + k];
+            double acc = 0.0;
+            for (int64_t h = 0; h < H; ++h) {
+                float gv = bf16_to_f32(g[t * H + h]);
+                if (grad_y) {
+                    float s = w ? w[t * K + k] * gv : gv;
+                    grad_y[r * H + h] = f32_to_bf16(s);
+                }
+                if (grad_w) {
+                    double v = (double)bf16_to_f32(y[r * H + h]);
+                    if (bias)
+                        v += (double)bf16_to_f32(bias[e * H + h]);
+                    acc += (double)gv * v;
+                }
+            }
+            if (grad_w)
+                grad_w[t * K + k] = acc;
+        }
+    }
+    if (!grad_bias)
+        return;
+    for (int64_t e = 0; e < E; ++e) {
+        for (int64_t h = 0; h < H; ++h) {
+            float acc = 0.0f;
+            for (int64_t r = psum[e]; r < (int64_t)psum[e] + counts[e]; ++r) {
+                int64_t i = src_meta[r];
+                int64_t t = i / K;
+                float gv = bf16_to_f32(g[t * H + h]);
+                float s = w ? w[i] * gv : gv;
+                acc = acc + s;
+            }
+            grad_bias[e * H + h] = acc;
+        }
+    }
+}
+
+/*
+ * Backward of dispatch [README, training example: the backward of dispatch
+ * is a combine of the gradient rows, returning the gradient of the
+ * dispatched top-k weights too].  With go = d loss / d out_x (bf16
+ * [capacity, H]) and gw = d loss / d out_w ([capacity], may be NULL):
+ *   grad_x[t]   = the combine of go with no weights and no bias
+ *   grad_w[t,k] = gw[dst[t,k]], 0 for an empty slot
+ */
+void oracle_dispatch_backward(int64_t T, int64_t K, int64_t H,
+                              const uint16_t *go, const float *gw,
+                              const int64_t *topk_idx, const int32_t *dst,
+                              uint16_t *grad_x, float *grad_w)
+{
+    if (grad_x)
+        oracle_combine(T, K, H, go, NULL, NULL, topk_idx, dst, grad_x);
+    if (!grad_w)
+        return;
+    for (int64_t i = 0; i < T * K; ++i)
+        grad_w[i] = (dst[i] >= 0 && gw) ? gw[dst[i]] : 0.0f;
+}

@@ -144,3 +144,39 @@ def combine_exact_sum(y_bits, topk_idx, dst, weights=None, bias_bits=None):
         acc += np.where(ok[:, None], v, 0.0)
         mag += np.where(ok[:, None], np.abs(v), 0.0)
     return acc, mag
+
+
+def combine_backward_expected(g_bits, topk_idx, dst, weights, y_bits, bias_bits, counts,
+                              psum, src_meta, E):
+    """Backward of combine written out directly: grad_y rows as bf16 of the
+    float32 product w * g, grad_w as a float64 dot product over channels,
+    grad_bias as a float32 running sum over each expert's rows in row order."""
+    idx = np.asarray(topk_idx, np.int64)
+    T, K = idx.shape
+    g = bf16_bits_to_f32(g_bits)
+    H = g.shape[1]
+    d = np.asarray(dst, np.int64).reshape(T, K)
+    w = None if weights is None else np.asarray(weights, np.float32)
+    rows = {}
+    gw = np.zeros((T, K), np.float64)
+    yf = bf16_bits_to_f32(y_bits).astype(np.float64)
+    bf = None if bias_bits is None else bf16_bits_to_f32(bias_bits).astype(np.float64)
+    for t in range(T):
+        for k in range(K):
+            r = d[t, k]
+            if r < 0:
+                continue
+            s = g[t] if w is None else (w[t, k] * g[t]).astype(np.float32)
+            rows[int(r)] = f32_to_bf16_bits_torch(s[None, :])[0]
+            v = yf[r] + (bf[idx[t, k]] if bf is not None else 0.0)
+            gw[t, k] = float(np.dot(g[t].astype(np.float64), v))
+    gb = np.zeros((E, H), np.float32)
+    for e in range(E):
+        acc = np.zeros(H, np.float32)
+        for r in range(int(psum[e]), int(psum[e]) + int(counts[e])):
+            i = int(src_meta[r])
+            t, k = divmod(i, K)
+            s = g[t] if w is None else (w[t, k] * g[t]).astype(np.float32)
+            acc = (acc + s).astype(np.float32)
+        gb[e] = acc
+    return rows, gw, gb

@@ -361,6 +361,81 @@ def pin_combine_single_slot_gather(lib):
     np.testing.assert_array_equal(out, exp)
 
 
+# ----------------------------------------------------------------------------
+# backward pair
+
+
+def _backward_case(rng, T=40, K=5, E=9, H=48, A=4, bias=True, weights=True):
+    idx = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int64)
+    idx = np.where(rng.random((T, K)) < 0.2, -1, idx)
+    idx[1] = -1
+    cap = T * K + A * E
+    lay = oracle.layout(idx, E, A, cap, lib=None)
+    g = _bf16_from_normal(rng, (T, H))
+    y = _bf16_from_normal(rng, (cap, H), 2.0)
+    w = (rng.random((T, K), dtype=np.float32) * 2 - 0.5) if weights else None
+    b = _bf16_from_normal(rng, (E, H), 0.3) if bias else None
+    return idx, lay, cap, g, y, w, b
+
+
+def pin_combine_backward_bruteforce(lib):
+    rng = np.random.default_rng(31)
+    for bias in (False, True):
+        for weights in (False, True):
+            idx, lay, cap, g, y, w, b = _backward_case(rng, bias=bias, weights=weights)
+            gy, gw, gb = oracle.combine_backward(g, lay, idx, w, y, b, capacity=cap,
+                                                 want_grad_bias=True, lib=lib)
+            rows, egw, egb = BF.combine_backward_expected(
+                g, idx, lay.dst, w, y, b, lay.counts, lay.psum, lay.src_meta, len(lay.counts))
+            for r, v in rows.items():
+                np.testing.assert_array_equal(gy[r], v)
+            np.testing.assert_allclose(gw, egw, rtol=1e-12, atol=1e-12)
+            np.testing.assert_array_equal(gb.view(np.uint32), egb.view(np.uint32))
+
+
+def pin_combine_backward_adjoint(lib):
+    """Without bias, combine is linear in y and in w:
+    <g, sum_k w_k y_k> = sum_r <grad_y_r, y_r> up to grad_y's bf16 rounding,
+    and sum_{t,k} w_k * grad_w[t,k] = <g, sum_k w_k y_k> (binary64)."""
+    rng = np.random.default_rng(37)
+    idx, lay, cap, g, y, w, _ = _backward_case(rng, bias=False)
+    gy, gw, _ = oracle.combine_backward(g, lay, idx, w, y, None, capacity=cap, lib=lib)
+    gf = _bits_to_float(g).astype(np.float64)
+    yf = _bits_to_float(y).astype(np.float64)
+    d = lay.dst
+    out = np.zeros_like(gf)
+    for k in range(idx.shape[1]):
+        ok = d[:, k] >= 0
+        out[ok] += w[ok, k:k + 1].astype(np.float64) * yf[d[ok, k]]
+    lhs = float((gf * out).sum())
+    valid = d[d >= 0]
+    rhs = float((_bits_to_float(gy[valid]).astype(np.float64) * yf[valid]).sum())
+    mag = float(np.abs(gf * out).sum()) + float(np.abs(_bits_to_float(gy[valid]) * yf[valid]).sum())
+    assert abs(lhs - rhs) <= 2.0 ** -8 * mag
+    assert abs(float((w.astype(np.float64) * gw).sum()) - lhs) <= 1e-9 * mag
+
+
+def pin_dispatch_backward(lib):
+    """grad_x is the plain combine of the gradient rows (adjoint of the copy:
+    <go, dispatch(x)> = <grad_x, x> up to bf16 rounding) and grad_w gathers
+    the per-row weight gradient of each slot."""
+    rng = np.random.default_rng(41)
+    idx, lay, cap, _, go, _, _ = _backward_case(rng)
+    x = _bf16_from_normal(rng, (idx.shape[0], go.shape[1]))
+    gwr = rng.standard_normal(cap).astype(np.float32)
+    gx, gw = oracle.dispatch_backward(go, idx, lay.dst, gwr, lib=lib)
+    np.testing.assert_array_equal(gx, BF.combine_f32(go, idx, lay.dst))
+    exp_w = np.where(lay.dst >= 0, gwr[np.maximum(lay.dst, 0)], 0.0).astype(np.float32)
+    np.testing.assert_array_equal(gw, exp_w)
+    xd, _, _ = oracle.dispatch(x.view(np.uint8), lay, cap, lib=lib)
+    valid = lay.dst[lay.dst >= 0]
+    gof = _bits_to_float(go).astype(np.float64)
+    lhs = float((gof[valid] * _bits_to_float(xd.view(np.uint16)[valid])).sum())
+    rhs = float((_bits_to_float(gx).astype(np.float64) * _bits_to_float(x)).sum())
+    mag = float(np.abs(gof[valid] * _bits_to_float(xd.view(np.uint16)[valid])).sum())
+    assert abs(lhs - rhs) <= 2.0 ** -7 * mag
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 

@@ -54,6 +54,18 @@ MUTANTS = {
                                    "                float p = w ? w[t * K + k] * v : v;\n                acc = w ? __builtin_fmaf(w[t * K + k], v, acc) : acc + p;"),
     "combine_neg_zero_start": ("float acc = 0.0f;\n            for (int64_t k = 0; k < K; ++k) {\n                int64_t r = dst[t * K + k];\n                if (r < 0)\n                    continue;\n                float v",
                                "float acc = -0.0f;\n            for (int64_t k = 0; k < K; ++k) {\n                int64_t r = dst[t * K + k];\n                if (r < 0)\n                    continue;\n                float v"),
+    "cb_grad_y_no_weight": ("float s = w ? w[t * K + k] * gv : gv;", "float s = gv;"),
+    "cb_grad_w_no_bias": ("v += (double)bf16_to_f32(bias[e * H + h]);", "v += 0.0;"),
+    "cb_grad_w_wrong_row": (
+        "if (grad_w) {\n                    double v = (double)bf16_to_f32(y[r * H + h]);",
+        "if (grad_w) {\n                    double v = (double)bf16_to_f32(y[(r > 0 ? r - 1 : r) * H + h]);"),
+    "cb_grad_w_no_grad": ("acc += (double)gv * v;", "acc += v;"),
+    "cb_grad_bias_reverse": (
+        "for (int64_t r = psum[e]; r < (int64_t)psum[e] + counts[e]; ++r) {",
+        "for (int64_t r = (int64_t)psum[e] + counts[e] - 1; r >= psum[e]; --r) {"),
+    "cb_grad_bias_no_weight": ("float s = w ? w[i] * gv : gv;", "float s = gv;"),
+    "db_grad_w_wrong_row": ("grad_w[i] = (dst[i] >= 0 && gw) ? gw[dst[i]] : 0.0f;",
+                            "grad_w[i] = (dst[i] >= 0 && gw) ? gw[i % 7] : 0.0f;"),
 }
 
 
