@@ -25,7 +25,7 @@ __all__ = [
     "EP_I64", "EpError", "ep_handle", "lib", "Handle", "ep_capacity_bound",
     "ep_workspace_bytes", "ep_handle_init", "ep_layout", "ep_handle_read_counts",
     "ep_handle_import", "ep_dispatch", "ep_combine", "ep_status_str", "ep_handle_sizeof",
-    "ep_time_next_call", "time_next_call",
+    "ep_time_next_call", "time_next_call", "ep_combine_backward", "ep_dispatch_backward",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libep.so")
@@ -85,6 +85,8 @@ _SIGNATURES = {
     "ep_combine": (ctypes.c_int, [_HP, _P, ctypes.c_int, _I32, _P, _P, _P, _P]),
     "ep_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "ep_time_next_call": (ctypes.c_int, [_P, _P]),
+    "ep_combine_backward": (ctypes.c_int, [_HP, _P, _I32, _P, _P, _P, _P, _P, _P, _P]),
+    "ep_dispatch_backward": (ctypes.c_int, [_HP, _P, _I32, _P, _P, _P, _P]),
 }
 
 _lib = None
@@ -161,6 +163,18 @@ def ep_dispatch(h: ep_handle, x_ptr, x_dtype, hidden, sf_ptr, sf_ts, sf_hs, w_pt
 def ep_combine(h: ep_handle, y_ptr, y_dtype, hidden, w_ptr, bias_ptr, out_ptr, stream) -> int:
     return lib().ep_combine(ctypes.byref(h), y_ptr, y_dtype, hidden, w_ptr, bias_ptr, out_ptr,
                             stream)
+
+
+def ep_combine_backward(h: ep_handle, grad_out_ptr, hidden, w_ptr, y_ptr, bias_ptr, grad_y_ptr,
+                        grad_w_ptr, grad_bias_ptr, stream) -> int:
+    return lib().ep_combine_backward(ctypes.byref(h), grad_out_ptr, hidden, w_ptr, y_ptr,
+                                     bias_ptr, grad_y_ptr, grad_w_ptr, grad_bias_ptr, stream)
+
+
+def ep_dispatch_backward(h: ep_handle, grad_out_x_ptr, hidden, grad_out_w_ptr, grad_x_ptr,
+                         grad_w_ptr, stream) -> int:
+    return lib().ep_dispatch_backward(ctypes.byref(h), grad_out_x_ptr, hidden, grad_out_w_ptr,
+                                      grad_x_ptr, grad_w_ptr, stream)
 
 
 def ep_status_str(status: int) -> str:
@@ -381,3 +395,67 @@ class Handle:
         _check(ep_combine(self.h, _ptr(y), EP_BF16, H, _ptr(topk_weights), _ptr(bias), _ptr(out),
                           _stream()), "ep_combine")
         return out
+
+
+    # ------------------------------------------------------------ backward
+
+    def combine_backward(self, grad_out: torch.Tensor, topk_weights=None, y=None, bias=None,
+                         grad_y=None, want_grad_y: bool = True, want_grad_weights: bool = False,
+                         want_grad_bias: bool = False):
+        """Backward of combine.  grad_out: bf16 [T, H].  Returns
+        (grad_y bf16 [capacity, H] or None, grad_topk_weights fp32 [T, K] or
+        None, grad_bias fp32 [E, H] or None).  Rows of grad_y without a slot
+        are left as they were (uninitialised when allocated here)."""
+        T, K, E = self.h.num_tokens, self.h.num_topk, self.h.num_experts
+        _dev(grad_out, "grad_out")
+        _need(grad_out.dtype == torch.bfloat16 and grad_out.dim() == 2 and
+              grad_out.shape[0] == T, "grad_out must be bf16 [T, H]")
+        H = grad_out.shape[1]
+        if topk_weights is not None:
+            _dev(topk_weights, "topk_weights")
+            _need(topk_weights.dtype == torch.float32 and tuple(topk_weights.shape) == (T, K),
+                  "topk_weights must be fp32 [T, K]")
+        if y is not None:
+            _dev(y, "y")
+            _need(y.dtype == torch.bfloat16 and tuple(y.shape) == (self.capacity, H),
+                  "y must be bf16 [capacity, H]")
+        if bias is not None:
+            _dev(bias, "bias")
+            _need(bias.dtype == torch.bfloat16 and tuple(bias.shape) == (E, H),
+                  "bias must be bf16 [E, H]")
+        if want_grad_y and grad_y is None:
+            grad_y = torch.empty((self.capacity, H), dtype=torch.bfloat16, device=grad_out.device)
+        if grad_y is not None:
+            _dev(grad_y, "grad_y")
+            _need(grad_y.dtype == torch.bfloat16 and tuple(grad_y.shape) == (self.capacity, H),
+                  "grad_y must be bf16 [capacity, H]")
+        gw = torch.empty((T, K), dtype=torch.float32, device=grad_out.device) \
+            if want_grad_weights else None
+        if gw is not None:
+            _need(y is not None, "the weight gradient needs y")
+        gb = torch.empty((E, H), dtype=torch.float32, device=grad_out.device) \
+            if want_grad_bias else None
+        _check(ep_combine_backward(self.h, _ptr(grad_out), H, _ptr(topk_weights), _ptr(y),
+                                   _ptr(bias), _ptr(grad_y), _ptr(gw), _ptr(gb), _stream()),
+               "ep_combine_backward")
+        return grad_y, gw, gb
+
+    def dispatch_backward(self, grad_out_x: torch.Tensor, grad_out_w=None,
+                          want_grad_weights: bool = False):
+        """Backward of dispatch.  grad_out_x: bf16 [capacity, H].  Returns
+        (grad_x bf16 [T, H], grad_topk_weights fp32 [T, K] or None)."""
+        T, K = self.h.num_tokens, self.h.num_topk
+        _dev(grad_out_x, "grad_out_x")
+        _need(grad_out_x.dtype == torch.bfloat16 and grad_out_x.dim() == 2 and
+              grad_out_x.shape[0] == self.capacity, "grad_out_x must be bf16 [capacity, H]")
+        H = grad_out_x.shape[1]
+        if grad_out_w is not None:
+            _dev(grad_out_w, "grad_out_w")
+            _need(grad_out_w.dtype == torch.float32 and grad_out_w.numel() == self.capacity,
+                  "grad_out_w must be fp32 [capacity]")
+        gx = torch.empty((T, H), dtype=torch.bfloat16, device=grad_out_x.device)
+        gw = torch.empty((T, K), dtype=torch.float32, device=grad_out_x.device) \
+            if want_grad_weights else None
+        _check(ep_dispatch_backward(self.h, _ptr(grad_out_x), H, _ptr(grad_out_w), _ptr(gx),
+                                    _ptr(gw), _stream()), "ep_dispatch_backward")
+        return gx, gw

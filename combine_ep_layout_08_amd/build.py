@@ -13,7 +13,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libep.so")
 
-SOURCES = ["ep_api.cpp", "ep_layout.hip", "ep_dispatch.hip", "ep_combine.hip"]
+SOURCES = ["ep_api.cpp", "ep_layout.hip", "ep_dispatch.hip", "ep_combine.hip", "ep_backward.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -315,6 +315,92 @@ ep_status ep_combine(const ep_handle *h, const void *y, ep_dtype y_dtype, int32_
     return hip_status(ep::launch_combine(a, stream, ev));
 }
 
+ep_status ep_combine_backward(const ep_handle *h, const void *grad_out, int32_t hidden,
+                              const float *topk_weights, const void *y, const void *bias,
+                              void *grad_y, float *grad_topk_weights, float *grad_bias,
+                              hipStream_t stream) {
+    const ep::CallEvents ev = take_events();
+    if (!h) return EP_ERR_NULL;
+    if (!handle_ready(h)) return EP_ERR_WORKSPACE;
+    if (!h->laid_out) return EP_ERR_NOT_LAID_OUT;
+    if (hidden <= 0) return EP_ERR_SHAPE;
+    if (hidden % 8 != 0) return EP_ERR_MISALIGNED;
+    const bool rows = h->num_tokens > 0;
+    if ((grad_y || grad_topk_weights || grad_bias) && rows && !grad_out) return EP_ERR_NULL;
+    if (grad_topk_weights && rows && !y) return EP_ERR_NULL;
+    if (bias && grad_topk_weights && rows && !h->topk_idx) return EP_ERR_NULL;
+    if (!aligned(grad_out, 16) || !aligned(y, 16) || !aligned(bias, 16) || !aligned(grad_y, 16))
+        return EP_ERR_MISALIGNED;
+    if (!aligned(topk_weights, 4) || !aligned(grad_topk_weights, 4) || !aligned(grad_bias, 4))
+        return EP_ERR_MISALIGNED;
+    ep::BackwardArgs a{};
+    a.g = grad_out;
+    a.row_vecs = hidden / 8;
+    a.num_tokens = h->num_tokens;
+    a.num_topk = h->num_topk;
+    a.num_experts = h->num_experts;
+    a.capacity = h->capacity;
+    a.dst = h->dst_slot;
+    a.counts = h->counts;
+    a.psum = h->psum;
+    a.src_meta = h->src_meta;
+    a.scalars = h->scalars;
+    a.w = topk_weights;
+    a.y = y;
+    a.bias = bias;
+    a.topk_idx = h->topk_idx;
+    a.idx_is_i64 = h->topk_idx_dtype == EP_I64;
+    a.grad_y = grad_y;
+    a.grad_w = grad_topk_weights;
+    a.grad_bias = grad_bias;
+    return hip_status(ep::launch_combine_backward(a, stream, ev));
+}
+
+ep_status ep_dispatch_backward(const ep_handle *h, const void *grad_out_x, int32_t hidden,
+                               const float *grad_out_w, void *grad_x, float *grad_topk_weights,
+                               hipStream_t stream) {
+    const ep::CallEvents ev = take_events();
+    if (!h) return EP_ERR_NULL;
+    if (!handle_ready(h)) return EP_ERR_WORKSPACE;
+    if (!h->laid_out) return EP_ERR_NOT_LAID_OUT;
+    if (hidden <= 0) return EP_ERR_SHAPE;
+    if (hidden % 8 != 0) return EP_ERR_MISALIGNED;
+    const bool rows = h->num_tokens > 0;
+    if (grad_x && rows && !grad_out_x) return EP_ERR_NULL;
+    if (!aligned(grad_out_x, 16) || !aligned(grad_x, 16)) return EP_ERR_MISALIGNED;
+    if (!aligned(grad_out_w, 4) || !aligned(grad_topk_weights, 4)) return EP_ERR_MISALIGNED;
+    const bool both = grad_x && grad_topk_weights && rows;
+    if (grad_x && rows) {
+        ep::CombineArgs c{};
+        c.y = grad_out_x;
+        c.row_vecs = hidden / 8;
+        c.num_tokens = h->num_tokens;
+        c.num_topk = h->num_topk;
+        c.num_experts = h->num_experts;
+        c.capacity = h->capacity;
+        c.dst = h->dst_slot;
+        c.scalars = h->scalars;
+        c.out = grad_x;
+        ep::CallEvents first = ev;
+        if (both) first.stop = nullptr;
+        const hipError_t e = ep::launch_combine(c, stream, first);
+        if (e != hipSuccess) return EP_ERR_HIP;
+    }
+    if (grad_topk_weights && rows) {
+        ep::GatherArgs g{};
+        g.row_values = grad_out_w;
+        g.num_slots = static_cast<int64_t>(h->num_tokens) * h->num_topk;
+        g.capacity = h->capacity;
+        g.dst = h->dst_slot;
+        g.scalars = h->scalars;
+        g.out = grad_topk_weights;
+        ep::CallEvents second = ev;
+        if (both) second.start = nullptr;
+        return hip_status(ep::launch_gather_rows(g, stream, second));
+    }
+    return EP_OK;
+}
+
 const char *ep_status_str(ep_status s) {
     switch (s) {
     case EP_OK: return "EP_OK: success";

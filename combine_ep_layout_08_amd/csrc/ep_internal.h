@@ -122,10 +122,35 @@ struct CombineArgs {
     void *out;
 };
 
+struct BackwardArgs {
+    const void *g;               // bf16 [T, H] gradient of combine's output
+    int64_t row_vecs;            // 16-byte vectors (8 bf16) per row
+    int32_t num_tokens, num_topk, num_experts;
+    int64_t capacity;
+    const int32_t *dst, *counts, *psum, *src_meta, *scalars;
+    const float *w;              // [T, K] or null
+    const void *y;               // bf16 [capacity, H] (weight gradient)
+    const void *bias;            // bf16 [E, H] or null
+    const void *topk_idx;
+    bool idx_is_i64;
+    void *grad_y;                // bf16 [capacity, H] or null
+    float *grad_w;               // [T, K] or null
+    float *grad_bias;            // [E, H] or null
+};
+
+struct GatherArgs {
+    const float *row_values;     // [capacity] or null (gathers zeros)
+    int64_t num_slots, capacity;
+    const int32_t *dst, *scalars;
+    float *out;                  // [T, K]
+};
+
 hipError_t launch_handle_clear(int32_t *scalars, uint64_t *tile_status,
                                int64_t status_words, hipStream_t stream);
 hipError_t launch_layout(const LayoutArgs &a, hipStream_t stream, CallEvents ev);
 hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t stream, CallEvents ev);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t stream, CallEvents ev);
+hipError_t launch_combine_backward(const BackwardArgs &a, hipStream_t stream, CallEvents ev);
+hipError_t launch_gather_rows(const GatherArgs &a, hipStream_t stream, CallEvents ev);
 
 }  // namespace ep

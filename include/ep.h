@@ -242,8 +242,45 @@ ep_status ep_combine(const ep_handle *h, const void *y, ep_dtype y_dtype,
                      const void *bias, void *out, hipStream_t stream);
 
 /*
+ * Backward of combine [README, training example: the backward of combine is
+ * a dispatch of the output gradient, and the combined top-k weights carry the
+ * weights' gradient; forward as in ep_combine].  With
+ * out[t] = sum_k w[t,k] * (y[r] + b[e]) and g = d loss / d out:
+ *   grad_y            NULL or bf16 [capacity, hidden]: routed row r = dst[t,k]
+ *                     gets bf16_rne(fl32(w[t,k] * g[t])) (g[t] without
+ *                     weights); other rows are not written.
+ *   grad_topk_weights NULL or fp32 [T, K]: sum_h g[t][h] * (y[r][h] + b[e][h]),
+ *                     0 for an empty slot (needs y; bias may be NULL).
+ *   grad_bias         NULL or fp32 [E, hidden]: sum over expert e's rows of
+ *                     w * g[t] (every expert written, 0 if it has no row).
+ * Both sums are accumulated in binary64 from exact terms and rounded once to
+ * binary32.  grad_out is bf16 [T, hidden]; topk_weights / bias as given to
+ * ep_combine.  Up to three kernels on `stream`.
+ */
+ep_status ep_combine_backward(const ep_handle *h, const void *grad_out, int32_t hidden,
+                              const float *topk_weights, const void *y, const void *bias,
+                              void *grad_y, float *grad_topk_weights, float *grad_bias,
+                              hipStream_t stream);
+
+/*
+ * Backward of dispatch [README, training example: the backward of dispatch
+ * is a combine of the gradient rows, returning the gradient of the received
+ * top-k weights as well].
+ *   grad_out_x        bf16 [capacity, hidden]: gradient of out_x (for an FP8
+ *                     dispatch the gradient is bf16).
+ *   grad_out_w        NULL or fp32 [capacity]: gradient of out_w.
+ *   grad_x            NULL or bf16 [T, hidden]: the combine of grad_out_x with
+ *                     no weights and no bias (slot order, binary32, RNE).
+ *   grad_topk_weights NULL or fp32 [T, K]: grad_out_w[dst[t,k]], 0 for an
+ *                     empty slot (0 everywhere when grad_out_w is NULL).
+ */
+ep_status ep_dispatch_backward(const ep_handle *h, const void *grad_out_x, int32_t hidden,
+                               const float *grad_out_w, void *grad_x, float *grad_topk_weights,
+                               hipStream_t stream);
+
+/*
  * Profiling hook (the tracing the pages leave to CUDA events, [Ch8 §8.2]):
- * the next ep_layout, ep_dispatch or ep_combine call made on this host
+ * the next layout, dispatch, combine or backward call made on this host
  * thread stamps `start` when its first kernel begins and `stop` when its
  * last kernel ends.  The events ride on the kernel dispatches themselves
  * (AMD's hipExtLaunchKernel), so the interval holds kernel execution only,

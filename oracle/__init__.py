@@ -196,7 +196,8 @@ def combine_backward(g_bits, lay: Layout, topk_idx, weights=None, y_bits=None, b
                      grad_y=None, lib=None):
     """Backward of combine.  g_bits: uint16 [T, H] (bf16 gradient of out).
     Returns (grad_y uint16 [capacity, H] or None, grad_w float64 [T, K] or
-    None, grad_bias float32 [E, H] or None).  grad_y may be passed pre-filled
+    None, grad_bias float64 [E, H] or None); the float64 outputs are binary64
+    reference sums.  grad_y may be passed pre-filled
     (rows without a slot keep their content)."""
     lib = lib or load()
     g = _c(g_bits, np.uint16)
@@ -211,7 +212,7 @@ def combine_backward(g_bits, lay: Layout, topk_idx, weights=None, y_bits=None, b
     if want_grad_y:
         gy = grad_y if grad_y is not None else np.zeros((capacity, H), np.uint16)
     gw = np.zeros((T, K), np.float64) if want_grad_w else None
-    gb = np.zeros((E, H), np.float32) if want_grad_bias else None
+    gb = np.zeros((E, H), np.float64) if want_grad_bias else None
     if want_grad_w:
         assert y is not None, "grad_w needs the expert outputs y"
     src = _c(lay.src_meta, np.int32)

@@ -296,9 +296,12 @@ void oracle_combine_f64(int64_t T, int64_t K, int64_t H, const uint16_t *y,
  *   grad_w[t,k]     = sum_h g[t][h] * (y[r][h] + b[e][h])   (binary64, no
  *                     rounding of the terms: the reference value), 0 for an
  *                     empty slot
- *   grad_bias[e][h] = sum over the rows of expert e in row order of
- *                     fl32(w * g[t][h]), binary32 from +0.0
- * Any output pointer may be NULL.  Rows of grad_y that hold no slot are not
+ *   grad_bias[e][h] = sum over the rows of expert e of w * g[t][h]
+ *                     (binary64; each product of a binary32 weight and a
+ *                     bf16 value is exact in binary64)
+ * grad_w and grad_bias are reference values: binary64 sums of exact terms,
+ * so their evaluation order changes them only by binary64 rounding.  Any
+ * output pointer may be NULL.  Rows of grad_y that hold no slot are not
  * written.
  */
 void oracle_combine_backward(int64_t T, int64_t K, int64_t E, int64_t H,
@@ -307,7 +310,7 @@ void oracle_combine_backward(int64_t T, int64_t K, int64_t E, int64_t H,
                              const int64_t *topk_idx, const int32_t *dst,
                              const int32_t *counts, const int32_t *psum,
                              const int32_t *src_meta, uint16_t *grad_y,
-                             double *grad_w, float *grad_bias)
+                             double *grad_w, double *grad_bias)
 {
     for (int64_t t = 0; t < T; ++t) {
         for (int64_t k = 0; k < K; ++k) {
@@ -339,13 +342,12 @@ void oracle_combine_backward(int64_t T, int64_t K, int64_t E, int64_t H,
         return;
     for (int64_t e = 0; e < E; ++e) {
         for (int64_t h = 0; h < H; ++h) {
-            float acc = 0.0f;
+            double acc = 0.0;
             for (int64_t r = psum[e]; r < (int64_t)psum[e] + counts[e]; ++r) {
                 int64_t i = src_meta[r];
                 int64_t t = i / K;
-                float gv = bf16_to_f32(g[t * H + h]);
-                float s = w ? w[i] * gv : gv;
-                acc = acc + s;
+                double gv = (double)bf16_to_f32(g[t * H + h]);
+                acc += w ? (double)w[i] * gv : gv;
             }
             grad_bias[e * H + h] = acc;
         }

@@ -150,7 +150,7 @@ def combine_backward_expected(g_bits, topk_idx, dst, weights, y_bits, bias_bits,
                               psum, src_meta, E):
     """Backward of combine written out directly: grad_y rows as bf16 of the
     float32 product w * g, grad_w as a float64 dot product over channels,
-    grad_bias as a float32 running sum over each expert's rows in row order."""
+    grad_bias as a float64 sum over each expert's rows."""
     idx = np.asarray(topk_idx, np.int64)
     T, K = idx.shape
     g = bf16_bits_to_f32(g_bits)
@@ -170,13 +170,13 @@ def combine_backward_expected(g_bits, topk_idx, dst, weights, y_bits, bias_bits,
             rows[int(r)] = f32_to_bf16_bits_torch(s[None, :])[0]
             v = yf[r] + (bf[idx[t, k]] if bf is not None else 0.0)
             gw[t, k] = float(np.dot(g[t].astype(np.float64), v))
-    gb = np.zeros((E, H), np.float32)
+    gb = np.zeros((E, H), np.float64)
     for e in range(E):
-        acc = np.zeros(H, np.float32)
+        acc = np.zeros(H, np.float64)
         for r in range(int(psum[e]), int(psum[e]) + int(counts[e])):
             i = int(src_meta[r])
             t, k = divmod(i, K)
-            s = g[t] if w is None else (w[t, k] * g[t]).astype(np.float32)
-            acc = (acc + s).astype(np.float32)
+            gd = g[t].astype(np.float64)
+            acc = acc + (gd if w is None else float(w[t, k]) * gd)
         gb[e] = acc
     return rows, gw, gb

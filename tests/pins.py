@@ -390,7 +390,7 @@ def pin_combine_backward_bruteforce(lib):
             for r, v in rows.items():
                 np.testing.assert_array_equal(gy[r], v)
             np.testing.assert_allclose(gw, egw, rtol=1e-12, atol=1e-12)
-            np.testing.assert_array_equal(gb.view(np.uint32), egb.view(np.uint32))
+            np.testing.assert_allclose(gb, egb, rtol=1e-12, atol=1e-12)
 
 
 def pin_combine_backward_adjoint(lib):

@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported():
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(ep.lib(), n), n
         assert n in ep._SIGNATURES, f"binding lacks {n}"
@@ -189,3 +189,20 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(ep, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         ep.lib()
+
+
+def test_backward_validation():
+    h = _fake_handle()
+    assert ep.ep_combine_backward(_fake_handle(laid_out=0), A16, 64, None, A16, None, A16, None,
+                                  None, None) == ep.EP_ERR_NOT_LAID_OUT
+    assert ep.ep_combine_backward(h, A16, 12, None, A16, None, A16, None, None,
+                                  None) == ep.EP_ERR_MISALIGNED
+    assert ep.ep_combine_backward(h, None, 64, None, A16, None, A16, None, None,
+                                  None) == ep.EP_ERR_NULL
+    assert ep.ep_combine_backward(h, A16, 64, None, None, None, None, A16, None,
+                                  None) == ep.EP_ERR_NULL          # grad_w needs y
+    assert ep.ep_combine_backward(h, A16 + 8, 64, None, A16, None, A16, None, None,
+                                  None) == ep.EP_ERR_MISALIGNED
+    assert ep.ep_dispatch_backward(h, None, 64, None, A16, None, None) == ep.EP_ERR_NULL
+    assert ep.ep_dispatch_backward(h, A16, 0, None, A16, None, None) == ep.EP_ERR_SHAPE
+    assert ep.ep_dispatch_backward(h, A16, 64, A16 + 2, A16, A16, None) == ep.EP_ERR_MISALIGNED

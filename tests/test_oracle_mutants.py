@@ -60,10 +60,10 @@ MUTANTS = {
         "if (grad_w) {\n                    double v = (double)bf16_to_f32(y[r * H + h]);",
         "if (grad_w) {\n                    double v = (double)bf16_to_f32(y[(r > 0 ? r - 1 : r) * H + h]);"),
     "cb_grad_w_no_grad": ("acc += (double)gv * v;", "acc += v;"),
-    "cb_grad_bias_reverse": (
+    "cb_grad_bias_skips_last_row": (
         "for (int64_t r = psum[e]; r < (int64_t)psum[e] + counts[e]; ++r) {",
-        "for (int64_t r = (int64_t)psum[e] + counts[e] - 1; r >= psum[e]; --r) {"),
-    "cb_grad_bias_no_weight": ("float s = w ? w[i] * gv : gv;", "float s = gv;"),
+        "for (int64_t r = psum[e]; r < (int64_t)psum[e] + counts[e] - 1; ++r) {"),
+    "cb_grad_bias_no_weight": ("acc += w ? (double)w[i] * gv : gv;", "acc += gv;"),
     "db_grad_w_wrong_row": ("grad_w[i] = (dst[i] >= 0 && gw) ? gw[dst[i]] : 0.0f;",
                             "grad_w[i] = (dst[i] >= 0 && gw) ? gw[i % 7] : 0.0f;"),
 }
