@@ -47,6 +47,8 @@ def parse():
                    help="minimum oracle time for the CPU baseline")
     p.add_argument("--cold-reps", type=int, default=30,
                    help="calls per kernel in the cold-cache phase after the timed steps (0 = skip)")
+    p.add_argument("--backward-reps", type=int, default=30,
+                   help="calls of each backward entry point after the timed steps (0 = skip)")
     p.add_argument("--flush", action="store_true",
                    help="read a 1 GiB scratch buffer before every call (outside the per-call "
                         "events) so each kernel starts with cold L2 and MALL")
@@ -272,6 +274,38 @@ def main():
                                   "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
         del big
 
+    # Backward pair on the same layout (a separate phase after the timed
+    # steps): combine backward with row and weight gradients, dispatch
+    # backward with the row combine and the weight gather.
+    backward = None
+    if args.backward_reps > 0:
+        T, K, H = cfg.tokens, cfg.topk, cfg.hidden
+        g = W.payload_bf16(T, H, cfg.seed + 1, 3, "cuda")
+        grad_y = torch.empty((cap, H), dtype=torch.bfloat16, device="cuda")
+        gw_rows = torch.randn(cap, device="cuda")
+        bb = {"combine_backward": T * 2 * H + V * 2 * H + V * 2 * H + 8 * T * K + 4 * T * K,
+              "dispatch_backward": V * 2 * H + T * 2 * H + 4 * T * K + 8 * T * K + 4 * T * K}
+        bcalls = {"combine_backward": lambda: h.combine_backward(
+                      g, topk_weights=w, y=wl.y, grad_y=grad_y, want_grad_weights=True),
+                  "dispatch_backward": lambda: h.dispatch_backward(
+                      wl.y, grad_out_w=gw_rows, want_grad_weights=True)}
+        backward = {}
+        for name, fn in bcalls.items():
+            fn()
+            pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                     for _ in range(args.backward_reps)]
+            for e0, e1 in pairs:
+                e0.record()
+                e1.record()
+            for e0, e1 in pairs:
+                ep.time_next_call(e0, e1)
+                fn()
+            torch.cuda.synchronize()
+            us = statistics.mean(e0.elapsed_time(e1) * 1e3 for e0, e1 in pairs)
+            gbps = bb[name] / (us * 1e-6) / 1e9
+            backward[name] = {"us_mean": round(us, 2), "bytes": bb[name], "GBps": round(gbps, 1),
+                              "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+
     total_bytes = sum(nbytes.values())
     if args.flush:
         # The wall time also holds the cache flushes; use the calls' own time.
@@ -329,6 +363,7 @@ def main():
         "cache_flush_between_calls": bool(args.flush),
         "kernels": kernels,
         "kernels_cold_cache": kernels_cold,
+        "backward": backward,
         "roofline": roofline,
         "ceilings": ceil,
         "cpu_baseline": cpu,

@@ -54,6 +54,15 @@ def _bind(lib):
                                             _P, _P, _P, _P]
     lib.oracle_dispatch_backward.restype = None
     lib.oracle_dispatch_backward.argtypes = [_I, _I, _I, _P, _P, _P, _P, _P, _P]
+    lib.oracle_rank_layout.restype = _I
+    lib.oracle_rank_layout.argtypes = [_I, _I, _I, _P, _P, _P]
+    lib.oracle_dispatch_rank.restype = None
+    lib.oracle_dispatch_rank.argtypes = [_I, _I, _I, _I, _P, _I, _P, _I, _I, _P, _P, _P, _P,
+                                         _P, _I, _I, _P, _P]
+    lib.oracle_combine_rank.restype = None
+    lib.oracle_combine_rank.argtypes = [_I, _I, _P, _P, _P, _P, _P]
+    lib.oracle_combine_token_bias.restype = None
+    lib.oracle_combine_token_bias.argtypes = [_I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P]
     return lib
 
 
@@ -237,3 +246,79 @@ def dispatch_backward(go_bits, topk_idx, dst, gw=None, lib=None):
     lib.oracle_dispatch_backward(T, K, H, _ptr(go), _ptr(g), _ptr(idx), _ptr(d), _ptr(gx),
                                  _ptr(gwo))
     return gx, gwo
+
+
+def rank_layout(topk_idx, num_experts: int, lib=None):
+    """Returns (recv_row int32 [T], recv_src int32 [num_recv], num_recv)."""
+    lib = lib or load()
+    idx = _c(topk_idx, np.int64)
+    T, K = idx.shape
+    row = np.full(T, -7, np.int32)
+    src = np.full(max(T, 1), -7, np.int32)
+    n = int(lib.oracle_rank_layout(T, K, num_experts, _ptr(idx), _ptr(row), _ptr(src)))
+    return row, src[:n], n
+
+
+def dispatch_rank(x_bytes, topk_idx, num_experts, recv_row, rows, sf=None, sf_strides=None,
+                  weights=None, out_x=None, out_sf=None, out_idx=None, out_w=None, lib=None):
+    """Rank-layout dispatch; outputs have ``rows`` rows (pre-fill to check
+    untouched rows).  Returns (out_x, out_sf, out_idx int64 [rows, K],
+    out_w float32 [rows, K])."""
+    lib = lib or load()
+    x = np.ascontiguousarray(x_bytes, dtype=np.uint8)
+    idx = _c(topk_idx, np.int64)
+    T, K = idx.shape
+    R = x.shape[1]
+    if out_x is None:
+        out_x = np.zeros((rows, R), np.uint8)
+    num_sf = ts = hs = ots = ohs = 0
+    sf_arr = None
+    if sf is not None:
+        sf_arr = np.asarray(sf)
+        ts, hs = sf_strides if sf_strides is not None else (sf_arr.shape[1], 1)
+        num_sf = R // 128
+        if out_sf is None:
+            out_sf = np.zeros((rows, num_sf), np.float32)
+        ots, ohs = num_sf, 1
+    if out_idx is None:
+        out_idx = np.zeros((rows, K), np.int64)
+    if out_w is None:
+        out_w = np.zeros((rows, K), np.float32)
+    w = None if weights is None else _c(weights, np.float32)
+    lib.oracle_dispatch_rank(T, K, num_experts, R, _ptr(x), num_sf, _ptr(sf_arr), ts, hs,
+                             _ptr(w), _ptr(idx), _ptr(_c(recv_row, np.int32)), _ptr(out_x),
+                             _ptr(out_sf), ots, ohs, _ptr(out_idx), _ptr(out_w))
+    return out_x, out_sf, out_idx, out_w
+
+
+def combine_rank(x_bits, recv_row, b0_bits=None, b1_bits=None, lib=None):
+    """x_bits: uint16 [rows, H]; returns uint16 [T, H]."""
+    lib = lib or load()
+    x = _c(x_bits, np.uint16)
+    row = _c(recv_row, np.int32)
+    T = row.shape[0]
+    H = x.shape[1]
+    out = np.zeros((T, H), np.uint16)
+    b0 = None if b0_bits is None else _c(b0_bits, np.uint16)
+    b1 = None if b1_bits is None else _c(b1_bits, np.uint16)
+    lib.oracle_combine_rank(T, H, _ptr(x), _ptr(row), _ptr(b0), _ptr(b1), _ptr(out))
+    return out
+
+
+def combine_token_bias(y_bits, topk_idx, dst, weights=None, bias_bits=None, b0_bits=None,
+                       b1_bits=None, lib=None):
+    """Expanded combine plus per-token biases bias_0, bias_1 (uint16 [T, H])."""
+    lib = lib or load()
+    y = _c(y_bits, np.uint16)
+    idx = _c(topk_idx, np.int64)
+    d = _c(dst, np.int32)
+    T, K = idx.shape
+    H = y.shape[1]
+    out = np.zeros((T, H), np.uint16)
+    w = None if weights is None else _c(weights, np.float32)
+    b = None if bias_bits is None else _c(bias_bits, np.uint16)
+    b0 = None if b0_bits is None else _c(b0_bits, np.uint16)
+    b1 = None if b1_bits is None else _c(b1_bits, np.uint16)
+    lib.oracle_combine_token_bias(T, K, H, _ptr(y), _ptr(w), _ptr(b), _ptr(idx), _ptr(d),
+                                  _ptr(b0), _ptr(b1), _ptr(out))
+    return out

@@ -232,9 +232,10 @@ static uint16_t f32_to_bf16(float f)
  * w    [T*K] fp32 or NULL; bias [E, H] bf16 bits or NULL
  * out  [T, H] bf16 bits
  */
-void oracle_combine(int64_t T, int64_t K, int64_t H, const uint16_t *y,
-                    const float *w, const uint16_t *bias,
-                    const int64_t *topk_idx, const int32_t *dst, uint16_t *out)
+static void combine_tokens(int64_t T, int64_t K, int64_t H, const uint16_t *y,
+                           const float *w, const uint16_t *bias,
+                           const int64_t *topk_idx, const int32_t *dst,
+                           const uint16_t *b0, const uint16_t *b1, uint16_t *out)
 {
     for (int64_t t = 0; t < T; ++t) {
         for (int64_t h = 0; h < H; ++h) {
@@ -251,9 +252,20 @@ void oracle_combine(int64_t T, int64_t K, int64_t H, const uint16_t *y,
                 float p = w ? w[t * K + k] * v : v;
                 acc = acc + p;
             }
+            if (b0)
+                acc = acc + bf16_to_f32(b0[t * H + h]);
+            if (b1)
+                acc = acc + bf16_to_f32(b1[t * H + h]);
             out[t * H + h] = f32_to_bf16(acc);
         }
     }
+}
+
+void oracle_combine(int64_t T, int64_t K, int64_t H, const uint16_t *y,
+                    const float *w, const uint16_t *bias,
+                    const int64_t *topk_idx, const int32_t *dst, uint16_t *out)
+{
+    combine_tokens(T, K, H, y, w, bias, topk_idx, dst, NULL, NULL, out);
 }
 
 /*
@@ -373,4 +385,108 @@ void oracle_dispatch_backward(int64_t T, int64_t K, int64_t H,
         return;
     for (int64_t i = 0; i < T * K; ++i)
         grad_w[i] = (dst[i] >= 0 && gw) ? gw[dst[i]] : 0.0f;
+}
+
+/*
+ * Non-expanded ("rank") layout [Ch7 §7.4: the normal layout keeps each
+ * received token once, [received_tokens, hidden] plus top-k metadata;
+ * §7.5: the handle keeps the received-token count].  At one rank a token is
+ * received when it has at least one valid slot (R12); received tokens keep
+ * their order.  recv_row[t] is its row (-1 if not received); recv_src[row]
+ * is the token of each row.  Returns the number of received tokens.
+ */
+int64_t oracle_rank_layout(int64_t T, int64_t K, int64_t E,
+                           const int64_t *topk_idx, int32_t *recv_row,
+                           int32_t *recv_src)
+{
+    int64_t rows = 0;
+    for (int64_t t = 0; t < T; ++t) {
+        int any = 0;
+        for (int64_t k = 0; k < K; ++k) {
+            int64_t e = topk_idx[t * K + k];
+            if (e >= 0 && e < E)
+                any = 1;
+        }
+        if (any) {
+            recv_row[t] = (int32_t)rows;
+            recv_src[rows] = (int32_t)t;
+            ++rows;
+        } else {
+            recv_row[t] = -1;
+        }
+    }
+    return rows;
+}
+
+/*
+ * Dispatch into the rank layout [Ch7 §7.3: the epilogue writes the received
+ * rows, their scale factors and the received top-k ids and weights].  Row
+ * recv_row[t] gets the bytes of x[t], its scales, the token's top-k ids
+ * (-1 for an empty or invalid slot) and weights (0 for such a slot; 1 for a
+ * valid slot when w is NULL).  Rows of tokens that are not received do not
+ * exist; nothing else is written.
+ */
+void oracle_dispatch_rank(int64_t T, int64_t K, int64_t E, int64_t row_bytes,
+                          const uint8_t *x, int64_t num_sf, const float *sf,
+                          int64_t sf_ts, int64_t sf_hs, const float *w,
+                          const int64_t *topk_idx, const int32_t *recv_row,
+                          uint8_t *out_x, float *out_sf, int64_t o_ts,
+                          int64_t o_hs, int64_t *out_idx, float *out_w)
+{
+    for (int64_t t = 0; t < T; ++t) {
+        int64_t r = recv_row[t];
+        if (r < 0)
+            continue;
+        memcpy(&out_x[r * row_bytes], &x[t * row_bytes], (size_t)row_bytes);
+        for (int64_t j = 0; j < num_sf; ++j)
+            out_sf[r * o_ts + o_hs * j] = sf[t * sf_ts + sf_hs * j];
+        for (int64_t k = 0; k < K; ++k) {
+            int64_t e = topk_idx[t * K + k];
+            int valid = e >= 0 && e < E;
+            if (out_idx)
+                out_idx[r * K + k] = valid ? e : -1;
+            if (out_w)
+                out_w[r * K + k] = valid ? (w ? w[t * K + k] : 1.0f) : 0.0f;
+        }
+    }
+}
+
+/*
+ * Combine from the rank layout with the two per-token biases [Ch8 §8.1: the
+ * combine takes bias_0 and bias_1 and reduces back to the source token].  At
+ * one rank each received token has exactly one row, already reduced over its
+ * experts, so out[t][h] = bf16(fl32(fl32(v + b0[t][h]) + b1[t][h])) with
+ * v = x[recv_row[t]][h], or +0.0 for a token that was not received.  Either
+ * bias may be NULL (its add is skipped).
+ */
+void oracle_combine_rank(int64_t T, int64_t H, const uint16_t *x,
+                         const int32_t *recv_row, const uint16_t *b0,
+                         const uint16_t *b1, uint16_t *out)
+{
+    for (int64_t t = 0; t < T; ++t) {
+        int64_t r = recv_row[t];
+        for (int64_t h = 0; h < H; ++h) {
+            float acc = r >= 0 ? bf16_to_f32(x[r * H + h]) : 0.0f;
+            if (b0)
+                acc = acc + bf16_to_f32(b0[t * H + h]);
+            if (b1)
+                acc = acc + bf16_to_f32(b1[t * H + h]);
+            out[t * H + h] = f32_to_bf16(acc);
+        }
+    }
+}
+
+/*
+ * The expanded combine with the per-token biases added after the slot
+ * reduction (R9 for the expert bias; bias_0 then bias_1 per token):
+ *   out[t][h] = bf16(fl32(fl32(acc + b0[t][h]) + b1[t][h]))
+ * where acc is oracle_combine's binary32 slot-order sum.
+ */
+void oracle_combine_token_bias(int64_t T, int64_t K, int64_t H,
+                               const uint16_t *y, const float *w,
+                               const uint16_t *bias, const int64_t *topk_idx,
+                               const int32_t *dst, const uint16_t *b0,
+                               const uint16_t *b1, uint16_t *out)
+{
+    combine_tokens(T, K, H, y, w, bias, topk_idx, dst, b0, b1, out);
 }

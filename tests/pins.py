@@ -436,6 +436,113 @@ def pin_dispatch_backward(lib):
     assert abs(lhs - rhs) <= 2.0 ** -7 * mag
 
 
+# ----------------------------------------------------------------------------
+# rank layout and per-token biases
+
+
+def pin_rank_layout_golden(lib):
+    g = _golden("layout_hand.json")["rank_layout"]
+    idx = np.array(g["topk_idx"])
+    row, src, n = oracle.rank_layout(idx, g["num_experts"], lib=lib)
+    assert row.tolist() == g["recv_row"] and src.tolist() == g["recv_src"] and n == 2
+    x = np.arange(4 * 16, dtype=np.uint8).reshape(4, 16)
+    ox, _, oi, ow = oracle.dispatch_rank(x, idx, g["num_experts"], row, 2,
+                                         weights=np.array(g["weights"], np.float32), lib=lib)
+    assert oi.tolist() == g["recv_topk_idx"]
+    assert ow.tolist() == g["recv_topk_weights"]
+    assert ox.tolist() == x[[1, 3]].tolist()
+
+
+def pin_rank_layout_cumsum(lib):
+    """Rank rows are the running count of received tokens (numpy cumsum)."""
+    rng = np.random.default_rng(43)
+    for _ in range(30):
+        T, K, E = int(rng.integers(0, 90)), int(rng.integers(1, 6)), int(rng.integers(1, 12))
+        idx = rng.integers(-3, E + 2, size=(T, K))
+        idx = np.where(rng.random((T, K)) < 0.5, -1, idx)
+        row, src, n = oracle.rank_layout(idx, E, lib=lib)
+        ok = ((idx >= 0) & (idx < E)).any(axis=1) if T else np.zeros(0, bool)
+        np.testing.assert_array_equal(row, np.where(ok, np.cumsum(ok) - 1, -1))
+        np.testing.assert_array_equal(src, np.nonzero(ok)[0])
+        assert n == int(ok.sum())
+
+
+def pin_dispatch_rank_closed_form(lib):
+    rng = np.random.default_rng(47)
+    T, K, E, H = 60, 4, 10, 256
+    idx = np.where(rng.random((T, K)) < 0.6, -1, rng.integers(0, E + 2, size=(T, K)))
+    row, src, n = oracle.rank_layout(idx, E, lib=lib)
+    x = rng.integers(0, 256, size=(T, H), dtype=np.uint8)
+    sf = rng.random((T, H // 128), dtype=np.float32)
+    w = rng.random((T, K), dtype=np.float32)
+    rows = n + 3
+    ox = np.full((rows, H), 0xA5, np.uint8)
+    ox, osf, oi, ow = oracle.dispatch_rank(x, idx, E, row, rows, sf=sf, weights=w, out_x=ox,
+                                           lib=lib)
+    np.testing.assert_array_equal(ox[:n], x[src])
+    assert np.all(ox[n:] == 0xA5)
+    np.testing.assert_array_equal(osf[:n], sf[src])
+    valid = (idx >= 0) & (idx < E)
+    np.testing.assert_array_equal(oi[:n], np.where(valid, idx, -1)[src])
+    np.testing.assert_array_equal(ow[:n], np.where(valid, w, 0.0).astype(np.float32)[src])
+
+
+def _f32_bf16(rng, shape, scale=1.0):
+    return _bf16_from_normal(rng, shape, scale)
+
+
+def pin_combine_rank_numpy(lib):
+    rng = np.random.default_rng(53)
+    T, K, E, H = 50, 3, 7, 40
+    idx = np.where(rng.random((T, K)) < 0.5, -1, rng.integers(0, E, size=(T, K)))
+    row, src, n = oracle.rank_layout(idx, E, lib=lib)
+    x = _f32_bf16(rng, (max(n, 1), H), 2.0)
+    b0, b1 = _f32_bf16(rng, (T, H)), _f32_bf16(rng, (T, H), 0.5)
+    for bb0, bb1 in ((None, None), (b0, None), (b0, b1), (None, b1)):
+        got = oracle.combine_rank(x, row, bb0, bb1, lib=lib)
+        acc = np.where((row >= 0)[:, None], _bits_to_float(x)[np.maximum(row, 0)], np.float32(0))
+        for b in (bb0, bb1):
+            if b is not None:
+                acc = (acc + _bits_to_float(b)).astype(np.float32)
+        np.testing.assert_array_equal(got, BF.f32_to_bf16_bits_torch(acc))
+
+
+def pin_combine_rank_golden(lib):
+    g = _golden("combine_hand.json")["rank_combine"]
+    got = oracle.combine_rank(_bf16_bits(g["x"]), np.array(g["recv_row"], np.int32),
+                              _bf16_bits(g["bias_0"]), _bf16_bits(g["bias_1"]), lib=lib)
+    assert got.tolist() == g["expected_bits"]
+
+
+def pin_combine_token_bias(lib):
+    """Zero-bias special case equals the plain combine; with biases it equals
+    a numpy float32 sum that adds bias_0 then bias_1 after the slots; and the
+    hand-worked order cases."""
+    rng = np.random.default_rng(59)
+    idx, dst, y, w, b = _combine_inputs(rng, 33, 6, 11, 24)
+    np.testing.assert_array_equal(oracle.combine_token_bias(y, idx, dst, w, b, lib=lib),
+                                  oracle.combine(y, idx, dst, w, b, lib=lib))
+    T, H = idx.shape[0], y.shape[1]
+    b0, b1 = _f32_bf16(rng, (T, H)), _f32_bf16(rng, (T, H), 0.1)
+    got = oracle.combine_token_bias(y, idx, dst, w, b, b0, b1, lib=lib)
+    yf = _bits_to_float(y)
+    bf = _bits_to_float(b)
+    acc = np.zeros((T, H), np.float32)
+    for k in range(idx.shape[1]):
+        ok = dst[:, k] >= 0
+        v = (yf[np.maximum(dst[:, k], 0)] + bf[np.maximum(idx[:, k], 0)]).astype(np.float32)
+        v = (w[:, k:k + 1] * v).astype(np.float32)
+        acc = np.where(ok[:, None], (acc + v).astype(np.float32), acc)
+    acc = (acc + _bits_to_float(b0)).astype(np.float32)
+    acc = (acc + _bits_to_float(b1)).astype(np.float32)
+    np.testing.assert_array_equal(got, BF.f32_to_bf16_bits_torch(acc))
+    g = _golden("combine_hand.json")["token_bias"]
+    got = oracle.combine_token_bias(_bf16_bits(g["y"]), np.array(g["topk_idx"]),
+                                    np.array(g["dst"]), b0_bits=_bf16_bits(g["bias_0"]),
+                                    b1_bits=_bf16_bits(g["bias_1"]), lib=lib)
+    assert got.tolist() == g["expected_bits"]
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 

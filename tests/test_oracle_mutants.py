@@ -66,6 +66,28 @@ MUTANTS = {
     "cb_grad_bias_no_weight": ("acc += w ? (double)w[i] * gv : gv;", "acc += gv;"),
     "db_grad_w_wrong_row": ("grad_w[i] = (dst[i] >= 0 && gw) ? gw[dst[i]] : 0.0f;",
                             "grad_w[i] = (dst[i] >= 0 && gw) ? gw[i % 7] : 0.0f;"),
+    "rank_counts_invalid_ids": ("            if (e >= 0 && e < E)\n                any = 1;",
+                                "            if (e != -1)\n                any = 1;"),
+    "rank_row_off_by_one": ("recv_row[t] = (int32_t)rows;", "recv_row[t] = (int32_t)rows + (t > 2);"),
+    "rank_idx_not_masked": ("out_idx[r * K + k] = valid ? e : -1;", "out_idx[r * K + k] = e;"),
+    "rank_weight_kept_on_empty": ("out_w[r * K + k] = valid ? (w ? w[t * K + k] : 1.0f) : 0.0f;",
+                                  "out_w[r * K + k] = w ? w[t * K + k] : 1.0f;"),
+    "rank_combine_b1_first": (
+        "            float acc = r >= 0 ? bf16_to_f32(x[r * H + h]) : 0.0f;\n"
+        "            if (b0)\n                acc = acc + bf16_to_f32(b0[t * H + h]);\n"
+        "            if (b1)\n                acc = acc + bf16_to_f32(b1[t * H + h]);",
+        "            float acc = r >= 0 ? bf16_to_f32(x[r * H + h]) : 0.0f;\n"
+        "            if (b1)\n                acc = acc + bf16_to_f32(b1[t * H + h]);\n"
+        "            if (b0)\n                acc = acc + bf16_to_f32(b0[t * H + h]);"),
+    "token_bias_before_slots": ('            float acc = 0.0f;\n            for (int64_t k = 0; k < K; ++k) {\n                int64_t r = dst[t * K + k];\n                if (r < 0)\n                    continue;\n                float v = bf16_to_f32(y[r * H + h]);\n                if (bias) {\n                    int64_t e = topk_idx[t * K + k];\n                    v = v + bf16_to_f32(bias[e * H + h]);\n                }\n                float p = w ? w[t * K + k] * v : v;\n                acc = acc + p;\n            }\n            if (b0)\n                acc = acc + bf16_to_f32(b0[t * H + h]);',
+        '            float acc = b0 ? bf16_to_f32(b0[t * H + h]) : 0.0f;\n            for (int64_t k = 0; k < K; ++k) {\n                int64_t r = dst[t * K + k];\n                if (r < 0)\n                    continue;\n                float v = bf16_to_f32(y[r * H + h]);\n                if (bias) {\n                    int64_t e = topk_idx[t * K + k];\n                    v = v + bf16_to_f32(bias[e * H + h]);\n                }\n                float p = w ? w[t * K + k] * v : v;\n                acc = acc + p;\n            }\n'),
+    "token_bias_b1_dropped": (
+        "                acc = acc + p;\n            }\n            if (b0)\n"
+        "                acc = acc + bf16_to_f32(b0[t * H + h]);\n            if (b1)\n"
+        "                acc = acc + bf16_to_f32(b1[t * H + h]);",
+        "                acc = acc + p;\n            }\n            if (b0)\n"
+        "                acc = acc + bf16_to_f32(b0[t * H + h]);\n            if (0)\n"
+        "                acc = acc + bf16_to_f32(b1[t * H + h]);"),
 }
 
 
