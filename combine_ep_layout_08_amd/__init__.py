@@ -26,6 +26,7 @@ __all__ = [
     "ep_workspace_bytes", "ep_handle_init", "ep_layout", "ep_handle_read_counts",
     "ep_handle_import", "ep_dispatch", "ep_combine", "ep_status_str", "ep_handle_sizeof",
     "ep_time_next_call", "time_next_call", "ep_combine_backward", "ep_dispatch_backward",
+    "ep_dispatch_rank", "ep_combine_rank",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libep.so")
@@ -58,6 +59,8 @@ class ep_handle(ctypes.Structure):
         ("topk_idx", ctypes.c_void_p),
         ("topk_idx_dtype", ctypes.c_int32),
         ("status_tiles", ctypes.c_int32),
+        ("recv_row", ctypes.c_void_p),
+        ("recv_src", ctypes.c_void_p),
     ]
 
 
@@ -82,7 +85,10 @@ _SIGNATURES = {
     "ep_handle_import": (ctypes.c_int, [_HP, _P, ctypes.c_int, _I32, _P, _P, _P, _P, _I32, _P]),
     "ep_dispatch": (ctypes.c_int, [_HP, _P, ctypes.c_int, _I32, _P, _I64, _I64, _P, _P, _P,
                                    _I64, _I64, _P, _I32, _P]),
-    "ep_combine": (ctypes.c_int, [_HP, _P, ctypes.c_int, _I32, _P, _P, _P, _P]),
+    "ep_combine": (ctypes.c_int, [_HP, _P, ctypes.c_int, _I32, _P, _P, _P, _P, _P, _P]),
+    "ep_dispatch_rank": (ctypes.c_int, [_HP, _P, ctypes.c_int, _I32, _P, _I64, _I64, _P, _P, _P,
+                                        _I64, _I64, _P, _P, _P]),
+    "ep_combine_rank": (ctypes.c_int, [_HP, _P, _I32, _P, _P, _P, _P]),
     "ep_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "ep_time_next_call": (ctypes.c_int, [_P, _P]),
     "ep_combine_backward": (ctypes.c_int, [_HP, _P, _I32, _P, _P, _P, _P, _P, _P, _P]),
@@ -160,9 +166,23 @@ def ep_dispatch(h: ep_handle, x_ptr, x_dtype, hidden, sf_ptr, sf_ts, sf_hs, w_pt
                              zero_padding, stream)
 
 
-def ep_combine(h: ep_handle, y_ptr, y_dtype, hidden, w_ptr, bias_ptr, out_ptr, stream) -> int:
-    return lib().ep_combine(ctypes.byref(h), y_ptr, y_dtype, hidden, w_ptr, bias_ptr, out_ptr,
-                            stream)
+def ep_combine(h: ep_handle, y_ptr, y_dtype, hidden, w_ptr, bias_ptr, bias0_ptr, bias1_ptr,
+               out_ptr, stream) -> int:
+    return lib().ep_combine(ctypes.byref(h), y_ptr, y_dtype, hidden, w_ptr, bias_ptr, bias0_ptr,
+                            bias1_ptr, out_ptr, stream)
+
+
+def ep_dispatch_rank(h: ep_handle, x_ptr, x_dtype, hidden, sf_ptr, sf_ts, sf_hs, w_ptr,
+                     out_x_ptr, out_sf_ptr, out_ts, out_hs, out_idx_ptr, out_w_ptr,
+                     stream) -> int:
+    return lib().ep_dispatch_rank(ctypes.byref(h), x_ptr, x_dtype, hidden, sf_ptr, sf_ts, sf_hs,
+                                  w_ptr, out_x_ptr, out_sf_ptr, out_ts, out_hs, out_idx_ptr,
+                                  out_w_ptr, stream)
+
+
+def ep_combine_rank(h: ep_handle, x_ptr, hidden, bias0_ptr, bias1_ptr, out_ptr, stream) -> int:
+    return lib().ep_combine_rank(ctypes.byref(h), x_ptr, hidden, bias0_ptr, bias1_ptr, out_ptr,
+                                 stream)
 
 
 def ep_combine_backward(h: ep_handle, grad_out_ptr, hidden, w_ptr, y_ptr, bias_ptr, grad_y_ptr,
@@ -272,6 +292,14 @@ class Handle:
     def scalars(self) -> torch.Tensor:
         return self._view(self.h.scalars, 8)
 
+    @property
+    def recv_row(self) -> torch.Tensor:
+        return self._view(self.h.recv_row, self.h.num_tokens)
+
+    @property
+    def recv_src(self) -> torch.Tensor:
+        return self._view(self.h.recv_src, self.h.max_tokens)
+
     def layout(self, topk_idx: torch.Tensor,
                cumulative_stats: Optional[torch.Tensor] = None) -> "Handle":
         _dev(topk_idx, "topk_idx")
@@ -372,8 +400,12 @@ class Handle:
 
     def combine(self, y: torch.Tensor, topk_weights: Optional[torch.Tensor] = None,
                 bias: Optional[torch.Tensor] = None,
-                out: Optional[torch.Tensor] = None) -> torch.Tensor:
-        """y: bf16 [capacity, H] expert outputs; returns bf16 [T, H]."""
+                out: Optional[torch.Tensor] = None,
+                bias_0: Optional[torch.Tensor] = None,
+                bias_1: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """y: bf16 [capacity, H] expert outputs; returns bf16 [T, H].  bias is
+        the per-expert [E, H] bias; bias_0 / bias_1 are per-token [T, H]
+        biases added after the reduction."""
         T = self.h.num_tokens
         _dev(y, "y")
         _need(y.dtype == torch.bfloat16, "combine input must be bf16")
@@ -388,12 +420,17 @@ class Handle:
             _dev(bias, "bias")
             _need(bias.dtype == torch.bfloat16 and tuple(bias.shape) == (self.h.num_experts, H),
                   "bias must be bf16 [E, H]")
+        for name, b in (("bias_0", bias_0), ("bias_1", bias_1)):
+            if b is not None:
+                _dev(b, name)
+                _need(b.dtype == torch.bfloat16 and tuple(b.shape) == (T, H),
+                      f"{name} must be bf16 [T, H]")
         if out is None:
             out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
         _dev(out, "out")
         _need(tuple(out.shape) == (T, H) and out.dtype == torch.bfloat16, "out must be bf16 [T, H]")
-        _check(ep_combine(self.h, _ptr(y), EP_BF16, H, _ptr(topk_weights), _ptr(bias), _ptr(out),
-                          _stream()), "ep_combine")
+        _check(ep_combine(self.h, _ptr(y), EP_BF16, H, _ptr(topk_weights), _ptr(bias),
+                          _ptr(bias_0), _ptr(bias_1), _ptr(out), _stream()), "ep_combine")
         return out
 
 
@@ -459,3 +496,64 @@ class Handle:
         _check(ep_dispatch_backward(self.h, _ptr(grad_out_x), H, _ptr(grad_out_w), _ptr(gx),
                                     _ptr(gw), _stream()), "ep_dispatch_backward")
         return gx, gw
+
+
+    # ------------------------------------------------------------ rank layout
+
+    def dispatch_rank(self, x: torch.Tensor, sf: Optional[torch.Tensor] = None,
+                      topk_weights: Optional[torch.Tensor] = None, out_x=None, out_sf=None,
+                      out_topk_idx=None, out_topk_weights=None):
+        """Rank (non-expanded) dispatch: one row per received token, in token
+        order, with [max_tokens] rows allocated; rows past num_recv_tokens are
+        not written.  Returns (out_x, out_sf, out_topk_idx, out_topk_weights)."""
+        T, K = self.h.num_tokens, self.h.num_topk
+        M = self.h.max_tokens
+        _dev(x, "x")
+        _need(x.dim() == 2 and x.shape[0] == T, "x must be [num_tokens, hidden]")
+        H = x.shape[1]
+        fp8 = x.dtype in (torch.float8_e4m3fn, torch.uint8)
+        _need(fp8 or x.dtype == torch.bfloat16, "x must be bf16 or FP8 e4m3")
+        if out_x is None:
+            out_x = torch.empty((M, H), dtype=x.dtype, device=x.device)
+        _need(tuple(out_x.shape) == (M, H) and out_x.dtype == x.dtype and out_x.is_cuda,
+              "out_x must be [max_tokens, H]")
+        sf_ts = sf_hs = o_ts = o_hs = 0
+        if fp8:
+            _need(sf is not None and sf.is_cuda and sf.dtype == torch.float32 and
+                  tuple(sf.shape) == (T, H // 128), "sf must be fp32 [T, H/128]")
+            sf_ts, sf_hs = sf.stride()
+            if out_sf is None:
+                out_sf = torch.empty((M, H // 128), dtype=torch.float32, device=x.device)
+            o_ts, o_hs = out_sf.stride()
+        idx_dtype = torch.int64 if self.h.topk_idx_dtype == EP_I64 else torch.int32
+        if out_topk_idx is None:
+            out_topk_idx = torch.empty((M, K), dtype=idx_dtype, device=x.device)
+        _need(out_topk_idx.dtype == idx_dtype and tuple(out_topk_idx.shape) == (M, K),
+              "out_topk_idx must be [max_tokens, K] of the layout's id dtype")
+        if out_topk_weights is None:
+            out_topk_weights = torch.empty((M, K), dtype=torch.float32, device=x.device)
+        if topk_weights is not None:
+            _dev(topk_weights, "topk_weights")
+        _check(ep_dispatch_rank(self.h, _ptr(x), EP_FP8_E4M3 if fp8 else EP_BF16, H, _ptr(sf),
+                                sf_ts, sf_hs, _ptr(topk_weights), _ptr(out_x), _ptr(out_sf),
+                                o_ts, o_hs, _ptr(out_topk_idx), _ptr(out_topk_weights),
+                                _stream()), "ep_dispatch_rank")
+        return out_x, out_sf, out_topk_idx, out_topk_weights
+
+    def combine_rank(self, x: torch.Tensor, bias_0=None, bias_1=None, out=None) -> torch.Tensor:
+        """x: bf16 [max_tokens, H] rank-layout rows; returns bf16 [T, H]."""
+        T, M = self.h.num_tokens, self.h.max_tokens
+        _dev(x, "x")
+        _need(x.dtype == torch.bfloat16 and x.dim() == 2 and x.shape[0] == M,
+              "x must be bf16 [max_tokens, H]")
+        H = x.shape[1]
+        for name, b in (("bias_0", bias_0), ("bias_1", bias_1)):
+            if b is not None:
+                _dev(b, name)
+                _need(b.dtype == torch.bfloat16 and tuple(b.shape) == (T, H),
+                      f"{name} must be bf16 [T, H]")
+        if out is None:
+            out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+        _check(ep_combine_rank(self.h, _ptr(x), H, _ptr(bias_0), _ptr(bias_1), _ptr(out),
+                               _stream()), "ep_combine_rank")
+        return out

@@ -13,7 +13,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libep.so")
 
-SOURCES = ["ep_api.cpp", "ep_layout.hip", "ep_dispatch.hip", "ep_combine.hip", "ep_backward.hip"]
+SOURCES = ["ep_api.cpp", "ep_layout.hip", "ep_dispatch.hip", "ep_combine.hip", "ep_backward.hip",
+           "ep_rank.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

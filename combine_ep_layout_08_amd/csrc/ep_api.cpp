@@ -5,6 +5,7 @@
 #include "../../include/ep.h"
 
 #include <cstring>
+#include <vector>
 
 #include "ep_internal.h"
 
@@ -17,7 +18,7 @@ size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 struct Carve {
-    size_t counts, psum, dst, src_meta, scalars, status, total;
+    size_t counts, psum, dst, src_meta, scalars, status, recv_row, recv_src, total;
     int64_t tiles;
 };
 
@@ -48,6 +49,8 @@ Carve carve(int32_t max_tokens, int32_t K, int32_t E, int64_t capacity) {
     c.src_meta = take(sizeof(int32_t) * static_cast<size_t>(capacity));
     c.scalars = take(sizeof(int32_t) * EP_NUM_SCALARS);
     c.status = take(sizeof(uint64_t) * static_cast<size_t>(c.tiles) * static_cast<size_t>(E + 2));
+    c.recv_row = take(sizeof(int32_t) * static_cast<size_t>(max_tokens));
+    c.recv_src = take(sizeof(int32_t) * static_cast<size_t>(max_tokens));
     c.total = off;
     return c;
 }
@@ -65,7 +68,7 @@ ep::CallEvents take_events() {
 
 bool handle_ready(const ep_handle *h) {
     return h && h->counts && h->psum && h->dst_slot && h->src_meta && h->scalars &&
-           h->tile_status;
+           h->tile_status && h->recv_row && h->recv_src;
 }
 
 }  // namespace
@@ -114,6 +117,8 @@ ep_status ep_handle_init(ep_handle *h, int32_t max_tokens, int32_t K, int32_t E,
     n.topk_idx = nullptr;
     n.topk_idx_dtype = EP_I64;
     n.status_tiles = static_cast<int32_t>(c.tiles);
+    n.recv_row = reinterpret_cast<int32_t *>(base + c.recv_row);
+    n.recv_src = reinterpret_cast<int32_t *>(base + c.recv_src);
     const hipError_t e = ep::launch_handle_clear(n.scalars, n.tile_status,
                                                  c.tiles * static_cast<int64_t>(E + 2), stream);
     if (e != hipSuccess) return EP_ERR_HIP;
@@ -152,6 +157,8 @@ ep_status ep_layout(ep_handle *h, const void *topk_idx, ep_dtype idx_dtype, int3
     a.scalars = h->scalars;
     a.tile_status = h->tile_status;
     a.cumulative_stats = cumulative_stats;
+    a.recv_row = h->recv_row;
+    a.recv_src = h->recv_src;
     const hipError_t e = ep::launch_layout(a, stream, ev);
     if (e != hipSuccess) return EP_ERR_HIP;
     h->num_tokens = num_tokens;
@@ -221,6 +228,22 @@ ep_status ep_handle_import(ep_handle *h, const void *topk_idx, ep_dtype idx_dtyp
         e = hipMemcpy(h->dst_slot, dst_slot, sizeof(int32_t) * slots, hipMemcpyHostToDevice);
     if (e == hipSuccess && expanded)
         e = hipMemcpy(h->src_meta, src_meta, sizeof(int32_t) * expanded, hipMemcpyHostToDevice);
+    if (e == hipSuccess && num_tokens > 0) {
+        // Rank layout from the slots: tokens with a routed slot, in order.
+        std::vector<int32_t> row(num_tokens), src(num_tokens);
+        int32_t n = 0;
+        for (int32_t t = 0; t < num_tokens; ++t) {
+            bool any = false;
+            for (int32_t k = 0; k < h->num_topk; ++k)
+                any = any || dst_slot[static_cast<int64_t>(t) * h->num_topk + k] >= 0;
+            row[t] = any ? n : -1;
+            if (any) src[n++] = t;
+        }
+        e = hipMemcpy(h->recv_row, row.data(), sizeof(int32_t) * num_tokens,
+                      hipMemcpyHostToDevice);
+        if (e == hipSuccess && n > 0)
+            e = hipMemcpy(h->recv_src, src.data(), sizeof(int32_t) * n, hipMemcpyHostToDevice);
+    }
     if (e == hipSuccess) e = hipMemcpy(h->scalars, sc, sizeof(sc), hipMemcpyHostToDevice);
     if (e == hipSuccess)
         e = hipMemcpy(h->scalars + EP_SCALAR_NUM_EXPANDED, &exp32, sizeof(exp32),
@@ -285,8 +308,8 @@ ep_status ep_dispatch(const ep_handle *h, const void *x, ep_dtype x_dtype, int32
 }
 
 ep_status ep_combine(const ep_handle *h, const void *y, ep_dtype y_dtype, int32_t hidden,
-                     const float *topk_weights, const void *bias, void *out,
-                     hipStream_t stream) {
+                     const float *topk_weights, const void *bias, const void *bias_0,
+                     const void *bias_1, void *out, hipStream_t stream) {
     const ep::CallEvents ev = take_events();
     if (!h) return EP_ERR_NULL;
     if (!handle_ready(h)) return EP_ERR_WORKSPACE;
@@ -296,7 +319,9 @@ ep_status ep_combine(const ep_handle *h, const void *y, ep_dtype y_dtype, int32_
     if (hidden % 8 != 0) return EP_ERR_MISALIGNED;
     if (h->num_tokens > 0 && (!y || !out)) return EP_ERR_NULL;
     if (bias && h->num_tokens > 0 && !h->topk_idx) return EP_ERR_NULL;
-    if (!aligned(y, 16) || !aligned(out, 16) || !aligned(bias, 16)) return EP_ERR_MISALIGNED;
+    if (!aligned(y, 16) || !aligned(out, 16) || !aligned(bias, 16) || !aligned(bias_0, 16) ||
+        !aligned(bias_1, 16))
+        return EP_ERR_MISALIGNED;
     if (!aligned(topk_weights, 4)) return EP_ERR_MISALIGNED;
     ep::CombineArgs a{};
     a.y = y;
@@ -311,6 +336,8 @@ ep_status ep_combine(const ep_handle *h, const void *y, ep_dtype y_dtype, int32_
     a.bias = bias;
     a.topk_idx = h->topk_idx;
     a.idx_is_i64 = h->topk_idx_dtype == EP_I64;
+    a.bias_0 = bias_0;
+    a.bias_1 = bias_1;
     a.out = out;
     return hip_status(ep::launch_combine(a, stream, ev));
 }
@@ -399,6 +426,82 @@ ep_status ep_dispatch_backward(const ep_handle *h, const void *grad_out_x, int32
         return hip_status(ep::launch_gather_rows(g, stream, second));
     }
     return EP_OK;
+}
+
+ep_status ep_dispatch_rank(const ep_handle *h, const void *x, ep_dtype x_dtype, int32_t hidden,
+                           const float *sf, int64_t sf_token_stride, int64_t sf_hidden_stride,
+                           const float *topk_weights, void *out_x, float *out_sf,
+                           int64_t out_sf_token_stride, int64_t out_sf_hidden_stride,
+                           void *out_topk_idx, float *out_topk_weights, hipStream_t stream) {
+    const ep::CallEvents ev = take_events();
+    if (!h) return EP_ERR_NULL;
+    if (!handle_ready(h)) return EP_ERR_WORKSPACE;
+    if (!h->laid_out) return EP_ERR_NOT_LAID_OUT;
+    if (x_dtype != EP_BF16 && x_dtype != EP_FP8_E4M3) return EP_ERR_DTYPE;
+    if (hidden <= 0) return EP_ERR_SHAPE;
+    const bool fp8 = x_dtype == EP_FP8_E4M3;
+    if (fp8 ? (hidden % 128) != 0 : (hidden % 8) != 0) return EP_ERR_MISALIGNED;
+    if (fp8 && hidden / 128 > 64 * ep::kMaxSfPerLane) return EP_ERR_UNSUPPORTED;
+    if (!fp8 && (sf || out_sf)) return EP_ERR_DTYPE;
+    const bool rows = h->num_tokens > 0;
+    if (fp8 && (!out_sf || (rows && !sf))) return EP_ERR_NULL;
+    if (sf_token_stride < 0 || sf_hidden_stride < 0 || out_sf_token_stride < 0 ||
+        out_sf_hidden_stride < 0)
+        return EP_ERR_SHAPE;
+    if (!out_x || (rows && !x)) return EP_ERR_NULL;
+    if ((out_topk_idx || out_topk_weights) && rows && !h->topk_idx) return EP_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(out_x, 16)) return EP_ERR_MISALIGNED;
+    if (!aligned(sf, 4) || !aligned(out_sf, 4) || !aligned(topk_weights, 4) ||
+        !aligned(out_topk_weights, 4) ||
+        !aligned(out_topk_idx, h->topk_idx_dtype == EP_I64 ? 8 : 4))
+        return EP_ERR_MISALIGNED;
+    ep::RankArgs a{};
+    a.x = x;
+    a.row_vecs = (fp8 ? hidden : 2 * static_cast<int64_t>(hidden)) / 16;
+    a.num_tokens = h->num_tokens;
+    a.num_topk = h->num_topk;
+    a.num_experts = h->num_experts;
+    a.recv_row = h->recv_row;
+    a.scalars = h->scalars;
+    a.topk_idx = h->topk_idx;
+    a.idx_is_i64 = h->topk_idx_dtype == EP_I64;
+    a.w = topk_weights;
+    a.sf = sf;
+    a.sf_ts = sf_token_stride;
+    a.sf_hs = sf_hidden_stride;
+    a.num_sf = fp8 ? hidden / 128 : 0;
+    a.out = out_x;
+    a.out_sf = out_sf;
+    a.out_ts = out_sf_token_stride;
+    a.out_hs = out_sf_hidden_stride;
+    a.out_idx = out_topk_idx;
+    a.out_w = out_topk_weights;
+    return hip_status(ep::launch_dispatch_rank(a, stream, ev));
+}
+
+ep_status ep_combine_rank(const ep_handle *h, const void *x, int32_t hidden, const void *bias_0,
+                          const void *bias_1, void *out, hipStream_t stream) {
+    const ep::CallEvents ev = take_events();
+    if (!h) return EP_ERR_NULL;
+    if (!handle_ready(h)) return EP_ERR_WORKSPACE;
+    if (!h->laid_out) return EP_ERR_NOT_LAID_OUT;
+    if (hidden <= 0) return EP_ERR_SHAPE;
+    if (hidden % 8 != 0) return EP_ERR_MISALIGNED;
+    if (h->num_tokens > 0 && (!x || !out)) return EP_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(out, 16) || !aligned(bias_0, 16) || !aligned(bias_1, 16))
+        return EP_ERR_MISALIGNED;
+    ep::RankArgs a{};
+    a.x = x;
+    a.row_vecs = hidden / 8;
+    a.num_tokens = h->num_tokens;
+    a.num_topk = h->num_topk;
+    a.num_experts = h->num_experts;
+    a.recv_row = h->recv_row;
+    a.scalars = h->scalars;
+    a.bias_0 = bias_0;
+    a.bias_1 = bias_1;
+    a.out = out;
+    return hip_status(ep::launch_combine_rank(a, stream, ev));
 }
 
 const char *ep_status_str(ep_status s) {

@@ -90,7 +90,7 @@ __device__ inline __amdgpu_buffer_rsrc_t row_rsrc(const void *base, int64_t row,
 
 // One group of columns of one token: loads of every slot first, then the
 // slot-order binary32 accumulation, then the bf16 store.
-template <bool HAS_BIAS, bool HAS_W, typename IdxT>
+template <bool HAS_BIAS, bool HAS_W, bool HAS_TB, typename IdxT>
 __device__ inline void combine_columns(const CombineArgs &a, int64_t t, int64_t v0) {
 #pragma clang fp contract(off)
     const int K = a.num_topk;
@@ -157,6 +157,25 @@ __device__ inline void combine_columns(const CombineArgs &a, int64_t t, int64_t 
             }
         }
     }
+    // Per-token biases after the reduction: bias_0, then bias_1.
+    if (HAS_TB) {
+#pragma unroll
+        for (int u = 0; u < kVecsPerThread; ++u) {
+            const int64_t v = v0 + static_cast<int64_t>(u) * blockDim.x;
+            if (v >= a.row_vecs) break;
+            float b[8];
+            if (a.bias_0) {
+                unpack_bf16x8(static_cast<const u32x4 *>(a.bias_0)[t * a.row_vecs + v], b);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[u][i] = acc[u][i] + b[i];
+            }
+            if (a.bias_1) {
+                unpack_bf16x8(static_cast<const u32x4 *>(a.bias_1)[t * a.row_vecs + v], b);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[u][i] = acc[u][i] + b[i];
+            }
+        }
+    }
     u32x4 *out = static_cast<u32x4 *>(a.out) + t * a.row_vecs;
 #pragma unroll
     for (int u = 0; u < kVecsPerThread; ++u) {
@@ -174,7 +193,7 @@ __device__ inline void combine_columns(const CombineArgs &a, int64_t t, int64_t 
     }
 }
 
-template <bool HAS_BIAS, bool HAS_W, typename IdxT>
+template <bool HAS_BIAS, bool HAS_W, bool HAS_TB, typename IdxT>
 __global__ __launch_bounds__(kMaxCombineThreads) void combine_kernel(CombineArgs a,
                                                                     int groups_per_token) {
     if (a.scalars[EP_SCALAR_ERROR_BITS] & EP_ERRBIT_FATAL) return;
@@ -183,18 +202,18 @@ __global__ __launch_bounds__(kMaxCombineThreads) void combine_kernel(CombineArgs
         // One unit per block, straight-line (measurably faster than the loop).
         const int64_t t = blockIdx.x / groups_per_token;
         const int64_t v0 = (blockIdx.x % groups_per_token) * group + threadIdx.x;
-        if (v0 < a.row_vecs) combine_columns<HAS_BIAS, HAS_W, IdxT>(a, t, v0);
+        if (v0 < a.row_vecs) combine_columns<HAS_BIAS, HAS_W, HAS_TB, IdxT>(a, t, v0);
         return;
     }
     const int64_t units = static_cast<int64_t>(a.num_tokens) * groups_per_token;
     for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
         const int64_t t = u / groups_per_token;
         const int64_t v0 = (u % groups_per_token) * group + threadIdx.x;
-        if (v0 < a.row_vecs) combine_columns<HAS_BIAS, HAS_W, IdxT>(a, t, v0);
+        if (v0 < a.row_vecs) combine_columns<HAS_BIAS, HAS_W, HAS_TB, IdxT>(a, t, v0);
     }
 }
 
-template <bool HAS_BIAS, bool HAS_W>
+template <bool HAS_BIAS, bool HAS_W, bool HAS_TB>
 hipError_t launch_bw(const CombineArgs &a, hipStream_t stream, CallEvents ev) {
     // Block size among 256 / 128 / 64 threads that wastes the fewest lanes
     // on the row's vector count (ties go to the larger block).
@@ -216,18 +235,26 @@ hipError_t launch_bw(const CombineArgs &a, hipStream_t stream, CallEvents ev) {
     if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
     const dim3 grid(static_cast<unsigned>(blocks)), block(threads);
     if (a.idx_is_i64)
-        return launch_kernel(combine_kernel<HAS_BIAS, HAS_W, int64_t>, grid, block, stream,
-                             ev.start, ev.stop, a, gpt);
-    return launch_kernel(combine_kernel<HAS_BIAS, HAS_W, int32_t>, grid, block, stream,
+        return launch_kernel(combine_kernel<HAS_BIAS, HAS_W, HAS_TB, int64_t>, grid, block,
+                             stream, ev.start, ev.stop, a, gpt);
+    return launch_kernel(combine_kernel<HAS_BIAS, HAS_W, HAS_TB, int32_t>, grid, block, stream,
                          ev.start, ev.stop, a, gpt);
 }
 
 }  // namespace
 
-hipError_t launch_combine(const CombineArgs &a, hipStream_t stream, CallEvents ev) {
+template <bool HAS_TB>
+hipError_t launch_tb(const CombineArgs &a, hipStream_t stream, CallEvents ev) {
     if (a.bias)
-        return a.w ? launch_bw<true, true>(a, stream, ev) : launch_bw<true, false>(a, stream, ev);
-    return a.w ? launch_bw<false, true>(a, stream, ev) : launch_bw<false, false>(a, stream, ev);
+        return a.w ? launch_bw<true, true, HAS_TB>(a, stream, ev)
+                   : launch_bw<true, false, HAS_TB>(a, stream, ev);
+    return a.w ? launch_bw<false, true, HAS_TB>(a, stream, ev)
+               : launch_bw<false, false, HAS_TB>(a, stream, ev);
+}
+
+hipError_t launch_combine(const CombineArgs &a, hipStream_t stream, CallEvents ev) {
+    if (a.bias_0 || a.bias_1) return launch_tb<true>(a, stream, ev);
+    return launch_tb<false>(a, stream, ev);
 }
 
 }  // namespace ep

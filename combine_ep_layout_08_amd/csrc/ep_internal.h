@@ -90,6 +90,7 @@ struct LayoutArgs {
     int32_t *counts, *psum, *dst, *src_meta, *scalars;
     uint64_t *tile_status;
     int32_t *cumulative_stats;
+    int32_t *recv_row, *recv_src;
 };
 
 struct DispatchArgs {
@@ -119,7 +120,27 @@ struct CombineArgs {
     const void *bias;            // bf16 [E, H] or null
     const void *topk_idx;        // ids, read only when bias is set
     bool idx_is_i64;
+    const void *bias_0, *bias_1; // bf16 [T, H] per-token biases or null
     void *out;
+};
+
+struct RankArgs {
+    const void *x;               // dispatch: [T, H] rows; combine: [rows, H]
+    int64_t row_vecs;
+    int32_t num_tokens, num_topk, num_experts;
+    const int32_t *recv_row, *scalars;
+    const void *topk_idx;
+    bool idx_is_i64;
+    const float *w;
+    const float *sf;
+    int64_t sf_ts, sf_hs;
+    int32_t num_sf;
+    void *out;                   // dispatch: [max_tokens, H]; combine: bf16 [T, H]
+    float *out_sf;
+    int64_t out_ts, out_hs;
+    void *out_idx;               // same dtype as topk_idx
+    float *out_w;
+    const void *bias_0, *bias_1;
 };
 
 struct BackwardArgs {
@@ -152,5 +173,7 @@ hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t stream, CallEvents
 hipError_t launch_combine(const CombineArgs &a, hipStream_t stream, CallEvents ev);
 hipError_t launch_combine_backward(const BackwardArgs &a, hipStream_t stream, CallEvents ev);
 hipError_t launch_gather_rows(const GatherArgs &a, hipStream_t stream, CallEvents ev);
+hipError_t launch_dispatch_rank(const RankArgs &a, hipStream_t stream, CallEvents ev);
+hipError_t launch_combine_rank(const RankArgs &a, hipStream_t stream, CallEvents ev);
 
 }  // namespace ep

@@ -22,10 +22,12 @@
 //     written with agent-scope atomics so every XCD sees them - gives each
 //     bucket's exclusive offset; each thread reads a window of 8 predecessors
 //     per round trip.  Each valid slot gets its position inside its expert's
-//     run.  The tile with the last ticket owns the inclusive totals: it writes
-//     counts, runs the aligned block scan over experts into psum and sets the
-//     scalars.  Tiles take their index from an atomic ticket, so every tile a
-//     block waits on has already started and waits end; a spin bound turns a
+//     run, and each received token its rank-layout row (a block scan of the
+//     tile's token flags after the earlier tiles' received count).  The tile
+//     with the last ticket owns the inclusive totals: it writes counts, runs
+//     the aligned block scan over experts into psum and sets the scalars.
+//     Tiles take their index from an atomic ticket, so every tile a block
+//     waits on has already started and waits end; a spin bound turns a
 //     broken invariant into an error bit instead of a hang.
 //  2. layout_finalize: thread per slot adds psum[e] to the position and
 //     scatters the source metadata; one block per expert marks its alignment
@@ -258,7 +260,32 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_scan_kernel(LayoutArgs 
         }
     }
 
-    // 5. The last tile owns the totals: counts, aligned scan, scalars.
+    // 5. Rank layout: the tile's received tokens get consecutive rows after
+    //    the received tokens of earlier tiles (bucket E+1's exclusive count).
+    {
+        const int per = (tokens_per_tile + kLayoutThreads - 1) / kLayoutThreads;
+        const int j0 = tid * per;
+        const int j1 = min(j0 + per, tokens_per_tile);
+        int64_t local = 0;
+        for (int j = j0; j < j1; ++j) local += s_tok[j];
+        int64_t unused = 0;
+        int64_t row = s_excl[B_RECV] + block_exclusive_scan(local, s_wave, &unused);
+        const int64_t tok0 = static_cast<int64_t>(tile) * tokens_per_tile;
+        for (int j = j0; j < j1; ++j) {
+            const int64_t t = tok0 + j;
+            if (t >= a.num_tokens) break;
+            if (s_tok[j]) {
+                a.recv_row[t] = static_cast<int32_t>(row);
+                a.recv_src[row] = static_cast<int32_t>(t);
+                ++row;
+            } else {
+                a.recv_row[t] = -1;
+            }
+        }
+    }
+    __syncthreads();                                   // s_wave is used again below
+
+    // 6. The last tile owns the totals: counts, aligned scan, scalars.
     if (tile != num_tiles - 1) return;
 #pragma unroll
     for (int q = 0; q < kBucketsPerThread; ++q) {

@@ -121,6 +121,11 @@ typedef struct ep_handle {
     const void *topk_idx;       /* BORROWED device [T, K] ids of the last layout*/
     int32_t topk_idx_dtype;     /* EP_I32 or EP_I64                             */
     int32_t status_tiles;       /* tiles the scratch is sized for               */
+    int32_t *recv_row;          /* device [max_tokens] rank-layout row of token */
+                                /* t (tokens with a valid slot, in token order),*/
+                                /* -1 if the token has no valid slot            */
+    int32_t *recv_src;          /* device [max_tokens] token of each rank row;  */
+                                /* entries past num_recv_tokens unspecified     */
 } ep_handle;
 
 /* Size of ep_handle in bytes, so bindings can check their struct layout. */
@@ -163,7 +168,8 @@ ep_status ep_handle_init(ep_handle *h, int32_t max_tokens, int32_t num_topk,
  *             (the per-expert receive statistics of [Ch7 §7.2]).
  * Order inside an expert segment: ascending slot index t*K+k.  Ids outside
  * [-1, E) are treated as empty and flagged.  Writes counts, psum, dst_slot,
- * src_meta (gap rows -1) and the scalars; all on `stream`.
+ * src_meta (gap rows -1), the rank layout (recv_row, recv_src: tokens with a
+ * valid slot in token order [Ch7 §7.4]) and the scalars; all on `stream`.
  */
 ep_status ep_layout(ep_handle *h, const void *topk_idx, ep_dtype idx_dtype,
                     int32_t num_tokens, int32_t *cumulative_stats,
@@ -232,14 +238,47 @@ ep_status ep_dispatch(const ep_handle *h, const void *x, ep_dtype x_dtype,
  *   topk_weights  NULL (weight 1) or device fp32 [num_tokens, K].
  *   bias     NULL or device bf16 [E, hidden]: expert e's output bias, added
  *            to the expert row before weighting.
+ *   bias_0, bias_1  NULL or device bf16 [num_tokens, hidden]: per-token
+ *            biases added after the reduction, bias_0 first [Ch8 §8.1].
  *   out      device bf16 [num_tokens, hidden].
- * out[t][h] = bf16_rne(sum over valid k in order of w[t,k]*(y[r][h]+b[e][h]))
+ * out[t][h] = bf16_rne(((sum over valid k in order of w[t,k]*(y[r][h]+b[e][h]))
+ *                       + b0[t][h]) + b1[t][h])
  * in fp32 from +0.0 with separately rounded multiply and add; a token with
- * no valid slot gets +0.0.
+ * no valid slot gets +0.0 (plus its per-token biases).
  */
 ep_status ep_combine(const ep_handle *h, const void *y, ep_dtype y_dtype,
                      int32_t hidden, const float *topk_weights,
-                     const void *bias, void *out, hipStream_t stream);
+                     const void *bias, const void *bias_0, const void *bias_1,
+                     void *out, hipStream_t stream);
+
+/*
+ * Dispatch into the non-expanded ("rank") layout [Ch7 §7.4: each received
+ * token once, [received_tokens, hidden] plus top-k metadata; §7.3: the
+ * epilogue also writes the received top-k ids and weights].  Row
+ * recv_row[t] of out_x (bf16 or FP8 bytes, [max_tokens, hidden]) gets x[t];
+ * FP8 scales as in ep_dispatch; out_topk_idx (NULL or [max_tokens, K], the
+ * dtype of the layout's topk_idx) gets the token's ids with -1 for empty or
+ * invalid slots; out_topk_weights (NULL or fp32 [max_tokens, K]) its weights
+ * with 0 for those slots (1 for valid slots when topk_weights is NULL).
+ * Rows at or past num_recv_tokens are not written.
+ */
+ep_status ep_dispatch_rank(const ep_handle *h, const void *x, ep_dtype x_dtype,
+                           int32_t hidden, const float *sf, int64_t sf_token_stride,
+                           int64_t sf_hidden_stride, const float *topk_weights,
+                           void *out_x, float *out_sf, int64_t out_sf_token_stride,
+                           int64_t out_sf_hidden_stride, void *out_topk_idx,
+                           float *out_topk_weights, hipStream_t stream);
+
+/*
+ * Combine from the rank layout [Ch8 §8.1: reduce back to the source token,
+ * optionally adding bias_0 and bias_1].  At one rank every received token has
+ * one row of x (bf16 [max_tokens, hidden], already reduced over its experts):
+ * out[t][h] = bf16_rne(fl32(fl32(v + b0[t][h]) + b1[t][h])), v = the row's
+ * value or +0.0 for a token with no valid slot; NULL biases are skipped.
+ */
+ep_status ep_combine_rank(const ep_handle *h, const void *x, int32_t hidden,
+                          const void *bias_0, const void *bias_1, void *out,
+                          hipStream_t stream);
 
 /*
  * Backward of combine [README, training example: the backward of combine is

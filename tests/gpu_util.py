@@ -44,7 +44,17 @@ def gpu_layout(idx: np.ndarray, E: int, A: int, capacity: int, idx_dtype=torch.i
     rc = h.read_counts(check=False)
     dst = h.dst_slot.cpu().numpy().copy()
     src = h.src_meta.cpu().numpy().copy()
+    rc["recv_row"] = h.recv_row.cpu().numpy().copy()
+    rc["recv_src"] = h.recv_src.cpu().numpy().copy()[:max(rc["num_recv_tokens"], 0)]
     return h, rc, dst, src
+
+
+def assert_rank_equal(rc, idx, E):
+    """Rank-layout rows of the GPU layout against the oracle's."""
+    row, src, n = oracle.rank_layout(idx, E)
+    np.testing.assert_array_equal(rc["recv_row"], row)
+    np.testing.assert_array_equal(rc["recv_src"], src)
+    assert rc["num_recv_tokens"] == n
 
 
 def assert_layout_equal(rc, dst, src, lay: oracle.Layout):

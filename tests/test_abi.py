@@ -31,14 +31,14 @@ def declared_functions():
 
 def test_every_declared_function_is_exported():
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(ep.lib(), n), n
         assert n in ep._SIGNATURES, f"binding lacks {n}"
 
 
 def test_handle_struct_layout_matches():
-    assert ep.ep_handle_sizeof() == ctypes.sizeof(ep.ep_handle) == 96
+    assert ep.ep_handle_sizeof() == ctypes.sizeof(ep.ep_handle) == 112
 
 
 def test_capacity_bound_golden():
@@ -60,9 +60,9 @@ def test_workspace_bytes():
     assert 0 < small < big
     assert big % 256 == 0
     # counts + psum + dst + src_meta + scalars + one 64-bit status word per
-    # (tile of 2048 slots, expert + 2 buckets)
-    need = 4 * 256 + 4 * 257 + 4 * 4096 * 8 + 4 * 65280 + 32 + 8 * 16 * 258
-    assert need <= big <= need + 6 * 256
+    # (tile of 2048 slots, expert + 2 buckets) + rank rows and sources
+    need = 4 * 256 + 4 * 257 + 4 * 4096 * 8 + 4 * 65280 + 32 + 8 * 16 * 258 + 2 * 4 * 4096
+    assert need <= big <= need + 8 * 256
     assert ep.ep_workspace_bytes(64, 65, 16, 1, 256) == 0       # K > 64
     assert ep.ep_workspace_bytes(64, 4, 1025, 1, 256) == 0      # E > 1024
     assert ep.ep_workspace_bytes(64, 4, 16, 1, 1 << 31) == 0    # capacity >= 2^31
@@ -96,7 +96,8 @@ def _fake_handle(laid_out=1):
     h = ep.ep_handle()
     h.max_tokens, h.num_tokens, h.num_topk, h.num_experts = 8, 8, 2, 4
     h.expert_alignment, h.laid_out, h.capacity = 1, laid_out, 16
-    for i, f in enumerate(("counts", "psum", "dst_slot", "src_meta", "scalars", "tile_status")):
+    for i, f in enumerate(("counts", "psum", "dst_slot", "src_meta", "scalars", "tile_status",
+                           "recv_row", "recv_src")):
         setattr(h, f, 0x100000 + 0x1000 * i)
     h.topk_idx = 0x200000
     h.topk_idx_dtype = ep.EP_I64
@@ -146,8 +147,8 @@ def test_dispatch_validation():
 def test_combine_validation():
     h = _fake_handle()
 
-    def call(hh=h, y=A16, dt=ep.EP_BF16, H=64, w=None, b=None, out=A16):
-        return ep.ep_combine(hh, y, dt, H, w, b, out, None)
+    def call(hh=h, y=A16, dt=ep.EP_BF16, H=64, w=None, b=None, out=A16, b0=None, b1=None):
+        return ep.ep_combine(hh, y, dt, H, w, b, b0, b1, out, None)
 
     assert call(hh=_fake_handle(laid_out=0)) == ep.EP_ERR_NOT_LAID_OUT
     assert call(dt=ep.EP_F32) == ep.EP_ERR_DTYPE             # combine input must be bf16
@@ -158,6 +159,8 @@ def test_combine_validation():
     assert call(out=None) == ep.EP_ERR_NULL
     assert call(b=A16 + 2) == ep.EP_ERR_MISALIGNED
     assert call(w=A16 + 1) == ep.EP_ERR_MISALIGNED
+    assert call(b0=A16 + 4) == ep.EP_ERR_MISALIGNED
+    assert call(b1=A16 + 2) == ep.EP_ERR_MISALIGNED
     nob = _fake_handle()
     nob.topk_idx = None
     assert call(hh=nob, b=A16) == ep.EP_ERR_NULL
@@ -206,3 +209,18 @@ def test_backward_validation():
     assert ep.ep_dispatch_backward(h, None, 64, None, A16, None, None) == ep.EP_ERR_NULL
     assert ep.ep_dispatch_backward(h, A16, 0, None, A16, None, None) == ep.EP_ERR_SHAPE
     assert ep.ep_dispatch_backward(h, A16, 64, A16 + 2, A16, A16, None) == ep.EP_ERR_MISALIGNED
+
+
+def test_rank_validation():
+    h = _fake_handle()
+    assert ep.ep_dispatch_rank(_fake_handle(laid_out=0), A16, ep.EP_BF16, 64, None, 0, 0, None,
+                               A16, None, 0, 0, None, None, None) == ep.EP_ERR_NOT_LAID_OUT
+    assert ep.ep_dispatch_rank(h, A16, ep.EP_F32, 64, None, 0, 0, None, A16, None, 0, 0, None,
+                               None, None) == ep.EP_ERR_DTYPE
+    assert ep.ep_dispatch_rank(h, A16, ep.EP_FP8_E4M3, 256, None, 0, 0, None, A16, A16, 0, 0,
+                               None, None, None) == ep.EP_ERR_NULL
+    assert ep.ep_dispatch_rank(h, A16, ep.EP_BF16, 64, None, 0, 0, None, A16, None, 0, 0,
+                               A16 + 4, None, None) == ep.EP_ERR_MISALIGNED
+    assert ep.ep_combine_rank(h, A16, 12, None, None, A16, None) == ep.EP_ERR_MISALIGNED
+    assert ep.ep_combine_rank(h, None, 64, None, None, A16, None) == ep.EP_ERR_NULL
+    assert ep.ep_combine_rank(h, A16, 64, A16 + 8, None, A16, None) == ep.EP_ERR_MISALIGNED

@@ -11,7 +11,7 @@ import combine_ep_layout_08_amd as ep
 import ep_workloads as W
 import oracle
 from tests import pins
-from tests.gpu_util import assert_layout_equal, gpu_layout, needs_gpu, say
+from tests.gpu_util import assert_layout_equal, assert_rank_equal, gpu_layout, needs_gpu, say
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
 
@@ -20,6 +20,7 @@ def _check(idx, E, A, capacity, **kw):
     lay = oracle.layout(idx, E, A, capacity)
     h, rc, dst, src = gpu_layout(idx, E, A, capacity, **kw)
     assert_layout_equal(rc, dst, src, lay)
+    assert_rank_equal(rc, idx, E)
     return h, lay
 
 
@@ -113,6 +114,7 @@ def test_layout_handle_reuse_and_determinism():
         lay = oracle.layout(idx, cfg.experts, cfg.alignment, cap)
         _, rc, dst, src = gpu_layout(idx, cfg.experts, cfg.alignment, cap, handle=h)
         assert_layout_equal(rc, dst, src, lay)
+        assert_rank_equal(rc, idx, cfg.experts)
         if seed == 1003 and ntok == cfg.tokens:
             if first is None:
                 first = dst.copy()

@@ -1,0 +1,148 @@
+"""Rank (non-expanded) layout and per-token biases on the GPU against the CPU
+oracle, bit-exact: rank dispatch (rows, FP8 scales, received top-k ids and
+weights; unwritten rows poison-checked), rank combine with bias_0 / bias_1,
+the expanded combine with per-token biases, and the hand-worked order cases."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import combine_ep_layout_08_amd as ep
+import ep_workloads as W
+import oracle
+from tests.gpu_util import (POISON, assert_rank_equal, gpu_layout, needs_gpu, poison_, say,
+                            u16, u8)
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _bf16(shape, seed, scale=1.0):
+    return torch.randn(shape, generator=torch.Generator().manual_seed(seed)).mul(scale).to(
+        torch.bfloat16)
+
+
+@pytest.mark.parametrize("fp8,H,idx32", [(False, 264, False), (True, 1024, False),
+                                         (False, 7168, True), (True, 7168, True)])
+def test_dispatch_rank(fp8, H, idx32):
+    rng = np.random.default_rng(H + fp8)
+    T, K, E = 700, 6, 20
+    idx = np.where(rng.random((T, K)) < 0.55, -1, rng.integers(-2, E + 2, size=(T, K)))
+    w = rng.random((T, K), dtype=np.float32)
+    h, rc, _, _ = gpu_layout(idx, E, 4, T * K + 4 * E,
+                             idx_dtype=torch.int32 if idx32 else torch.int64)
+    assert_rank_equal(rc, idx, E)
+    if fp8:
+        x = torch.from_numpy(rng.integers(0, 256, size=(T, H), dtype=np.uint8))
+        sf = torch.from_numpy(rng.random((T, H // 128), dtype=np.float32))
+    else:
+        x, sf = _bf16((T, H), 1), None
+    out_x = poison_(torch.empty((T, H), dtype=x.dtype, device="cuda"))
+    out_sf = poison_(torch.empty((T, H // 128), dtype=torch.float32, device="cuda")) if fp8 \
+        else None
+    out_i = poison_(torch.empty((T, K), dtype=torch.int32 if idx32 else torch.int64,
+                                device="cuda"))
+    out_w = poison_(torch.empty((T, K), dtype=torch.float32, device="cuda"))
+    say("dispatch rank", fp8, H, idx32)
+    h.dispatch_rank(x.cuda(), sf=None if sf is None else sf.cuda(),
+                    topk_weights=torch.from_numpy(w).cuda(), out_x=out_x, out_sf=out_sf,
+                    out_topk_idx=out_i, out_topk_weights=out_w)
+    torch.cuda.synchronize()
+    row, src, n = oracle.rank_layout(idx, E)
+    pf = np.frombuffer(bytes([POISON] * 4), np.float32)[0]
+    ox = np.full((T, u8(x[:1]).shape[1]), POISON, np.uint8)
+    osf = np.full((T, H // 128), pf, np.float32) if fp8 else None
+    oi = np.full((T, K), np.frombuffer(bytes([POISON] * 8), np.int64)[0], np.int64)
+    ow = np.full((T, K), pf, np.float32)
+    oracle.dispatch_rank(u8(x), idx, E, row, T, sf=None if sf is None else sf.numpy(),
+                         weights=w, out_x=ox, out_sf=osf, out_idx=oi, out_w=ow)
+    np.testing.assert_array_equal(u8(out_x), ox)
+    if fp8:
+        np.testing.assert_array_equal(out_sf.cpu().numpy().view(np.uint32), osf.view(np.uint32))
+    gi = out_i.cpu().numpy().astype(np.int64)
+    np.testing.assert_array_equal(gi[:n], oi[:n])
+    np.testing.assert_array_equal(out_w.cpu().numpy()[:n], ow[:n])
+    assert np.all(u8(out_w)[n:] == POISON)
+
+
+@pytest.mark.parametrize("biases", [(False, False), (True, False), (True, True), (False, True)])
+def test_combine_rank(biases):
+    rng = np.random.default_rng(7)
+    T, K, E, H = 900, 4, 16, 2056
+    idx = np.where(rng.random((T, K)) < 0.6, -1, rng.integers(0, E, size=(T, K)))
+    h, rc, _, _ = gpu_layout(idx, E, 1, T * K)
+    x = _bf16((T, H), 2, 3.0)
+    b0 = _bf16((T, H), 3) if biases[0] else None
+    b1 = _bf16((T, H), 4, 0.1) if biases[1] else None
+    say("combine rank", biases)
+    out = h.combine_rank(x.cuda(), bias_0=None if b0 is None else b0.cuda(),
+                         bias_1=None if b1 is None else b1.cuda())
+    torch.cuda.synchronize()
+    row, _, _ = oracle.rank_layout(idx, E)
+    exp = oracle.combine_rank(u16(x), row, None if b0 is None else u16(b0),
+                              None if b1 is None else u16(b1))
+    np.testing.assert_array_equal(u16(out), exp)
+
+
+@pytest.mark.parametrize("name", ["prefill", "skewed"])
+def test_combine_token_biases(name):
+    cfg = W.CONFIGS[name]
+    cap = ep.ep_capacity_bound(cfg.tokens, cfg.topk, cfg.experts, cfg.alignment)
+    wl = W.make(cfg, y_rows=cap, with_x=False)
+    b0 = W.payload_bf16(cfg.tokens, cfg.hidden, 11, 3, std=0.5)
+    b1 = W.payload_bf16(cfg.tokens, cfg.hidden, 12, 3, std=0.1)
+    say("combine token biases", name)
+    h, rc, dst, _ = gpu_layout(wl.topk_idx, cfg.experts, cfg.alignment, cap)
+    out = h.combine(wl.y.cuda(), topk_weights=torch.from_numpy(wl.topk_weights).cuda(),
+                    bias=None if wl.bias is None else wl.bias.cuda(), bias_0=b0.cuda(),
+                    bias_1=b1.cuda())
+    torch.cuda.synchronize()
+    lay = oracle.layout(wl.topk_idx, cfg.experts, cfg.alignment, cap)
+    exp = oracle.combine_token_bias(u16(wl.y), wl.topk_idx, lay.dst, wl.topk_weights,
+                                    None if wl.bias is None else u16(wl.bias), u16(b0), u16(b1))
+    np.testing.assert_array_equal(u16(out), exp)
+
+
+def _pad8(vals) -> torch.Tensor:
+    v = torch.tensor(vals, dtype=torch.float32)
+    out = torch.zeros((v.shape[0], 8), dtype=torch.float32)
+    out[:, :v.shape[1]] = v
+    return out.to(torch.bfloat16)
+
+
+def test_golden_bias_order():
+    g = json.load(open(os.path.join(GOLDEN, "combine_hand.json")))
+    tb = g["token_bias"]
+    h, _, dst, _ = gpu_layout(np.array(tb["topk_idx"]), 1, 1, 3)
+    assert dst.tolist() == tb["dst"]
+    say("golden token bias")
+    out = h.combine(_pad8(tb["y"]).cuda(), bias_0=_pad8(tb["bias_0"]).cuda(),
+                    bias_1=_pad8(tb["bias_1"]).cuda())
+    torch.cuda.synchronize()
+    assert u16(out)[:, :1].tolist() == tb["expected_bits"]
+    rk = g["rank_combine"]
+    idx = np.array([[0], [-1]])                    # token 0 received (row 0), token 1 not
+    h, rc, _, _ = gpu_layout(idx, 1, 1, 1)
+    assert rc["recv_row"].tolist() == rk["recv_row"]
+    x = torch.zeros((2, 8), dtype=torch.bfloat16)
+    x[:1] = _pad8(rk["x"])
+    out = h.combine_rank(x.cuda(), bias_0=_pad8(rk["bias_0"]).cuda(),
+                         bias_1=_pad8(rk["bias_1"]).cuda())
+    torch.cuda.synchronize()
+    assert u16(out)[:, :1].tolist() == rk["expected_bits"]
+
+
+def test_imported_layout_has_rank_rows():
+    rng = np.random.default_rng(3)
+    T, K, E = 500, 4, 12
+    idx = np.where(rng.random((T, K)) < 0.7, -1, rng.integers(0, E, size=(T, K)))
+    lay = oracle.layout(idx, E, 2, T * K + 2 * E)
+    h = ep.Handle(T, K, E, 2, T * K + 2 * E)
+    say("import rank rows")
+    h.import_layout(torch.from_numpy(idx).cuda(), lay.counts, lay.psum, lay.dst,
+                    lay.src_meta[:lay.num_expanded], lay.num_recv_tokens)
+    row, src, n = oracle.rank_layout(idx, E)
+    np.testing.assert_array_equal(h.recv_row.cpu().numpy(), row)
+    np.testing.assert_array_equal(h.recv_src.cpu().numpy()[:n], src)
