@@ -49,6 +49,8 @@ def parse():
                    help="calls per kernel in the cold-cache phase after the timed steps (0 = skip)")
     p.add_argument("--backward-reps", type=int, default=30,
                    help="calls of each backward entry point after the timed steps (0 = skip)")
+    p.add_argument("--rank-reps", type=int, default=30,
+                   help="calls of the rank-layout and per-token-bias entry points (0 = skip)")
     p.add_argument("--flush", action="store_true",
                    help="read a 1 GiB scratch buffer before every call (outside the per-call "
                         "events) so each kernel starts with cold L2 and MALL")
@@ -306,6 +308,47 @@ def main():
             backward[name] = {"us_mean": round(us, 2), "bytes": bb[name], "GBps": round(gbps, 1),
                               "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
 
+    # Rank (non-expanded) layout and per-token biases, on the same layout.
+    rank = None
+    if args.rank_reps > 0:
+        T, K, H = cfg.tokens, cfg.topk, cfg.hidden
+        nrecv = int(rc["num_recv_tokens"])
+        R = H if cfg.fp8 else 2 * H
+        S = 4 * (H // 128) if cfg.fp8 else 0
+        rx = torch.empty((T, H), dtype=wl.x.dtype, device="cuda")
+        rsf = torch.empty((T, H // 128), dtype=torch.float32, device="cuda") if cfg.fp8 else None
+        ri = torch.empty((T, K), dtype=torch.int64, device="cuda")
+        rw = torch.empty((T, K), dtype=torch.float32, device="cuda")
+        xr = W.payload_bf16(T, H, cfg.seed + 2, 3, "cuda")
+        b0 = W.payload_bf16(T, H, cfg.seed + 3, 3, "cuda")
+        b1 = W.payload_bf16(T, H, cfg.seed + 4, 3, "cuda")
+        rb = {"dispatch_rank": T * (R + S) + nrecv * (R + S) + T * K * 12 + nrecv * K * 12 + 4 * T,
+              "combine_rank": nrecv * 2 * H + 3 * T * 2 * H + 4 * T,
+              "combine_token_biases": nbytes["combine"] + 2 * T * 2 * H}
+        rcalls = {"dispatch_rank": lambda: h.dispatch_rank(
+                      wl.x, sf=wl.sf, topk_weights=w, out_x=rx, out_sf=rsf, out_topk_idx=ri,
+                      out_topk_weights=rw),
+                  "combine_rank": lambda: h.combine_rank(xr, bias_0=b0, bias_1=b1, out=out),
+                  "combine_token_biases": lambda: h.combine(wl.y, topk_weights=w, bias=wl.bias,
+                                                            out=out, bias_0=b0, bias_1=b1)}
+        rank = {}
+        for name, fn in rcalls.items():
+            fn()
+            pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                     for _ in range(args.rank_reps)]
+            for e0, e1 in pairs:
+                e0.record()
+                e1.record()
+            for e0, e1 in pairs:
+                ep.time_next_call(e0, e1)
+                fn()
+            torch.cuda.synchronize()
+            us = statistics.mean(e0.elapsed_time(e1) * 1e3 for e0, e1 in pairs)
+            gbps = rb[name] / (us * 1e-6) / 1e9
+            rank[name] = {"us_mean": round(us, 2), "bytes": rb[name], "GBps": round(gbps, 1),
+                          "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+        del rx, rsf, ri, rw, xr, b0, b1
+
     total_bytes = sum(nbytes.values())
     if args.flush:
         # The wall time also holds the cache flushes; use the calls' own time.
@@ -364,6 +407,7 @@ def main():
         "kernels": kernels,
         "kernels_cold_cache": kernels_cold,
         "backward": backward,
+        "rank_and_token_bias": rank,
         "roofline": roofline,
         "ceilings": ceil,
         "cpu_baseline": cpu,
