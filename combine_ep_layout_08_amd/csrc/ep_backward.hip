@@ -16,12 +16,13 @@
 // the order of the partial sums.
 //
 // Kernels:
-//  * scatter_scaled: one wave per token; the gradient row is loaded once into
-//    registers and stored, scaled per slot, to every routed row (like
-//    dispatch).
-//  * weight_grad: one block per token; threads stride over the row's 16-byte
-//    columns and keep one binary64 partial per slot of a chunk of 8; a
-//    shuffle tree and an ordered pass over the 4 waves finish each dot.
+//  * combine_backward (row pass): one block per token whose threads tile the
+//    row's 16-byte columns (up to 1024 threads, striding beyond).  The
+//    gradient is read once; grad_y and the weight gradient come out of the
+//    same pass (two separate passes re-read g and did not overlap the y
+//    reads with the grad_y writes).  Per chunk of 8 slots, one binary64
+//    partial per slot; a shuffle tree and an ordered pass over the waves
+//    finish each dot.
 //  * bias_grad: one block per (expert, 64 columns); the block's 4 waves take
 //    every 4th row of the expert's segment, 8 rows in flight per lane, and
 //    the 4 binary64 partials are added in wave order.
@@ -76,107 +77,111 @@ __device__ inline u32x4 scale_bf16x8(const u32x4 v, float s) {
     return o;
 }
 
-template <int VPL, bool HAS_W>
-__global__ __launch_bounds__(kThreads) void scatter_scaled_kernel(BackwardArgs a) {
-    if (a.scalars[EP_SCALAR_ERROR_BITS] & EP_ERRBIT_FATAL) return;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t t = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + wave;
-    if (t >= a.num_tokens) return;
-    const int K = a.num_topk;
-    const int64_t V = a.row_vecs;
-    int32_t my_dst = lane < K ? a.dst[t * K + lane] : -1;
-    if (my_dst >= a.capacity) my_dst = -1;
-    const float my_w = (HAS_W && lane < K) ? a.w[t * K + lane] : 1.0f;
-    const u32x4 *src = static_cast<const u32x4 *>(a.g) + t * V;
-    u32x4 *out = static_cast<u32x4 *>(a.grad_y);
-    for (int64_t c0 = 0; c0 < V; c0 += 64 * VPL) {
-        u32x4 v[VPL];
-#pragma unroll
-        for (int q = 0; q < VPL; ++q) {
-            const int64_t c = c0 + q * 64 + lane;
-            if (c < V) v[q] = src[c];
-        }
-        for (int k = 0; k < K; ++k) {
-            const int32_t r = __builtin_amdgcn_readlane(my_dst, k);
-            if (r < 0) continue;
-            const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), k));
-            u32x4 *d = out + static_cast<int64_t>(r) * V;
-#pragma unroll
-            for (int q = 0; q < VPL; ++q) {
-                const int64_t c = c0 + q * 64 + lane;
-                if (c < V) d[c] = HAS_W ? scale_bf16x8(v[q], wk) : v[q];
-            }
-        }
-    }
-}
+// Row pass block size: ceil(row vectors / EP_BACKWARD_VECS_PER_THREAD)
+// threads rounded up to whole waves, at most 1024 (512 with expert biases,
+// whose second set of row loads needs the larger register budget).
+#ifndef EP_BACKWARD_VECS_PER_THREAD
+#define EP_BACKWARD_VECS_PER_THREAD 16
+#endif
+#ifndef EP_BACKWARD_NT_STORE
+#define EP_BACKWARD_NT_STORE 1
+#endif
+constexpr int kMaxRowThreads = 1024;
+constexpr int row_threads_cap(bool has_bias) { return has_bias ? 512 : kMaxRowThreads; }
 
-template <bool HAS_BIAS, typename IdxT>
-__global__ __launch_bounds__(kThreads) void weight_grad_kernel(BackwardArgs a) {
-    __shared__ double s_part[kThreads / 64][kChunk];
+// Row pass: one block per token, threads tiling the row's 16-byte columns.
+// The gradient vector is loaded once; per chunk of 8 slots the expert rows
+// (and expert biases) are loaded branch-free, the scaled gradient is stored
+// to each routed row, and binary64 dot partials are kept per slot.
+template <bool WANT_Y, bool WANT_W, bool HAS_W, bool HAS_BIAS, typename IdxT>
+__global__ __launch_bounds__(row_threads_cap(WANT_W && HAS_BIAS)) void combine_backward_kernel(
+    BackwardArgs a) {
+    __shared__ double s_part[kMaxRowThreads / 64][kChunk];
     if (a.scalars[EP_SCALAR_ERROR_BITS] & EP_ERRBIT_FATAL) return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int waves = static_cast<int>(blockDim.x / 64);
     const int64_t t = blockIdx.x;
     const int K = a.num_topk, E = a.num_experts;
     const int64_t V = a.row_vecs;
+    const int32_t row_bytes = static_cast<int32_t>(V * 16);
     const u32x4 *g = static_cast<const u32x4 *>(a.g) + t * V;
+    u32x4 *gy = static_cast<u32x4 *>(a.grad_y);
     const IdxT *idx = static_cast<const IdxT *>(a.topk_idx);
     for (int k0 = 0; k0 < K; k0 += kChunk) {
         int32_t r[kChunk];
         int64_t e[kChunk];
+        float wk[kChunk];
 #pragma unroll
         for (int j = 0; j < kChunk; ++j) {
             r[j] = k0 + j < K ? a.dst[t * K + k0 + j] : -1;
             if (r[j] >= a.capacity) r[j] = -1;
-            e[j] = (HAS_BIAS && r[j] >= 0) ? static_cast<int64_t>(idx[t * K + k0 + j]) : -1;
+            e[j] = (WANT_W && HAS_BIAS && r[j] >= 0) ? static_cast<int64_t>(idx[t * K + k0 + j])
+                                                      : -1;
             if (e[j] >= E) e[j] = -1;
+            wk[j] = (WANT_Y && HAS_W && r[j] >= 0) ? a.w[t * K + k0 + j] : 1.0f;
         }
         double acc[kChunk];
 #pragma unroll
         for (int j = 0; j < kChunk; ++j) acc[j] = 0.0;
-        const int32_t row_bytes = static_cast<int32_t>(V * 16);
-        for (int64_t c = threadIdx.x; c < V; c += kThreads) {
-            float gf[8];
-            unpack8(g[c], gf);
-            u32x4 yv[kChunk], bv[kChunk];
+        for (int64_t c = threadIdx.x; c < V; c += blockDim.x) {
+            const u32x4 gv = g[c];
             const int32_t col = static_cast<int32_t>(c * 16);
+            u32x4 yv[kChunk], bv[kChunk];
+            if (WANT_W) {
 #pragma unroll
-            for (int j = 0; j < kChunk; ++j) {
-                yv[j] = __builtin_amdgcn_raw_buffer_load_b128(
-                    row_rsrc(a.y, r[j], row_bytes, r[j] >= 0), col, 0, 2);
-                if (HAS_BIAS)
-                    bv[j] = __builtin_amdgcn_raw_buffer_load_b128(
-                        row_rsrc(a.bias, e[j], row_bytes, e[j] >= 0), col, 0, 0);
+                for (int j = 0; j < kChunk; ++j) {
+                    yv[j] = __builtin_amdgcn_raw_buffer_load_b128(
+                        row_rsrc(a.y, r[j], row_bytes, r[j] >= 0), col, 0, 2);
+                    if (HAS_BIAS)
+                        bv[j] = __builtin_amdgcn_raw_buffer_load_b128(
+                            row_rsrc(a.bias, e[j], row_bytes, e[j] >= 0), col, 0, 0);
+                }
             }
+            if (WANT_Y) {
 #pragma unroll
-            for (int j = 0; j < kChunk; ++j) {
-                if (r[j] < 0) continue;
-                float yf[8], bf[8];
-                unpack8(yv[j], yf);
-                if (HAS_BIAS && e[j] >= 0) unpack8(bv[j], bf);
+                for (int j = 0; j < kChunk; ++j)
+                    if (r[j] >= 0) {
+                        const u32x4 o = HAS_W ? scale_bf16x8(gv, wk[j]) : gv;
+                        u32x4 *d = gy + static_cast<int64_t>(r[j]) * V + c;
+                        if (EP_BACKWARD_NT_STORE) __builtin_nontemporal_store(o, d);
+                        else *d = o;
+                    }
+            }
+            if (WANT_W) {
+                float gf[8];
+                unpack8(gv, gf);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    double v = static_cast<double>(yf[i]);
-                    if (HAS_BIAS && e[j] >= 0) v += static_cast<double>(bf[i]);
-                    acc[j] += static_cast<double>(gf[i]) * v;
+                for (int j = 0; j < kChunk; ++j) {
+                    if (r[j] < 0) continue;
+                    float yf[8], bf[8];
+                    unpack8(yv[j], yf);
+                    if (HAS_BIAS) unpack8(bv[j], bf);     // zeros when e[j] < 0
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        double v = static_cast<double>(yf[i]);
+                        if (HAS_BIAS) v += static_cast<double>(bf[i]);
+                        acc[j] += static_cast<double>(gf[i]) * v;
+                    }
                 }
             }
         }
+        if (WANT_W) {
 #pragma unroll
-        for (int j = 0; j < kChunk; ++j) {
-            double x = acc[j];
+            for (int j = 0; j < kChunk; ++j) {
+                double x = acc[j];
 #pragma unroll
-            for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
-            if (lane == 0) s_part[wave][j] = x;
+                for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+                if (lane == 0) s_part[wave][j] = x;
+            }
+            __syncthreads();
+            if (threadIdx.x < kChunk && k0 + static_cast<int>(threadIdx.x) < K) {
+                const int j = threadIdx.x;
+                double sum = 0.0;
+                for (int w = 0; w < waves; ++w) sum += s_part[w][j];
+                a.grad_w[t * K + k0 + j] = r[j] >= 0 ? static_cast<float>(sum) : 0.0f;
+            }
+            __syncthreads();
         }
-        __syncthreads();
-        if (threadIdx.x < kChunk && k0 + static_cast<int>(threadIdx.x) < K) {
-            const int j = threadIdx.x;
-            double sum = 0.0;
-#pragma unroll
-            for (int w = 0; w < kThreads / 64; ++w) sum += s_part[w][j];
-            a.grad_w[t * K + k0 + j] = r[j] >= 0 ? static_cast<float>(sum) : 0.0f;
-        }
-        __syncthreads();
     }
 }
 
@@ -246,65 +251,54 @@ __global__ void gather_rows_kernel(GatherArgs a) {
     a.out[i] = (r >= 0 && r < a.capacity && a.row_values) ? a.row_values[r] : 0.0f;
 }
 
-template <int VPL>
-hipError_t launch_scatter(const BackwardArgs &a, hipStream_t s, hipEvent_t start,
-                          hipEvent_t stop) {
-    const dim3 grid(static_cast<unsigned>((a.num_tokens + 3) / 4));
-    if (a.w)
-        return launch_kernel(scatter_scaled_kernel<VPL, true>, grid, dim3(kThreads), s, start,
-                             stop, a);
-    return launch_kernel(scatter_scaled_kernel<VPL, false>, grid, dim3(kThreads), s, start, stop,
-                         a);
+template <bool WANT_Y, bool WANT_W, bool HAS_W>
+hipError_t launch_rows3(const BackwardArgs &a, hipStream_t s, hipEvent_t st, hipEvent_t sp) {
+    const bool has_bias = WANT_W && a.bias;
+    const int64_t per = EP_BACKWARD_VECS_PER_THREAD;
+    int64_t threads = ((a.row_vecs + per - 1) / per + 63) / 64 * 64;
+    if (threads > row_threads_cap(has_bias)) threads = row_threads_cap(has_bias);
+    const dim3 grid(static_cast<unsigned>(a.num_tokens)), block(static_cast<unsigned>(threads));
+    if (has_bias) {
+        if (a.idx_is_i64)
+            return launch_kernel(combine_backward_kernel<WANT_Y, WANT_W, HAS_W, true, int64_t>,
+                                 grid, block, s, st, sp, a);
+        return launch_kernel(combine_backward_kernel<WANT_Y, WANT_W, HAS_W, true, int32_t>, grid,
+                             block, s, st, sp, a);
+    }
+    return launch_kernel(combine_backward_kernel<WANT_Y, WANT_W, HAS_W, false, int64_t>, grid,
+                         block, s, st, sp, a);
+}
+
+template <bool WANT_Y, bool WANT_W>
+hipError_t launch_rows2(const BackwardArgs &a, hipStream_t s, hipEvent_t st, hipEvent_t sp) {
+    return a.w ? launch_rows3<WANT_Y, WANT_W, true>(a, s, st, sp)
+               : launch_rows3<WANT_Y, WANT_W, false>(a, s, st, sp);
 }
 
 }  // namespace
 
 hipError_t launch_combine_backward(const BackwardArgs &a, hipStream_t stream, CallEvents ev) {
-    // Up to three kernels; the call's start event goes on the first launched
-    // and its stop event on the last.
-    const int n = (a.grad_y && a.num_tokens > 0) + (a.grad_w && a.num_tokens > 0) +
-                  (a.grad_bias != nullptr);
-    if (n == 0) return hipSuccess;
-    int done = 0;
-    auto evs = [&](hipEvent_t *st, hipEvent_t *sp) {
-        *st = done == 0 ? ev.start : nullptr;
-        *sp = done == n - 1 ? ev.stop : nullptr;
-        ++done;
-    };
+    // The row pass (grad_y and/or grad_w) and the bias pass; the call's start
+    // event goes on the first kernel launched and its stop event on the last.
+    const bool rows = (a.grad_y || a.grad_w) && a.num_tokens > 0;
+    const bool bias = a.grad_bias != nullptr;
+    if (!rows && !bias) return hipSuccess;
     hipError_t e = hipSuccess;
-    hipEvent_t st, sp;
-    if (a.grad_y && a.num_tokens > 0) {
-        evs(&st, &sp);
-        const int64_t per_lane = (a.row_vecs + 63) / 64;
-        if (per_lane <= 1) e = launch_scatter<1>(a, stream, st, sp);
-        else if (per_lane <= 2) e = launch_scatter<2>(a, stream, st, sp);
-        else if (per_lane <= 4) e = launch_scatter<4>(a, stream, st, sp);
-        else if (per_lane <= 8) e = launch_scatter<8>(a, stream, st, sp);
-        else e = launch_scatter<16>(a, stream, st, sp);
+    if (rows) {
+        hipEvent_t sp = bias ? nullptr : ev.stop;
+        if (a.grad_y && a.grad_w) e = launch_rows2<true, true>(a, stream, ev.start, sp);
+        else if (a.grad_y) e = launch_rows2<true, false>(a, stream, ev.start, sp);
+        else e = launch_rows2<false, true>(a, stream, ev.start, sp);
         if (e != hipSuccess) return e;
     }
-    if (a.grad_w && a.num_tokens > 0) {
-        evs(&st, &sp);
-        const dim3 grid(static_cast<unsigned>(a.num_tokens));
-        if (a.bias)
-            e = a.idx_is_i64
-                    ? launch_kernel(weight_grad_kernel<true, int64_t>, grid, dim3(kThreads), stream,
-                                    st, sp, a)
-                    : launch_kernel(weight_grad_kernel<true, int32_t>, grid, dim3(kThreads), stream,
-                                    st, sp, a);
-        else
-            e = launch_kernel(weight_grad_kernel<false, int64_t>, grid, dim3(kThreads), stream, st,
-                              sp, a);
-        if (e != hipSuccess) return e;
-    }
-    if (a.grad_bias) {
-        evs(&st, &sp);
+    if (bias) {
         const int groups = static_cast<int>((a.row_vecs + 63) / 64);
         const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.num_experts) * groups));
-        e = a.w ? launch_kernel(bias_grad_kernel<true>, grid, dim3(kThreads), stream, st, sp, a,
-                                groups)
-                : launch_kernel(bias_grad_kernel<false>, grid, dim3(kThreads), stream, st, sp, a,
-                                groups);
+        hipEvent_t st = rows ? nullptr : ev.start;
+        e = a.w ? launch_kernel(bias_grad_kernel<true>, grid, dim3(kThreads), stream, st, ev.stop,
+                                a, groups)
+                : launch_kernel(bias_grad_kernel<false>, grid, dim3(kThreads), stream, st,
+                                ev.stop, a, groups);
     }
     return e;
 }
