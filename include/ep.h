@@ -294,7 +294,7 @@ ep_status ep_combine_rank(const ep_handle *h, const void *x, int32_t hidden,
  *                     w * g[t] (every expert written, 0 if it has no row).
  * Both sums are accumulated in binary64 from exact terms and rounded once to
  * binary32.  grad_out is bf16 [T, hidden]; topk_weights / bias as given to
- * ep_combine.  Up to three kernels on `stream`.
+ * ep_combine.  One row pass plus one bias pass (when grad_bias) on `stream`.
  */
 ep_status ep_combine_backward(const ep_handle *h, const void *grad_out, int32_t hidden,
                               const float *topk_weights, const void *y, const void *bias,

@@ -41,25 +41,29 @@ def _check_sum(got, ref, mag, n):
         float(np.max(np.abs(got.astype(np.float64) - ref) - bound))
 
 
-def _run(idx, E, A, cap, g, y, w=None, b=None, want_bias=True):
+def _run(idx, E, A, cap, g, y, w=None, b=None, want_bias=True, want_y=True, want_w=True):
     T, K = idx.shape
     H = g.shape[1]
     h, rc, dst, _ = gpu_layout(idx, E, A, cap)
     lay = oracle.layout(idx, E, A, cap)
-    gy = poison_(torch.empty((cap, H), dtype=torch.bfloat16, device="cuda"))
+    gy = poison_(torch.empty((cap, H), dtype=torch.bfloat16, device="cuda")) if want_y else None
     wd = None if w is None else torch.from_numpy(w).cuda()
     bd = None if b is None else b.cuda()
-    _, gw, gb = h.combine_backward(g.cuda(), topk_weights=wd, y=y.cuda(), bias=bd, grad_y=gy,
-                                   want_grad_weights=True, want_grad_bias=want_bias)
+    r_gy, gw, gb = h.combine_backward(g.cuda(), topk_weights=wd, y=y.cuda(), bias=bd, grad_y=gy,
+                                      want_grad_y=want_y, want_grad_weights=want_w,
+                                      want_grad_bias=want_bias)
     torch.cuda.synchronize()
+    assert (r_gy is None) == (not want_y) and (gw is None) == (not want_w)
     o_gy = np.full((cap, H), np.uint16(POISON | POISON << 8), np.uint16)
     o_gy, o_gw, o_gb = oracle.combine_backward(u16(g), lay, idx, w, u16(y),
                                                None if b is None else u16(b), capacity=cap,
                                                want_grad_bias=want_bias, grad_y=o_gy)
-    np.testing.assert_array_equal(u16(gy), o_gy)
-    mw = _magnitudes(u16(g), idx, lay.dst, w, u16(y), None if b is None else u16(b))
-    _check_sum(gw.cpu().numpy(), o_gw, mw, H)
-    assert np.all(gw.cpu().numpy()[lay.dst < 0] == 0)
+    if want_y:
+        np.testing.assert_array_equal(u16(gy), o_gy)
+    if want_w:
+        mw = _magnitudes(u16(g), idx, lay.dst, w, u16(y), None if b is None else u16(b))
+        _check_sum(gw.cpu().numpy(), o_gw, mw, H)
+        assert np.all(gw.cpu().numpy()[lay.dst < 0] == 0)
     if want_bias:
         gf = np.abs(BF.bf16_bits_to_f32(u16(g)).astype(np.float64))
         wa = np.ones(idx.shape) if w is None else np.abs(w.astype(np.float64))
@@ -87,6 +91,24 @@ def test_combine_backward_small(K, H, weights, bias):
         torch.bfloat16) if bias else None
     say("combine backward", K, H, weights, bias)
     _run(idx, E, A, cap, g, y, w, b)
+
+
+@pytest.mark.parametrize("want_y,want_w,bias", [(True, False, True), (False, True, True),
+                                                (False, True, False), (True, False, False),
+                                                (False, False, True)])
+def test_combine_backward_partial_outputs(want_y, want_w, bias):
+    """Each output on its own (the row pass has grad_y-only and weight-only forms)."""
+    rng = np.random.default_rng(int(want_y) * 4 + int(want_w) * 2 + int(bias))
+    T, K, E, A, H = 257, 20, 40, 4, 1160
+    idx = rng.integers(-1, E, size=(T, K))
+    cap = T * K + A * E
+    g = torch.randn((T, H), generator=torch.Generator().manual_seed(11)).to(torch.bfloat16)
+    y = torch.randn((cap, H), generator=torch.Generator().manual_seed(12)).to(torch.bfloat16)
+    w = rng.random((T, K), dtype=np.float32)
+    b = torch.randn((E, H), generator=torch.Generator().manual_seed(13)).mul(0.1).to(
+        torch.bfloat16) if bias else None
+    say("combine backward partial", want_y, want_w, bias)
+    _run(idx, E, A, cap, g, y, w, b, want_bias=bias, want_y=want_y, want_w=want_w)
 
 
 @pytest.mark.parametrize("name", ["prefill", "skewed"])
