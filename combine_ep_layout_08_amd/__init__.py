@@ -26,7 +26,7 @@ __all__ = [
     "ep_workspace_bytes", "ep_handle_init", "ep_layout", "ep_handle_read_counts",
     "ep_handle_import", "ep_dispatch", "ep_combine", "ep_status_str", "ep_handle_sizeof",
     "ep_time_next_call", "time_next_call", "ep_combine_backward", "ep_dispatch_backward",
-    "ep_dispatch_rank", "ep_combine_rank",
+    "ep_dispatch_rank", "ep_combine_rank", "ep_tma_aligned_rows",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libep.so")
@@ -83,11 +83,12 @@ _SIGNATURES = {
     "ep_layout": (ctypes.c_int, [_HP, _P, ctypes.c_int, _I32, _P, _P]),
     "ep_handle_read_counts": (ctypes.c_int, [_HP, _P, _P, _P, _P, _P, _P, _P]),
     "ep_handle_import": (ctypes.c_int, [_HP, _P, ctypes.c_int, _I32, _P, _P, _P, _P, _I32, _P]),
-    "ep_dispatch": (ctypes.c_int, [_HP, _P, ctypes.c_int, _I32, _P, _I64, _I64, _P, _P, _P,
-                                   _I64, _I64, _P, _I32, _P]),
+    "ep_dispatch": (ctypes.c_int, [_HP, _P, ctypes.c_int, _I32, _P, _I64, _I64, _I32, _P, _P,
+                                   _P, _I64, _I64, _P, _I32, _P]),
+    "ep_tma_aligned_rows": (_I64, [_I64]),
     "ep_combine": (ctypes.c_int, [_HP, _P, ctypes.c_int, _I32, _P, _P, _P, _P, _P, _P]),
-    "ep_dispatch_rank": (ctypes.c_int, [_HP, _P, ctypes.c_int, _I32, _P, _I64, _I64, _P, _P, _P,
-                                        _I64, _I64, _P, _P, _P]),
+    "ep_dispatch_rank": (ctypes.c_int, [_HP, _P, ctypes.c_int, _I32, _P, _I64, _I64, _I32, _P,
+                                        _P, _P, _I64, _I64, _P, _P, _P]),
     "ep_combine_rank": (ctypes.c_int, [_HP, _P, _I32, _P, _P, _P, _P]),
     "ep_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "ep_time_next_call": (ctypes.c_int, [_P, _P]),
@@ -159,11 +160,16 @@ def ep_handle_import(h: ep_handle, topk_idx_ptr, idx_dtype, num_tokens, counts_p
                                   num_recv_tokens, stream)
 
 
-def ep_dispatch(h: ep_handle, x_ptr, x_dtype, hidden, sf_ptr, sf_ts, sf_hs, w_ptr, out_x_ptr,
-                out_sf_ptr, out_ts, out_hs, out_w_ptr, zero_padding, stream) -> int:
+def ep_dispatch(h: ep_handle, x_ptr, x_dtype, hidden, sf_ptr, sf_ts, sf_hs, num_sf_packs,
+                w_ptr, out_x_ptr, out_sf_ptr, out_ts, out_hs, out_w_ptr, zero_padding,
+                stream) -> int:
     return lib().ep_dispatch(ctypes.byref(h), x_ptr, x_dtype, hidden, sf_ptr, sf_ts, sf_hs,
-                             w_ptr, out_x_ptr, out_sf_ptr, out_ts, out_hs, out_w_ptr,
-                             zero_padding, stream)
+                             num_sf_packs, w_ptr, out_x_ptr, out_sf_ptr, out_ts, out_hs,
+                             out_w_ptr, zero_padding, stream)
+
+
+def ep_tma_aligned_rows(rows: int) -> int:
+    return int(lib().ep_tma_aligned_rows(rows))
 
 
 def ep_combine(h: ep_handle, y_ptr, y_dtype, hidden, w_ptr, bias_ptr, bias0_ptr, bias1_ptr,
@@ -172,12 +178,12 @@ def ep_combine(h: ep_handle, y_ptr, y_dtype, hidden, w_ptr, bias_ptr, bias0_ptr,
                             bias1_ptr, out_ptr, stream)
 
 
-def ep_dispatch_rank(h: ep_handle, x_ptr, x_dtype, hidden, sf_ptr, sf_ts, sf_hs, w_ptr,
-                     out_x_ptr, out_sf_ptr, out_ts, out_hs, out_idx_ptr, out_w_ptr,
-                     stream) -> int:
+def ep_dispatch_rank(h: ep_handle, x_ptr, x_dtype, hidden, sf_ptr, sf_ts, sf_hs,
+                     num_sf_packs, w_ptr, out_x_ptr, out_sf_ptr, out_ts, out_hs, out_idx_ptr,
+                     out_w_ptr, stream) -> int:
     return lib().ep_dispatch_rank(ctypes.byref(h), x_ptr, x_dtype, hidden, sf_ptr, sf_ts, sf_hs,
-                                  w_ptr, out_x_ptr, out_sf_ptr, out_ts, out_hs, out_idx_ptr,
-                                  out_w_ptr, stream)
+                                  num_sf_packs, w_ptr, out_x_ptr, out_sf_ptr, out_ts, out_hs,
+                                  out_idx_ptr, out_w_ptr, stream)
 
 
 def ep_combine_rank(h: ep_handle, x_ptr, hidden, bias0_ptr, bias1_ptr, out_ptr, stream) -> int:
@@ -238,6 +244,33 @@ def _need(cond: bool, msg: str):
 def _dev(t: torch.Tensor, name: str):
     _need(t.is_cuda, f"{name} must be a device tensor")
     _need(t.is_contiguous(), f"{name} must be contiguous")
+
+
+_SF_DTYPES = (torch.float32, torch.int32)
+
+
+def _scale_packs(sf, T, H, rows, out_sf, col_major, device):
+    """Check FP8 scale packs and allocate their output.  sf: fp32 [T, H/128]
+    (one scale per 128 channels) or int32 [T, P] (P packs of four UE8M0
+    exponent bytes), any strides.  Returns (packs, sf strides, out_sf, out
+    strides); a column-major out_sf has token stride 1 and pack stride
+    ep_tma_aligned_rows(rows)."""
+    _need(sf is not None, "FP8 dispatch needs scale factors")
+    _dev(sf, "sf")
+    _need(sf.dtype in _SF_DTYPES and sf.dim() == 2 and sf.shape[0] == T,
+          "sf must be fp32 [T, H/128] or int32 packs [T, P]")
+    packs = sf.shape[1]
+    _need(sf.dtype == torch.int32 or packs == H // 128, "fp32 sf must be [T, H/128]")
+    if out_sf is None:
+        if col_major:
+            store = torch.empty((packs, ep_tma_aligned_rows(rows)), dtype=sf.dtype, device=device)
+            out_sf = store[:, :rows].t()
+        else:
+            out_sf = torch.empty((rows, packs), dtype=sf.dtype, device=device)
+    _dev(out_sf, "out_sf")
+    _need(out_sf.dtype == sf.dtype and tuple(out_sf.shape) == (rows, packs),
+          f"out_sf must be [{rows}, {packs}] of sf's dtype")
+    return packs, sf.stride(), out_sf, out_sf.stride()
 
 
 class Handle:
@@ -354,10 +387,13 @@ class Handle:
     def dispatch(self, x: torch.Tensor, sf: Optional[torch.Tensor] = None,
                  topk_weights: Optional[torch.Tensor] = None, zero_padding: bool = False,
                  out_x: Optional[torch.Tensor] = None, out_sf: Optional[torch.Tensor] = None,
-                 out_w: Optional[torch.Tensor] = None, want_weights: bool = False):
-        """x: bf16 [T, H], or FP8 (float8_e4m3fn or uint8 codes) [T, H] with fp32
-        scales ``sf`` [T, H/128] (any strides).  Returns (out_x, out_sf, out_w);
-        outputs are allocated with ``capacity`` rows unless given."""
+                 out_w: Optional[torch.Tensor] = None, want_weights: bool = False,
+                 col_major_sf: bool = False):
+        """x: bf16 [T, H], or FP8 (float8_e4m3fn or uint8 codes) [T, H] with
+        scales ``sf``: fp32 [T, H/128] or int32 packs [T, P] (any strides).
+        Returns (out_x, out_sf, out_w); outputs are allocated with
+        ``capacity`` rows unless given (out_sf column-major, TMA-aligned, when
+        ``col_major_sf``)."""
         T = self.h.num_tokens
         _dev(x, "x")
         _need(x.dim() == 2 and x.shape[0] == T, "x must be [num_tokens, hidden]")
@@ -369,19 +405,12 @@ class Handle:
             out_x = torch.empty((cap, H), dtype=x.dtype, device=x.device)
         _dev(out_x, "out_x")
         _need(out_x.shape == (cap, H) and out_x.dtype == x.dtype, "out_x must be [capacity, H]")
-        sf_ts = sf_hs = o_ts = o_hs = 0
+        packs, (sf_ts, sf_hs), (o_ts, o_hs) = 0, (0, 0), (0, 0)
         if fp8:
-            _need(sf is not None, "FP8 dispatch needs scale factors")
-            _need(sf.is_cuda and sf.dtype == torch.float32 and sf.dim() == 2 and
-                  tuple(sf.shape) == (T, H // 128), "sf must be fp32 [T, H/128]")
-            sf_ts, sf_hs = sf.stride()
-            if out_sf is None:
-                out_sf = torch.empty((cap, H // 128), dtype=torch.float32, device=x.device)
-            _need(out_sf.is_cuda and out_sf.dtype == torch.float32 and
-                  tuple(out_sf.shape) == (cap, H // 128), "out_sf must be fp32 [capacity, H/128]")
-            o_ts, o_hs = out_sf.stride()
+            packs, (sf_ts, sf_hs), out_sf, (o_ts, o_hs) = _scale_packs(
+                sf, T, H, cap, out_sf, col_major_sf, x.device)
         else:
-            _need(sf is None, "scale factors are for FP8 only")
+            _need(sf is None and out_sf is None, "scale factors are for FP8 only")
         if topk_weights is not None:
             _dev(topk_weights, "topk_weights")
             _need(topk_weights.dtype == torch.float32 and
@@ -393,7 +422,7 @@ class Handle:
             _dev(out_w, "out_w")
             _need(out_w.dtype == torch.float32 and out_w.numel() == cap, "out_w: fp32 [capacity]")
         _check(ep_dispatch(self.h, _ptr(x), EP_FP8_E4M3 if fp8 else EP_BF16, H, _ptr(sf),
-                           sf_ts, sf_hs, _ptr(topk_weights), _ptr(out_x), _ptr(out_sf),
+                           sf_ts, sf_hs, packs, _ptr(topk_weights), _ptr(out_x), _ptr(out_sf),
                            o_ts, o_hs, _ptr(out_w), 1 if zero_padding else 0, _stream()),
                "ep_dispatch")
         return out_x, out_sf, out_w
@@ -502,7 +531,7 @@ class Handle:
 
     def dispatch_rank(self, x: torch.Tensor, sf: Optional[torch.Tensor] = None,
                       topk_weights: Optional[torch.Tensor] = None, out_x=None, out_sf=None,
-                      out_topk_idx=None, out_topk_weights=None):
+                      out_topk_idx=None, out_topk_weights=None, col_major_sf: bool = False):
         """Rank (non-expanded) dispatch: one row per received token, in token
         order, with [max_tokens] rows allocated; rows past num_recv_tokens are
         not written.  Returns (out_x, out_sf, out_topk_idx, out_topk_weights)."""
@@ -517,14 +546,12 @@ class Handle:
             out_x = torch.empty((M, H), dtype=x.dtype, device=x.device)
         _need(tuple(out_x.shape) == (M, H) and out_x.dtype == x.dtype and out_x.is_cuda,
               "out_x must be [max_tokens, H]")
-        sf_ts = sf_hs = o_ts = o_hs = 0
+        packs, (sf_ts, sf_hs), (o_ts, o_hs) = 0, (0, 0), (0, 0)
         if fp8:
-            _need(sf is not None and sf.is_cuda and sf.dtype == torch.float32 and
-                  tuple(sf.shape) == (T, H // 128), "sf must be fp32 [T, H/128]")
-            sf_ts, sf_hs = sf.stride()
-            if out_sf is None:
-                out_sf = torch.empty((M, H // 128), dtype=torch.float32, device=x.device)
-            o_ts, o_hs = out_sf.stride()
+            packs, (sf_ts, sf_hs), out_sf, (o_ts, o_hs) = _scale_packs(
+                sf, T, H, M, out_sf, col_major_sf, x.device)
+        else:
+            _need(sf is None and out_sf is None, "scale factors are for FP8 only")
         idx_dtype = torch.int64 if self.h.topk_idx_dtype == EP_I64 else torch.int32
         if out_topk_idx is None:
             out_topk_idx = torch.empty((M, K), dtype=idx_dtype, device=x.device)
@@ -535,7 +562,8 @@ class Handle:
         if topk_weights is not None:
             _dev(topk_weights, "topk_weights")
         _check(ep_dispatch_rank(self.h, _ptr(x), EP_FP8_E4M3 if fp8 else EP_BF16, H, _ptr(sf),
-                                sf_ts, sf_hs, _ptr(topk_weights), _ptr(out_x), _ptr(out_sf),
+                                sf_ts, sf_hs, packs, _ptr(topk_weights), _ptr(out_x),
+                                _ptr(out_sf),
                                 o_ts, o_hs, _ptr(out_topk_idx), _ptr(out_topk_weights),
                                 _stream()), "ep_dispatch_rank")
         return out_x, out_sf, out_topk_idx, out_topk_weights

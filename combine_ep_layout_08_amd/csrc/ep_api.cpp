@@ -256,9 +256,31 @@ ep_status ep_handle_import(ep_handle *h, const void *topk_idx, ep_dtype idx_dtyp
     return EP_OK;
 }
 
+// Scale-pack arguments shared by the two dispatches: returns EP_OK and the
+// pack count (0 for bf16) or the status to report.
+static ep_status check_sf(bool fp8, int32_t hidden, const void *sf, const void *out_sf,
+                          int32_t num_sf_packs, bool rows, int64_t sf_ts, int64_t sf_hs,
+                          int64_t out_ts, int64_t out_hs, int32_t *packs) {
+    *packs = 0;
+    if (!fp8) return (sf || out_sf || num_sf_packs != 0) ? EP_ERR_DTYPE : EP_OK;
+    if (num_sf_packs < 0) return EP_ERR_SHAPE;
+    const int32_t n = num_sf_packs == 0 ? hidden / 128 : num_sf_packs;
+    if (n > 64 * ep::kMaxSfPerLane) return EP_ERR_UNSUPPORTED;
+    if (!out_sf || (rows && !sf)) return EP_ERR_NULL;
+    if (sf_ts < 0 || sf_hs < 0 || out_ts < 0 || out_hs < 0) return EP_ERR_SHAPE;
+    if (!aligned(sf, 4) || !aligned(out_sf, 4)) return EP_ERR_MISALIGNED;
+    *packs = n;
+    return EP_OK;
+}
+
+int64_t ep_tma_aligned_rows(int64_t rows) {
+    if (rows < 0) return -1;
+    return (rows + 3) / 4 * 4;
+}
+
 ep_status ep_dispatch(const ep_handle *h, const void *x, ep_dtype x_dtype, int32_t hidden,
-                      const float *sf, int64_t sf_token_stride, int64_t sf_hidden_stride,
-                      const float *topk_weights, void *out_x, float *out_sf,
+                      const void *sf, int64_t sf_token_stride, int64_t sf_hidden_stride,
+                      int32_t num_sf_packs, const float *topk_weights, void *out_x, void *out_sf,
                       int64_t out_sf_token_stride, int64_t out_sf_hidden_stride, float *out_w,
                       int32_t zero_padding, hipStream_t stream) {
     const ep::CallEvents ev = take_events();
@@ -269,17 +291,14 @@ ep_status ep_dispatch(const ep_handle *h, const void *x, ep_dtype x_dtype, int32
     if (hidden <= 0) return EP_ERR_SHAPE;
     const bool fp8 = x_dtype == EP_FP8_E4M3;
     if (fp8 ? (hidden % 128) != 0 : (hidden % 8) != 0) return EP_ERR_MISALIGNED;
-    if (fp8 && hidden / 128 > 64 * ep::kMaxSfPerLane) return EP_ERR_UNSUPPORTED;
-    if (!fp8 && (sf || out_sf)) return EP_ERR_DTYPE;
-    if (fp8 && (!out_sf || (h->num_tokens > 0 && !sf))) return EP_ERR_NULL;
-    if (sf_token_stride < 0 || sf_hidden_stride < 0 || out_sf_token_stride < 0 ||
-        out_sf_hidden_stride < 0)
-        return EP_ERR_SHAPE;
+    int32_t packs = 0;
+    const ep_status st = check_sf(fp8, hidden, sf, out_sf, num_sf_packs, h->num_tokens > 0,
+                                  sf_token_stride, sf_hidden_stride, out_sf_token_stride,
+                                  out_sf_hidden_stride, &packs);
+    if (st != EP_OK) return st;
     if (!out_x || (h->num_tokens > 0 && !x)) return EP_ERR_NULL;
     if (!aligned(x, 16) || !aligned(out_x, 16)) return EP_ERR_MISALIGNED;
-    if (!aligned(sf, 4) || !aligned(out_sf, 4) || !aligned(topk_weights, 4) ||
-        !aligned(out_w, 4))
-        return EP_ERR_MISALIGNED;
+    if (!aligned(topk_weights, 4) || !aligned(out_w, 4)) return EP_ERR_MISALIGNED;
     const int64_t row_bytes = fp8 ? hidden : 2 * static_cast<int64_t>(hidden);
     ep::DispatchArgs a{};
     a.x = x;
@@ -295,11 +314,11 @@ ep_status ep_dispatch(const ep_handle *h, const void *x, ep_dtype x_dtype, int32
     a.scalars = h->scalars;
     a.w = topk_weights;
     a.out_x = out_x;
-    a.sf = sf;
+    a.sf = static_cast<const uint32_t *>(sf);
     a.sf_ts = sf_token_stride;
     a.sf_hs = sf_hidden_stride;
-    a.num_sf = fp8 ? hidden / 128 : 0;
-    a.out_sf = out_sf;
+    a.num_sf = packs;
+    a.out_sf = static_cast<uint32_t *>(out_sf);
     a.out_ts = out_sf_token_stride;
     a.out_hs = out_sf_hidden_stride;
     a.out_w = out_w;
@@ -429,10 +448,11 @@ ep_status ep_dispatch_backward(const ep_handle *h, const void *grad_out_x, int32
 }
 
 ep_status ep_dispatch_rank(const ep_handle *h, const void *x, ep_dtype x_dtype, int32_t hidden,
-                           const float *sf, int64_t sf_token_stride, int64_t sf_hidden_stride,
-                           const float *topk_weights, void *out_x, float *out_sf,
-                           int64_t out_sf_token_stride, int64_t out_sf_hidden_stride,
-                           void *out_topk_idx, float *out_topk_weights, hipStream_t stream) {
+                           const void *sf, int64_t sf_token_stride, int64_t sf_hidden_stride,
+                           int32_t num_sf_packs, const float *topk_weights, void *out_x,
+                           void *out_sf, int64_t out_sf_token_stride,
+                           int64_t out_sf_hidden_stride, void *out_topk_idx,
+                           float *out_topk_weights, hipStream_t stream) {
     const ep::CallEvents ev = take_events();
     if (!h) return EP_ERR_NULL;
     if (!handle_ready(h)) return EP_ERR_WORKSPACE;
@@ -441,18 +461,16 @@ ep_status ep_dispatch_rank(const ep_handle *h, const void *x, ep_dtype x_dtype, 
     if (hidden <= 0) return EP_ERR_SHAPE;
     const bool fp8 = x_dtype == EP_FP8_E4M3;
     if (fp8 ? (hidden % 128) != 0 : (hidden % 8) != 0) return EP_ERR_MISALIGNED;
-    if (fp8 && hidden / 128 > 64 * ep::kMaxSfPerLane) return EP_ERR_UNSUPPORTED;
-    if (!fp8 && (sf || out_sf)) return EP_ERR_DTYPE;
     const bool rows = h->num_tokens > 0;
-    if (fp8 && (!out_sf || (rows && !sf))) return EP_ERR_NULL;
-    if (sf_token_stride < 0 || sf_hidden_stride < 0 || out_sf_token_stride < 0 ||
-        out_sf_hidden_stride < 0)
-        return EP_ERR_SHAPE;
+    int32_t packs = 0;
+    const ep_status st = check_sf(fp8, hidden, sf, out_sf, num_sf_packs, rows, sf_token_stride,
+                                  sf_hidden_stride, out_sf_token_stride, out_sf_hidden_stride,
+                                  &packs);
+    if (st != EP_OK) return st;
     if (!out_x || (rows && !x)) return EP_ERR_NULL;
     if ((out_topk_idx || out_topk_weights) && rows && !h->topk_idx) return EP_ERR_NULL;
     if (!aligned(x, 16) || !aligned(out_x, 16)) return EP_ERR_MISALIGNED;
-    if (!aligned(sf, 4) || !aligned(out_sf, 4) || !aligned(topk_weights, 4) ||
-        !aligned(out_topk_weights, 4) ||
+    if (!aligned(topk_weights, 4) || !aligned(out_topk_weights, 4) ||
         !aligned(out_topk_idx, h->topk_idx_dtype == EP_I64 ? 8 : 4))
         return EP_ERR_MISALIGNED;
     ep::RankArgs a{};
@@ -466,12 +484,12 @@ ep_status ep_dispatch_rank(const ep_handle *h, const void *x, ep_dtype x_dtype, 
     a.topk_idx = h->topk_idx;
     a.idx_is_i64 = h->topk_idx_dtype == EP_I64;
     a.w = topk_weights;
-    a.sf = sf;
+    a.sf = static_cast<const uint32_t *>(sf);
     a.sf_ts = sf_token_stride;
     a.sf_hs = sf_hidden_stride;
-    a.num_sf = fp8 ? hidden / 128 : 0;
+    a.num_sf = packs;
     a.out = out_x;
-    a.out_sf = out_sf;
+    a.out_sf = static_cast<uint32_t *>(out_sf);
     a.out_ts = out_sf_token_stride;
     a.out_hs = out_sf_hidden_stride;
     a.out_idx = out_topk_idx;

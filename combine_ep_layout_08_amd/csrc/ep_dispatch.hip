@@ -1,7 +1,8 @@
 // Dispatch copy epilogue into the expert-expanded layout on gfx950.
 //
 // What is computed follows DeepEP notes ch.7 "V2: how dispatch builds expert
-// inputs": s7.1 (x is a bf16 matrix or FP8 bytes plus fp32 scale factors;
+// inputs": s7.1 (x is a bf16 matrix or FP8 bytes plus scale factors, here
+// any 4-byte packs: fp32 per 128 channels or packed UE8M0 exponents;
 // top-k weights optional), s7.3 (the copy epilogue writes each received row
 // into its expert's aligned range, copies scale factors with their own token
 // and hidden strides and the received weights, and optionally zero-fills the
@@ -63,13 +64,13 @@ __device__ inline void dispatch_token(const DispatchArgs &a, int64_t t, int part
     if (part == 0) {
         if (a.out_w && my_dst >= 0) a.out_w[my_dst] = a.w ? a.w[t * K + lane] : 1.0f;
         if (a.num_sf) {
-            // A token's scale factors (at most 64 * kMaxSfPerLane) go to
+            // A token's scale packs (at most 64 * kMaxSfPerLane) go to
             // registers once and are stored for every valid slot.
-            float sfv[kMaxSfPerLane];
+            uint32_t sfv[kMaxSfPerLane];
 #pragma unroll
             for (int q = 0; q < kMaxSfPerLane; ++q) {
                 const int j = lane + 64 * q;
-                sfv[q] = j < a.num_sf ? a.sf[t * a.sf_ts + j * a.sf_hs] : 0.0f;
+                sfv[q] = j < a.num_sf ? a.sf[t * a.sf_ts + j * a.sf_hs] : 0u;
             }
             for (int k = 0; k < K; ++k) {
                 const int32_t r = __builtin_amdgcn_readlane(my_dst, k);
@@ -113,7 +114,7 @@ __device__ inline void dispatch_gap_row(const DispatchArgs &a, int e, int64_t r,
     const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
     u32x4 *d = static_cast<u32x4 *>(a.out_x) + r * V;
     for (int64_t c = lane; c < V; c += 64) store_row_vec(d + c, zero);
-    for (int j = lane; j < a.num_sf; j += 64) a.out_sf[r * a.out_ts + j * a.out_hs] = 0.0f;
+    for (int j = lane; j < a.num_sf; j += 64) a.out_sf[r * a.out_ts + j * a.out_hs] = 0u;
     if (a.out_w && lane == 0) a.out_w[r] = 0.0f;
 }
 

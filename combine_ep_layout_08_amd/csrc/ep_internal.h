@@ -101,10 +101,10 @@ struct DispatchArgs {
     const int32_t *dst, *counts, *psum, *scalars;
     const float *w;
     void *out_x;
-    const float *sf;
+    const uint32_t *sf;          // 4-byte scale packs, copied as bits
     int64_t sf_ts, sf_hs;
-    int32_t num_sf;
-    float *out_sf;
+    int32_t num_sf;              // packs per token
+    uint32_t *out_sf;
     int64_t out_ts, out_hs;
     float *out_w;
     bool zero_padding;
@@ -132,11 +132,11 @@ struct RankArgs {
     const void *topk_idx;
     bool idx_is_i64;
     const float *w;
-    const float *sf;
+    const uint32_t *sf;          // 4-byte scale packs, copied as bits
     int64_t sf_ts, sf_hs;
     int32_t num_sf;
     void *out;                   // dispatch: [max_tokens, H]; combine: bf16 [T, H]
-    float *out_sf;
+    uint32_t *out_sf;
     int64_t out_ts, out_hs;
     void *out_idx;               // same dtype as topk_idx
     float *out_w;

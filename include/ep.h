@@ -209,12 +209,19 @@ ep_status ep_handle_import(ep_handle *h, const void *topk_idx, ep_dtype idx_dtyp
  * §7.4 (contiguous aligned expert ranges for a grouped GEMM)].
  *   x        device [num_tokens, hidden]: bf16 (hidden % 8 == 0) or FP8
  *            bytes (hidden % 128 == 0); 16-byte aligned.
- *   sf       FP8 only (NULL for bf16): fp32 element (t, j), j < hidden/128,
- *            at sf[t*sf_token_stride + j*sf_hidden_stride].
+ *   sf       FP8 only (NULL for bf16): the token's scale factors as 4-byte
+ *            packs [Ch7 §7.3 names the pack count and both strides]; pack
+ *            (t, j), j < num_sf_packs, at sf[t*sf_token_stride +
+ *            j*sf_hidden_stride] (strides in packs).  Packs are copied as
+ *            bits: one fp32 per 128 channels, or four UE8M0 exponent bytes.
+ *   num_sf_packs  FP8 only: packs per token, 1..256; 0 means hidden/128
+ *            (one fp32 per 128-channel block).  Must be 0 for bf16.
  *   topk_weights  NULL or device fp32 [num_tokens, K].
  *   out_x    device [capacity, hidden] of x's type, 16-byte aligned.
- *   out_sf   FP8 only: element (r, j) at out_sf[r*out_sf_token_stride +
- *            j*out_sf_hidden_stride].
+ *   out_sf   FP8 only: pack (r, j) at out_sf[r*out_sf_token_stride +
+ *            j*out_sf_hidden_stride]; a column-major buffer whose token
+ *            stride is 1 and whose pack stride is ep_tma_aligned_rows(rows)
+ *            is the grouped-GEMM scale layout.
  *   out_w    NULL or device fp32 [capacity]: weight of the row's slot
  *            (1.0 when topk_weights is NULL).
  *   zero_padding  nonzero: gap rows get zero bytes, zero scales, weight 0.
@@ -222,11 +229,19 @@ ep_status ep_handle_import(ep_handle *h, const void *topk_idx, ep_dtype idx_dtyp
  * written.  Reuses the handle, so a cached re-dispatch is just another call.
  */
 ep_status ep_dispatch(const ep_handle *h, const void *x, ep_dtype x_dtype,
-                      int32_t hidden, const float *sf, int64_t sf_token_stride,
-                      int64_t sf_hidden_stride, const float *topk_weights,
-                      void *out_x, float *out_sf, int64_t out_sf_token_stride,
-                      int64_t out_sf_hidden_stride, float *out_w,
-                      int32_t zero_padding, hipStream_t stream);
+                      int32_t hidden, const void *sf, int64_t sf_token_stride,
+                      int64_t sf_hidden_stride, int32_t num_sf_packs,
+                      const float *topk_weights, void *out_x, void *out_sf,
+                      int64_t out_sf_token_stride, int64_t out_sf_hidden_stride,
+                      float *out_w, int32_t zero_padding, hipStream_t stream);
+
+/*
+ * Rows of a column-major scale buffer aligned for the tensor-memory loads of
+ * a grouped GEMM [Ch7 §7.3: the FP8 scales may use a column-major stride
+ * aligned for TMA]: `rows` rounded up to a whole 16 bytes of 4-byte packs,
+ * i.e. to a multiple of 4.  Returns -1 for rows < 0.
+ */
+int64_t ep_tma_aligned_rows(int64_t rows);
 
 /*
  * Combine [Ch8 §8.1: reduce along the handle back to the source, with
@@ -256,18 +271,19 @@ ep_status ep_combine(const ep_handle *h, const void *y, ep_dtype y_dtype,
  * token once, [received_tokens, hidden] plus top-k metadata; §7.3: the
  * epilogue also writes the received top-k ids and weights].  Row
  * recv_row[t] of out_x (bf16 or FP8 bytes, [max_tokens, hidden]) gets x[t];
- * FP8 scales as in ep_dispatch; out_topk_idx (NULL or [max_tokens, K], the
+ * FP8 scale packs as in ep_dispatch; out_topk_idx (NULL or [max_tokens, K], the
  * dtype of the layout's topk_idx) gets the token's ids with -1 for empty or
  * invalid slots; out_topk_weights (NULL or fp32 [max_tokens, K]) its weights
  * with 0 for those slots (1 for valid slots when topk_weights is NULL).
  * Rows at or past num_recv_tokens are not written.
  */
 ep_status ep_dispatch_rank(const ep_handle *h, const void *x, ep_dtype x_dtype,
-                           int32_t hidden, const float *sf, int64_t sf_token_stride,
-                           int64_t sf_hidden_stride, const float *topk_weights,
-                           void *out_x, float *out_sf, int64_t out_sf_token_stride,
-                           int64_t out_sf_hidden_stride, void *out_topk_idx,
-                           float *out_topk_weights, hipStream_t stream);
+                           int32_t hidden, const void *sf, int64_t sf_token_stride,
+                           int64_t sf_hidden_stride, int32_t num_sf_packs,
+                           const float *topk_weights, void *out_x, void *out_sf,
+                           int64_t out_sf_token_stride, int64_t out_sf_hidden_stride,
+                           void *out_topk_idx, float *out_topk_weights,
+                           hipStream_t stream);
 
 /*
  * Combine from the rank layout [Ch8 §8.1: reduce back to the source token,

@@ -72,7 +72,8 @@ def dispatch_expected(x_bytes, dst, counts, psum, capacity, poison=0xA5,
     out = np.full((capacity, R), poison, np.uint8)
     pf = np.frombuffer(bytes([poison] * 4), np.float32)[0]
     nsf = 0 if sf is None else sf.shape[1]
-    osf = np.full((capacity, nsf), pf, np.float32)
+    sdt = np.float32 if sf is None else sf.dtype          # 4-byte packs, kept as bits
+    osf = np.full((capacity, nsf), np.frombuffer(bytes([poison] * 4), sdt)[0], sdt)
     ow = np.full(capacity, pf, np.float32)
     d = np.asarray(dst).reshape(T, K)
     tt, kk = np.nonzero(d >= 0)
@@ -85,7 +86,7 @@ def dispatch_expected(x_bytes, dst, counts, psum, capacity, poison=0xA5,
         for e in range(len(counts)):
             g0, g1 = int(psum[e]) + int(counts[e]), int(psum[e + 1])
             out[g0:g1] = 0
-            osf[g0:g1] = 0.0
+            osf[g0:g1] = 0
             ow[g0:g1] = 0.0
     return out, osf, ow
 

@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported():
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(ep.lib(), n), n
         assert n in ep._SIGNATURES, f"binding lacks {n}"
@@ -121,12 +121,12 @@ def test_layout_validation():
 
 def test_dispatch_validation():
     h = _fake_handle()
-    args = dict(x=A16, dt=ep.EP_BF16, H=64, sf=None, w=None, out=A16, osf=None, ow=None)
+    args = dict(x=A16, dt=ep.EP_BF16, H=64, sf=None, w=None, out=A16, osf=None, ow=None, np=0)
 
     def call(hh=h, **kw):
         a = dict(args, **kw)
-        return ep.ep_dispatch(hh, a["x"], a["dt"], a["H"], a["sf"], 0, 0, a["w"], a["out"],
-                              a["osf"], 0, 0, a["ow"], 0, None)
+        return ep.ep_dispatch(hh, a["x"], a["dt"], a["H"], a["sf"], 0, 0, a["np"], a["w"],
+                              a["out"], a["osf"], 0, 0, a["ow"], 0, None)
 
     assert call(hh=_fake_handle(laid_out=0)) == ep.EP_ERR_NOT_LAID_OUT
     assert call(dt=ep.EP_F32) == ep.EP_ERR_DTYPE
@@ -136,12 +136,22 @@ def test_dispatch_validation():
     assert call(dt=ep.EP_FP8_E4M3, H=7168) == ep.EP_ERR_NULL  # FP8 without scales
     assert call(dt=ep.EP_FP8_E4M3, H=7000, sf=A16, osf=A16) == ep.EP_ERR_MISALIGNED
     assert call(dt=ep.EP_FP8_E4M3, H=32768 + 128, sf=A16, osf=A16) == ep.EP_ERR_UNSUPPORTED
+    assert call(np=14) == ep.EP_ERR_DTYPE                    # scale packs with bf16
+    assert call(dt=ep.EP_FP8_E4M3, H=7168, sf=A16, osf=A16, np=-1) == ep.EP_ERR_SHAPE
+    assert call(dt=ep.EP_FP8_E4M3, H=7168, sf=A16, osf=A16, np=257) == ep.EP_ERR_UNSUPPORTED
+    assert call(dt=ep.EP_FP8_E4M3, H=7168, sf=A16 + 2, osf=A16, np=14) == ep.EP_ERR_MISALIGNED
     assert call(x=None) == ep.EP_ERR_NULL
     assert call(out=None) == ep.EP_ERR_NULL
     assert call(x=A16 + 8) == ep.EP_ERR_MISALIGNED
     assert call(w=A16 + 2) == ep.EP_ERR_MISALIGNED
-    assert ep.ep_dispatch(h, A16, ep.EP_BF16, 64, None, -1, 0, None, A16, None, 0, 0, None, 0,
-                          None) == ep.EP_ERR_SHAPE
+    assert ep.ep_dispatch(h, A16, ep.EP_FP8_E4M3, 128, A16, -1, 0, 0, None, A16, A16, 0, 0,
+                          None, 0, None) == ep.EP_ERR_SHAPE
+
+
+def test_tma_aligned_rows():
+    assert [ep.ep_tma_aligned_rows(r) for r in (0, 1, 3, 4, 5, 65280, 65281)] == \
+        [0, 4, 4, 4, 8, 65280, 65284]
+    assert ep.ep_tma_aligned_rows(-1) == -1
 
 
 def test_combine_validation():
@@ -213,14 +223,16 @@ def test_backward_validation():
 
 def test_rank_validation():
     h = _fake_handle()
-    assert ep.ep_dispatch_rank(_fake_handle(laid_out=0), A16, ep.EP_BF16, 64, None, 0, 0, None,
-                               A16, None, 0, 0, None, None, None) == ep.EP_ERR_NOT_LAID_OUT
-    assert ep.ep_dispatch_rank(h, A16, ep.EP_F32, 64, None, 0, 0, None, A16, None, 0, 0, None,
+    assert ep.ep_dispatch_rank(_fake_handle(laid_out=0), A16, ep.EP_BF16, 64, None, 0, 0, 0,
+                               None, A16, None, 0, 0, None, None, None) == ep.EP_ERR_NOT_LAID_OUT
+    assert ep.ep_dispatch_rank(h, A16, ep.EP_F32, 64, None, 0, 0, 0, None, A16, None, 0, 0, None,
                                None, None) == ep.EP_ERR_DTYPE
-    assert ep.ep_dispatch_rank(h, A16, ep.EP_FP8_E4M3, 256, None, 0, 0, None, A16, A16, 0, 0,
+    assert ep.ep_dispatch_rank(h, A16, ep.EP_FP8_E4M3, 256, None, 0, 0, 0, None, A16, A16, 0, 0,
                                None, None, None) == ep.EP_ERR_NULL
-    assert ep.ep_dispatch_rank(h, A16, ep.EP_BF16, 64, None, 0, 0, None, A16, None, 0, 0,
+    assert ep.ep_dispatch_rank(h, A16, ep.EP_BF16, 64, None, 0, 0, 0, None, A16, None, 0, 0,
                                A16 + 4, None, None) == ep.EP_ERR_MISALIGNED
+    assert ep.ep_dispatch_rank(h, A16, ep.EP_BF16, 64, None, 0, 0, 2, None, A16, None, 0, 0,
+                               None, None, None) == ep.EP_ERR_DTYPE
     assert ep.ep_combine_rank(h, A16, 12, None, None, A16, None) == ep.EP_ERR_MISALIGNED
     assert ep.ep_combine_rank(h, None, 64, None, None, A16, None) == ep.EP_ERR_NULL
     assert ep.ep_combine_rank(h, A16, 64, A16 + 8, None, A16, None) == ep.EP_ERR_MISALIGNED

@@ -99,6 +99,43 @@ def test_dispatch_strided_scales_and_no_weights():
     _assert_same(g, o)
 
 
+@pytest.mark.parametrize("zp", [False, True])
+def test_dispatch_packed_scales_column_major(zp):
+    """Four UE8M0 exponents per 4-byte pack (hidden 7168: 14 packs), read from
+    a column-major source and copied as bits into a column-major scale buffer
+    whose columns are 16-byte aligned (the grouped-GEMM layout)."""
+    rng = np.random.default_rng(31 + zp)
+    T, K, E, A, H = 300, 8, 64, 32, 7168
+    packs = H // 512
+    idx = rng.integers(-1, E, size=(T, K))
+    cap = ep.ep_capacity_bound(T, K, E, A)
+    x = torch.from_numpy(rng.integers(0, 256, size=(T, H), dtype=np.uint8))
+    sf_np = rng.integers(0, 2 ** 32, size=(T, packs), dtype=np.uint64).astype(np.uint32)
+    sf_np[::5, 3] = 0x7FC00001                      # NaN payload as a float
+    sf_cols = np.ascontiguousarray(sf_np.T)         # stored [packs, T]
+    sf_dev = torch.from_numpy(sf_cols.view(np.int32)).cuda().t()
+    h, rc, dst, _ = gpu_layout(idx, E, A, cap)
+    tma = ep.ep_tma_aligned_rows(cap)
+    store = poison_(torch.empty((packs, tma), dtype=torch.int32, device="cuda"))
+    out_x = poison_(torch.empty((cap, H), dtype=torch.uint8, device="cuda"))
+    say("dispatch packed scales", zp)
+    h.dispatch(x.cuda(), sf=sf_dev, zero_padding=zp, out_x=out_x, out_sf=store[:, :cap].t())
+    _, osf2, _ = h.dispatch(x.cuda(), sf=sf_dev, zero_padding=zp, col_major_sf=True)
+    torch.cuda.synchronize()
+    lay = oracle.layout(idx, E, A, cap)
+    o_x = np.full((cap, H), POISON, np.uint8)
+    o_store = np.full((packs, tma), np.uint32(0xA5A5A5A5), np.uint32)
+    oracle.dispatch(u8(x), lay, cap, sf=sf_cols, sf_strides=(1, T), zero_padding=zp,
+                    out_x=o_x, out_sf=o_store, out_sf_strides=(1, tma), num_sf_packs=packs)
+    np.testing.assert_array_equal(u8(out_x), o_x)
+    np.testing.assert_array_equal(store.cpu().numpy().view(np.uint32), o_store)
+    assert osf2.shape == (cap, packs) and osf2.stride() == (1, tma)
+    n = lay.num_expanded
+    written = np.nonzero(lay.src_meta[:n] >= 0)[0] if not zp else np.arange(n)
+    np.testing.assert_array_equal(osf2.cpu().numpy().view(np.uint32)[written],
+                                  o_store[:, :cap].T[written])
+
+
 def test_dispatch_many_slots_per_token():
     rng = np.random.default_rng(2)
     T, K, E, A = 50, 40, 16, 8          # K > E: duplicates, 40 stores per row

@@ -67,6 +67,35 @@ def test_dispatch_rank(fp8, H, idx32):
     assert np.all(u8(out_w)[n:] == POISON)
 
 
+def test_dispatch_rank_packed_scales_column_major():
+    """Rank dispatch with int32 scale packs into a column-major, 16-byte
+    aligned scale buffer, bit-exact with the oracle."""
+    rng = np.random.default_rng(77)
+    T, K, E, H = 333, 4, 16, 2048
+    packs = H // 512
+    idx = np.where(rng.random((T, K)) < 0.6, -1, rng.integers(0, E, size=(T, K)))
+    h, rc, _, _ = gpu_layout(idx, E, 4, T * K + 4 * E)
+    x = torch.from_numpy(rng.integers(0, 256, size=(T, H), dtype=np.uint8))
+    sf = rng.integers(0, 2 ** 32, size=(T, packs), dtype=np.uint64).astype(np.uint32)
+    tma = ep.ep_tma_aligned_rows(T)
+    store = poison_(torch.empty((packs, tma), dtype=torch.int32, device="cuda"))
+    out_x = poison_(torch.empty((T, H), dtype=torch.uint8, device="cuda"))
+    say("dispatch rank packed scales")
+    h.dispatch_rank(x.cuda(), sf=torch.from_numpy(sf.view(np.int32)).cuda(), out_x=out_x,
+                    out_sf=store[:, :T].t())
+    torch.cuda.synchronize()
+    row, _, n = oracle.rank_layout(idx, E)
+    ox = np.full((T, H), POISON, np.uint8)
+    o_store = np.full((packs, tma), np.uint32(0xA5A5A5A5), np.uint32)
+    oracle.dispatch_rank(u8(x), idx, E, row, T, sf=sf, out_x=ox, num_sf_packs=packs)
+    np.testing.assert_array_equal(u8(out_x), ox)
+    # the oracle's rank dispatch writes row-major scales: compare through the view
+    o_rows = oracle.dispatch_rank(u8(x), idx, E, row, T, sf=sf, num_sf_packs=packs)[1]
+    got = store.cpu().numpy().view(np.uint32)
+    np.testing.assert_array_equal(got[:, :n].T, o_rows[:n])
+    assert np.all(got[:, n:] == 0xA5A5A5A5)
+
+
 @pytest.mark.parametrize("biases", [(False, False), (True, False), (True, True), (False, True)])
 def test_combine_rank(biases):
     rng = np.random.default_rng(7)
