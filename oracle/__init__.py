@@ -63,6 +63,15 @@ def _bind(lib):
     lib.oracle_combine_rank.argtypes = [_I, _I, _P, _P, _P, _P, _P]
     lib.oracle_combine_token_bias.restype = None
     lib.oracle_combine_token_bias.argtypes = [_I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P]
+    lib.oracle_f32_to_e4m3.restype = None
+    lib.oracle_f32_to_e4m3.argtypes = [_I, _P, _P]
+    lib.oracle_sf_packs.restype = _I
+    lib.oracle_sf_packs.argtypes = [_I, ctypes.c_int]
+    lib.oracle_quantize_fp8.restype = None
+    lib.oracle_quantize_fp8.argtypes = [_I, _I, _P, ctypes.c_int, _P, _P, _I, _I]
+    lib.oracle_dispatch_quant.restype = None
+    lib.oracle_dispatch_quant.argtypes = [_I, _I, _I, _I, _P, ctypes.c_int, _P, _P, _P, _P,
+                                          _P, _P, _I, _I, _P, ctypes.c_int]
     return lib
 
 
@@ -130,12 +139,14 @@ def dispatch(x_bytes: np.ndarray, lay: Layout, capacity: int,
              sf: Optional[np.ndarray] = None, sf_strides=None,
              weights: Optional[np.ndarray] = None, want_w: bool = False,
              zero_padding: bool = False, out_x=None, out_sf=None,
-             out_sf_strides=None, out_w=None, lib=None):
+             out_sf_strides=None, out_w=None, num_sf_packs=None, lib=None):
     """x_bytes: uint8 [T, row_bytes] (the raw row bytes of bf16 or FP8 x).
 
     Outputs may be passed in (pre-filled, e.g. with a poison pattern) to show
     which rows are left untouched; otherwise they are zero-initialised.
-    ``sf`` is float32 and addressed with (token, hidden) element strides.
+    ``sf`` holds 4-byte scale packs (float32, or int32/uint32 packed
+    exponents), addressed with (token, pack) element strides; there are
+    ``num_sf_packs`` per token (default row_bytes / 128, one fp32 per block).
     """
     lib = lib or load()
     x = np.ascontiguousarray(x_bytes, dtype=np.uint8)
@@ -149,11 +160,12 @@ def dispatch(x_bytes: np.ndarray, lay: Layout, capacity: int,
     sf_arr = None
     if sf is not None:
         sf_arr = np.asarray(sf)
-        assert sf_arr.dtype == np.float32
+        assert sf_arr.dtype.itemsize == 4 and sf_arr.flags.c_contiguous
         ts, hs = sf_strides if sf_strides is not None else (sf_arr.shape[1], 1)
-        num_sf = row_bytes // 128
+        num_sf = num_sf_packs or row_bytes // 128
         if out_sf is None:
-            out_sf = np.zeros((capacity, num_sf), np.float32)
+            out_sf = np.zeros((capacity, num_sf), sf_arr.dtype)
+        assert out_sf.dtype.itemsize == 4 and out_sf.flags.c_contiguous
         ots, ohs = out_sf_strides if out_sf_strides is not None else (num_sf, 1)
     if want_w and out_w is None:
         out_w = np.zeros(capacity, np.float32)
@@ -260,7 +272,8 @@ def rank_layout(topk_idx, num_experts: int, lib=None):
 
 
 def dispatch_rank(x_bytes, topk_idx, num_experts, recv_row, rows, sf=None, sf_strides=None,
-                  weights=None, out_x=None, out_sf=None, out_idx=None, out_w=None, lib=None):
+                  weights=None, out_x=None, out_sf=None, out_idx=None, out_w=None,
+                  num_sf_packs=None, lib=None):
     """Rank-layout dispatch; outputs have ``rows`` rows (pre-fill to check
     untouched rows).  Returns (out_x, out_sf, out_idx int64 [rows, K],
     out_w float32 [rows, K])."""
@@ -275,10 +288,11 @@ def dispatch_rank(x_bytes, topk_idx, num_experts, recv_row, rows, sf=None, sf_st
     sf_arr = None
     if sf is not None:
         sf_arr = np.asarray(sf)
+        assert sf_arr.dtype.itemsize == 4 and sf_arr.flags.c_contiguous
         ts, hs = sf_strides if sf_strides is not None else (sf_arr.shape[1], 1)
-        num_sf = R // 128
+        num_sf = num_sf_packs or R // 128
         if out_sf is None:
-            out_sf = np.zeros((rows, num_sf), np.float32)
+            out_sf = np.zeros((rows, num_sf), sf_arr.dtype)
         ots, ohs = num_sf, 1
     if out_idx is None:
         out_idx = np.zeros((rows, K), np.int64)
@@ -322,3 +336,61 @@ def combine_token_bias(y_bits, topk_idx, dst, weights=None, bias_bits=None, b0_b
     lib.oracle_combine_token_bias(T, K, H, _ptr(y), _ptr(w), _ptr(b), _ptr(idx), _ptr(d),
                                   _ptr(b0), _ptr(b1), _ptr(out))
     return out
+
+
+SF_F32 = 0
+SF_UE8M0 = 1
+
+
+def sf_packs(H: int, fmt: int, lib=None) -> int:
+    lib = lib or load()
+    return int(lib.oracle_sf_packs(H, fmt))
+
+
+def f32_to_e4m3(values, lib=None) -> np.ndarray:
+    """E4M3FN codes (uint8) of binary32 values, nearest with ties to even."""
+    lib = lib or load()
+    v = _c(values, np.float32)
+    out = np.zeros(v.shape, np.uint8)
+    lib.oracle_f32_to_e4m3(v.size, _ptr(v), _ptr(out))
+    return out
+
+
+def quantize_fp8(x_bits, fmt=SF_F32, lib=None):
+    """x_bits: uint16 [T, H] bf16.  Returns (codes uint8 [T, H], packs uint32
+    [T, sf_packs(H, fmt)])."""
+    lib = lib or load()
+    x = _c(x_bits, np.uint16)
+    T, H = x.shape
+    P = sf_packs(H, fmt, lib)
+    q = np.zeros((T, H), np.uint8)
+    sf = np.zeros((T, P), np.uint32)
+    lib.oracle_quantize_fp8(T, H, _ptr(x), fmt, _ptr(q), _ptr(sf), P, 1)
+    return q, sf
+
+
+def dispatch_quant(x_bits, lay: Layout, capacity: int, fmt=SF_F32, weights=None,
+                   want_w: bool = False, zero_padding: bool = False, out_x=None, out_sf=None,
+                   out_sf_strides=None, out_w=None, lib=None):
+    """Quantise bf16 rows then dispatch the codes and packs.  Outputs may be
+    passed pre-filled (untouched rows keep their content)."""
+    lib = lib or load()
+    x = _c(x_bits, np.uint16)
+    T, H = x.shape
+    K = lay.dst.shape[1]
+    E = lay.counts.shape[0]
+    P = sf_packs(H, fmt, lib)
+    if out_x is None:
+        out_x = np.zeros((capacity, H), np.uint8)
+    if out_sf is None:
+        out_sf = np.zeros((capacity, P), np.uint32)
+    assert out_sf.dtype.itemsize == 4 and out_sf.flags.c_contiguous
+    ots, ohs = out_sf_strides if out_sf_strides is not None else (P, 1)
+    if want_w and out_w is None:
+        out_w = np.zeros(capacity, np.float32)
+    w = None if weights is None else _c(weights, np.float32)
+    lib.oracle_dispatch_quant(T, K, E, H, _ptr(x), fmt, _ptr(w), _ptr(lay.counts),
+                              _ptr(lay.psum), _ptr(_c(lay.dst, np.int32)), _ptr(out_x),
+                              _ptr(out_sf), ots, ohs, _ptr(out_w), 1 if zero_padding else 0)
+    return out_x, out_sf, out_w
+

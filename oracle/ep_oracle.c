@@ -41,6 +41,11 @@
  *       +0.0, with separately rounded multiply and add; the result is rounded
  *       to bf16 to nearest even (NaN becomes the quiet NaN 0x7FC0).
  *   R12 num_recv_tokens is the number of tokens with at least one valid slot.
+ *   R17-R22 (rank layout, per-token biases, gradients) are stated with the
+ *       functions that use them below.
+ *   R23 the FP8 quantiser (which the pages do not give) follows the
+ *       per-128-channel recipe of the workload inputs; see
+ *       oracle_quantize_fp8.
  *
  * Where no reading is needed the definition is the pages' own.
  */
@@ -158,8 +163,10 @@ int oracle_layout(int64_t T, int64_t K, int64_t E, int64_t A, int64_t capacity,
  * §7.4 (each expert owns one contiguous, aligned range)].
  *
  * x          [T, row_bytes] raw bytes (bf16: 2H bytes, FP8: H bytes)
- * sf         FP8 scale factors, element (t, j) at sf[t*sf_ts + j*sf_hs],
- *            j < num_sf; NULL when num_sf == 0
+ * sf         FP8 scale factors as 4-byte packs (one fp32, or four UE8M0
+ *            exponent bytes; the pack count is an argument of the pages'
+ *            epilogue), pack (t, j) at sf[t*sf_ts + j*sf_hs], j < num_sf;
+ *            copied as bits; NULL when num_sf == 0
  * w          [T*K] top-k weights or NULL (R10: weight 1)
  * out_x      [capacity, row_bytes]
  * out_sf     element (r, j) at out_sf[r*o_ts + j*o_hs]; NULL if num_sf == 0
@@ -168,10 +175,10 @@ int oracle_layout(int64_t T, int64_t K, int64_t E, int64_t A, int64_t capacity,
  * they were.
  */
 void oracle_dispatch(int64_t T, int64_t K, int64_t E, int64_t row_bytes,
-                     const uint8_t *x, int64_t num_sf, const float *sf,
+                     const uint8_t *x, int64_t num_sf, const uint32_t *sf,
                      int64_t sf_ts, int64_t sf_hs, const float *w,
                      const int32_t *counts, const int32_t *psum,
-                     const int32_t *dst, uint8_t *out_x, float *out_sf,
+                     const int32_t *dst, uint8_t *out_x, uint32_t *out_sf,
                      int64_t o_ts, int64_t o_hs, float *out_w, int zero_padding)
 {
     for (int64_t t = 0; t < T; ++t) {
@@ -192,7 +199,7 @@ void oracle_dispatch(int64_t T, int64_t K, int64_t E, int64_t row_bytes,
         for (int64_t r = (int64_t)psum[e] + counts[e]; r < psum[e + 1]; ++r) {
             memset(out_x + r * row_bytes, 0, (size_t)row_bytes);
             for (int64_t j = 0; j < num_sf; ++j)
-                out_sf[r * o_ts + j * o_hs] = 0.0f;
+                out_sf[r * o_ts + j * o_hs] = 0;
             if (out_w)
                 out_w[r] = 0.0f;
         }
@@ -427,10 +434,10 @@ int64_t oracle_rank_layout(int64_t T, int64_t K, int64_t E,
  * exist; nothing else is written.
  */
 void oracle_dispatch_rank(int64_t T, int64_t K, int64_t E, int64_t row_bytes,
-                          const uint8_t *x, int64_t num_sf, const float *sf,
+                          const uint8_t *x, int64_t num_sf, const uint32_t *sf,
                           int64_t sf_ts, int64_t sf_hs, const float *w,
                           const int64_t *topk_idx, const int32_t *recv_row,
-                          uint8_t *out_x, float *out_sf, int64_t o_ts,
+                          uint8_t *out_x, uint32_t *out_sf, int64_t o_ts,
                           int64_t o_hs, int64_t *out_idx, float *out_w)
 {
     for (int64_t t = 0; t < T; ++t) {
@@ -489,4 +496,154 @@ void oracle_combine_token_bias(int64_t T, int64_t K, int64_t H,
                                const uint16_t *b1, uint16_t *out)
 {
     combine_tokens(T, K, H, y, w, bias, topk_idx, dst, b0, b1, out);
+}
+
+/*
+ * FP8 quantisation of bf16 rows, the producer of dispatch's FP8 input
+ * [Ch7 §7.1: FP8 data travels with per-block scale factors; §7.3: the
+ * epilogue takes the number of 4-byte scale packs].  The pages give no
+ * quantiser; the reading used (R23) is the per-128-channel recipe of the
+ * workload inputs, plus a power-of-two (UE8M0) variant:
+ *   amax  = largest |x| of the block (NaN entries skipped), binary32
+ *   s     = max(amax, 1e-12f) / 448, one binary32 division
+ *   F32   : the block's pack is the binary32 s; divisor = s
+ *   UE8M0 : s rounded up to a power of two 2^(e-127); the block's byte is e,
+ *           four blocks per pack, the lowest block in the low byte (a last
+ *           partial pack is zero-filled); divisor = 2^(e-127)
+ *   code  = E4M3FN nearest to clamp(x / divisor, -448, 448) (binary32
+ *           division), ties to the even code; a NaN quotient gives 0x7F.
+ * E4M3FN: sign, 4 exponent bits with bias 7, 3 mantissa bits, no
+ * infinities, code 0x7F (and 0xFF) NaN, largest finite 448.
+ */
+#define ORACLE_SF_F32 0
+#define ORACLE_SF_UE8M0 1
+
+/* exact value of 2^n for |n| < 200 */
+static double pow2(int n)
+{
+    double v = 1.0;
+    for (; n > 0; --n)
+        v *= 2.0;
+    for (; n < 0; ++n)
+        v *= 0.5;
+    return v;
+}
+
+/* magnitude of the E4M3FN code c, 0 <= c <= 126 */
+static double e4m3_magnitude(int c)
+{
+    int e = c >> 3, m = c & 7;
+    return e == 0 ? m * pow2(-9) : (8 + m) * pow2(e - 10);
+}
+
+static uint32_t f32_bits(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return u;
+}
+
+static float bits_f32(uint32_t u)
+{
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* binary32 -> E4M3FN: clamp to +-448, nearest magnitude, ties to even code */
+static uint8_t e4m3_from_f32(float v)
+{
+    if (v != v)
+        return 0x7F;
+    uint8_t sign = (f32_bits(v) >> 31) ? 0x80 : 0x00;
+    double a = v < 0 ? -(double)v : (double)v;
+    if (a > 448.0)
+        a = 448.0;
+    int lo = 0;                           /* largest code whose value <= a */
+    while (lo < 126 && e4m3_magnitude(lo + 1) <= a)
+        ++lo;
+    int code = lo;
+    if (lo < 126) {
+        double dlo = a - e4m3_magnitude(lo), dhi = e4m3_magnitude(lo + 1) - a;
+        if (dhi < dlo || (dhi == dlo && ((lo + 1) & 1) == 0))
+            code = lo + 1;
+    }
+    return (uint8_t)(sign | code);
+}
+
+/* Codes of n binary32 values (exported for pinning the conversion). */
+void oracle_f32_to_e4m3(int64_t n, const float *in, uint8_t *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = e4m3_from_f32(in[i]);
+}
+
+/* Scale packs per row: H/128 for F32, ceil(H/512) for UE8M0. */
+int64_t oracle_sf_packs(int64_t H, int format)
+{
+    int64_t blocks = H / 128;
+    return format == ORACLE_SF_UE8M0 ? (blocks + 3) / 4 : blocks;
+}
+
+/*
+ * x bf16 [T, H] (H % 128 == 0) -> q E4M3FN codes [T, H] and scale packs
+ * sf[t*s_ts + p*s_hs], p < oracle_sf_packs(H, format).
+ */
+void oracle_quantize_fp8(int64_t T, int64_t H, const uint16_t *x, int format,
+                         uint8_t *q, uint32_t *sf, int64_t s_ts, int64_t s_hs)
+{
+    int64_t packs = oracle_sf_packs(H, format);
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t p = 0; p < packs; ++p)
+            sf[t * s_ts + p * s_hs] = 0;
+        for (int64_t j = 0; j < H / 128; ++j) {
+            const uint16_t *blk = x + t * H + j * 128;
+            float amax = 0.0f;
+            for (int i = 0; i < 128; ++i) {
+                float a = bits_f32(f32_bits(bf16_to_f32(blk[i])) & 0x7FFFFFFFu);
+                if (a > amax)
+                    amax = a;
+            }
+            float s = (amax > 1e-12f ? amax : 1e-12f) / 448.0f;
+            float divisor = s;
+            if (format == ORACLE_SF_UE8M0) {
+                uint32_t e = (f32_bits(s) >> 23) & 0xFF;
+                if (f32_bits(s) & 0x7FFFFFu)
+                    ++e;                  /* round up to the next power of two */
+                divisor = bits_f32(e << 23);
+                sf[t * s_ts + (j / 4) * s_hs] |= e << (8 * (j % 4));
+            } else {
+                sf[t * s_ts + j * s_hs] = f32_bits(s);
+            }
+            for (int i = 0; i < 128; ++i)
+                q[t * H + j * 128 + i] = e4m3_from_f32(bf16_to_f32(blk[i]) / divisor);
+        }
+    }
+}
+
+/*
+ * Quantising dispatch: the quantiser above followed by the dispatch copy of
+ * the codes and scale packs into the expanded layout (same weights and zero
+ * padding rules as oracle_dispatch).
+ */
+void oracle_dispatch_quant(int64_t T, int64_t K, int64_t E, int64_t H,
+                           const uint16_t *x, int format, const float *w,
+                           const int32_t *counts, const int32_t *psum,
+                           const int32_t *dst, uint8_t *out_x, uint32_t *out_sf,
+                           int64_t o_ts, int64_t o_hs, float *out_w,
+                           int zero_padding)
+{
+    int64_t packs = oracle_sf_packs(H, format);
+    uint8_t *q = malloc((size_t)(T * H > 0 ? T * H : 1));
+    uint32_t *sf = malloc((size_t)(T * packs > 0 ? T * packs : 1) * sizeof *sf);
+    if (!q || !sf) {
+        free(q);
+        free(sf);
+        return;
+    }
+    oracle_quantize_fp8(T, H, x, format, q, sf, packs, 1);
+    oracle_dispatch(T, K, E, H, q, packs, sf, packs, 1, w, counts, psum, dst,
+                    out_x, out_sf, o_ts, o_hs, out_w, zero_padding);
+    free(q);
+    free(sf);
 }

@@ -16,6 +16,7 @@ import os
 import sys
 
 import numpy as np
+import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, os.path.dirname(_HERE))
@@ -244,6 +245,32 @@ def pin_dispatch_closed_form(lib):
                                    int(rng.integers(1, 20)), int(rng.choice([1, 4, 16])),
                                    256 if fp8 else 2 * 24, fp8, zp, with_w, rng,
                                    sf_layout)
+
+
+def pin_dispatch_scale_packs(lib):
+    """Scale packs are 4-byte words copied as bits (one fp32 per block, or four
+    UE8M0 exponent bytes; DeepEP notes ch.7 s7.3 passes the pack count and
+    both strides): random words, many of them NaN patterns as floats, go to a
+    column-major output whose pack stride is the row count rounded up to 4
+    (16-byte aligned columns), and equal the closed form bit for bit."""
+    rng = np.random.default_rng(29)
+    for zp in (False, True):
+        T, K, E, A, row_bytes = 37, 5, 11, 8, 640
+        packs = (row_bytes // 128 + 3) // 4                  # four exponents per word
+        idx = rng.integers(-1, E, size=(T, K))
+        cap = T * K + (A - 1) * E + A
+        lay = oracle.layout(idx, E, A, cap, lib=lib)
+        x = rng.integers(0, 256, size=(T, row_bytes), dtype=np.uint8)
+        sf = rng.integers(0, 2 ** 32, size=(T, packs), dtype=np.uint64).astype(np.uint32)
+        sf[::3, 0] = 0x7FC00001                               # a NaN payload must survive
+        tma = (cap + 3) // 4 * 4
+        store = np.full((packs, tma), 0xA5A5A5A5, np.uint32)
+        _, osf, _ = oracle.dispatch(x, lay, cap, sf=sf, zero_padding=zp, out_sf=store,
+                                    out_sf_strides=(1, tma), num_sf_packs=packs, lib=lib)
+        _, esf, _ = BF.dispatch_expected(x, lay.dst, lay.counts, lay.psum, cap, sf=sf,
+                                         zero_padding=zp)
+        np.testing.assert_array_equal(osf[:, :cap].T, esf)
+        assert np.all(osf[:, cap:] == 0xA5A5A5A5)
 
 
 # ----------------------------------------------------------------------------
@@ -541,6 +568,133 @@ def pin_combine_token_bias(lib):
                                     np.array(g["dst"]), b0_bits=_bf16_bits(g["bias_0"]),
                                     b1_bits=_bf16_bits(g["bias_1"]), lib=lib)
     assert got.tolist() == g["expected_bits"]
+
+
+# ----------------------------------------------------------------------------
+# FP8 quantiser (reading R23: the per-128-channel recipe of the workload inputs)
+
+
+def _torch_e4m3(vals_f32: np.ndarray) -> np.ndarray:
+    """torch's binary32 -> float8_e4m3fn conversion (nearest, ties to even) of
+    values already inside [-448, 448]."""
+    t = torch.from_numpy(np.ascontiguousarray(vals_f32, np.float32))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def pin_e4m3_conversion_matches_torch(lib):
+    """Every bf16 value in [-448, 448], every midpoint between neighbouring
+    E4M3FN magnitudes and the binary32 neighbours of each midpoint convert
+    like torch's float8_e4m3fn cast (a library routine)."""
+    bits = np.arange(1 << 16, dtype=np.uint32) << 16
+    v = bits.view(np.float32)
+    v = v[np.isfinite(v) & (np.abs(v) <= 448)]
+    e = np.arange(16)[:, None]
+    m = np.arange(8)[None, :]
+    mags = np.where(e == 0, m * 2.0 ** -9, (8 + m) * 2.0 ** (e - 10)).reshape(-1)[:127]
+    mids = ((mags[:-1] + mags[1:]) / 2).astype(np.float32)
+    near = np.concatenate([mids, np.nextafter(mids, np.float32(0)),
+                           np.nextafter(mids, np.float32(1000))]).astype(np.float32)
+    vals = np.concatenate([v, near, -near, mags.astype(np.float32)]).astype(np.float32)
+    np.testing.assert_array_equal(oracle.f32_to_e4m3(vals, lib=lib), _torch_e4m3(vals))
+    big = np.array([448.5, 464.0, 1e30, np.inf, -np.inf, -500.0], np.float32)
+    np.testing.assert_array_equal(oracle.f32_to_e4m3(big, lib=lib),
+                                  _torch_e4m3(np.clip(big, -448, 448)))
+    assert oracle.f32_to_e4m3(np.array([np.nan], np.float32), lib=lib)[0] == 0x7F
+
+
+def _quant_inputs(rng, T, H):
+    """bf16 rows whose blocks span many magnitudes, with an all-zero block,
+    a block below 1e-12 and blocks whose largest magnitude is negative."""
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    x *= (10.0 ** rng.integers(-8, 6, size=(T, H // 128, 1))).repeat(128, axis=2).reshape(T, H)
+    x[0, :128] = 0.0
+    x[1, 128:256] *= 1e-14
+    x[2, :128] = -np.abs(x[2, :128])
+    return BF.f32_to_bf16_bits_torch(x)
+
+
+def pin_quantize_f32_matches_torch_recipe(lib):
+    """F32 scales: the same recipe written with torch ops (amax per block,
+    clamp_min(1e-12) / 448, division, clamp, float8_e4m3fn cast)."""
+    rng = np.random.default_rng(53)
+    T, H = 24, 1280
+    xb = _quant_inputs(rng, T, H)
+    q, sf = oracle.quantize_fp8(xb, oracle.SF_F32, lib=lib)
+    xf = torch.from_numpy(_bits_to_float(xb)).reshape(T, H // 128, 128)
+    s = xf.abs().amax(dim=2).clamp_min(1e-12) / 448.0
+    codes = (xf / s[:, :, None]).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
+    np.testing.assert_array_equal(q, codes.view(torch.uint8).numpy().reshape(T, H))
+    np.testing.assert_array_equal(sf, s.numpy().view(np.uint32))
+
+
+def pin_quantize_ue8m0_power_of_two(lib):
+    """UE8M0: the scale byte is 127 + ceil(log2(s)) (numpy frexp: s = f * 2^k,
+    f in [0.5, 1)), four bytes per pack from the lowest block up, and the
+    codes are torch's cast of x / 2^(byte - 127)."""
+    rng = np.random.default_rng(59)
+    T, H = 20, 1664                                   # 13 blocks: a partial last pack
+    xb = _quant_inputs(rng, T, H)
+    q, sf = oracle.quantize_fp8(xb, oracle.SF_UE8M0, lib=lib)
+    xf = _bits_to_float(xb).reshape(T, H // 128, 128)
+    s = np.maximum(np.abs(xf).max(axis=2), np.float32(1e-12)).astype(np.float32) / np.float32(448)
+    f, k = np.frexp(s.astype(np.float64))
+    ex = np.where(f == 0.5, k - 1, k) + 127
+    packs = np.zeros((T, (H // 128 + 3) // 4), np.uint64)
+    for j in range(H // 128):
+        packs[:, j // 4] |= ex[:, j].astype(np.uint64) << np.uint64(8 * (j % 4))
+    np.testing.assert_array_equal(sf, packs.astype(np.uint32))
+    div = np.ldexp(np.float32(1), (ex - 127).astype(np.int32)).astype(np.float32)
+    vals = np.clip(xf / div[:, :, None], -448, 448).astype(np.float32)
+    np.testing.assert_array_equal(q, _torch_e4m3(vals.reshape(T, H)))
+
+
+def pin_quantize_golden(lib):
+    g = _golden("quant_hand.json")
+    H = g["hidden"]
+    x = np.zeros((1, H), np.float32)
+    for c, v in g["nonzero"].items():
+        x[0, int(c)] = np.nan if v == "nan" else v
+    xb = _bf16_bits(x)
+    q, sf = oracle.quantize_fp8(xb, oracle.SF_F32, lib=lib)
+    for c, code in g["f32_codes"].items():
+        assert q[0, int(c)] == code, (c, q[0, int(c)], code)
+    assert np.count_nonzero(q) == len(g["f32_codes"]) - sum(1 for v in g["f32_codes"].values()
+                                                             if v == 0)
+    amax = np.array(g["block_amax"], np.float32)
+    want = np.maximum(amax, np.float32(1e-12)) / np.float32(448)
+    np.testing.assert_array_equal(sf[0], want.astype(np.float32).view(np.uint32))
+    q, sf = oracle.quantize_fp8(xb, oracle.SF_UE8M0, lib=lib)
+    for c, code in g["ue8m0_codes"].items():
+        assert q[0, int(c)] == code, (c, q[0, int(c)], code)
+    assert sf[0].tolist() == g["ue8m0_packs"]
+    for j, e in enumerate(g["ue8m0_exponents"]):
+        assert (int(sf[0, j // 4]) >> (8 * (j % 4))) & 0xFF == e
+
+
+def pin_dispatch_quant_is_quantize_then_copy(lib):
+    """The quantising dispatch equals the closed-form copy of the quantised
+    rows and their packs (both formats, with and without zero padding)."""
+    rng = np.random.default_rng(61)
+    for fmt in (oracle.SF_F32, oracle.SF_UE8M0):
+        for zp in (False, True):
+            T, K, E, A, H = 30, 4, 9, 8, 640
+            idx = rng.integers(-1, E, size=(T, K))
+            cap = T * K + (A - 1) * E + A
+            lay = oracle.layout(idx, E, A, cap, lib=lib)
+            xb = _quant_inputs(rng, T, H)
+            w = rng.random((T, K), dtype=np.float32)
+            P = oracle.sf_packs(H, fmt, lib=lib)
+            ox = np.full((cap, H), 0xA5, np.uint8)
+            osf = np.full((cap, P), 0xA5A5A5A5, np.uint32)
+            ow = np.full(cap, np.frombuffer(b"\xa5" * 4, np.float32)[0], np.float32)
+            oracle.dispatch_quant(xb, lay, cap, fmt, weights=w, zero_padding=zp, out_x=ox,
+                                  out_sf=osf, out_w=ow, lib=lib)
+            q, sf = oracle.quantize_fp8(xb, fmt, lib=lib)
+            ex, esf, ew = BF.dispatch_expected(q, lay.dst, lay.counts, lay.psum, cap, sf=sf,
+                                               weights=w, zero_padding=zp)
+            np.testing.assert_array_equal(ox, ex)
+            np.testing.assert_array_equal(osf, esf)
+            np.testing.assert_array_equal(ow.view(np.uint32), ew.view(np.uint32))
 
 
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -33,7 +33,7 @@ MUTANTS = {
     "dispatch_wrong_token": ("x + t * row_bytes, (size_t)row_bytes);",
                              "x + ((t + 1) % T) * row_bytes, (size_t)row_bytes);"),
     "dispatch_sf_strides_swapped": ("sf[t * sf_ts + j * sf_hs]", "sf[t * sf_hs + j * sf_ts]"),
-    "dispatch_gap_sf_kept": ("                out_sf[r * o_ts + j * o_hs] = 0.0f;\n", "\n"),
+    "dispatch_gap_sf_kept": ("                out_sf[r * o_ts + j * o_hs] = 0;\n", "\n"),
     "dispatch_weight_index": ("out_w[r] = w ? w[t * K + k] : 1.0f;",
                               "out_w[r] = w ? w[t * K] : 1.0f;"),
     "dispatch_pads_no_weight": ("                out_w[r] = 0.0f;\n", "                ;\n"),
@@ -88,6 +88,18 @@ MUTANTS = {
         "                acc = acc + p;\n            }\n            if (b0)\n"
         "                acc = acc + bf16_to_f32(b0[t * H + h]);\n            if (0)\n"
         "                acc = acc + bf16_to_f32(b1[t * H + h]);"),
+    "quant_ties_up": ("if (dhi < dlo || (dhi == dlo && ((lo + 1) & 1) == 0))",
+                      "if (dhi < dlo || dhi == dlo)"),
+    "quant_no_scale_floor": ("float s = (amax > 1e-12f ? amax : 1e-12f) / 448.0f;",
+                             "float s = amax / 448.0f;"),
+    "quant_ue8m0_rounds_down": ("                    ++e;                  /* round up", 
+                                "                    e += 0;               /* round up"),
+    "quant_pack_order": ("|= e << (8 * (j % 4));", "|= e << (8 * (3 - j % 4));"),
+    "quant_signed_amax": ("& 0x7FFFFFFFu);\n                if (a > amax)",
+                          "& 0xFFFFFFFFu);\n                if (a > amax)"),
+    "quant_nan_code": ("    if (v != v)\n        return 0x7F;", "    if (v != v)\n        return 0x00;"),
+    "quant_subnormal_step": ("return e == 0 ? m * pow2(-9)", "return e == 0 ? m * pow2(-10)"),
+    "quant_ue8m0_divides_by_s": ("divisor = bits_f32(e << 23);", "divisor = s;"),
 }
 
 
