@@ -51,6 +51,8 @@ def parse():
                    help="calls of each backward entry point after the timed steps (0 = skip)")
     p.add_argument("--rank-reps", type=int, default=30,
                    help="calls of the rank-layout and per-token-bias entry points (0 = skip)")
+    p.add_argument("--quant-reps", type=int, default=30,
+                   help="calls timed for the FP8 quantiser phase (0 skips it)")
     p.add_argument("--flush", action="store_true",
                    help="read a 1 GiB scratch buffer before every call (outside the per-call "
                         "events) so each kernel starts with cold L2 and MALL")
@@ -157,6 +159,30 @@ def cpu_baseline(cfg, wl, y_host, min_seconds: float):
         if time.perf_counter() >= t_end and len(times) >= 1:
             break
     return statistics.median(times), len(times), lay
+
+
+def time_calls(calls, nbytes, reps):
+    """Each call once untimed, then `reps` calls whose kernel intervals are
+    stamped by ep_time_next_call; mean µs, GB/s of the algorithmic bytes."""
+    import torch
+    import combine_ep_layout_08_amd as ep
+    out = {}
+    for name, fn in calls.items():
+        fn()
+        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(reps)]
+        for e0, e1 in pairs:
+            e0.record()
+            e1.record()
+        for e0, e1 in pairs:
+            ep.time_next_call(e0, e1)
+            fn()
+        torch.cuda.synchronize()
+        us = statistics.mean(e0.elapsed_time(e1) * 1e3 for e0, e1 in pairs)
+        gbps = nbytes[name] / (us * 1e-6) / 1e9
+        out[name] = {"us_mean": round(us, 2), "bytes": nbytes[name], "GBps": round(gbps, 1),
+                     "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+    return out
 
 
 def main():
@@ -291,22 +317,7 @@ def main():
                       g, topk_weights=w, y=wl.y, grad_y=grad_y, want_grad_weights=True),
                   "dispatch_backward": lambda: h.dispatch_backward(
                       wl.y, grad_out_w=gw_rows, want_grad_weights=True)}
-        backward = {}
-        for name, fn in bcalls.items():
-            fn()
-            pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                     for _ in range(args.backward_reps)]
-            for e0, e1 in pairs:
-                e0.record()
-                e1.record()
-            for e0, e1 in pairs:
-                ep.time_next_call(e0, e1)
-                fn()
-            torch.cuda.synchronize()
-            us = statistics.mean(e0.elapsed_time(e1) * 1e3 for e0, e1 in pairs)
-            gbps = bb[name] / (us * 1e-6) / 1e9
-            backward[name] = {"us_mean": round(us, 2), "bytes": bb[name], "GBps": round(gbps, 1),
-                              "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+        backward = time_calls(bcalls, bb, args.backward_reps)
 
     # Rank (non-expanded) layout and per-token biases, on the same layout.
     rank = None
@@ -331,23 +342,33 @@ def main():
                   "combine_rank": lambda: h.combine_rank(xr, bias_0=b0, bias_1=b1, out=out),
                   "combine_token_biases": lambda: h.combine(wl.y, topk_weights=w, bias=wl.bias,
                                                             out=out, bias_0=b0, bias_1=b1)}
-        rank = {}
-        for name, fn in rcalls.items():
-            fn()
-            pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                     for _ in range(args.rank_reps)]
-            for e0, e1 in pairs:
-                e0.record()
-                e1.record()
-            for e0, e1 in pairs:
-                ep.time_next_call(e0, e1)
-                fn()
-            torch.cuda.synchronize()
-            us = statistics.mean(e0.elapsed_time(e1) * 1e3 for e0, e1 in pairs)
-            gbps = rb[name] / (us * 1e-6) / 1e9
-            rank[name] = {"us_mean": round(us, 2), "bytes": rb[name], "GBps": round(gbps, 1),
-                          "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+        rank = time_calls(rcalls, rb, args.rank_reps)
         del rx, rsf, ri, rw, xr, b0, b1
+
+    # FP8 quantiser on its own and fused with dispatch: bf16 rows of the
+    # same workload, on the same layout, fp32 and packed UE8M0 scales.
+    quant = None
+    if args.quant_reps > 0 and cfg.hidden % 128 == 0:
+        T, K, H = cfg.tokens, cfg.topk, cfg.hidden
+        xq = W.payload_bf16(T, H, cfg.seed + 5, 3, "cuda")
+        qx = torch.empty((cap, H), dtype=torch.uint8, device="cuda")
+        qt = torch.empty((T, H), dtype=torch.uint8, device="cuda")
+        sfs = {f: torch.empty((cap, ep.ep_sf_packs(H, c)),
+                              dtype=torch.float32 if f == "f32" else torch.int32, device="cuda")
+               for f, c in (("f32", ep.EP_SF_F32), ("ue8m0", ep.EP_SF_UE8M0))}
+        sft = torch.empty((T, H // 128), dtype=torch.float32, device="cuda")
+        P = {f: ep.ep_sf_packs(H, c) for f, c in (("f32", ep.EP_SF_F32),
+                                                    ("ue8m0", ep.EP_SF_UE8M0))}
+        qb = {"quantize_f32": T * 2 * H + T * H + 4 * T * P["f32"],
+              "dispatch_quant_f32": T * 2 * H + V * (H + 4 * P["f32"]) + 4 * T * K,
+              "dispatch_quant_ue8m0": T * 2 * H + V * (H + 4 * P["ue8m0"]) + 4 * T * K}
+        qcalls = {"quantize_f32": lambda: ep.quantize_fp8(xq, "f32", out_q=qt, out_sf=sft),
+                  "dispatch_quant_f32": lambda: h.dispatch_quant(xq, "f32", out_x=qx,
+                                                                 out_sf=sfs["f32"]),
+                  "dispatch_quant_ue8m0": lambda: h.dispatch_quant(xq, "ue8m0", out_x=qx,
+                                                                   out_sf=sfs["ue8m0"])}
+        quant = time_calls(qcalls, qb, args.quant_reps)
+        del xq, qx, qt, sfs, sft
 
     total_bytes = sum(nbytes.values())
     if args.flush:
@@ -408,6 +429,7 @@ def main():
         "kernels_cold_cache": kernels_cold,
         "backward": backward,
         "rank_and_token_bias": rank,
+        "quantize": quant,
         "roofline": roofline,
         "ceilings": ceil,
         "cpu_baseline": cpu,

@@ -26,15 +26,19 @@ __all__ = [
     "ep_workspace_bytes", "ep_handle_init", "ep_layout", "ep_handle_read_counts",
     "ep_handle_import", "ep_dispatch", "ep_combine", "ep_status_str", "ep_handle_sizeof",
     "ep_time_next_call", "time_next_call", "ep_combine_backward", "ep_dispatch_backward",
-    "ep_dispatch_rank", "ep_combine_rank", "ep_tma_aligned_rows",
+    "ep_dispatch_rank", "ep_combine_rank", "ep_tma_aligned_rows", "ep_sf_packs",
+    "ep_quantize_fp8", "ep_dispatch_quant", "EP_SF_F32", "EP_SF_UE8M0", "quantize_fp8",
 ]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libep.so")
+LIB_PATH = os.environ.get("EP_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libep.so")
 
 (EP_OK, EP_ERR_NULL, EP_ERR_SHAPE, EP_ERR_DTYPE, EP_ERR_UNSUPPORTED, EP_ERR_MISALIGNED,
  EP_ERR_WORKSPACE, EP_ERR_NOT_LAID_OUT, EP_ERR_CAPACITY, EP_ERR_INVALID_ID,
  EP_ERR_HIP, EP_ERR_TIMEOUT) = range(12)
 EP_BF16, EP_FP8_E4M3, EP_F32, EP_I32, EP_I64 = range(5)
+EP_SF_F32, EP_SF_UE8M0 = 0, 1
+_SF_FORMATS = {"f32": EP_SF_F32, "ue8m0": EP_SF_UE8M0}
 EP_ERRBIT_CAPACITY = 1
 EP_ERRBIT_INVALID_ID = 2
 EP_ERRBIT_SCAN_TIMEOUT = 4
@@ -86,6 +90,10 @@ _SIGNATURES = {
     "ep_dispatch": (ctypes.c_int, [_HP, _P, ctypes.c_int, _I32, _P, _I64, _I64, _I32, _P, _P,
                                    _P, _I64, _I64, _P, _I32, _P]),
     "ep_tma_aligned_rows": (_I64, [_I64]),
+    "ep_sf_packs": (_I32, [_I32, ctypes.c_int]),
+    "ep_quantize_fp8": (ctypes.c_int, [_P, _I32, _I32, ctypes.c_int, _P, _P, _I64, _I64, _P]),
+    "ep_dispatch_quant": (ctypes.c_int, [_HP, _P, _I32, ctypes.c_int, _P, _P, _P, _I64, _I64,
+                                         _P, _I32, _P]),
     "ep_combine": (ctypes.c_int, [_HP, _P, ctypes.c_int, _I32, _P, _P, _P, _P, _P, _P]),
     "ep_dispatch_rank": (ctypes.c_int, [_HP, _P, ctypes.c_int, _I32, _P, _I64, _I64, _I32, _P,
                                         _P, _P, _I64, _I64, _P, _P, _P]),
@@ -172,6 +180,22 @@ def ep_tma_aligned_rows(rows: int) -> int:
     return int(lib().ep_tma_aligned_rows(rows))
 
 
+def ep_sf_packs(hidden: int, fmt: int) -> int:
+    return int(lib().ep_sf_packs(hidden, fmt))
+
+
+def ep_quantize_fp8(x_ptr, num_tokens, hidden, fmt, out_q_ptr, out_sf_ptr, out_ts, out_hs,
+                    stream) -> int:
+    return lib().ep_quantize_fp8(x_ptr, num_tokens, hidden, fmt, out_q_ptr, out_sf_ptr, out_ts,
+                                 out_hs, stream)
+
+
+def ep_dispatch_quant(h: ep_handle, x_ptr, hidden, fmt, w_ptr, out_x_ptr, out_sf_ptr, out_ts,
+                      out_hs, out_w_ptr, zero_padding, stream) -> int:
+    return lib().ep_dispatch_quant(ctypes.byref(h), x_ptr, hidden, fmt, w_ptr, out_x_ptr,
+                                   out_sf_ptr, out_ts, out_hs, out_w_ptr, zero_padding, stream)
+
+
 def ep_combine(h: ep_handle, y_ptr, y_dtype, hidden, w_ptr, bias_ptr, bias0_ptr, bias1_ptr,
                out_ptr, stream) -> int:
     return lib().ep_combine(ctypes.byref(h), y_ptr, y_dtype, hidden, w_ptr, bias_ptr, bias0_ptr,
@@ -246,6 +270,12 @@ def _dev(t: torch.Tensor, name: str):
     _need(t.is_contiguous(), f"{name} must be contiguous")
 
 
+def _dev_strided(t: torch.Tensor, name: str):
+    """Scale tensors may have any non-negative strides (the kernels take them)."""
+    _need(t.is_cuda, f"{name} must be a device tensor")
+    _need(t.dim() == 2 and min(t.stride()) >= 0, f"{name} must be a 2-D strided view")
+
+
 _SF_DTYPES = (torch.float32, torch.int32)
 
 
@@ -256,7 +286,7 @@ def _scale_packs(sf, T, H, rows, out_sf, col_major, device):
     strides); a column-major out_sf has token stride 1 and pack stride
     ep_tma_aligned_rows(rows)."""
     _need(sf is not None, "FP8 dispatch needs scale factors")
-    _dev(sf, "sf")
+    _dev_strided(sf, "sf")
     _need(sf.dtype in _SF_DTYPES and sf.dim() == 2 and sf.shape[0] == T,
           "sf must be fp32 [T, H/128] or int32 packs [T, P]")
     packs = sf.shape[1]
@@ -267,10 +297,52 @@ def _scale_packs(sf, T, H, rows, out_sf, col_major, device):
             out_sf = store[:, :rows].t()
         else:
             out_sf = torch.empty((rows, packs), dtype=sf.dtype, device=device)
-    _dev(out_sf, "out_sf")
+    _dev_strided(out_sf, "out_sf")
     _need(out_sf.dtype == sf.dtype and tuple(out_sf.shape) == (rows, packs),
           f"out_sf must be [{rows}, {packs}] of sf's dtype")
     return packs, sf.stride(), out_sf, out_sf.stride()
+
+
+def _sf_format(scale_format) -> int:
+    fmt = _SF_FORMATS.get(scale_format, scale_format)
+    _need(fmt in (EP_SF_F32, EP_SF_UE8M0), "scale_format must be 'f32' or 'ue8m0'")
+    return fmt
+
+
+def _quant_sf_out(out_sf, rows, packs, fmt, col_major, device):
+    dt = torch.float32 if fmt == EP_SF_F32 else torch.int32
+    if out_sf is None:
+        if col_major:
+            out_sf = torch.empty((packs, ep_tma_aligned_rows(rows)), dtype=dt,
+                                 device=device)[:, :rows].t()
+        else:
+            out_sf = torch.empty((rows, packs), dtype=dt, device=device)
+    _dev_strided(out_sf, "out_sf")
+    _need(out_sf.dtype == dt and tuple(out_sf.shape) == (rows, packs),
+          f"out_sf must be [{rows}, {packs}] {dt}")
+    return out_sf
+
+
+def quantize_fp8(x: torch.Tensor, scale_format="f32", out_q=None, out_sf=None,
+                 col_major_sf: bool = False):
+    """bf16 [T, H] -> (E4M3FN codes uint8 [T, H], scales): fp32 [T, H/128]
+    for 'f32', int32 packs [T, ceil(H/512)] of UE8M0 exponents for 'ue8m0'."""
+    _dev(x, "x")
+    _need(x.dtype == torch.bfloat16 and x.dim() == 2, "x must be bf16 [T, H]")
+    T, H = x.shape
+    fmt = _sf_format(scale_format)
+    packs = ep_sf_packs(H, fmt)
+    _need(packs > 0, "hidden must be a positive multiple of 128")
+    if out_q is None:
+        out_q = torch.empty((T, H), dtype=torch.uint8, device=x.device)
+    _dev(out_q, "out_q")
+    _need(out_q.dtype in (torch.uint8, torch.float8_e4m3fn) and tuple(out_q.shape) == (T, H),
+          "out_q must be FP8 codes [T, H]")
+    out_sf = _quant_sf_out(out_sf, T, packs, fmt, col_major_sf, x.device)
+    ts, hs = out_sf.stride()
+    _check(ep_quantize_fp8(_ptr(x), T, H, fmt, _ptr(out_q), _ptr(out_sf), ts, hs, _stream()),
+           "ep_quantize_fp8")
+    return out_q, out_sf
 
 
 class Handle:
@@ -425,6 +497,43 @@ class Handle:
                            sf_ts, sf_hs, packs, _ptr(topk_weights), _ptr(out_x), _ptr(out_sf),
                            o_ts, o_hs, _ptr(out_w), 1 if zero_padding else 0, _stream()),
                "ep_dispatch")
+        return out_x, out_sf, out_w
+
+    def dispatch_quant(self, x: torch.Tensor, scale_format="f32",
+                       topk_weights: Optional[torch.Tensor] = None, zero_padding: bool = False,
+                       out_x=None, out_sf=None, out_w=None, want_weights: bool = False,
+                       col_major_sf: bool = False):
+        """Quantise bf16 x [T, H] to FP8 and dispatch in one pass.  Returns
+        (codes uint8 [capacity, H], scales [capacity, packs], out_w)."""
+        T = self.h.num_tokens
+        _dev(x, "x")
+        _need(x.dtype == torch.bfloat16 and x.dim() == 2 and x.shape[0] == T,
+              "x must be bf16 [num_tokens, H]")
+        H = x.shape[1]
+        fmt = _sf_format(scale_format)
+        packs = ep_sf_packs(H, fmt)
+        _need(packs > 0, "hidden must be a positive multiple of 128")
+        cap = self.capacity
+        if out_x is None:
+            out_x = torch.empty((cap, H), dtype=torch.uint8, device=x.device)
+        _dev(out_x, "out_x")
+        _need(out_x.dtype in (torch.uint8, torch.float8_e4m3fn) and
+              tuple(out_x.shape) == (cap, H), "out_x must be FP8 codes [capacity, H]")
+        out_sf = _quant_sf_out(out_sf, cap, packs, fmt, col_major_sf, x.device)
+        o_ts, o_hs = out_sf.stride()
+        if topk_weights is not None:
+            _dev(topk_weights, "topk_weights")
+            _need(topk_weights.dtype == torch.float32 and
+                  tuple(topk_weights.shape) == (T, self.h.num_topk),
+                  "topk_weights must be fp32 [T, K]")
+        if want_weights and out_w is None:
+            out_w = torch.empty(cap, dtype=torch.float32, device=x.device)
+        if out_w is not None:
+            _dev(out_w, "out_w")
+            _need(out_w.dtype == torch.float32 and out_w.numel() == cap, "out_w: fp32 [capacity]")
+        _check(ep_dispatch_quant(self.h, _ptr(x), H, fmt, _ptr(topk_weights), _ptr(out_x),
+                                 _ptr(out_sf), o_ts, o_hs, _ptr(out_w),
+                                 1 if zero_padding else 0, _stream()), "ep_dispatch_quant")
         return out_x, out_sf, out_w
 
     def combine(self, y: torch.Tensor, topk_weights: Optional[torch.Tensor] = None,

@@ -326,6 +326,78 @@ ep_status ep_dispatch(const ep_handle *h, const void *x, ep_dtype x_dtype, int32
     return hip_status(ep::launch_dispatch(a, stream, ev));
 }
 
+int32_t ep_sf_packs(int32_t hidden, ep_sf_format fmt) {
+    if (hidden <= 0 || hidden % 128 != 0) return -1;
+    if (fmt == EP_SF_F32) return hidden / 128;
+    if (fmt == EP_SF_UE8M0) return (hidden / 128 + 3) / 4;
+    return -1;
+}
+
+// Shared checks of the two quantising calls; fills the copy-free fields.
+static ep_status quant_args(const void *x, int32_t hidden, ep_sf_format fmt, const void *out_x,
+                            const void *out_sf, int64_t ts, int64_t hs, bool rows,
+                            ep::DispatchArgs *a) {
+    if (fmt != EP_SF_F32 && fmt != EP_SF_UE8M0) return EP_ERR_DTYPE;
+    if (hidden <= 0) return EP_ERR_SHAPE;
+    if (hidden % 128 != 0) return EP_ERR_MISALIGNED;
+    if (ts < 0 || hs < 0) return EP_ERR_SHAPE;
+    if (rows && (!x || !out_x || !out_sf)) return EP_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(out_x, 16) || !aligned(out_sf, 4)) return EP_ERR_MISALIGNED;
+    a->x = x;
+    a->row_vecs = hidden / 16;
+    a->out_x = const_cast<void *>(out_x);
+    a->num_sf = ep_sf_packs(hidden, fmt);
+    a->out_sf = static_cast<uint32_t *>(const_cast<void *>(out_sf));
+    a->out_ts = ts;
+    a->out_hs = hs;
+    a->quant = static_cast<int32_t>(fmt) + 1;
+    return EP_OK;
+}
+
+ep_status ep_quantize_fp8(const void *x, int32_t num_tokens, int32_t hidden, ep_sf_format fmt,
+                          void *out_q, void *out_sf, int64_t out_sf_token_stride,
+                          int64_t out_sf_hidden_stride, hipStream_t stream) {
+    const ep::CallEvents ev = take_events();
+    if (num_tokens < 0) return EP_ERR_SHAPE;
+    ep::DispatchArgs a{};
+    const ep_status st = quant_args(x, hidden, fmt, out_q, out_sf, out_sf_token_stride,
+                                    out_sf_hidden_stride, num_tokens > 0, &a);
+    if (st != EP_OK) return st;
+    a.num_tokens = num_tokens;
+    a.num_topk = 1;
+    a.alignment = 1;
+    a.capacity = num_tokens;          // one destination row per token: its own
+    return hip_status(ep::launch_dispatch(a, stream, ev));
+}
+
+ep_status ep_dispatch_quant(const ep_handle *h, const void *x, int32_t hidden, ep_sf_format fmt,
+                            const float *topk_weights, void *out_x, void *out_sf,
+                            int64_t out_sf_token_stride, int64_t out_sf_hidden_stride,
+                            float *out_w, int32_t zero_padding, hipStream_t stream) {
+    const ep::CallEvents ev = take_events();
+    if (!h) return EP_ERR_NULL;
+    if (!handle_ready(h)) return EP_ERR_WORKSPACE;
+    if (!h->laid_out) return EP_ERR_NOT_LAID_OUT;
+    ep::DispatchArgs a{};
+    const ep_status st = quant_args(x, hidden, fmt, out_x, out_sf, out_sf_token_stride,
+                                    out_sf_hidden_stride, h->num_tokens > 0, &a);
+    if (st != EP_OK) return st;
+    if (!aligned(topk_weights, 4) || !aligned(out_w, 4)) return EP_ERR_MISALIGNED;
+    a.num_tokens = h->num_tokens;
+    a.num_topk = h->num_topk;
+    a.num_experts = h->num_experts;
+    a.alignment = h->expert_alignment;
+    a.capacity = h->capacity;
+    a.dst = h->dst_slot;
+    a.counts = h->counts;
+    a.psum = h->psum;
+    a.scalars = h->scalars;
+    a.w = topk_weights;
+    a.out_w = out_w;
+    a.zero_padding = zero_padding != 0;
+    return hip_status(ep::launch_dispatch(a, stream, ev));
+}
+
 ep_status ep_combine(const ep_handle *h, const void *y, ep_dtype y_dtype, int32_t hidden,
                      const float *topk_weights, const void *bias, const void *bias_0,
                      const void *bias_1, void *out, hipStream_t stream) {

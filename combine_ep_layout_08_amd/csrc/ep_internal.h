@@ -108,6 +108,7 @@ struct DispatchArgs {
     int64_t out_ts, out_hs;
     float *out_w;
     bool zero_padding;
+    int32_t quant;               // 0: copy x; EP_SF_F32 + 1 / EP_SF_UE8M0 + 1: quantise bf16 x
 };
 
 struct CombineArgs {

@@ -79,6 +79,13 @@ typedef enum ep_dtype {
     EP_I64 = 4
 } ep_dtype;
 
+/* Scale-factor formats written by the FP8 quantiser. */
+typedef enum ep_sf_format {
+    EP_SF_F32 = 0,            /* one binary32 scale per 128-channel block       */
+    EP_SF_UE8M0 = 1           /* one exponent byte per block, four per 4-byte   */
+                              /* pack, lowest block in the low byte            */
+} ep_sf_format;
+
 /* Device error word bits (scalars[EP_SCALAR_ERROR_BITS]). */
 #define EP_ERRBIT_CAPACITY 1u
 #define EP_ERRBIT_INVALID_ID 2u
@@ -242,6 +249,41 @@ ep_status ep_dispatch(const ep_handle *h, const void *x, ep_dtype x_dtype,
  * i.e. to a multiple of 4.  Returns -1 for rows < 0.
  */
 int64_t ep_tma_aligned_rows(int64_t rows);
+
+/*
+ * FP8 quantiser: the producer of dispatch's FP8 input [Ch7 §7.1: FP8 data
+ * travels with per-block scale factors; §7.3: the scale factors are 4-byte
+ * packs with their own strides].  The pages give no recipe; this one is the
+ * per-128-channel recipe of the benchmark inputs:
+ *   amax = largest |x| of the block (NaN skipped); s = max(amax, 1e-12)/448
+ *   (binary32); EP_SF_F32 stores s, EP_SF_UE8M0 stores the exponent byte of
+ *   s rounded up to a power of two; the divisor is the stored scale's value;
+ *   code = E4M3FN nearest to clamp(x / divisor, -448, 448) (binary32
+ *   division), ties to even; a NaN quotient gives 0x7F.
+ *   x        device bf16 [num_tokens, hidden], hidden % 128 == 0, 16-byte
+ *            aligned.
+ *   out_q    device [num_tokens, hidden] E4M3FN codes, 16-byte aligned.
+ *   out_sf   device 4-byte packs, pack (t, j) at out_sf[t*token_stride +
+ *            j*hidden_stride], j < ep_sf_packs(hidden, fmt).
+ */
+int32_t ep_sf_packs(int32_t hidden, ep_sf_format fmt);   /* -1 if invalid */
+ep_status ep_quantize_fp8(const void *x, int32_t num_tokens, int32_t hidden,
+                          ep_sf_format fmt, void *out_q, void *out_sf,
+                          int64_t out_sf_token_stride, int64_t out_sf_hidden_stride,
+                          hipStream_t stream);
+
+/*
+ * Quantising dispatch: ep_quantize_fp8 of bf16 x fused with ep_dispatch of
+ * the codes and packs (same layout, weights and zero-padding rules), so x is
+ * read once in bf16 and every routed row is written once in FP8 [Ch7 §7.3,
+ * §7.4].  out_x is [capacity, hidden] codes; out_sf is [capacity,
+ * ep_sf_packs(hidden, fmt)] packs with the given strides.
+ */
+ep_status ep_dispatch_quant(const ep_handle *h, const void *x, int32_t hidden,
+                            ep_sf_format fmt, const float *topk_weights, void *out_x,
+                            void *out_sf, int64_t out_sf_token_stride,
+                            int64_t out_sf_hidden_stride, float *out_w,
+                            int32_t zero_padding, hipStream_t stream);
 
 /*
  * Combine [Ch8 §8.1: reduce along the handle back to the source, with

@@ -26,12 +26,12 @@ def built():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(ep_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(ep_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_every_declared_function_is_exported():
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 19, names
     for n in names:
         assert hasattr(ep.lib(), n), n
         assert n in ep._SIGNATURES, f"binding lacks {n}"
@@ -236,3 +236,30 @@ def test_rank_validation():
     assert ep.ep_combine_rank(h, A16, 12, None, None, A16, None) == ep.EP_ERR_MISALIGNED
     assert ep.ep_combine_rank(h, None, 64, None, None, A16, None) == ep.EP_ERR_NULL
     assert ep.ep_combine_rank(h, A16, 64, A16 + 8, None, A16, None) == ep.EP_ERR_MISALIGNED
+
+
+def test_quant_validation():
+    assert ep.ep_sf_packs(7168, ep.EP_SF_F32) == 56
+    assert ep.ep_sf_packs(7168, ep.EP_SF_UE8M0) == 14
+    assert ep.ep_sf_packs(640, ep.EP_SF_UE8M0) == 2
+    assert ep.ep_sf_packs(100, ep.EP_SF_F32) == -1
+    assert ep.ep_sf_packs(128, 7) == -1
+    q = ep.ep_quantize_fp8
+    assert q(A16, 4, 7168, 3, A16, A16, 0, 0, None) == ep.EP_ERR_DTYPE
+    assert q(A16, 4, 7100, 0, A16, A16, 0, 0, None) == ep.EP_ERR_MISALIGNED
+    assert q(A16, 4, 0, 0, A16, A16, 0, 0, None) == ep.EP_ERR_SHAPE
+    assert q(A16, -1, 128, 0, A16, A16, 0, 0, None) == ep.EP_ERR_SHAPE
+    assert q(None, 4, 128, 0, A16, A16, 0, 0, None) == ep.EP_ERR_NULL
+    assert q(A16, 4, 128, 0, A16, None, 0, 0, None) == ep.EP_ERR_NULL
+    assert q(A16 + 8, 4, 128, 0, A16, A16, 0, 0, None) == ep.EP_ERR_MISALIGNED
+    assert q(A16, 4, 128, 0, A16, A16 + 2, 0, 0, None) == ep.EP_ERR_MISALIGNED
+    assert q(A16, 4, 128, 0, A16, A16, -1, 0, None) == ep.EP_ERR_SHAPE
+    h = _fake_handle()
+    d = ep.ep_dispatch_quant
+    assert d(_fake_handle(laid_out=0), A16, 128, 0, None, A16, A16, 1, 0, None, 0,
+             None) == ep.EP_ERR_NOT_LAID_OUT
+    assert d(h, A16, 120, 0, None, A16, A16, 1, 0, None, 0, None) == ep.EP_ERR_MISALIGNED
+    assert d(h, A16, 128, 2, None, A16, A16, 1, 0, None, 0, None) == ep.EP_ERR_DTYPE
+    assert d(h, A16, 128, 0, None, None, A16, 1, 0, None, 0, None) == ep.EP_ERR_NULL
+    assert d(h, A16, 128, 0, A16 + 2, A16, A16, 1, 0, None, 0, None) == ep.EP_ERR_MISALIGNED
+
