@@ -51,6 +51,8 @@ def parse():
                    help="calls of each backward entry point after the timed steps (0 = skip)")
     p.add_argument("--rank-reps", type=int, default=30,
                    help="calls of the rank-layout and per-token-bias entry points (0 = skip)")
+    p.add_argument("--cpu-row-tokens", type=int, default=512,
+                   help="tokens of the CPU-oracle sample for the calls beyond the step")
     p.add_argument("--quant-reps", type=int, default=30,
                    help="calls timed for the FP8 quantiser phase (0 skips it)")
     p.add_argument("--flush", action="store_true",
@@ -161,27 +163,102 @@ def cpu_baseline(cfg, wl, y_host, min_seconds: float):
     return statistics.median(times), len(times), lay
 
 
-def time_calls(calls, nbytes, reps):
+def cpu_oracle_rows(cfg, wl, tokens: int):
+    """The CPU oracle (single thread, as it stands) on the first `tokens`
+    tokens of the workload for every call beyond layout + dispatch +
+    combine: GB/s of each call's algorithmic bytes at that sample size
+    (median over repetitions filling 0.25 s, at least one).  Expert rows are zeros; the rows the quantiser and the
+    backward read are N(0,1) bf16, so the quantiser's search does its real
+    work (timing only)."""
+    import numpy as np
+    import oracle
+    import ep_workloads as W
+    T, K, E, A, H = min(tokens, cfg.tokens), cfg.topk, cfg.experts, cfg.alignment, cfg.hidden
+    idx = np.ascontiguousarray(wl.topk_idx[:T])
+    w = np.ascontiguousarray(wl.topk_weights[:T])
+    cap = oracle.capacity_bound(T, K, E, A)
+    lay = oracle.layout(idx, E, A, cap)
+    V = int((lay.dst >= 0).sum())
+    row, _, nrecv = oracle.rank_layout(idx, E)
+    y = np.zeros((cap, H), np.uint16)
+    def bits(t):
+        return t.view(torch.int16).numpy().view(np.uint16)
+    import torch
+    g = bits(W.payload_bf16(T, H, cfg.seed + 1, 3, "cpu"))
+    b = np.zeros((T, H), np.uint16)
+    gwr = np.zeros(cap, np.float32)
+    xq = bits(W.payload_bf16(T, H, cfg.seed + 5, 3, "cpu"))
+    R, S = (H, 4 * (H // 128)) if cfg.fp8 else (2 * H, 0)
+    x_bytes = np.zeros((T, R), np.uint8)
+    sf = np.zeros((T, H // 128), np.float32) if cfg.fp8 else None
+    P = {"f32": H // 128, "ue8m0": (H // 128 + 3) // 4}
+    calls = {
+        "combine_backward": (lambda: oracle.combine_backward(g, lay, idx, w, y, None, capacity=cap),
+                             T * 2 * H + 2 * V * 2 * H + 12 * T * K),
+        "dispatch_backward": (lambda: oracle.dispatch_backward(y, idx, lay.dst, gwr),
+                              V * 2 * H + T * 2 * H + 16 * T * K),
+        "dispatch_rank": (lambda: oracle.dispatch_rank(x_bytes, idx, E, row, T, sf=sf, weights=w),
+                          T * (R + S) + nrecv * (R + S) + T * K * 12 + nrecv * K * 12 + 4 * T),
+        "combine_rank": (lambda: oracle.combine_rank(g, row, b, b), nrecv * 2 * H + 3 * T * 2 * H + 4 * T),
+        "combine_token_biases": (lambda: oracle.combine_token_bias(y, idx, lay.dst, w, None, b, b),
+                                 V * 2 * H + 3 * T * 2 * H + 8 * T * K),
+        "quantize_f32": (lambda: oracle.quantize_fp8(xq, oracle.SF_F32),
+                         T * 2 * H + T * H + 4 * T * P["f32"]),
+        "dispatch_quant_f32": (lambda: oracle.dispatch_quant(xq, lay, cap, oracle.SF_F32),
+                               T * 2 * H + V * (H + 4 * P["f32"]) + 4 * T * K),
+        "dispatch_quant_ue8m0": (lambda: oracle.dispatch_quant(xq, lay, cap, oracle.SF_UE8M0),
+                                 T * 2 * H + V * (H + 4 * P["ue8m0"]) + 4 * T * K),
+    }
+    out = {}
+    for name, (fn, nb) in calls.items():
+        times = []
+        t_end = time.perf_counter() + 0.25            # repeat short calls; median
+        while not times or time.perf_counter() < t_end:
+            t0 = time.perf_counter()
+            fn()
+            times.append(time.perf_counter() - t0)
+        dt = statistics.median(times)
+        out[name] = {"GBps": round(nb / dt / 1e9, 3), "seconds": round(dt, 4), "tokens": T,
+                     "repetitions": len(times), "cores": 1}
+    return out
+
+
+def time_calls(calls, nbytes, reps, flush=None):
     """Each call once untimed, then `reps` calls whose kernel intervals are
-    stamped by ep_time_next_call; mean µs, GB/s of the algorithmic bytes."""
+    stamped by ep_time_next_call; mean µs, GB/s of the algorithmic bytes.
+    With `flush` (a 1 GiB device tensor), `reps` more calls each run right
+    after a full read of it (outside the stamped interval), so inputs that
+    would fit the 256 MB MALL between repeated calls come from HBM: the
+    cold_* figures."""
     import torch
     import combine_ep_layout_08_amd as ep
-    out = {}
-    for name, fn in calls.items():
-        fn()
+
+    def run(fn, cold):
         pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                  for _ in range(reps)]
         for e0, e1 in pairs:
             e0.record()
             e1.record()
         for e0, e1 in pairs:
+            if cold:
+                flush.sum()
             ep.time_next_call(e0, e1)
             fn()
         torch.cuda.synchronize()
-        us = statistics.mean(e0.elapsed_time(e1) * 1e3 for e0, e1 in pairs)
+        return statistics.mean(e0.elapsed_time(e1) * 1e3 for e0, e1 in pairs)
+
+    out = {}
+    for name, fn in calls.items():
+        fn()
+        us = run(fn, False)
         gbps = nbytes[name] / (us * 1e-6) / 1e9
         out[name] = {"us_mean": round(us, 2), "bytes": nbytes[name], "GBps": round(gbps, 1),
                      "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+        if flush is not None:
+            cus = run(fn, True)
+            cg = nbytes[name] / (cus * 1e-6) / 1e9
+            out[name].update({"cold_us_mean": round(cus, 2), "cold_GBps": round(cg, 1),
+                              "cold_frac_hbm_peak": round(cg / HBM_PEAK_GBPS, 4)})
     return out
 
 
@@ -278,6 +355,7 @@ def main():
     # 1 GiB read that leaves L2 and the MALL full of unrelated clean lines, so
     # its inputs come from HBM; timed by the events on its own kernels.
     kernels_cold = None
+    big = None
     if args.cold_reps > 0:
         big = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
         calls = {"layout": lambda: h.layout(idx),
@@ -300,7 +378,6 @@ def main():
             gbps = nbytes[name] / (us * 1e-6) / 1e9
             kernels_cold[name] = {"us_mean": round(us, 2), "GBps": round(gbps, 1),
                                   "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
-        del big
 
     # Backward pair on the same layout (a separate phase after the timed
     # steps): combine backward with row and weight gradients, dispatch
@@ -317,7 +394,7 @@ def main():
                       g, topk_weights=w, y=wl.y, grad_y=grad_y, want_grad_weights=True),
                   "dispatch_backward": lambda: h.dispatch_backward(
                       wl.y, grad_out_w=gw_rows, want_grad_weights=True)}
-        backward = time_calls(bcalls, bb, args.backward_reps)
+        backward = time_calls(bcalls, bb, args.backward_reps, big)
 
     # Rank (non-expanded) layout and per-token biases, on the same layout.
     rank = None
@@ -342,7 +419,7 @@ def main():
                   "combine_rank": lambda: h.combine_rank(xr, bias_0=b0, bias_1=b1, out=out),
                   "combine_token_biases": lambda: h.combine(wl.y, topk_weights=w, bias=wl.bias,
                                                             out=out, bias_0=b0, bias_1=b1)}
-        rank = time_calls(rcalls, rb, args.rank_reps)
+        rank = time_calls(rcalls, rb, args.rank_reps, big)
         del rx, rsf, ri, rw, xr, b0, b1
 
     # FP8 quantiser on its own and fused with dispatch: bf16 rows of the
@@ -367,8 +444,9 @@ def main():
                                                                  out_sf=sfs["f32"]),
                   "dispatch_quant_ue8m0": lambda: h.dispatch_quant(xq, "ue8m0", out_x=qx,
                                                                    out_sf=sfs["ue8m0"])}
-        quant = time_calls(qcalls, qb, args.quant_reps)
+        quant = time_calls(qcalls, qb, args.quant_reps, big)
         del xq, qx, qt, sfs, sft
+    del big
 
     total_bytes = sum(nbytes.values())
     if args.flush:
@@ -387,6 +465,7 @@ def main():
     ceil = ceilings(torch)
 
     cpu = None
+    cpu_rows = None
     if not args.no_cpu_baseline:
         y_host = wl.y.view(torch.int16).cpu().numpy().view(np.uint16)
         wl_host = W.Workload(cfg, wl.topk_idx, wl.topk_weights, wl.x.cpu(),
@@ -398,6 +477,7 @@ def main():
                          f"combine, {reps} repetitions, median {med:.3f} s per step, "
                          "single-threaded C oracle",
                "ms_per_step": round(med * 1e3, 1)}
+        cpu_rows = cpu_oracle_rows(cfg, wl_host, args.cpu_row_tokens)
 
     line = {
         "metric": "dispatch+combine µs/call and HBM GB/s (% of peak) at 4096×7168 top-8",
@@ -433,6 +513,7 @@ def main():
         "roofline": roofline,
         "ceilings": ceil,
         "cpu_baseline": cpu,
+        "cpu_oracle_other_calls": cpu_rows,
     }
     print(json.dumps(line), flush=True)
 
