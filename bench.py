@@ -167,9 +167,9 @@ def cpu_oracle_rows(cfg, wl, tokens: int):
     """The CPU oracle (single thread, as it stands) on the first `tokens`
     tokens of the workload for every call beyond layout + dispatch +
     combine: GB/s of each call's algorithmic bytes at that sample size
-    (median over repetitions filling 0.25 s, at least one).  Expert rows are zeros; the rows the quantiser and the
-    backward read are N(0,1) bf16, so the quantiser's search does its real
-    work (timing only)."""
+    (median over repetitions filling 0.25 s, at least one).  Expert rows are
+    zeros; the rows the quantiser and the backward read are N(0,1) bf16, so
+    the quantiser's search does its real work (timing only)."""
     import numpy as np
     import oracle
     import ep_workloads as W
