@@ -217,6 +217,24 @@ ep_status ep_handle_import(ep_handle *h, const void *topk_idx, ep_dtype idx_dtyp
             return EP_ERR_SHAPE;
     for (int64_t i = 0; i < slots; ++i)
         if (dst_slot[i] < -1 || dst_slot[i] >= expanded) return EP_ERR_SHAPE;
+    // src_meta must be the inverse of dst_slot: every row of an expert's run
+    // names a slot that points back at it and every gap row is -1 (the
+    // dispatch and combine walk dst_slot, the bias gradient walks src_meta).
+    int64_t routed = 0;
+    for (int64_t i = 0; i < slots; ++i) routed += dst_slot[i] >= 0;
+    int64_t runs = 0;
+    for (int32_t e = 0; e < E; ++e) {
+        for (int64_t r = psum[e]; r < psum[e + 1]; ++r) {
+            const int32_t i = src_meta[r];
+            if (r < static_cast<int64_t>(psum[e]) + counts[e]) {
+                if (i < 0 || i >= slots || dst_slot[i] != r) return EP_ERR_SHAPE;
+                ++runs;
+            } else if (i != -1) {
+                return EP_ERR_SHAPE;
+            }
+        }
+    }
+    if (runs != routed) return EP_ERR_SHAPE;
     int32_t sc[3] = {num_recv_tokens, 0, 0};
     const int32_t exp32 = static_cast<int32_t>(expanded);
     hipError_t e = hipStreamSynchronize(stream);

@@ -9,11 +9,11 @@
 // alignment gaps), s7.4 (contiguous aligned expert ranges for grouped GEMM).
 //
 // On one GPU the whole epilogue is HBM traffic: read every token row once and
-// write it to each of its slots' rows.  Token blocks: one wave per token; the
-// wave loads the row into registers as 16-byte vectors (64 lanes x VPL vectors
-// per chunk) and stores the chunk once for every valid slot, so x is read
-// from HBM exactly once.  The K destination rows are wave-uniform (readlane
-// into scalar registers).  Gap blocks, when zero padding is on: one block per
+// write it to each of its slots' rows.  Token blocks: one wave per (token,
+// pass); the wave loads its pass of the row into registers as 16-byte
+// vectors (64 lanes x VPL vectors) and stores it once for every valid slot,
+// so x is read from HBM exactly once.  The K destination rows are
+// wave-uniform (readlane into scalar registers).  Gap blocks, when zero padding is on: one block per
 // (expert, 4-row chunk of the gap), one wave per gap row.
 #include "ep_internal.h"
 #include "../../include/ep.h"
@@ -25,11 +25,14 @@ constexpr int kDispatchThreads = 256;
 constexpr int kWavesPerBlock = kDispatchThreads / 64;
 constexpr int kGapRowsPerBlock = kWavesPerBlock;
 
-// Launch shape: waves that share one token's row (each copies a contiguous
-// part of it), and whether row stores are non-temporal (streamed past the
-// caches).
-#ifndef EP_DISPATCH_WAVES_PER_TOKEN
-#define EP_DISPATCH_WAVES_PER_TOKEN 1
+// Launch shape: each wave copies one pass of a token's row, 64 * VPL
+// 16-byte vectors, to every slot; EP_DISPATCH_MAX_VPL caps VPL (a smaller
+// cap spreads a token over more waves: 1 measured equal on the FP8 prefill
+// dispatch and 9 % faster on 32768 bf16 rows of 7168 than one pass per
+// token).  EP_DISPATCH_NT_STORE streams the row stores past the caches
+// (measured 2-6 % slower).
+#ifndef EP_DISPATCH_MAX_VPL
+#define EP_DISPATCH_MAX_VPL 1
 #endif
 #ifndef EP_DISPATCH_NT_STORE
 #define EP_DISPATCH_NT_STORE 0
@@ -40,9 +43,6 @@ constexpr int kGapRowsPerBlock = kWavesPerBlock;
 #define EP_DISPATCH_BLOCKS_PER_CU 0
 #endif
 constexpr int kDispatchBlocksPerCu = EP_DISPATCH_BLOCKS_PER_CU;
-constexpr int kWavesPerToken = EP_DISPATCH_WAVES_PER_TOKEN;
-constexpr int kTokensPerBlock = kWavesPerBlock / kWavesPerToken;
-static_assert(kWavesPerBlock % kWavesPerToken == 0, "waves per token must divide 4");
 
 __device__ inline void store_row_vec(u32x4 *p, u32x4 v) {
     if (EP_DISPATCH_NT_STORE)
@@ -51,9 +51,10 @@ __device__ inline void store_row_vec(u32x4 *p, u32x4 v) {
         *p = v;
 }
 
-// Copy one token's part of the row (one wave) to every valid slot's row.
+// Copy one pass of a token's row (one wave: vectors [64*VPL*pass, +64*VPL))
+// to every valid slot's row; pass 0 also copies the scale packs and weight.
 template <int VPL>
-__device__ inline void dispatch_token(const DispatchArgs &a, int64_t t, int part, int lane) {
+__device__ inline void dispatch_token(const DispatchArgs &a, int64_t t, int64_t pass, int lane) {
     const int64_t V = a.row_vecs;
     u32x4 *out = static_cast<u32x4 *>(a.out_x);
     const int K = a.num_topk;
@@ -61,7 +62,7 @@ __device__ inline void dispatch_token(const DispatchArgs &a, int64_t t, int part
     // store out of the output buffers.
     int32_t my_dst = lane < K ? a.dst[t * K + lane] : -1;
     if (my_dst >= a.capacity) my_dst = -1;
-    if (part == 0) {
+    if (pass == 0) {
         if (a.out_w && my_dst >= 0) a.out_w[my_dst] = a.w ? a.w[t * K + lane] : 1.0f;
         if (a.num_sf) {
             // A token's scale packs (at most 64 * kMaxSfPerLane) go to
@@ -83,26 +84,22 @@ __device__ inline void dispatch_token(const DispatchArgs &a, int64_t t, int part
             }
         }
     }
-    const int64_t per_part = (V + kWavesPerToken - 1) / kWavesPerToken;
-    const int64_t p0 = part * per_part;
-    const int64_t p1 = p0 + per_part < V ? p0 + per_part : V;
     const u32x4 *src = static_cast<const u32x4 *>(a.x) + t * V;
-    for (int64_t c0 = p0; c0 < p1; c0 += 64 * VPL) {
-        u32x4 v[VPL];
+    const int64_t c0 = pass * 64 * VPL;
+    u32x4 v[VPL];
+#pragma unroll
+    for (int q = 0; q < VPL; ++q) {
+        const int64_t c = c0 + q * 64 + lane;
+        if (c < V) v[q] = src[c];
+    }
+    for (int k = 0; k < K; ++k) {
+        const int32_t r = __builtin_amdgcn_readlane(my_dst, k);
+        if (r < 0) continue;
+        u32x4 *d = out + static_cast<int64_t>(r) * V;
 #pragma unroll
         for (int q = 0; q < VPL; ++q) {
             const int64_t c = c0 + q * 64 + lane;
-            if (c < p1) v[q] = src[c];
-        }
-        for (int k = 0; k < K; ++k) {
-            const int32_t r = __builtin_amdgcn_readlane(my_dst, k);
-            if (r < 0) continue;
-            u32x4 *d = out + static_cast<int64_t>(r) * V;
-#pragma unroll
-            for (int q = 0; q < VPL; ++q) {
-                const int64_t c = c0 + q * 64 + lane;
-                if (c < p1) store_row_vec(d + c, v[q]);
-            }
+            if (c < V) store_row_vec(d + c, v[q]);
         }
     }
 }
@@ -300,9 +297,9 @@ __device__ inline void dispatch_gap_row(const DispatchArgs &a, int e, int64_t r,
 }
 
 // Grid over work units (one block per unit unless a persistent grid is
-// configured): units [0, token_units) copy kTokensPerBlock tokens each
-// (MODE 0) or quantise one (token, pass) per wave (MODE 1, 2; `passes` per
-// token), the rest zero kGapRowsPerBlock gap rows each.
+// configured): units [0, token_units) give each wave one (token, pass) to
+// copy (MODE 0) or quantise (MODE 1, 2), `passes` per token; the rest zero
+// kGapRowsPerBlock gap rows each.
 template <int VPL, int MODE>
 __global__ __launch_bounds__(kDispatchThreads) void dispatch_kernel(DispatchArgs a,
                                                                    int64_t token_units,
@@ -312,14 +309,11 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_kernel(DispatchArgs
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     for (int64_t u = blockIdx.x; u < total_units; u += gridDim.x) {
         if (u < token_units) {
-            if (MODE == 0) {
-                const int64_t t = u * kTokensPerBlock + wave / kWavesPerToken;
-                if (t < a.num_tokens) dispatch_token<VPL>(a, t, wave % kWavesPerToken, lane);
-            } else {
-                const int64_t wv = u * kWavesPerBlock + wave;
-                const int64_t t = wv / passes;
-                if (t < a.num_tokens) quant_token<VPL, MODE>(a, t, wv % passes, lane);
-            }
+            const int64_t wv = u * kWavesPerBlock + wave;
+            const int64_t t = wv / passes;
+            if (t >= a.num_tokens) continue;
+            if (MODE == 0) dispatch_token<VPL>(a, t, wv % passes, lane);
+            else quant_token<VPL, MODE>(a, t, wv % passes, lane);
         } else {
             const int64_t g = u - token_units;
             const int e = static_cast<int>(g / gap_chunks);
@@ -333,10 +327,8 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_kernel(DispatchArgs
 
 template <int VPL, int MODE>
 hipError_t launch_vpl(const DispatchArgs &a, hipStream_t stream, CallEvents ev) {
-    const int64_t passes = MODE == 0 ? 1 : (a.row_vecs + 64 * VPL - 1) / (64 * VPL);
-    const int64_t token_units =
-        MODE == 0 ? (a.num_tokens + kTokensPerBlock - 1) / kTokensPerBlock
-                  : (a.num_tokens * passes + kWavesPerBlock - 1) / kWavesPerBlock;
+    const int64_t passes = (a.row_vecs + 64 * VPL - 1) / (64 * VPL);
+    const int64_t token_units = (a.num_tokens * passes + kWavesPerBlock - 1) / kWavesPerBlock;
     int gap_chunks = 0;
     if (a.zero_padding && a.alignment > 1)
         gap_chunks = (a.alignment - 1 + kGapRowsPerBlock - 1) / kGapRowsPerBlock;
@@ -370,12 +362,11 @@ hipError_t launch_quant(const DispatchArgs &a, hipStream_t stream, CallEvents ev
 hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t stream, CallEvents ev) {
     if (a.quant == kQuantF32) return launch_quant<kQuantF32>(a, stream, ev);
     if (a.quant == kQuantUe8m0) return launch_quant<kQuantUe8m0>(a, stream, ev);
-    const int64_t per_wave = (a.row_vecs + kWavesPerToken - 1) / kWavesPerToken;
-    const int64_t per_lane = (per_wave + 63) / 64;
-    if (per_lane <= 1) return launch_vpl<1, 0>(a, stream, ev);
-    if (per_lane <= 2) return launch_vpl<2, 0>(a, stream, ev);
-    if (per_lane <= 4) return launch_vpl<4, 0>(a, stream, ev);
-    if (per_lane <= 8) return launch_vpl<8, 0>(a, stream, ev);
+    const int64_t per_lane = (a.row_vecs + 63) / 64;
+    if (per_lane <= 1 || EP_DISPATCH_MAX_VPL == 1) return launch_vpl<1, 0>(a, stream, ev);
+    if (per_lane <= 2 || EP_DISPATCH_MAX_VPL == 2) return launch_vpl<2, 0>(a, stream, ev);
+    if (per_lane <= 4 || EP_DISPATCH_MAX_VPL == 4) return launch_vpl<4, 0>(a, stream, ev);
+    if (per_lane <= 8 || EP_DISPATCH_MAX_VPL == 8) return launch_vpl<8, 0>(a, stream, ev);
     return launch_vpl<16, 0>(a, stream, ev);
 }
 

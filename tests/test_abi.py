@@ -197,6 +197,28 @@ def test_import_validation_rejects_rows_out_of_range():
                                None) == ep.EP_ERR_SHAPE
 
 
+def test_import_requires_src_meta_to_invert_dst():
+    """Rejected on the host before any device call: a run row naming a slot
+    that points elsewhere, a gap row that is not -1, two slots on one row."""
+    import numpy as np
+    h = _fake_handle()
+    counts = np.array([1, 0, 0, 0], np.int32)
+    dst = np.full(16, -1, np.int32)
+    dst[0] = 0
+
+    def imp(psum, src, d=dst):
+        return ep.ep_handle_import(h, A16, ep.EP_I64, 8, counts.ctypes.data, psum.ctypes.data,
+                                   d.ctypes.data, src.ctypes.data, 1, None)
+
+    one = np.array([0, 1, 1, 1, 1], np.int32)
+    assert imp(one, np.array([3], np.int32)) == ep.EP_ERR_SHAPE       # dst[3] is -1
+    two = np.array([0, 2, 2, 2, 2], np.int32)
+    assert imp(two, np.array([0, 5], np.int32)) == ep.EP_ERR_SHAPE    # gap row holds a slot
+    d2 = dst.copy()
+    d2[1] = 0
+    assert imp(one, np.array([0], np.int32), d2) == ep.EP_ERR_SHAPE   # two slots on row 0
+
+
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(ep, "LIB_PATH", str(tmp_path / "missing.so"))
     monkeypatch.setattr(ep, "_lib", None)
