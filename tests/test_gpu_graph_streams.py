@@ -5,7 +5,9 @@ PR digest on graph-safe joins) require that the path can run inside a graph
 and on any stream.  Here layout + dispatch + combine are captured once in a
 HIP graph and replayed with new routing and payloads copied into the captured
 inputs, with eager work between replays; every replay is checked against the
-oracle.  A second test runs two handles on two streams at once."""
+oracle.  The same is done for the quantising dispatch, the combine backward
+and the rank-layout calls.  A last test runs two handles on two streams at
+once."""
 import numpy as np
 import pytest
 import torch
@@ -105,3 +107,79 @@ def test_two_handles_on_two_streams():
         torch.cuda.synchronize()
         for j in jobs:
             _check(*j)
+
+
+def test_graph_capture_of_the_other_calls():
+    """The quantising dispatch, the backward pair and the rank-layout calls
+    captured after a layout in one graph, replayed with new routing and rows
+    (eager work between replays); every replay checked against the oracle."""
+    rng = np.random.default_rng(3)
+    T2, K2, E2, A2, H2 = 600, 4, 32, 8, 512
+    h = ep.Handle(T2, K2, E2, A2)
+    cap = h.capacity
+    idx_s = torch.zeros((T2, K2), dtype=torch.int64, device="cuda")
+    w_s = torch.zeros((T2, K2), dtype=torch.float32, device="cuda")
+    x_s = torch.zeros((T2, H2), dtype=torch.bfloat16, device="cuda")
+    y_s = torch.zeros((cap, H2), dtype=torch.bfloat16, device="cuda")
+    g_s = torch.zeros((T2, H2), dtype=torch.bfloat16, device="cuda")
+    qx = torch.zeros((cap, H2), dtype=torch.uint8, device="cuda")
+    qsf = torch.zeros((cap, H2 // 128), dtype=torch.float32, device="cuda")
+    gy = torch.zeros((cap, H2), dtype=torch.bfloat16, device="cuda")
+    rx = torch.zeros((T2, H2), dtype=torch.bfloat16, device="cuda")
+    ri = torch.zeros((T2, K2), dtype=torch.int64, device="cuda")
+    rw = torch.zeros((T2, K2), dtype=torch.float32, device="cuda")
+    rout = torch.zeros((T2, H2), dtype=torch.bfloat16, device="cuda")
+
+    def calls():
+        h.layout(idx_s)
+        h.dispatch_quant(x_s, "f32", out_x=qx, out_sf=qsf)
+        h.combine_backward(g_s, topk_weights=w_s, y=y_s, grad_y=gy)
+        h.dispatch_rank(x_s, topk_weights=w_s, out_x=rx, out_topk_idx=ri, out_topk_weights=rw)
+        h.combine_rank(rx, bias_0=g_s, out=rout)
+
+    def route():
+        idx = np.stack([rng.permutation(E2)[:K2] for _ in range(T2)]).astype(np.int64)
+        return np.where(rng.random((T2, K2)) < 0.2, -1, idx)
+
+    idx_s.copy_(torch.from_numpy(route()))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    say("graph capture other calls")
+    with torch.cuda.graph(g):
+        calls()
+    other = ep.Handle(T2, K2, E2, A2)
+    for rep in range(3):
+        idx = route()
+        w = rng.random((T2, K2), dtype=np.float32)
+        gen = torch.Generator().manual_seed(rep)
+        x = torch.randn((T2, H2), generator=gen).to(torch.bfloat16)
+        y = torch.randn((cap, H2), generator=gen).to(torch.bfloat16)
+        gr = torch.randn((T2, H2), generator=gen).to(torch.bfloat16)
+        for dst_t, src_t in ((idx_s, torch.from_numpy(idx)), (w_s, torch.from_numpy(w)),
+                             (x_s, x), (y_s, y), (g_s, gr)):
+            dst_t.copy_(src_t)
+        say("graph replay other calls", rep)
+        g.replay()
+        other.layout(torch.from_numpy(route()).cuda())          # eager work between
+        torch.cuda.synchronize()
+        lay = oracle.layout(idx, E2, A2, cap)
+        n = lay.num_expanded
+        routed = np.nonzero(lay.src_meta[:n] >= 0)[0]
+        oq, osf, _ = oracle.dispatch_quant(u16(x), lay, cap, oracle.SF_F32)
+        np.testing.assert_array_equal(qx.cpu().numpy()[routed], oq[routed])
+        np.testing.assert_array_equal(qsf.cpu().numpy().view(np.uint32)[routed], osf[routed])
+        ogy = np.zeros((cap, H2), np.uint16)
+        ogy, _, _ = oracle.combine_backward(u16(gr), lay, idx, w, u16(y), None, capacity=cap,
+                                            want_grad_w=False, grad_y=ogy)
+        np.testing.assert_array_equal(u16(gy)[routed], ogy[routed])
+        row, _, nr = oracle.rank_layout(idx, E2)
+        ox, _, oi, ow = oracle.dispatch_rank(u16(x).view(np.uint8), idx, E2, row, T2, weights=w)
+        np.testing.assert_array_equal(u16(rx)[:nr], ox[:nr].view(np.uint16))
+        np.testing.assert_array_equal(ri.cpu().numpy()[:nr], oi[:nr])
+        np.testing.assert_array_equal(rw.cpu().numpy()[:nr], ow[:nr])
+        np.testing.assert_array_equal(u16(rout), oracle.combine_rank(u16(rx), row, u16(gr)))
