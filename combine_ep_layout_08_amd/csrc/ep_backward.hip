@@ -78,8 +78,10 @@ __device__ inline u32x4 scale_bf16x8(const u32x4 v, float s) {
 }
 
 // Row pass block size: ceil(row vectors / EP_BACKWARD_VECS_PER_THREAD)
-// threads rounded up to whole waves, at most 1024 (512 with expert biases,
-// whose second set of row loads needs the larger register budget).
+// threads rounded up to whole waves, raised for small batches until the
+// grid holds about kBackwardTargetThreads threads (one 256-thread block per
+// compute unit), at most the row's vectors, 1024, or 512 with expert biases
+// (whose second set of row loads needs the larger register budget).
 #ifndef EP_BACKWARD_VECS_PER_THREAD
 #define EP_BACKWARD_VECS_PER_THREAD 16
 #endif
@@ -87,6 +89,7 @@ __device__ inline u32x4 scale_bf16x8(const u32x4 v, float s) {
 #define EP_BACKWARD_NT_STORE 1
 #endif
 constexpr int kMaxRowThreads = 1024;
+constexpr int64_t kBackwardTargetThreads = 256 * 256;
 constexpr int row_threads_cap(bool has_bias) { return has_bias ? 512 : kMaxRowThreads; }
 
 // Row pass: one block per token, threads tiling the row's 16-byte columns.
@@ -255,7 +258,10 @@ template <bool WANT_Y, bool WANT_W, bool HAS_W>
 hipError_t launch_rows3(const BackwardArgs &a, hipStream_t s, hipEvent_t st, hipEvent_t sp) {
     const bool has_bias = WANT_W && a.bias;
     const int64_t per = EP_BACKWARD_VECS_PER_THREAD;
-    int64_t threads = ((a.row_vecs + per - 1) / per + 63) / 64 * 64;
+    int64_t threads = (a.row_vecs + per - 1) / per;
+    const int64_t spread = (kBackwardTargetThreads + a.num_tokens - 1) / a.num_tokens;
+    if (threads < spread) threads = spread < a.row_vecs ? spread : a.row_vecs;
+    threads = (threads + 63) / 64 * 64;
     if (threads > row_threads_cap(has_bias)) threads = row_threads_cap(has_bias);
     const dim3 grid(static_cast<unsigned>(a.num_tokens)), block(static_cast<unsigned>(threads));
     if (has_bias) {
