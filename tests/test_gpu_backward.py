@@ -15,6 +15,7 @@ import ep_workloads as W
 import oracle
 from tests import bruteforce as BF
 from tests.gpu_util import POISON, gpu_layout, needs_gpu, poison_, say, u16
+from tests.tolerance import check_sum
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
 
@@ -35,10 +36,7 @@ def _magnitudes(g, idx, dst, w, y, b):
     return mw
 
 
-def _check_sum(got, ref, mag, n):
-    bound = 2.0 ** -24 * np.abs(ref) + n * 2.0 ** -52 * mag + 1e-300
-    assert np.all(np.abs(got.astype(np.float64) - ref) <= bound), \
-        float(np.max(np.abs(got.astype(np.float64) - ref) - bound))
+_check_sum = check_sum
 
 
 def _run(idx, E, A, cap, g, y, w=None, b=None, want_bias=True, want_y=True, want_w=True):
