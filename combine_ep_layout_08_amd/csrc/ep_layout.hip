@@ -20,7 +20,7 @@
 //     A decoupled lookback over earlier tiles - one 64-bit status word per
 //     (tile, bucket) holding epoch, aggregate/prefix flag and count, read and
 //     written with agent-scope atomics so every XCD sees them - gives each
-//     bucket's exclusive offset; each thread reads a window of 8 predecessors
+//     bucket's exclusive offset; each thread reads a window of 16 predecessors
 //     per round trip.  Each valid slot gets its position inside its expert's
 //     run, and each received token its rank-layout row (a block scan of the
 //     tile's token flags after the earlier tiles' received count).  The tile
@@ -41,7 +41,7 @@ namespace {
 constexpr uint64_t kFlagAggregate = 1;
 constexpr uint64_t kFlagPrefix = 2;
 constexpr uint32_t kMaxSpins = 1u << 21;
-constexpr int kLookbackWindow = 8;
+constexpr int kLookbackWindow = 16;
 constexpr int kBucketsPerThread = (kMaxBuckets + kLayoutThreads - 1) / kLayoutThreads;
 
 __device__ inline uint64_t pack_status(uint32_t epoch, uint64_t flag, uint32_t value) {
@@ -168,6 +168,10 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_scan_kernel(LayoutArgs 
     }
     const int nbits = 32 - __builtin_clz(static_cast<unsigned>(E));   // bits of 0..E
     const uint64_t below = (1ull << lane) - 1ull;
+    // token of a slot inside the tile: s / K as a multiply-high by
+    // ceil(2^32 / K), exact for s < 2^32 / K (here s < kTileSlots)
+    const uint32_t k_magic = 0xFFFFFFFFu / static_cast<uint32_t>(K) + 1u;
+    const uint32_t wave_slot0 = static_cast<uint32_t>(wave_base - tile_base);
     int bucket[kLayoutRounds];
     int rank[kLayoutRounds];
 #pragma unroll
@@ -186,10 +190,9 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_scan_kernel(LayoutArgs 
             const int old = s_hist[wave][b];
             if (before == 0) s_hist[wave][b] = old + __popcll(match);
             r = old + before;
-            if (b < E) {
-                const int64_t i = wave_base + j * 64 + lane;
-                s_tok[(i - tile_base) / K] = 1;        // this token has a valid slot
-            }
+            if (b < E)                                 // this token has a valid slot
+                s_tok[K == 1 ? wave_slot0 + j * 64 + lane
+                             : __umulhi(wave_slot0 + j * 64 + lane, k_magic)] = 1;
         }
         bucket[j] = b;
         rank[j] = r;
