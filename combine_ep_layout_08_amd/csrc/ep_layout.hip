@@ -7,7 +7,12 @@
 // alignment; s7.5 handle fields).  Inside an expert's segment rows follow the
 // ascending slot index t*K+k (a stable counting sort).
 //
-// Two kernels:
+// Two forms, both two kernels over tiles of whole tokens.  Up to
+// kCountPlaceMaxTiles tiles (524288 slots): layout_count + layout_place
+// (below), which exchange the tiles' counts through the kernel boundary and
+// never wait on another block; measured 1-2 us faster than the lookback form
+// at every size from 64 x 4 to 32768 x 8 slots.  Beyond that, where every
+// place block would read too many tiles' counts, the single-pass lookback:
 //  1. layout_scan: one 256-thread block per tile of whole tokens (at most
 //     kTileSlots slots).  The block first loads all of its ids (every load in
 //     flight at once), then each wave takes 64 slots per round: lanes holding
@@ -125,40 +130,22 @@ __device__ bool lookback(const uint64_t *status, int NB, int tile, int b, uint32
     return true;
 }
 
+// Work of one tile shared by both layout forms.  Loads every id of the tile
+// (all loads in flight), ranks each slot inside its wave by match-any (lanes
+// with the same bucket find each other with one ballot per bucket-id bit; a
+// lane's rank is the popcount of matching lower lanes; the group leader bumps
+// the wave's LDS counter), flags received tokens in s_tok and counts them
+// into bucket E+1, then turns the per-wave counts in s_hist into in-tile
+// offsets.  Returns each slot's bucket (-1 empty, E invalid) and rank inside
+// its wave, and in agg[q] the tile's count of bucket tid + q * kLayoutThreads.
 template <typename IdxT>
-__global__ __launch_bounds__(kLayoutThreads) void layout_scan_kernel(LayoutArgs a,
-                                                                    int tokens_per_tile,
-                                                                    int num_tiles) {
-    __shared__ int32_t s_hist[kLayoutWaves][kMaxBuckets];
-    __shared__ int32_t s_excl[kMaxBuckets];
-    __shared__ int32_t s_total[kMaxBuckets];
-    __shared__ uint8_t s_tok[kTileSlots];
-    __shared__ int64_t s_wave[kLayoutWaves];
-    __shared__ int32_t s_tile;
-    __shared__ uint32_t s_epoch;
-
+__device__ void rank_tile(const LayoutArgs &a, int64_t tile_base, int64_t tile_end,
+                          int tokens_per_tile, int32_t (*s_hist)[kMaxBuckets], uint8_t *s_tok,
+                          int bucket[kLayoutRounds], int rank[kLayoutRounds],
+                          int32_t agg[kBucketsPerThread]) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int E = a.num_experts, NB = E + 2, K = a.num_topk;
-    const int B_INVALID = E, B_RECV = E + 1;
-    if (tid == 0) {
-        s_tile = __hip_atomic_fetch_add(&a.scalars[EP_SCALAR_TICKET], 1, __ATOMIC_RELAXED,
-                                        __HIP_MEMORY_SCOPE_AGENT);
-        s_epoch = static_cast<uint32_t>(a.scalars[EP_SCALAR_EPOCH]);
-    }
-    for (int w = 0; w < kLayoutWaves; ++w)
-        for (int b = tid; b < NB; b += kLayoutThreads) s_hist[w][b] = 0;
-    for (int i = tid; i < kTileSlots; i += kLayoutThreads) s_tok[i] = 0;
-    __syncthreads();
-    const int tile = s_tile;
-    const uint32_t epoch = s_epoch;
-
-    const int64_t num_slots = static_cast<int64_t>(a.num_tokens) * K;
-    const int64_t tile_base = static_cast<int64_t>(tile) * tokens_per_tile * K;
-    const int64_t tile_end_full = tile_base + static_cast<int64_t>(tokens_per_tile) * K;
-    const int64_t tile_end = tile_end_full < num_slots ? tile_end_full : num_slots;
     const int64_t wave_base = tile_base + static_cast<int64_t>(wave) * (kLayoutRounds * 64);
-
-    // 1. Load every id of the tile first (all loads in flight), then match.
     const IdxT *idx = static_cast<const IdxT *>(a.topk_idx);
     int64_t ids[kLayoutRounds];
 #pragma unroll
@@ -166,18 +153,20 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_scan_kernel(LayoutArgs 
         const int64_t i = wave_base + j * 64 + lane;
         ids[j] = i < tile_end ? static_cast<int64_t>(idx[i]) : -1;
     }
+    for (int w = 0; w < kLayoutWaves; ++w)
+        for (int b = tid; b < NB; b += kLayoutThreads) s_hist[w][b] = 0;
+    for (int i = tid; i < kTileSlots; i += kLayoutThreads) s_tok[i] = 0;
+    __syncthreads();
     const int nbits = 32 - __builtin_clz(static_cast<unsigned>(E));   // bits of 0..E
     const uint64_t below = (1ull << lane) - 1ull;
     // token of a slot inside the tile: s / K as a multiply-high by
     // ceil(2^32 / K), exact for s < 2^32 / K (here s < kTileSlots)
     const uint32_t k_magic = 0xFFFFFFFFu / static_cast<uint32_t>(K) + 1u;
     const uint32_t wave_slot0 = static_cast<uint32_t>(wave_base - tile_base);
-    int bucket[kLayoutRounds];
-    int rank[kLayoutRounds];
 #pragma unroll
     for (int j = 0; j < kLayoutRounds; ++j) {
         const int64_t e = ids[j];
-        const int b = (e >= 0 && e < E) ? static_cast<int>(e) : (e == -1 ? -1 : B_INVALID);
+        const int b = (e >= 0 && e < E) ? static_cast<int>(e) : (e == -1 ? -1 : E);
         uint64_t match = __ballot(b >= 0);
         for (int bit = 0; bit < nbits; ++bit) {
             const bool one = (b >> bit) & 1;
@@ -205,12 +194,11 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_scan_kernel(LayoutArgs 
         for (int i = tid; i < tokens_per_tile; i += kLayoutThreads) c += s_tok[i];
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off, 64);
-        if (lane == 0) s_hist[wave][B_RECV] = c;
+        if (lane == 0) s_hist[wave][E + 1] = c;
     }
     __syncthreads();
 
-    // 2. Per-wave counts -> in-tile offsets; tile aggregate per bucket.
-    int32_t agg[kBucketsPerThread];
+    // Per-wave counts -> in-tile offsets; tile aggregate per bucket.
 #pragma unroll
     for (int q = 0; q < kBucketsPerThread; ++q) {
         const int b = tid + q * kLayoutThreads;
@@ -226,6 +214,43 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_scan_kernel(LayoutArgs 
             agg[q] = run;
         }
     }
+}
+
+template <typename IdxT>
+__global__ __launch_bounds__(kLayoutThreads) void layout_scan_kernel(LayoutArgs a,
+                                                                    int tokens_per_tile,
+                                                                    int num_tiles) {
+    __shared__ int32_t s_hist[kLayoutWaves][kMaxBuckets];
+    __shared__ int32_t s_excl[kMaxBuckets];
+    __shared__ int32_t s_total[kMaxBuckets];
+    __shared__ uint8_t s_tok[kTileSlots];
+    __shared__ int64_t s_wave[kLayoutWaves];
+    __shared__ int32_t s_tile;
+    __shared__ uint32_t s_epoch;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int E = a.num_experts, NB = E + 2, K = a.num_topk;
+    const int B_INVALID = E, B_RECV = E + 1;
+    if (tid == 0) {
+        s_tile = __hip_atomic_fetch_add(&a.scalars[EP_SCALAR_TICKET], 1, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
+        s_epoch = static_cast<uint32_t>(a.scalars[EP_SCALAR_EPOCH]);
+    }
+    __syncthreads();
+    const int tile = s_tile;
+    const uint32_t epoch = s_epoch;
+
+    const int64_t num_slots = static_cast<int64_t>(a.num_tokens) * K;
+    const int64_t tile_base = static_cast<int64_t>(tile) * tokens_per_tile * K;
+    const int64_t tile_end_full = tile_base + static_cast<int64_t>(tokens_per_tile) * K;
+    const int64_t tile_end = tile_end_full < num_slots ? tile_end_full : num_slots;
+    const int64_t wave_base = tile_base + static_cast<int64_t>(wave) * (kLayoutRounds * 64);
+
+    // 1-2. Rank the tile's slots; in-tile offsets and the tile's counts.
+    int bucket[kLayoutRounds];
+    int rank[kLayoutRounds];
+    int32_t agg[kBucketsPerThread];
+    rank_tile<IdxT>(a, tile_base, tile_end, tokens_per_tile, s_hist, s_tok, bucket, rank, agg);
 
     // 3. Decoupled lookback across tiles.
     uint64_t *my_status = a.tile_status + static_cast<int64_t>(tile) * NB;
@@ -360,6 +385,217 @@ __global__ __launch_bounds__(256) void layout_finalize_kernel(LayoutArgs a, int 
         a.src_meta[r] = -1;
 }
 
+// ---------------------------------------------------------------- count + place
+// Batches of at most kCountPlaceMaxTiles tiles.  layout_count: one block per
+// tile ranks its slots (rank_tile), publishes the tile's counts as status
+// words tagged with this call's epoch, and parks each slot's bucket and
+// in-tile position in dst.  layout_place (after the kernel boundary, so every
+// count is visible): one block per tile sums the counts of the tiles before it
+// and of all tiles, scans the aligned totals into psum (every block the same
+// way), writes its slots' final rows and source metadata and its tokens' rank
+// rows; one more block per expert (same totals and scan) marks that expert's
+// alignment gap; tile 0 writes counts, psum and the scalars and finally moves
+// the epoch on, so no later call can mistake these status words for its own.
+// Nothing waits on another block.
+#ifndef EP_LAYOUT_COUNT_PLACE_MAX_TILES
+#define EP_LAYOUT_COUNT_PLACE_MAX_TILES 256
+#endif
+constexpr int kCountPlaceMaxTiles = EP_LAYOUT_COUNT_PLACE_MAX_TILES;
+
+__device__ inline uint32_t park(int b, int pos) {
+    return static_cast<uint32_t>(b + 1) | (static_cast<uint32_t>(pos) << 11);
+}
+
+template <typename IdxT>
+__global__ __launch_bounds__(kLayoutThreads) void layout_count_kernel(LayoutArgs a,
+                                                                     int tokens_per_tile) {
+    __shared__ int32_t s_hist[kLayoutWaves][kMaxBuckets];
+    __shared__ uint8_t s_tok[kTileSlots];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int E = a.num_experts, NB = E + 2, K = a.num_topk;
+    const int tile = blockIdx.x;
+    const uint32_t epoch = static_cast<uint32_t>(a.scalars[EP_SCALAR_EPOCH]);
+    const int64_t num_slots = static_cast<int64_t>(a.num_tokens) * K;
+    const int64_t tile_base = static_cast<int64_t>(tile) * tokens_per_tile * K;
+    const int64_t tile_end_full = tile_base + static_cast<int64_t>(tokens_per_tile) * K;
+    const int64_t tile_end = tile_end_full < num_slots ? tile_end_full : num_slots;
+    const int64_t wave_base = tile_base + static_cast<int64_t>(wave) * (kLayoutRounds * 64);
+    int bucket[kLayoutRounds];
+    int rank[kLayoutRounds];
+    int32_t agg[kBucketsPerThread];
+    rank_tile<IdxT>(a, tile_base, tile_end, tokens_per_tile, s_hist, s_tok, bucket, rank, agg);
+    uint64_t *my_status = a.tile_status + static_cast<int64_t>(tile) * NB;
+#pragma unroll
+    for (int q = 0; q < kBucketsPerThread; ++q) {
+        const int b = tid + q * kLayoutThreads;
+        if (b < NB)
+            store_status(&my_status[b],
+                         pack_status(epoch, kFlagAggregate, static_cast<uint32_t>(agg[q])));
+    }
+#pragma unroll
+    for (int j = 0; j < kLayoutRounds; ++j) {
+        const int64_t i = wave_base + j * 64 + lane;
+        if (i < tile_end) {
+            const int b = bucket[j];
+            a.dst[i] = static_cast<int32_t>(b < 0 ? 0u : park(b, s_hist[wave][b] + rank[j]));
+        }
+    }
+}
+
+template <typename IdxT>
+__global__ __launch_bounds__(kLayoutThreads) void layout_place_kernel(LayoutArgs a,
+                                                                     int tokens_per_tile,
+                                                                     int num_tiles) {
+    __shared__ int32_t s_excl[kMaxBuckets];
+    __shared__ int32_t s_total[kMaxBuckets];
+    __shared__ int32_t s_psum[kMaxExperts + 1];
+    __shared__ uint8_t s_tok[kTileSlots];
+    __shared__ int64_t s_wave[kLayoutWaves];
+    __shared__ int32_t s_fatal;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int E = a.num_experts, NB = E + 2, K = a.num_topk;
+    const bool gap_block = static_cast<int>(blockIdx.x) >= num_tiles;
+    const int tile = gap_block ? -1 : static_cast<int>(blockIdx.x);
+    const int64_t num_slots = static_cast<int64_t>(a.num_tokens) * K;
+    const int64_t tile_base = static_cast<int64_t>(gap_block ? 0 : tile) * tokens_per_tile * K;
+    const int64_t tile_end_full = tile_base + static_cast<int64_t>(tokens_per_tile) * K;
+    const int64_t tile_end = gap_block ? 0 : (tile_end_full < num_slots ? tile_end_full : num_slots);
+    const int64_t wave_base = tile_base + static_cast<int64_t>(wave) * (kLayoutRounds * 64);
+
+    // The tile's parked slots (independent of the counts: loads issued first).
+    uint32_t parked[kLayoutRounds];
+#pragma unroll
+    for (int j = 0; j < kLayoutRounds; ++j) {
+        const int64_t i = wave_base + j * 64 + lane;
+        parked[j] = i < tile_end ? static_cast<uint32_t>(a.dst[i]) : 0u;
+    }
+    for (int i = tid; i < tokens_per_tile; i += kLayoutThreads) s_tok[i] = 0;
+
+    // 1. Every tile's counts: this tile's exclusive offsets and the totals.
+    for (int b = tid; b < NB; b += kLayoutThreads) {
+        uint32_t ex = 0, tot = 0;
+        for (int t0 = 0; t0 < num_tiles; t0 += kLookbackWindow) {
+            uint32_t c[kLookbackWindow];
+#pragma unroll
+            for (int w = 0; w < kLookbackWindow; ++w)
+                c[w] = t0 + w < num_tiles
+                           ? static_cast<uint32_t>(load_status(
+                                 &a.tile_status[static_cast<int64_t>(t0 + w) * NB + b]))
+                           : 0u;
+#pragma unroll
+            for (int w = 0; w < kLookbackWindow; ++w) {
+                if (t0 + w < tile) ex += c[w];
+                tot += c[w];
+            }
+        }
+        s_excl[b] = static_cast<int32_t>(ex);
+        s_total[b] = static_cast<int32_t>(tot);
+    }
+    __syncthreads();
+
+    // 2. Aligned exclusive scan over experts (identical in every block).
+    const int per = (E + kLayoutThreads - 1) / kLayoutThreads;
+    const int b0 = tid * per;
+    const int b1 = min(b0 + per, E);
+    int64_t local = 0;
+    for (int b = b0; b < b1; ++b) local += align_up(s_total[b], a.alignment);
+    int64_t total = 0;
+    int64_t run = block_exclusive_scan(local, s_wave, &total);
+    for (int b = b0; b < b1; ++b) {
+        s_psum[b] = static_cast<int32_t>(min(run, static_cast<int64_t>(INT32_MAX)));
+        run += align_up(s_total[b], a.alignment);
+    }
+    if (tid == 0) {
+        s_psum[E] = static_cast<int32_t>(min(total, static_cast<int64_t>(INT32_MAX)));
+        // Every block reaches the same verdict: the capacity test uses the
+        // same totals, and the sticky timeout bit is the same before and
+        // after tile 0 rewrites the word.
+        uint32_t err = static_cast<uint32_t>(a.scalars[EP_SCALAR_ERROR_BITS]) &
+                       EP_ERRBIT_SCAN_TIMEOUT;
+        if (total > a.capacity) err |= EP_ERRBIT_CAPACITY;
+        if (s_total[E] > 0) err |= EP_ERRBIT_INVALID_ID;
+        s_fatal = (err & EP_ERRBIT_FATAL) != 0;
+        if (tile == 0) {
+            a.scalars[EP_SCALAR_NUM_EXPANDED] = s_psum[E];
+            a.scalars[EP_SCALAR_INVALID_COUNT] = s_total[E];
+            a.scalars[EP_SCALAR_NUM_RECV_TOKENS] = s_total[E + 1];
+            a.scalars[EP_SCALAR_ERROR_BITS] = static_cast<int32_t>(err);
+        }
+    }
+    __syncthreads();
+    const bool fatal = s_fatal != 0;
+    if (gap_block) {
+        // Gap markers of expert blockIdx.x - num_tiles.
+        const int e = static_cast<int>(blockIdx.x) - num_tiles;
+        if (fatal) return;
+        const int64_t end = s_psum[e + 1] < a.capacity ? s_psum[e + 1] : a.capacity;
+        for (int64_t r = static_cast<int64_t>(s_psum[e]) + s_total[e] + tid; r < end;
+             r += kLayoutThreads)
+            a.src_meta[r] = -1;
+        return;
+    }
+    if (tile == 0) {
+        for (int b = tid; b < E; b += kLayoutThreads) {
+            a.counts[b] = s_total[b];
+            if (a.cumulative_stats) a.cumulative_stats[b] += s_total[b];
+        }
+        for (int b = tid; b <= E; b += kLayoutThreads) a.psum[b] = s_psum[b];
+    }
+
+    // 3. Final rows and source metadata; flags of received tokens.
+    const uint32_t k_magic = 0xFFFFFFFFu / static_cast<uint32_t>(K) + 1u;
+    const uint32_t wave_slot0 = static_cast<uint32_t>(wave_base - tile_base);
+#pragma unroll
+    for (int j = 0; j < kLayoutRounds; ++j) {
+        const int64_t i = wave_base + j * 64 + lane;
+        if (i >= tile_end) continue;
+        const int b = static_cast<int>(parked[j] & 0x7FFu) - 1;
+        if (b >= 0 && b < E) {
+            const uint32_t s = wave_slot0 + j * 64 + lane;
+            s_tok[K == 1 ? s : __umulhi(s, k_magic)] = 1;
+        }
+        if (fatal) continue;
+        int32_t r = -1;
+        if (b >= 0 && b < E) {
+            r = s_psum[b] + s_excl[b] + static_cast<int32_t>(parked[j] >> 11);
+            a.src_meta[r] = static_cast<int32_t>(i);
+        }
+        a.dst[i] = r;
+    }
+    __syncthreads();
+
+    // 4. Rank layout: the tile's received tokens after those of earlier tiles.
+    {
+        const int tper = (tokens_per_tile + kLayoutThreads - 1) / kLayoutThreads;
+        const int j0 = tid * tper;
+        const int j1 = min(j0 + tper, tokens_per_tile);
+        int64_t cnt = 0;
+        for (int j = j0; j < j1; ++j) cnt += s_tok[j];
+        int64_t unused = 0;
+        int64_t row = s_excl[E + 1] + block_exclusive_scan(cnt, s_wave, &unused);
+        const int64_t tok0 = static_cast<int64_t>(tile) * tokens_per_tile;
+        for (int j = j0; j < j1; ++j) {
+            const int64_t t = tok0 + j;
+            if (t >= a.num_tokens) break;
+            if (s_tok[j]) {
+                a.recv_row[t] = static_cast<int32_t>(row);
+                a.recv_src[row] = static_cast<int32_t>(t);
+                ++row;
+            } else {
+                a.recv_row[t] = -1;
+            }
+        }
+    }
+
+    // 5. Tile 0 retires this call's status words.
+    if (tile == 0 && tid == 0) {
+        a.scalars[EP_SCALAR_TICKET] = 0;
+        uint32_t next = static_cast<uint32_t>(a.scalars[EP_SCALAR_EPOCH]) + 1u;
+        if (next >= (1u << 30)) next = 1u;
+        a.scalars[EP_SCALAR_EPOCH] = static_cast<int32_t>(next);
+    }
+}
+
 __global__ void handle_clear_kernel(int32_t *scalars, uint64_t *status, int64_t n) {
     const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
@@ -382,6 +618,23 @@ hipError_t launch_handle_clear(int32_t *scalars, uint64_t *tile_status, int64_t 
 hipError_t launch_layout(const LayoutArgs &a, hipStream_t stream, CallEvents ev) {
     const int tpt = layout_tokens_per_tile(a.num_topk);
     const int tiles = static_cast<int>(layout_tiles(a.num_tokens, a.num_topk));
+    if (tiles <= kCountPlaceMaxTiles) {
+        hipError_t e;
+        if (a.idx_is_i64) {
+            e = launch_kernel(layout_count_kernel<int64_t>, dim3(tiles), dim3(kLayoutThreads),
+                              stream, ev.start, nullptr, a, tpt);
+            if (e == hipSuccess)
+                e = launch_kernel(layout_place_kernel<int64_t>, dim3(tiles + a.num_experts),
+                                  dim3(kLayoutThreads), stream, nullptr, ev.stop, a, tpt, tiles);
+        } else {
+            e = launch_kernel(layout_count_kernel<int32_t>, dim3(tiles), dim3(kLayoutThreads),
+                              stream, ev.start, nullptr, a, tpt);
+            if (e == hipSuccess)
+                e = launch_kernel(layout_place_kernel<int32_t>, dim3(tiles + a.num_experts),
+                                  dim3(kLayoutThreads), stream, nullptr, ev.stop, a, tpt, tiles);
+        }
+        return e;
+    }
     const int64_t slots = static_cast<int64_t>(a.num_tokens) * a.num_topk;
     const int slot_blocks = static_cast<int>((slots + 255) / 256);
     const dim3 fin_blocks(static_cast<unsigned>(slot_blocks + a.num_experts));
