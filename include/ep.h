@@ -12,12 +12,17 @@
  *              the exclusive prefix sums of the counts aligned up to
  *              expert_alignment, the expanded row of every slot and the
  *              source slot of every expanded row.
- *   dispatch - copy every token row (bf16, or FP8 bytes plus fp32 scale
- *              factors) into the expanded row of each of its slots; each
+ *   dispatch - copy every token row (bf16, or FP8 bytes plus 4-byte scale
+ *              packs) into the expanded row of each of its slots; each
  *              expert owns one contiguous range whose start is a multiple
  *              of expert_alignment; alignment gaps can be zero-filled.
  *   combine  - for every token, sum its expert rows in slot order k = 0..K-1
- *              in fp32 as w[t,k] * (y[row] + bias[e]) and round to bf16.
+ *              in fp32 as w[t,k] * (y[row] + bias[e]), add the per-token
+ *              biases, and round to bf16.
+ * and around them: the non-expanded ("rank") layout (each received token
+ * once) with its dispatch and combine, the backward of combine and of
+ * dispatch, and an FP8 quantiser (alone or fused into dispatch) with fp32 or
+ * packed UE8M0 scales.
  *
  * Memory ownership: the library never allocates, frees or keeps memory.  All
  * device buffers (workspace, inputs, outputs) belong to the caller and must
@@ -28,8 +33,9 @@
  * only enqueues work on the given stream (0 = the null stream) and returns.
  * Ordering against other streams is the caller's job (events), which covers
  * the previous-event / compute-stream controls of [Ch8 §8.2].  Because only
- * those two calls synchronise, layout, dispatch and combine can be captured
- * in a HIP graph.
+ * those two calls synchronise, every other call can be captured in a HIP
+ * graph (none records a memset; device state such as the layout's call tag
+ * lives in the handle's workspace).
  *
  * Errors: a call returns a status.  Problems visible on the host (null
  * pointers, sizes, dtypes, alignment, workspace size) are reported before
@@ -60,7 +66,7 @@ typedef enum ep_status {
     EP_ERR_DTYPE = 3,         /* element type not accepted by this call        */
     EP_ERR_UNSUPPORTED = 4,   /* valid for the method, beyond this library's   */
                               /* limits (K > 64, E > 1024, capacity >= 2^31, */
-                              /* FP8 hidden > 32768)                           */
+                              /* more than 256 scale packs per token)          */
     EP_ERR_MISALIGNED = 5,    /* pointer or row size not 16-byte aligned       */
     EP_ERR_WORKSPACE = 6,     /* workspace NULL or smaller than required       */
     EP_ERR_NOT_LAID_OUT = 7,  /* dispatch / combine before a layout            */
@@ -124,7 +130,7 @@ typedef struct ep_handle {
     int32_t *src_meta;          /* device [capacity] slot t*K+k of a row, -1 on */
                                 /* gap rows, unspecified at or past psum[E]     */
     int32_t *scalars;           /* device [EP_NUM_SCALARS]                      */
-    uint64_t *tile_status;      /* device scratch of the layout scan            */
+    uint64_t *tile_status;      /* device scratch: per-tile counts of a layout  */
     const void *topk_idx;       /* BORROWED device [T, K] ids of the last layout*/
     int32_t topk_idx_dtype;     /* EP_I32 or EP_I64                             */
     int32_t status_tiles;       /* tiles the scratch is sized for               */
@@ -201,6 +207,11 @@ ep_status ep_handle_read_counts(const ep_handle *h, int32_t *counts,
  * dst_slot [num_tokens*K], src_meta [psum[E]]) and the device topk_idx it
  * belongs to.  Synchronous (host buffers may be reused on return).  Meant
  * for interop and for checking dispatch/combine against a reference layout.
+ * Validated on the host before anything is copied: psum[0] = 0, each
+ * expert's run fits its segment, every dst_slot lies in [-1, psum[E]), and
+ * src_meta is the inverse of dst_slot (every run row names a slot that
+ * points back at it, every gap row is -1) - else EP_ERR_SHAPE; psum[E] >
+ * capacity gives EP_ERR_CAPACITY.  The rank rows are derived on the host.
  */
 ep_status ep_handle_import(ep_handle *h, const void *topk_idx, ep_dtype idx_dtype,
                            int32_t num_tokens, const int32_t *counts,
