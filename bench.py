@@ -204,6 +204,8 @@ def cpu_oracle_rows(cfg, wl, tokens: int):
                                  V * 2 * H + 3 * T * 2 * H + 8 * T * K),
         "quantize_f32": (lambda: oracle.quantize_fp8(xq, oracle.SF_F32),
                          T * 2 * H + T * H + 4 * T * P["f32"]),
+        "quantize_ue8m0": (lambda: oracle.quantize_fp8(xq, oracle.SF_UE8M0),
+                           T * 2 * H + T * H + 4 * T * P["ue8m0"]),
         "dispatch_quant_f32": (lambda: oracle.dispatch_quant(xq, lay, cap, oracle.SF_F32),
                                T * 2 * H + V * (H + 4 * P["f32"]) + 4 * T * K),
         "dispatch_quant_ue8m0": (lambda: oracle.dispatch_quant(xq, lay, cap, oracle.SF_UE8M0),
@@ -445,13 +447,17 @@ def main():
         sfs = {f: torch.empty((cap, ep.ep_sf_packs(H, c)),
                               dtype=torch.float32 if f == "f32" else torch.int32, device="cuda")
                for f, c in (("f32", ep.EP_SF_F32), ("ue8m0", ep.EP_SF_UE8M0))}
-        sft = torch.empty((T, H // 128), dtype=torch.float32, device="cuda")
         P = {f: ep.ep_sf_packs(H, c) for f, c in (("f32", ep.EP_SF_F32),
                                                     ("ue8m0", ep.EP_SF_UE8M0))}
+        sft = {f: torch.empty((T, P[f]), dtype=torch.float32 if f == "f32" else torch.int32,
+                              device="cuda") for f in P}
         qb = {"quantize_f32": T * 2 * H + T * H + 4 * T * P["f32"],
+              "quantize_ue8m0": T * 2 * H + T * H + 4 * T * P["ue8m0"],
               "dispatch_quant_f32": T * 2 * H + V * (H + 4 * P["f32"]) + 4 * T * K,
               "dispatch_quant_ue8m0": T * 2 * H + V * (H + 4 * P["ue8m0"]) + 4 * T * K}
-        qcalls = {"quantize_f32": lambda: ep.quantize_fp8(xq, "f32", out_q=qt, out_sf=sft),
+        qcalls = {"quantize_f32": lambda: ep.quantize_fp8(xq, "f32", out_q=qt, out_sf=sft["f32"]),
+                  "quantize_ue8m0": lambda: ep.quantize_fp8(xq, "ue8m0", out_q=qt,
+                                                            out_sf=sft["ue8m0"]),
                   "dispatch_quant_f32": lambda: h.dispatch_quant(xq, "f32", out_x=qx,
                                                                  out_sf=sfs["f32"]),
                   "dispatch_quant_ue8m0": lambda: h.dispatch_quant(xq, "ue8m0", out_x=qx,

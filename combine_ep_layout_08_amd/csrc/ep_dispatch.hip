@@ -160,16 +160,93 @@ __device__ inline void unpack_bf16x8(const u32x4 v, float f[8]) {
     f[7] = __uint_as_float(v.w & 0xFFFF0000u);
 }
 
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+
+// Largest |x| bf16 bit pattern over the block (the lane's 16 values, two per
+// word with packed 16-bit maxima, then the block's 8 lanes).  Non-negative
+// bf16 values order like their bits; a NaN pattern orders above infinity, so
+// a result of 0x7F80 or more means the block holds an infinity or a NaN.
+__device__ inline uint32_t block_max_bits(const u32x4 lo, const u32x4 hi) {
+    const uint32_t words[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    u16x2 m = u16x2{0, 0};
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, words[i] & 0x7FFF7FFFu));
+    uint32_t r = m.x > m.y ? m.x : m.y;
+#pragma unroll
+    for (int off = 1; off < 8; off <<= 1) {
+        const uint32_t o = static_cast<uint32_t>(__shfl_xor(static_cast<int>(r), off, 8));
+        r = o > r ? o : r;
+    }
+    return r;
+}
+
+// Codes of 16 quotients already known to lie in [-448, 448] up to one ulp.
+__device__ inline u32x4 e4m3_pack16(const float v[16]) {
+    uint32_t w[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        if (EP_QUANT_HW_CVT) {
+            float c[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                c[i] = __builtin_fminf(__builtin_fmaxf(v[4 * g + i], -448.0f), 448.0f);
+            int word = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+            word = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], word, true);
+            w[g] = static_cast<uint32_t>(word);
+        } else {
+            w[g] = e4m3_code(v[4 * g]) | (e4m3_code(v[4 * g + 1]) << 8) |
+                   (e4m3_code(v[4 * g + 2]) << 16) | (e4m3_code(v[4 * g + 3]) << 24);
+        }
+    }
+    return u32x4{w[0], w[1], w[2], w[3]};
+}
+
 // Quantise one 16-channel vector pair (lane-owned) of a valid block: returns
 // the 16 codes and, in *pack, the block's fp32 scale bits or exponent byte.
+//
+// Blocks of finite values (the common case) take a short path: fp32 scales
+// divide through one correctly rounded reciprocal y = 1/s per block, q0 =
+// x*y, then one remainder correction q = q0 + (x - q0*s)*y with fused
+// multiply-adds (Markstein's division scheme).  For every bf16 x with
+// |x| <= amax and every block maximum amax, this q is the correctly rounded
+// x/s bit for bit wherever |x/s| >= 2^-11; below that both round to the zero
+// code, and the sign is taken from x (so -0 keeps its sign).  A host-side
+// test enumerates that whole domain.  Blocks holding an infinity or a NaN
+// take the general path: NaN skipped in amax, true divisions, NaN codes.
 template <int MODE>
 __device__ inline u32x4 quantise16(const u32x4 lo, const u32x4 hi, uint32_t *pack) {
 #pragma clang fp contract(off)
     float f[16];
     unpack_bf16x8(lo, f);
     unpack_bf16x8(hi, f + 8);
-    // amax on the bit patterns of |x| (non-negative floats order like their
-    // bits); NaN patterns are skipped, infinity is kept.
+    float v[16];
+    const uint32_t mb = block_max_bits(lo, hi);
+    if (mb < 0x7F80u) {
+        const float amax = __uint_as_float(mb << 16);
+        const float s = __fdiv_rn(amax > 1e-12f ? amax : 1e-12f, 448.0f);
+        if (MODE == kQuantUe8m0) {
+            // s <= 3.4e38 / 448, so the rounded-up power of two 2^k has
+            // k <= 126 and x / 2^k equals x * 2^-k exactly.
+            uint32_t e = (__float_as_uint(s) >> 23) & 0xFFu;
+            if (__float_as_uint(s) & 0x7FFFFFu) ++e;
+            *pack = e;
+            const float y = __uint_as_float((254u - e) << 23);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v[i] = f[i] * y;
+        } else {
+            *pack = __float_as_uint(s);
+            const float y = __fdiv_rn(1.0f, s);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float q0 = f[i] * y;
+                const float r = __builtin_fmaf(-q0, s, f[i]);
+                v[i] = __builtin_copysignf(__builtin_fmaf(r, y, q0), f[i]);
+            }
+        }
+        return e4m3_pack16(v);
+    }
+    // amax on the bit patterns of |x|, NaN patterns skipped, infinity kept.
     uint32_t m = 0;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -192,7 +269,6 @@ __device__ inline u32x4 quantise16(const u32x4 lo, const u32x4 hi, uint32_t *pac
     } else {
         *pack = __float_as_uint(s);
     }
-    float v[16];
     if (MODE == kQuantUe8m0 && __float_as_uint(divisor) < (254u << 23)) {
         // x / 2^k equals x * 2^-k exactly: both are the exact quotient rounded
         // once, and 2^-k (k <= 126 here, a normal number) is representable.
@@ -204,28 +280,14 @@ __device__ inline u32x4 quantise16(const u32x4 lo, const u32x4 hi, uint32_t *pac
 #pragma unroll
         for (int i = 0; i < 16; ++i) v[i] = __fdiv_rn(f[i], divisor);
     }
-    uint32_t w[4];
-    if (EP_QUANT_HW_CVT) {
+    u32x4 codes = e4m3_pack16(v);
+    uint32_t w[4] = {codes.x, codes.y, codes.z, codes.w};
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            float c[4];
+    for (int g = 0; g < 4; ++g)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                c[i] = __builtin_fminf(__builtin_fmaxf(v[4 * g + i], -448.0f), 448.0f);
-            int word = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
-            word = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], word, true);
-            w[g] = static_cast<uint32_t>(word);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (v[4 * g + i] != v[4 * g + i])
-                    w[g] = (w[g] & ~(0xFFu << (8 * i))) | (0x7Fu << (8 * i));
-        }
-    } else {
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-            w[g] = e4m3_code(v[4 * g]) | (e4m3_code(v[4 * g + 1]) << 8) |
-                   (e4m3_code(v[4 * g + 2]) << 16) | (e4m3_code(v[4 * g + 3]) << 24);
-    }
+        for (int i = 0; i < 4; ++i)
+            if (v[4 * g + i] != v[4 * g + i])
+                w[g] = (w[g] & ~(0xFFu << (8 * i))) | (0x7Fu << (8 * i));
     return u32x4{w[0], w[1], w[2], w[3]};
 }
 

@@ -67,6 +67,29 @@ def test_quantize_every_bf16_value_at_unit_scale(name, fmt):
 
 
 @pytest.mark.parametrize("name,fmt", FORMATS)
+def test_quantize_every_block_maximum(name, fmt):
+    """One block for every finite bf16 magnitude as its maximum (0 through
+    0x7F7F, so every scale the quantiser can derive from finite input,
+    including the 1e-12 floor), the other 127 entries random bf16 values of
+    either sign no larger in magnitude: every divisor meets many quotients."""
+    rng = np.random.default_rng(11 + fmt)
+    amax = np.arange(0x7F80, dtype=np.uint32)
+    rest = (rng.random((amax.size, 127)) * (amax[:, None] + 1)).astype(np.uint32)
+    blocks = np.concatenate([amax[:, None], rest], axis=1)
+    perm = rng.permuted(np.tile(np.arange(128), (amax.size, 1)), axis=1)
+    blocks = np.take_along_axis(blocks, perm, axis=1)
+    blocks |= rng.integers(0, 2, size=blocks.shape, dtype=np.uint32) << 15
+    xb = blocks.astype(np.uint16).reshape(-1, 1024)
+    say("quantize every block maximum", name)
+    q, sf = ep.quantize_fp8(torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).cuda(),
+                            name)
+    torch.cuda.synchronize()
+    oq, osf = oracle.quantize_fp8(xb, fmt)
+    np.testing.assert_array_equal(u8(q), oq)
+    np.testing.assert_array_equal(_sf_np(sf), osf)
+
+
+@pytest.mark.parametrize("name,fmt", FORMATS)
 @pytest.mark.parametrize("T,H", [(1, 128), (37, 640), (300, 1664), (64, 7168), (9, 8320),
                                  (0, 256)])
 def test_quantize_matches_oracle(name, fmt, T, H):
