@@ -36,7 +36,7 @@ ep_status limits(int32_t max_tokens, int32_t K, int32_t E, int64_t capacity) {
 Carve carve(int32_t max_tokens, int32_t K, int32_t E, int64_t capacity) {
     Carve c{};
     const int64_t slots = static_cast<int64_t>(max_tokens) * K;
-    c.tiles = ep::layout_tiles(max_tokens, K);
+    c.tiles = ep::layout_status_tiles(max_tokens, K);
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t at = off;
@@ -66,9 +66,13 @@ ep::CallEvents take_events() {
     return ev;
 }
 
+// A handle from ep_handle_init (or a plain copy of one): workspace carved and
+// sizes within the limits it was carved for.
 bool handle_ready(const ep_handle *h) {
     return h && h->counts && h->psum && h->dst_slot && h->src_meta && h->scalars &&
-           h->tile_status && h->recv_row && h->recv_src;
+           h->tile_status && h->recv_row && h->recv_src && h->max_tokens >= 0 &&
+           h->num_topk >= 1 && h->num_topk <= ep::kMaxTopk && h->num_experts >= 1 &&
+           h->num_experts <= ep::kMaxExperts && h->expert_alignment >= 1 && h->capacity >= 0;
 }
 
 }  // namespace
@@ -139,6 +143,8 @@ ep_status ep_layout(ep_handle *h, const void *topk_idx, ep_dtype idx_dtype, int3
     if (!handle_ready(h)) return EP_ERR_WORKSPACE;
     if (idx_dtype != EP_I64 && idx_dtype != EP_I32) return EP_ERR_DTYPE;
     if (num_tokens < 0 || num_tokens > h->max_tokens) return EP_ERR_SHAPE;
+    if (ep::layout_status_tiles(num_tokens, h->num_topk) > h->status_tiles)
+        return EP_ERR_WORKSPACE;
     if (num_tokens > 0 && !topk_idx) return EP_ERR_NULL;
     if (!aligned(topk_idx, idx_dtype == EP_I64 ? 8 : 4)) return EP_ERR_MISALIGNED;
     if (!aligned(cumulative_stats, 4)) return EP_ERR_MISALIGNED;

@@ -12,32 +12,46 @@ namespace ep {
 // load/store builtins, which lower to global_load/store_dwordx4 ... nt).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// Layout scan: a tile is at most kTileSlots slots (kLayoutThreads threads x
-// kLayoutRounds rounds of 64 consecutive slots per wave) and always holds
-// whole tokens.
-#ifndef EP_LAYOUT_ROUNDS
-#define EP_LAYOUT_ROUNDS 8
-#endif
+// Layout tiles: kLayoutThreads threads x R rounds of 64 consecutive slots per
+// wave, always whole tokens.  Batches that fit in kSmallTilesMax tiles of
+// kRoundsSmall rounds use those short tiles (more blocks share the ranking);
+// larger batches use kRoundsLarge rounds (fewer tiles' counts to sum).
 constexpr int kLayoutThreads = 256;
 constexpr int kLayoutWaves = kLayoutThreads / 64;
-constexpr int kLayoutRounds = EP_LAYOUT_ROUNDS;
-constexpr int kTileSlots = kLayoutThreads * kLayoutRounds;
+constexpr int kRoundsSmall = 4;
+constexpr int kRoundsLarge = 8;
+constexpr int kSmallTilesMax = 64;
+constexpr int kTileSlots = kLayoutThreads * kRoundsLarge;   // the longest tile
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopk = 64;
-static_assert(kTileSlots >= kMaxTopk, "a tile must hold at least one token");
+static_assert(kLayoutThreads * kRoundsSmall >= kMaxTopk, "a tile must hold at least one token");
 // Buckets of the scan: experts, then ids outside [-1, E), then received tokens.
 constexpr int kMaxBuckets = kMaxExperts + 2;
 constexpr int kMaxSfPerLane = 4;                             // FP8 hidden <= 32768
 
-inline int layout_tokens_per_tile(int num_topk) {
-    const int t = kTileSlots / num_topk;
+inline int layout_tokens_per_tile(int num_topk, int rounds) {
+    const int t = kLayoutThreads * rounds / num_topk;
     return t < 1 ? 1 : t;
 }
 
-inline int64_t layout_tiles(int64_t num_tokens, int num_topk) {
-    const int64_t tpt = layout_tokens_per_tile(num_topk);
+inline int64_t layout_tiles(int64_t num_tokens, int num_topk, int rounds) {
+    const int64_t tpt = layout_tokens_per_tile(num_topk, rounds);
     const int64_t t = (num_tokens + tpt - 1) / tpt;
     return t < 1 ? 1 : t;
+}
+
+// Rounds per tile for a batch of num_tokens.
+inline int layout_rounds(int64_t num_tokens, int num_topk) {
+    return layout_tiles(num_tokens, num_topk, kRoundsSmall) <= kSmallTilesMax ? kRoundsSmall
+                                                                               : kRoundsLarge;
+}
+
+// Tiles whose status words a handle for up to max_tokens tokens must hold.
+inline int64_t layout_status_tiles(int64_t max_tokens, int num_topk) {
+    const int64_t small = layout_tiles(max_tokens, num_topk, kRoundsSmall);
+    const int64_t large = layout_tiles(max_tokens, num_topk, kRoundsLarge);
+    const int64_t s = small < kSmallTilesMax ? small : kSmallTilesMax;
+    return s > large ? s : large;
 }
 
 // Launch with optional events attached to the kernel dispatch itself

@@ -60,8 +60,9 @@ def test_workspace_bytes():
     assert 0 < small < big
     assert big % 256 == 0
     # counts + psum + dst + src_meta + scalars + one 64-bit status word per
-    # (tile of 2048 slots, expert + 2 buckets) + rank rows and sources
-    need = 4 * 256 + 4 * 257 + 4 * 4096 * 8 + 4 * 65280 + 32 + 8 * 16 * 258 + 2 * 4 * 4096
+    # (tile, expert + 2 buckets) for the most tiles 4096 tokens of top-8 can
+    # use (32 short tiles of 1024 slots) + rank rows and sources
+    need = 4 * 256 + 4 * 257 + 4 * 4096 * 8 + 4 * 65280 + 32 + 8 * 32 * 258 + 2 * 4 * 4096
     assert need <= big <= need + 8 * 256
     assert ep.ep_workspace_bytes(64, 65, 16, 1, 256) == 0       # K > 64
     assert ep.ep_workspace_bytes(64, 4, 1025, 1, 256) == 0      # E > 1024
@@ -117,6 +118,12 @@ def test_layout_validation():
     assert ep.ep_layout(h, A16 + 4, ep.EP_I64, 8, None, None) == ep.EP_ERR_MISALIGNED
     empty = ep.ep_handle()
     assert ep.ep_layout(empty, A16, ep.EP_I64, 0, None, None) == ep.EP_ERR_WORKSPACE
+    bad = _fake_handle()
+    bad.num_topk = 0                              # not a handle from ep_handle_init
+    assert ep.ep_layout(bad, A16, ep.EP_I64, 8, None, None) == ep.EP_ERR_WORKSPACE
+    small = _fake_handle()
+    small.max_tokens, small.status_tiles = 1024, 1    # scratch for fewer tiles than asked
+    assert ep.ep_layout(small, A16, ep.EP_I64, 1024, None, None) == ep.EP_ERR_WORKSPACE
 
 
 def test_dispatch_validation():

@@ -51,11 +51,14 @@ def test_layout_tile_boundaries(slots, K, E):
     _check(idx, E, 4, T * K + 4 * E)
 
 
-@pytest.mark.parametrize("T,K,E", [(65536, 8, 256), (65537, 8, 256), (8229, 64, 1024)])
+@pytest.mark.parametrize("T,K,E", [(8192, 8, 256), (8193, 8, 256), (10880, 6, 64),
+                                   (10881, 6, 64), (65536, 8, 256), (65537, 8, 256),
+                                   (8229, 64, 1024)])
 def test_layout_count_place_and_lookback_forms_meet(T, K, E):
-    """Up to 256 tiles of 2048 slots the layout exchanges tile counts through
-    a kernel boundary; beyond that it takes the single-pass lookback.  Both
-    sides of the switch, bit-exact, with empty and invalid ids."""
+    """Up to 64 short tiles (1024 slots) the layout ranks short tiles, up to
+    256 tiles of 2048 slots long ones, both exchanging tile counts through a
+    kernel boundary; beyond that it takes the single-pass lookback.  Both
+    sides of each switch, bit-exact, with empty and invalid ids."""
     rng = np.random.default_rng(T + K)
     idx = rng.integers(-1, E, size=(T, K))
     idx[::101, 0] = E + 3                               # invalid ids
