@@ -281,16 +281,17 @@ ep_status ep_handle_import(ep_handle *h, const void *topk_idx, ep_dtype idx_dtyp
 }
 
 // Scale-pack arguments shared by the two dispatches: returns EP_OK and the
-// pack count (0 for bf16) or the status to report.
+// pack count (0 for bf16) or the status to report.  `reads`: the call reads
+// token rows; `writes`: it may write output rows.
 static ep_status check_sf(bool fp8, int32_t hidden, const void *sf, const void *out_sf,
-                          int32_t num_sf_packs, bool rows, int64_t sf_ts, int64_t sf_hs,
-                          int64_t out_ts, int64_t out_hs, int32_t *packs) {
+                          int32_t num_sf_packs, bool reads, bool writes, int64_t sf_ts,
+                          int64_t sf_hs, int64_t out_ts, int64_t out_hs, int32_t *packs) {
     *packs = 0;
     if (!fp8) return (sf || out_sf || num_sf_packs != 0) ? EP_ERR_DTYPE : EP_OK;
     if (num_sf_packs < 0) return EP_ERR_SHAPE;
     const int32_t n = num_sf_packs == 0 ? hidden / 128 : num_sf_packs;
     if (n > 64 * ep::kMaxSfPerLane) return EP_ERR_UNSUPPORTED;
-    if (!out_sf || (rows && !sf)) return EP_ERR_NULL;
+    if ((writes && !out_sf) || (reads && !sf)) return EP_ERR_NULL;
     if (sf_ts < 0 || sf_hs < 0 || out_ts < 0 || out_hs < 0) return EP_ERR_SHAPE;
     if (!aligned(sf, 4) || !aligned(out_sf, 4)) return EP_ERR_MISALIGNED;
     *packs = n;
@@ -315,12 +316,16 @@ ep_status ep_dispatch(const ep_handle *h, const void *x, ep_dtype x_dtype, int32
     if (hidden <= 0) return EP_ERR_SHAPE;
     const bool fp8 = x_dtype == EP_FP8_E4M3;
     if (fp8 ? (hidden % 128) != 0 : (hidden % 8) != 0) return EP_ERR_MISALIGNED;
+    // With no tokens nothing is read, and only zero padding can write (the
+    // gap rows of an imported layout, inside the capacity).
+    const bool reads = h->num_tokens > 0;
+    const bool writes = reads || (zero_padding != 0 && h->capacity > 0);
     int32_t packs = 0;
-    const ep_status st = check_sf(fp8, hidden, sf, out_sf, num_sf_packs, h->num_tokens > 0,
+    const ep_status st = check_sf(fp8, hidden, sf, out_sf, num_sf_packs, reads, writes,
                                   sf_token_stride, sf_hidden_stride, out_sf_token_stride,
                                   out_sf_hidden_stride, &packs);
     if (st != EP_OK) return st;
-    if (!out_x || (h->num_tokens > 0 && !x)) return EP_ERR_NULL;
+    if ((writes && !out_x) || (reads && !x)) return EP_ERR_NULL;
     if (!aligned(x, 16) || !aligned(out_x, 16)) return EP_ERR_MISALIGNED;
     if (!aligned(topk_weights, 4) || !aligned(out_w, 4)) return EP_ERR_MISALIGNED;
     const int64_t row_bytes = fp8 ? hidden : 2 * static_cast<int64_t>(hidden);
@@ -359,13 +364,13 @@ int32_t ep_sf_packs(int32_t hidden, ep_sf_format fmt) {
 
 // Shared checks of the two quantising calls; fills the copy-free fields.
 static ep_status quant_args(const void *x, int32_t hidden, ep_sf_format fmt, const void *out_x,
-                            const void *out_sf, int64_t ts, int64_t hs, bool rows,
+                            const void *out_sf, int64_t ts, int64_t hs, bool reads, bool writes,
                             ep::DispatchArgs *a) {
     if (fmt != EP_SF_F32 && fmt != EP_SF_UE8M0) return EP_ERR_DTYPE;
     if (hidden <= 0) return EP_ERR_SHAPE;
     if (hidden % 128 != 0) return EP_ERR_MISALIGNED;
     if (ts < 0 || hs < 0) return EP_ERR_SHAPE;
-    if (rows && (!x || !out_x || !out_sf)) return EP_ERR_NULL;
+    if ((reads && !x) || (writes && (!out_x || !out_sf))) return EP_ERR_NULL;
     if (!aligned(x, 16) || !aligned(out_x, 16) || !aligned(out_sf, 4)) return EP_ERR_MISALIGNED;
     a->x = x;
     a->row_vecs = hidden / 16;
@@ -385,7 +390,7 @@ ep_status ep_quantize_fp8(const void *x, int32_t num_tokens, int32_t hidden, ep_
     if (num_tokens < 0) return EP_ERR_SHAPE;
     ep::DispatchArgs a{};
     const ep_status st = quant_args(x, hidden, fmt, out_q, out_sf, out_sf_token_stride,
-                                    out_sf_hidden_stride, num_tokens > 0, &a);
+                                    out_sf_hidden_stride, num_tokens > 0, num_tokens > 0, &a);
     if (st != EP_OK) return st;
     a.num_tokens = num_tokens;
     a.num_topk = 1;
@@ -403,8 +408,10 @@ ep_status ep_dispatch_quant(const ep_handle *h, const void *x, int32_t hidden, e
     if (!handle_ready(h)) return EP_ERR_WORKSPACE;
     if (!h->laid_out) return EP_ERR_NOT_LAID_OUT;
     ep::DispatchArgs a{};
+    const bool reads = h->num_tokens > 0;
+    const bool writes = reads || (zero_padding != 0 && h->capacity > 0);
     const ep_status st = quant_args(x, hidden, fmt, out_x, out_sf, out_sf_token_stride,
-                                    out_sf_hidden_stride, h->num_tokens > 0, &a);
+                                    out_sf_hidden_stride, reads, writes, &a);
     if (st != EP_OK) return st;
     if (!aligned(topk_weights, 4) || !aligned(out_w, 4)) return EP_ERR_MISALIGNED;
     a.num_tokens = h->num_tokens;
@@ -559,11 +566,11 @@ ep_status ep_dispatch_rank(const ep_handle *h, const void *x, ep_dtype x_dtype, 
     if (fp8 ? (hidden % 128) != 0 : (hidden % 8) != 0) return EP_ERR_MISALIGNED;
     const bool rows = h->num_tokens > 0;
     int32_t packs = 0;
-    const ep_status st = check_sf(fp8, hidden, sf, out_sf, num_sf_packs, rows, sf_token_stride,
-                                  sf_hidden_stride, out_sf_token_stride, out_sf_hidden_stride,
-                                  &packs);
+    const ep_status st = check_sf(fp8, hidden, sf, out_sf, num_sf_packs, rows, rows,
+                                  sf_token_stride, sf_hidden_stride, out_sf_token_stride,
+                                  out_sf_hidden_stride, &packs);
     if (st != EP_OK) return st;
-    if (!out_x || (rows && !x)) return EP_ERR_NULL;
+    if (rows && (!out_x || !x)) return EP_ERR_NULL;
     if ((out_topk_idx || out_topk_weights) && rows && !h->topk_idx) return EP_ERR_NULL;
     if (!aligned(x, 16) || !aligned(out_x, 16)) return EP_ERR_MISALIGNED;
     if (!aligned(topk_weights, 4) || !aligned(out_topk_weights, 4) ||

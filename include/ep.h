@@ -243,6 +243,9 @@ ep_status ep_handle_import(ep_handle *h, const void *topk_idx, ep_dtype idx_dtyp
  *   out_w    NULL or device fp32 [capacity]: weight of the row's slot
  *            (1.0 when topk_weights is NULL).
  *   zero_padding  nonzero: gap rows get zero bytes, zero scales, weight 0.
+ * With no tokens in the layout, x and sf may be NULL, and so may out_x and
+ * out_sf unless zero_padding is set and capacity > 0 (an imported layout
+ * can have gap rows and no tokens).
  * Rows at or past psum[E], and gap rows without zero padding, are not
  * written.  Reuses the handle, so a cached re-dispatch is just another call.
  */
@@ -285,7 +288,7 @@ ep_status ep_quantize_fp8(const void *x, int32_t num_tokens, int32_t hidden,
 
 /*
  * Quantising dispatch: ep_quantize_fp8 of bf16 x fused with ep_dispatch of
- * the codes and packs (same layout, weights and zero-padding rules), so x is
+ * the codes and packs (same layout, weights, zero-padding and NULL rules), so x is
  * read once in bf16 and every routed row is written once in FP8 [Ch7 §7.3,
  * §7.4].  out_x is [capacity, hidden] codes; out_sf is [capacity,
  * ep_sf_packs(hidden, fmt)] packs with the given strides.
@@ -328,7 +331,8 @@ ep_status ep_combine(const ep_handle *h, const void *y, ep_dtype y_dtype,
  * dtype of the layout's topk_idx) gets the token's ids with -1 for empty or
  * invalid slots; out_topk_weights (NULL or fp32 [max_tokens, K]) its weights
  * with 0 for those slots (1 for valid slots when topk_weights is NULL).
- * Rows at or past num_recv_tokens are not written.
+ * Rows at or past num_recv_tokens are not written; with no tokens in the
+ * layout every buffer may be NULL.
  */
 ep_status ep_dispatch_rank(const ep_handle *h, const void *x, ep_dtype x_dtype,
                            int32_t hidden, const void *sf, int64_t sf_token_stride,

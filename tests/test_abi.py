@@ -153,6 +153,16 @@ def test_dispatch_validation():
     assert call(w=A16 + 2) == ep.EP_ERR_MISALIGNED
     assert ep.ep_dispatch(h, A16, ep.EP_FP8_E4M3, 128, A16, -1, 0, 0, None, A16, A16, 0, 0,
                           None, 0, None) == ep.EP_ERR_SHAPE
+    # No tokens: nothing is read, but zero padding into a non-empty capacity
+    # may still write gap rows (an imported layout), so it needs out_x / out_sf.
+    empty = _fake_handle()
+    empty.num_tokens = 0
+    assert ep.ep_dispatch(empty, None, ep.EP_BF16, 64, None, 0, 0, 0, None, None, None, 0, 0,
+                          None, 1, None) == ep.EP_ERR_NULL
+    assert ep.ep_dispatch(empty, None, ep.EP_FP8_E4M3, 128, None, 0, 0, 0, None, A16, None,
+                          0, 0, None, 1, None) == ep.EP_ERR_NULL
+    assert ep.ep_dispatch_quant(empty, None, 128, ep.EP_SF_F32, None, None, A16, 0, 0, None, 1,
+                                None) == ep.EP_ERR_NULL
 
 
 def test_tma_aligned_rows():
