@@ -6,7 +6,7 @@ The pins are: hand-worked golden fixtures (``tests/golden``), brute force on
 tiny inputs (``bruteforce.py``), a special case that reduces to numpy's stable
 argsort, closed forms (identity expert, exact gather) and invariants.
 
-Run as ``python -m tests.pins <oracle.so>`` to get a one-line verdict per pin;
+Run as ``python -m tests.pins <oracle.so>`` to get a one-line result per pin;
 the mutation test uses that to show every planted mistake is caught.
 """
 from __future__ import annotations
