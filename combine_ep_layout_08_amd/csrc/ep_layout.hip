@@ -7,7 +7,10 @@
 // alignment; s7.5 handle fields).  Inside an expert's segment rows follow the
 // ascending slot index t*K+k (a stable counting sort).
 //
-// Two forms, both two kernels over tiles of whole tokens.  Up to
+// A batch that fits in one tile (at most 2048 slots) is laid out in one
+// launch (layout_single, below; tiny 64 x 4 and decode 128 x 8: 11-13 ->
+// 6 us).  Larger batches take one of two forms, both two kernels over tiles
+// of whole tokens.  Up to
 // kCountPlaceMaxTiles long tiles (524288 slots): layout_count + layout_place
 // (below), which exchange the tiles' counts through the kernel boundary and
 // never wait on another block; measured 1-2 us faster than the lookback form
@@ -220,6 +223,79 @@ __device__ void rank_tile(const LayoutArgs &a, int64_t tile_base, int64_t tile_e
     }
 }
 
+// Aligned exclusive scan of the experts' totals (s_total, buckets 0..E+1)
+// into s_psum, and the call's error verdict in *s_fatal (nonzero: capacity
+// exceeded or an earlier timeout; the layout is void).  Every block that
+// calls it on the same totals gets the same result; with `publish` the block
+// also writes the scalars, counts, psum and cumulative stats.  Ends after a
+// block barrier.
+__device__ void scan_experts(const LayoutArgs &a, const int32_t *s_total, int32_t *s_psum,
+                             int64_t *s_wave, int32_t *s_fatal, bool publish) {
+    const int tid = threadIdx.x, E = a.num_experts;
+    const int per = (E + kLayoutThreads - 1) / kLayoutThreads;
+    const int b0 = tid * per;
+    const int b1 = min(b0 + per, E);
+    int64_t local = 0;
+    for (int b = b0; b < b1; ++b) local += align_up(s_total[b], a.alignment);
+    int64_t total = 0;
+    int64_t run = block_exclusive_scan(local, s_wave, &total);
+    for (int b = b0; b < b1; ++b) {
+        s_psum[b] = static_cast<int32_t>(min(run, static_cast<int64_t>(INT32_MAX)));
+        run += align_up(s_total[b], a.alignment);
+    }
+    if (tid == 0) {
+        s_psum[E] = static_cast<int32_t>(min(total, static_cast<int64_t>(INT32_MAX)));
+        // Every block reaches the same verdict: the capacity test uses the
+        // same totals, and the sticky timeout bit is the same before and
+        // after the publishing block rewrites the word.
+        uint32_t err = static_cast<uint32_t>(a.scalars[EP_SCALAR_ERROR_BITS]) &
+                       EP_ERRBIT_SCAN_TIMEOUT;
+        if (total > a.capacity) err |= EP_ERRBIT_CAPACITY;
+        if (s_total[E] > 0) err |= EP_ERRBIT_INVALID_ID;
+        *s_fatal = (err & EP_ERRBIT_FATAL) != 0;
+        if (publish) {
+            a.scalars[EP_SCALAR_NUM_EXPANDED] = s_psum[E];
+            a.scalars[EP_SCALAR_INVALID_COUNT] = s_total[E];
+            a.scalars[EP_SCALAR_NUM_RECV_TOKENS] = s_total[E + 1];
+            a.scalars[EP_SCALAR_ERROR_BITS] = static_cast<int32_t>(err);
+        }
+    }
+    __syncthreads();
+    if (publish) {
+        for (int b = tid; b < E; b += kLayoutThreads) {
+            a.counts[b] = s_total[b];
+            if (a.cumulative_stats) a.cumulative_stats[b] += s_total[b];
+        }
+        for (int b = tid; b <= E; b += kLayoutThreads) a.psum[b] = s_psum[b];
+    }
+}
+
+// Rank-layout rows of a tile's tokens [tok0, tok0 + tokens_per_tile): the
+// received ones (flag set in s_tok) numbered from `first` in token order,
+// the others -1.
+__device__ void number_rank_rows(const LayoutArgs &a, int64_t tok0, int tokens_per_tile,
+                                 const uint8_t *s_tok, int64_t first, int64_t *s_wave) {
+    const int tid = threadIdx.x;
+    const int tper = (tokens_per_tile + kLayoutThreads - 1) / kLayoutThreads;
+    const int j0 = tid * tper;
+    const int j1 = min(j0 + tper, tokens_per_tile);
+    int64_t cnt = 0;
+    for (int j = j0; j < j1; ++j) cnt += s_tok[j];
+    int64_t unused = 0;
+    int64_t row = first + block_exclusive_scan(cnt, s_wave, &unused);
+    for (int j = j0; j < j1; ++j) {
+        const int64_t t = tok0 + j;
+        if (t >= a.num_tokens) break;
+        if (s_tok[j]) {
+            a.recv_row[t] = static_cast<int32_t>(row);
+            a.recv_src[row] = static_cast<int32_t>(t);
+            ++row;
+        } else {
+            a.recv_row[t] = -1;
+        }
+    }
+}
+
 template <typename IdxT>
 __global__ __launch_bounds__(kLayoutThreads) void layout_scan_kernel(LayoutArgs a,
                                                                     int tokens_per_tile,
@@ -294,27 +370,8 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_scan_kernel(LayoutArgs 
 
     // 5. Rank layout: the tile's received tokens get consecutive rows after
     //    the received tokens of earlier tiles (bucket E+1's exclusive count).
-    {
-        const int per = (tokens_per_tile + kLayoutThreads - 1) / kLayoutThreads;
-        const int j0 = tid * per;
-        const int j1 = min(j0 + per, tokens_per_tile);
-        int64_t local = 0;
-        for (int j = j0; j < j1; ++j) local += s_tok[j];
-        int64_t unused = 0;
-        int64_t row = s_excl[B_RECV] + block_exclusive_scan(local, s_wave, &unused);
-        const int64_t tok0 = static_cast<int64_t>(tile) * tokens_per_tile;
-        for (int j = j0; j < j1; ++j) {
-            const int64_t t = tok0 + j;
-            if (t >= a.num_tokens) break;
-            if (s_tok[j]) {
-                a.recv_row[t] = static_cast<int32_t>(row);
-                a.recv_src[row] = static_cast<int32_t>(t);
-                ++row;
-            } else {
-                a.recv_row[t] = -1;
-            }
-        }
-    }
+    number_rank_rows(a, static_cast<int64_t>(tile) * tokens_per_tile, tokens_per_tile, s_tok,
+                     s_excl[B_RECV], s_wave);
     __syncthreads();                                   // s_wave is used again below
 
     // 6. The last tile owns the totals: counts, aligned scan, scalars.
@@ -387,6 +444,83 @@ __global__ __launch_bounds__(256) void layout_finalize_kernel(LayoutArgs a, int 
     const int64_t end = g1 < a.capacity ? g1 : a.capacity;
     for (int64_t r = static_cast<int64_t>(a.psum[e]) + a.counts[e] + tid; r < end; r += 256)
         a.src_meta[r] = -1;
+}
+
+// ---------------------------------------------------------------- one tile
+// A batch that fits in one tile needs no exchange between blocks.  Block 0
+// ranks every slot (rank_tile), scans the aligned counts, writes counts,
+// psum, the scalars, every slot's row and source metadata and the rank rows.
+// The alignment gaps are marked either by block 0's four waves (a one-block
+// grid) or by the other blocks, each of which counts the batch's ids again
+// (no ranking: at most kTileSlots of them), repeats the scan and marks the
+// gaps of every (gridDim.x - 1)-th expert.  One launch; no block waits on
+// another; no status words and no epoch.
+template <typename IdxT, int R>
+__global__ __launch_bounds__(kLayoutThreads) void layout_single_kernel(LayoutArgs a,
+                                                                      int tokens_per_tile) {
+    __shared__ int32_t s_hist[kLayoutWaves][kMaxBuckets];
+    __shared__ int32_t s_total[kMaxBuckets];
+    __shared__ int32_t s_psum[kMaxExperts + 1];
+    __shared__ uint8_t s_tok[kLayoutThreads * R];
+    __shared__ int64_t s_wave[kLayoutWaves];
+    __shared__ int32_t s_fatal;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int E = a.num_experts, NB = E + 2;
+    const int64_t num_slots = static_cast<int64_t>(a.num_tokens) * a.num_topk;
+    const int64_t wave_base = static_cast<int64_t>(wave) * (R * 64);
+    if (blockIdx.x > 0) {
+        const IdxT *idx = static_cast<const IdxT *>(a.topk_idx);
+        for (int b = tid; b < NB; b += kLayoutThreads) s_total[b] = 0;
+        __syncthreads();
+        for (int64_t i = tid; i < num_slots; i += kLayoutThreads) {
+            const int64_t e = static_cast<int64_t>(idx[i]);
+            if (e >= 0 && e < E) atomicAdd(&s_total[e], 1);
+            else if (e != -1) atomicAdd(&s_total[E], 1);
+        }
+        __syncthreads();
+        scan_experts(a, s_total, s_psum, s_wave, &s_fatal, false);
+        if (s_fatal) return;
+        for (int e = blockIdx.x - 1; e < E; e += gridDim.x - 1) {
+            const int64_t end = s_psum[e + 1] < a.capacity ? s_psum[e + 1] : a.capacity;
+            for (int64_t r = static_cast<int64_t>(s_psum[e]) + s_total[e] + tid; r < end;
+                 r += kLayoutThreads)
+                a.src_meta[r] = -1;
+        }
+        return;
+    }
+    int bucket[R];
+    int rank[R];
+    int32_t agg[kBucketsPerThread];
+    rank_tile<IdxT, R>(a, 0, num_slots, tokens_per_tile, s_hist, s_tok, bucket, rank, agg);
+#pragma unroll
+    for (int q = 0; q < kBucketsPerThread; ++q) {
+        const int b = tid + q * kLayoutThreads;
+        if (b < NB) s_total[b] = agg[q];
+    }
+    __syncthreads();
+    scan_experts(a, s_total, s_psum, s_wave, &s_fatal, true);
+    const bool fatal = s_fatal != 0;
+    if (!fatal) {
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+            const int64_t i = wave_base + j * 64 + lane;
+            if (i >= num_slots) continue;
+            const int b = bucket[j];
+            int32_t r = -1;
+            if (b >= 0 && b < E) {
+                r = s_psum[b] + s_hist[wave][b] + rank[j];
+                a.src_meta[r] = static_cast<int32_t>(i);
+            }
+            a.dst[i] = r;
+        }
+    }
+    number_rank_rows(a, 0, tokens_per_tile, s_tok, 0, s_wave);
+    if (fatal || gridDim.x > 1) return;
+    for (int e = wave; e < E; e += kLayoutWaves) {
+        const int64_t end = s_psum[e + 1] < a.capacity ? s_psum[e + 1] : a.capacity;
+        for (int64_t r = static_cast<int64_t>(s_psum[e]) + s_total[e] + lane; r < end; r += 64)
+            a.src_meta[r] = -1;
+    }
 }
 
 // ---------------------------------------------------------------- count + place
@@ -501,35 +635,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_place_kernel(LayoutArgs
     __syncthreads();
 
     // 2. Aligned exclusive scan over experts (identical in every block).
-    const int per = (E + kLayoutThreads - 1) / kLayoutThreads;
-    const int b0 = tid * per;
-    const int b1 = min(b0 + per, E);
-    int64_t local = 0;
-    for (int b = b0; b < b1; ++b) local += align_up(s_total[b], a.alignment);
-    int64_t total = 0;
-    int64_t run = block_exclusive_scan(local, s_wave, &total);
-    for (int b = b0; b < b1; ++b) {
-        s_psum[b] = static_cast<int32_t>(min(run, static_cast<int64_t>(INT32_MAX)));
-        run += align_up(s_total[b], a.alignment);
-    }
-    if (tid == 0) {
-        s_psum[E] = static_cast<int32_t>(min(total, static_cast<int64_t>(INT32_MAX)));
-        // Every block reaches the same verdict: the capacity test uses the
-        // same totals, and the sticky timeout bit is the same before and
-        // after tile 0 rewrites the word.
-        uint32_t err = static_cast<uint32_t>(a.scalars[EP_SCALAR_ERROR_BITS]) &
-                       EP_ERRBIT_SCAN_TIMEOUT;
-        if (total > a.capacity) err |= EP_ERRBIT_CAPACITY;
-        if (s_total[E] > 0) err |= EP_ERRBIT_INVALID_ID;
-        s_fatal = (err & EP_ERRBIT_FATAL) != 0;
-        if (tile == 0) {
-            a.scalars[EP_SCALAR_NUM_EXPANDED] = s_psum[E];
-            a.scalars[EP_SCALAR_INVALID_COUNT] = s_total[E];
-            a.scalars[EP_SCALAR_NUM_RECV_TOKENS] = s_total[E + 1];
-            a.scalars[EP_SCALAR_ERROR_BITS] = static_cast<int32_t>(err);
-        }
-    }
-    __syncthreads();
+    scan_experts(a, s_total, s_psum, s_wave, &s_fatal, tile == 0);
     const bool fatal = s_fatal != 0;
     if (gap_block) {
         // Gap markers of expert blockIdx.x - num_tiles.
@@ -540,13 +646,6 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_place_kernel(LayoutArgs
              r += kLayoutThreads)
             a.src_meta[r] = -1;
         return;
-    }
-    if (tile == 0) {
-        for (int b = tid; b < E; b += kLayoutThreads) {
-            a.counts[b] = s_total[b];
-            if (a.cumulative_stats) a.cumulative_stats[b] += s_total[b];
-        }
-        for (int b = tid; b <= E; b += kLayoutThreads) a.psum[b] = s_psum[b];
     }
 
     // 3. Final rows and source metadata; flags of received tokens.
@@ -572,27 +671,8 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_place_kernel(LayoutArgs
     __syncthreads();
 
     // 4. Rank layout: the tile's received tokens after those of earlier tiles.
-    {
-        const int tper = (tokens_per_tile + kLayoutThreads - 1) / kLayoutThreads;
-        const int j0 = tid * tper;
-        const int j1 = min(j0 + tper, tokens_per_tile);
-        int64_t cnt = 0;
-        for (int j = j0; j < j1; ++j) cnt += s_tok[j];
-        int64_t unused = 0;
-        int64_t row = s_excl[E + 1] + block_exclusive_scan(cnt, s_wave, &unused);
-        const int64_t tok0 = static_cast<int64_t>(tile) * tokens_per_tile;
-        for (int j = j0; j < j1; ++j) {
-            const int64_t t = tok0 + j;
-            if (t >= a.num_tokens) break;
-            if (s_tok[j]) {
-                a.recv_row[t] = static_cast<int32_t>(row);
-                a.recv_src[row] = static_cast<int32_t>(t);
-                ++row;
-            } else {
-                a.recv_row[t] = -1;
-            }
-        }
-    }
+    number_rank_rows(a, static_cast<int64_t>(tile) * tokens_per_tile, tokens_per_tile, s_tok,
+                     s_excl[E + 1], s_wave);
 
     // 5. Tile 0 retires this call's status words.
     if (tile == 0 && tid == 0) {
@@ -651,8 +731,28 @@ hipError_t launch_scan_finalize(const LayoutArgs &a, hipStream_t stream, CallEve
     return e;
 }
 
+// Gap-marking blocks of the one-tile layout when there are alignment gaps.
+#ifndef EP_LAYOUT_SINGLE_GAP_BLOCKS
+#define EP_LAYOUT_SINGLE_GAP_BLOCKS 16
+#endif
+
+template <typename IdxT, int R>
+hipError_t launch_single(const LayoutArgs &a, hipStream_t stream, CallEvents ev) {
+    int gap_blocks = 0;
+    if (a.alignment > 1)
+        gap_blocks = a.num_experts < EP_LAYOUT_SINGLE_GAP_BLOCKS ? a.num_experts
+                                                                 : EP_LAYOUT_SINGLE_GAP_BLOCKS;
+    return launch_kernel(layout_single_kernel<IdxT, R>, dim3(1 + gap_blocks),
+                         dim3(kLayoutThreads), stream, ev.start, ev.stop, a,
+                         layout_tokens_per_tile(a.num_topk, R));
+}
+
 template <typename IdxT>
 hipError_t launch_layout_idx(const LayoutArgs &a, hipStream_t stream, CallEvents ev) {
+    if (layout_tiles(a.num_tokens, a.num_topk, kRoundsSmall) == 1)
+        return launch_single<IdxT, kRoundsSmall>(a, stream, ev);
+    if (layout_tiles(a.num_tokens, a.num_topk, kRoundsLarge) == 1)
+        return launch_single<IdxT, kRoundsLarge>(a, stream, ev);
     if (layout_rounds(a.num_tokens, a.num_topk) == kRoundsSmall)
         return launch_count_place<IdxT, kRoundsSmall>(a, stream, ev);
     if (layout_tiles(a.num_tokens, a.num_topk, kRoundsLarge) <= kCountPlaceMaxTiles)

@@ -41,7 +41,8 @@ def test_layout_random_small_cases():
         _check(idx, E, A, cap)
 
 
-@pytest.mark.parametrize("slots", [1, 63, 64, 65, 2047, 2048, 2049, 4096, 4097, 2048 * 7 + 5])
+@pytest.mark.parametrize("slots", [1, 63, 64, 65, 1024, 1025, 2047, 2048, 2049, 4096, 4097,
+                                   2048 * 7 + 5])
 @pytest.mark.parametrize("K,E", [(8, 256), (1, 1024), (4, 1), (3, 5)])
 def test_layout_tile_boundaries(slots, K, E):
     T = max(1, slots // K)
@@ -51,14 +52,16 @@ def test_layout_tile_boundaries(slots, K, E):
     _check(idx, E, 4, T * K + 4 * E)
 
 
-@pytest.mark.parametrize("T,K,E", [(8192, 8, 256), (8193, 8, 256), (10880, 6, 64),
+@pytest.mark.parametrize("T,K,E", [(128, 8, 256), (129, 8, 256), (256, 8, 256), (257, 8, 256),
+                                   (8192, 8, 256), (8193, 8, 256), (10880, 6, 64),
                                    (10881, 6, 64), (65536, 8, 256), (65537, 8, 256),
                                    (8229, 64, 1024)])
-def test_layout_count_place_and_lookback_forms_meet(T, K, E):
-    """Up to 64 short tiles (1024 slots) the layout ranks short tiles, up to
-    256 tiles of 2048 slots long ones, both exchanging tile counts through a
-    kernel boundary; beyond that it takes the single-pass lookback.  Both
-    sides of each switch, bit-exact, with empty and invalid ids."""
+def test_layout_forms_meet(T, K, E):
+    """A batch within one tile (up to 2048 slots) is laid out by one block in
+    one launch; up to 64 short tiles (1024 slots) by count + place over short
+    tiles, up to 256 tiles of 2048 slots over long ones; beyond that by the
+    single-pass lookback.  Both sides of each switch, bit-exact, with empty
+    and invalid ids."""
     rng = np.random.default_rng(T + K)
     idx = rng.integers(-1, E, size=(T, K))
     idx[::101, 0] = E + 3                               # invalid ids
