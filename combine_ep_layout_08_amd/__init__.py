@@ -248,7 +248,10 @@ def time_next_call(start: "torch.cuda.Event", stop: "torch.cuda.Event") -> None:
 # ---------------------------------------------------------------- torch wrapper
 
 def _stream() -> int:
-    return torch.cuda.current_stream().cuda_stream
+    """Raw handle of the current device's current stream: the value of
+    torch.cuda.current_stream().cuda_stream, read without building a Stream
+    object (0.3 us instead of 2.8 us per call on MI355X)."""
+    return torch._C._cuda_getCurrentRawStream(torch.cuda.current_device())
 
 
 def _ptr(t: Optional[torch.Tensor]):

@@ -183,3 +183,13 @@ def test_graph_capture_of_the_other_calls():
         np.testing.assert_array_equal(ri.cpu().numpy()[:nr], oi[:nr])
         np.testing.assert_array_equal(rw.cpu().numpy()[:nr], ow[:nr])
         np.testing.assert_array_equal(u16(rout), oracle.combine_rank(u16(rx), row, u16(gr)))
+
+
+def test_binding_passes_the_current_stream():
+    """The binding hands the library the raw handle of the current stream,
+    the same value torch reports for it, on the default stream and inside a
+    stream context."""
+    assert ep._stream() == torch.cuda.current_stream().cuda_stream
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        assert ep._stream() == s.cuda_stream == torch.cuda.current_stream().cuda_stream
