@@ -75,3 +75,20 @@ def assert_layout_equal(rc, dst, src, lay: oracle.Layout):
     assert rc["num_recv_tokens"] == lay.num_recv_tokens
     want = ep.EP_ERR_INVALID_ID if lay.invalid_count else ep.EP_OK
     assert rc["status"] == want
+
+
+def assert_rows_equal(got: np.ndarray, exp: np.ndarray, what: str):
+    """Bit-exact comparison of two [rows, cols] arrays that, on a mismatch,
+    names the rows that differ, how many elements each, and whether a wrong
+    row equals the expected row of another index (stale or misplaced data)."""
+    if np.array_equal(got, exp):
+        return
+    bad = np.nonzero((got != exp).any(axis=1))[0]
+    lines = [f"{what}: {len(bad)} of {got.shape[0]} rows differ"]
+    keys = {exp[r].tobytes(): r for r in range(exp.shape[0])}
+    for r in bad[:12]:
+        n = int((got[r] != exp[r]).sum())
+        other = keys.get(got[r].tobytes())
+        lines.append(f"  row {r}: {n} elements differ" +
+                     (f"; equals expected row {other}" if other is not None else ""))
+    raise AssertionError("\n".join(lines))

@@ -14,7 +14,7 @@ import combine_ep_layout_08_amd as ep
 import ep_workloads as W
 import oracle
 from tests import bruteforce as BF
-from tests.gpu_util import POISON, gpu_layout, needs_gpu, poison_, say, u16
+from tests.gpu_util import POISON, assert_rows_equal, gpu_layout, needs_gpu, poison_, say, u16
 from tests.tolerance import check_sum
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
@@ -132,7 +132,7 @@ def test_dispatch_backward():
     torch.cuda.synchronize()
     lay = oracle.layout(wl.topk_idx, cfg.experts, cfg.alignment, cap)
     o_gx, o_gw = oracle.dispatch_backward(u16(go), wl.topk_idx, lay.dst, gwr.numpy())
-    np.testing.assert_array_equal(u16(gx), o_gx)
+    assert_rows_equal(u16(gx), o_gx, "grad_x")
     np.testing.assert_array_equal(gw.cpu().numpy(), o_gw)
     gx2, gw2 = h.dispatch_backward(go.cuda(), want_grad_weights=True)   # no weight gradient in
     torch.cuda.synchronize()

@@ -13,7 +13,7 @@ import torch
 import combine_ep_layout_08_amd as ep
 import ep_workloads as W
 import oracle
-from tests.gpu_util import POISON, gpu_layout, needs_gpu, poison_, say, u16, u8
+from tests.gpu_util import assert_rows_equal, gpu_layout, needs_gpu, POISON, poison_, say, u16, u8
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
 
@@ -37,7 +37,7 @@ def _check(idx, E, A, cap, y, w=None, bias=None):
     got = _gpu_combine(h, y, w, bias)
     lay = oracle.layout(idx, E, A, cap)
     exp = oracle.combine(u16(y), idx, lay.dst, w, None if bias is None else u16(bias))
-    np.testing.assert_array_equal(got, exp)
+    assert_rows_equal(got, exp, "combine")
     return got
 
 
