@@ -7,19 +7,19 @@
 // alignment; s7.5 handle fields).  Inside an expert's segment rows follow the
 // ascending slot index t*K+k (a stable counting sort).
 //
-// A batch that fits in one tile (at most 2048 slots) is laid out in one
-// launch (layout_single, below; tiny 64 x 4 and decode 128 x 8: 11-13 ->
-// 6 us).  Larger batches take one of two forms, both two kernels over tiles
-// of whole tokens.  Up to
-// kCountPlaceMaxTiles long tiles (524288 slots): layout_count + layout_place
-// (below), which exchange the tiles' counts through the kernel boundary and
-// never wait on another block; measured 1-2 us faster than the lookback form
-// at every size from 64 x 4 to 32768 x 8 slots.  Batches that fit in
-// kSmallTilesMax short tiles (4 rounds, 1024 slots) use those: twice the
-// blocks share the ranking, and every place thread still reads all tiles'
-// counts in one or two round trips (prefill 4096 x 8: 16.3 -> 14.5 us).
-// Beyond kCountPlaceMaxTiles long tiles, where every place block would read
-// too many tiles' counts, the single-pass lookback:
+// Three forms.  A batch that fits in one tile (at most 2048 slots) is laid
+// out in one launch (layout_single, below; tiny 64 x 4 and decode 128 x 8:
+// 11-13 -> 6 us).  Larger batches take two kernels over tiles of whole
+// tokens.  Up to kCountPlaceMaxTiles long tiles (524288 slots):
+// layout_count + layout_place (below), which exchange the tiles' counts
+// through the kernel boundary and never wait on another block; measured
+// 1-2 us faster than the lookback form at every size from 64 x 4 to
+// 32768 x 8 slots.  Batches that fit in kSmallTilesMax short tiles
+// (4 rounds, 1024 slots) use those: twice the blocks share the ranking, and
+// every place thread still reads all tiles' counts in one or two round trips
+// (prefill 4096 x 8: 16.3 -> 14.5 us).  Beyond kCountPlaceMaxTiles long
+// tiles, where every place block would read too many tiles' counts, the
+// single-pass lookback:
 //  1. layout_scan: one 256-thread block per long tile of whole tokens (at
 //     most kTileSlots slots).  The block first loads all of its ids (every load in
 //     flight at once), then each wave takes 64 slots per round: lanes holding
