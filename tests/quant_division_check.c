@@ -3,10 +3,11 @@
  * finite bf16 block maximum amax (bit patterns 0 .. 0x7F7F), with
  * s = RN(max(amax, 1e-12) / 448) and y = RN(1 / s), and for every bf16 x of
  * either sign with |x| <= amax:
- *   q0 = RN(x * y), r = RN(x - q0 * s), q = copysign(RN(q0 + r * y), x)
- * (fused multiply-adds) must equal the correctly rounded quotient RN(x / s)
- * bit for bit, unless both lie below 2^-11 in magnitude with the same sign
- * (the E4M3 code is then the signed zero either way).  The UE8M0 form,
+ *   q0 = RN(x * y), n = RN(q0 * s - x), q = RN(q0 - n * y)
+ * (fused multiply-adds; n is the negated remainder, so that x = -0 gives
+ * q = -0 without a sign fix) must equal the correctly rounded quotient
+ * RN(x / s) bit for bit, unless both lie below 2^-11 in magnitude with the
+ * same sign (the E4M3 code is then the signed zero either way).  The UE8M0 form,
  * x * 2^-k for the rounded-up power of two 2^k >= s, must equal x / 2^k
  * exactly.  Prints the number of pairs and of failures of each kind.
  * Plain C with IEEE binary32 arithmetic (no flush to zero, no contraction). */
@@ -43,8 +44,8 @@ int main(void) {
                 const float x = from_bits((xb | sign << 15) << 16);
                 const float q = x / s;
                 const float q0 = x * y;
-                const float r = fmaf(-q0, s, x);
-                const float q1 = copysignf(fmaf(r, y, q0), x);
+                const float n = fmaf(q0, s, -x);
+                const float q1 = fmaf(-n, y, q0);
                 ++pairs;
                 if (to_bits(q1) != to_bits(q) &&
                     !(fabsf(q) < 0x1p-11f && fabsf(q1) < 0x1p-11f && signbit(q) == signbit(q1)))
