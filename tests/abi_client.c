@@ -115,8 +115,6 @@ int ep_client_run(const char *dir, int32_t T, int32_t K, int32_t E, int32_t A, i
     HIP_TRY(hipMalloc(&out_x, 2 * rows * H + 16));
     HIP_TRY(hipMalloc((void **)&out_w, 4 * rows + 16));
     HIP_TRY(hipMalloc(&out, 2 * (size_t)T * H + 16));
-    HIP_TRY(hipMemset(out_x, 0xA5, 2 * rows * H));
-    HIP_TRY(hipMemset(out_w, 0xA5, 4 * rows));
     ws_bytes = ep_workspace_bytes(T, K, E, A, cap);
     if (ws_bytes == 0) {
         fprintf(stderr, "ep_workspace_bytes rejected the sizes\n");
@@ -125,6 +123,10 @@ int ep_client_run(const char *dir, int32_t T, int32_t K, int32_t E, int32_t A, i
     HIP_TRY(hipMalloc(&ws, ws_bytes));                  /* 256-byte aligned */
     HIP_TRY(hipStreamCreateWithFlags(&stream, hipStreamNonBlocking));
     stream_made = 1;
+    /* Poison on the same stream: a non-blocking stream is not ordered after
+     * work on the null stream. */
+    HIP_TRY(hipMemsetAsync(out_x, 0xA5, 2 * rows * H, stream));
+    HIP_TRY(hipMemsetAsync(out_w, 0xA5, 4 * rows, stream));
 
     EP_TRY(ep_handle_init(&h, T, K, E, A, cap, ws, ws_bytes, stream));
     EP_TRY(ep_layout(&h, idx, EP_I64, T, NULL, stream));
