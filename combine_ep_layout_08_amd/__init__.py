@@ -42,6 +42,9 @@ _SF_FORMATS = {"f32": EP_SF_F32, "ue8m0": EP_SF_UE8M0}
 EP_ERRBIT_CAPACITY = 1
 EP_ERRBIT_INVALID_ID = 2
 EP_ERRBIT_SCAN_TIMEOUT = 4
+# Indices into the handle's device scalars (Handle.scalars), as in ep.h.
+EP_SCALAR_NUM_RECV_TOKENS, EP_SCALAR_ERROR_BITS, EP_SCALAR_INVALID_COUNT = 0, 1, 2
+EP_SCALAR_NUM_EXPANDED = 5
 
 
 class ep_handle(ctypes.Structure):

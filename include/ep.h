@@ -42,10 +42,12 @@
  * anything is launched.  Problems only the device can see (capacity exceeded,
  * expert ids outside [-1, E)) set bits in the handle's device error word,
  * which ep_handle_read_counts turns into EP_ERR_CAPACITY / EP_ERR_INVALID_ID
- * (or EP_ERR_TIMEOUT if the layout scan's bounded wait ever gave up).  After
- * a capacity or timeout error, dispatch and combine on that handle write
- * nothing.  Calls on one handle must be ordered on one stream; overlapping
- * calls on the same handle race.
+ * (or EP_ERR_TIMEOUT if the layout scan's bounded wait ever gave up; that
+ * bit is sticky: every later layout on the handle keeps it until
+ * ep_handle_init sets the handle up again).  After a capacity or timeout
+ * error, dispatch and combine on that handle write nothing.  Calls on one
+ * handle must be ordered on one stream; overlapping calls on the same
+ * handle race.
  */
 #ifndef EP_H
 #define EP_H

@@ -11,7 +11,8 @@ import combine_ep_layout_08_amd as ep
 import ep_workloads as W
 import oracle
 from tests import pins
-from tests.gpu_util import assert_layout_equal, assert_rank_equal, gpu_layout, needs_gpu, say
+from tests.gpu_util import (POISON, assert_layout_equal, assert_rank_equal, gpu_layout,
+                             needs_gpu, poison_, say, u8)
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
 
@@ -116,6 +117,33 @@ def test_layout_capacity_error():
     say("layout capacity error")
     _check(idx, 3, 4, 11)                        # needs 12 rows
     _check(idx, 3, 4, 12)
+
+
+@pytest.mark.parametrize("T", [64, 4096, 70000])     # one-tile, count + place, lookback forms
+def test_layout_timeout_bit_is_sticky(T):
+    """Once a layout scan's bounded wait has given up, the handle stays void
+    until it is set up again.  The timeout bit is set here from the host in the
+    handle's error word (no wait has to time out): a later layout still
+    reports EP_ERR_TIMEOUT, dispatch and combine write nothing, and a new
+    ep_handle_init on the same workspace clears it."""
+    K, E, A, H = 8, 64, 4, 64
+    idx = torch.from_numpy(np.random.default_rng(T).integers(-1, E, size=(T, K))).cuda()
+    h = ep.Handle(T, K, E, A)
+    h.scalars[ep.EP_SCALAR_ERROR_BITS] = ep.EP_ERRBIT_SCAN_TIMEOUT
+    say("layout sticky timeout", T)
+    h.layout(idx)
+    assert h.read_counts(check=False)["status"] == ep.EP_ERR_TIMEOUT
+    out_x = poison_(torch.empty((h.capacity, H), dtype=torch.bfloat16, device="cuda"))
+    out = poison_(torch.empty((T, H), dtype=torch.bfloat16, device="cuda"))
+    h.dispatch(torch.ones((T, H), dtype=torch.bfloat16, device="cuda"), out_x=out_x,
+               zero_padding=True)
+    h.combine(torch.ones((h.capacity, H), dtype=torch.bfloat16, device="cuda"), out=out)
+    torch.cuda.synchronize()
+    assert np.all(u8(out_x) == POISON) and np.all(u8(out) == POISON)
+    assert ep.ep_handle_init(h.h, T, K, E, A, h.capacity, h.workspace.data_ptr(),
+                             h.workspace.numel(), ep._stream()) == ep.EP_OK
+    h.layout(idx)
+    assert h.read_counts(check=False)["status"] in (ep.EP_OK, ep.EP_ERR_INVALID_ID)
 
 
 def test_layout_handle_reuse_and_determinism():
