@@ -21,10 +21,10 @@ pytestmark = [pytest.mark.gpu, needs_gpu]
 T, K, E, A, H = 1500, 8, 64, 16, 1024
 
 
-def _routing(rng):
-    idx = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int64)
-    idx = np.where(rng.random((T, K)) < 0.15, -1, idx)
-    w = rng.random((T, K), dtype=np.float32)
+def _routing(rng, t=T):
+    idx = np.stack([rng.permutation(E)[:K] for _ in range(t)]).astype(np.int64)
+    idx = np.where(rng.random((t, K)) < 0.15, -1, idx)
+    w = rng.random((t, K), dtype=np.float32)
     return idx, w
 
 
@@ -38,7 +38,8 @@ def _check(idx, w, x, y, out_x, out, cap):
     np.testing.assert_array_equal(u16(out), exp)
 
 
-def test_graph_capture_and_replay():
+@pytest.mark.parametrize("T", [T, 200])     # count + place, and the one-launch layout
+def test_graph_capture_and_replay(T):
     rng = np.random.default_rng(0)
     h = ep.Handle(T, K, E, A)
     cap = h.capacity
@@ -48,7 +49,7 @@ def test_graph_capture_and_replay():
     y_s = torch.zeros((cap, H), dtype=torch.bfloat16, device="cuda")
     out_x = torch.zeros((cap, H), dtype=torch.bfloat16, device="cuda")
     out = torch.zeros((T, H), dtype=torch.bfloat16, device="cuda")
-    idx0, w0 = _routing(rng)
+    idx0, w0 = _routing(rng, T)
     idx_s.copy_(torch.from_numpy(idx0))
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -59,14 +60,14 @@ def test_graph_capture_and_replay():
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
-    say("graph capture")
+    say("graph capture", T)
     with torch.cuda.graph(g):
         h.layout(idx_s)
         h.dispatch(x_s, out_x=out_x)
         h.combine(y_s, topk_weights=w_s, out=out)
     other = ep.Handle(T, K, E, A)
     for rep in range(5):
-        idx, w = _routing(rng)
+        idx, w = _routing(rng, T)
         x = torch.randn((T, H), generator=torch.Generator().manual_seed(rep)).to(torch.bfloat16)
         y = torch.randn((cap, H), generator=torch.Generator().manual_seed(100 + rep)).to(
             torch.bfloat16)
@@ -76,7 +77,7 @@ def test_graph_capture_and_replay():
         y_s.copy_(y)
         say("graph replay", rep)
         g.replay()
-        other.layout(torch.from_numpy(_routing(rng)[0]).cuda())     # eager work between
+        other.layout(torch.from_numpy(_routing(rng, T)[0]).cuda())     # eager work between
         torch.cuda.synchronize()
         _check(idx, w, x, y, out_x, out, cap)
 
