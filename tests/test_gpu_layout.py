@@ -167,6 +167,27 @@ def test_layout_handle_reuse_and_determinism():
             np.testing.assert_array_equal(dst, first)
 
 
+def test_layout_forms_alternate_on_one_handle():
+    """One handle sized for 70000 tokens lays out batches that take every form
+    in turn - lookback (70000 x 8), count + place over long tiles (40000) and
+    short tiles (8192, 5000), one launch (256, 100) and the empty batch - in
+    an order that switches form on every call, so each form starts from the
+    call tags, counters and status words another form left behind."""
+    K, E, A, Tmax = 8, 64, 4, 70000
+    cap = ep.ep_capacity_bound(Tmax, K, E, A)
+    h = ep.Handle(Tmax, K, E, A, cap)
+    rng = np.random.default_rng(77)
+    for n, T in enumerate([70000, 256, 40000, 100, 8192, 0, 70000, 5000, 256, 40000, 70000]):
+        idx = rng.integers(-1, E, size=(T, K))
+        if T:
+            idx[rng.integers(0, T, size=3), 0] = E + 1          # a few invalid ids
+        say("layout forms on one handle", n, T)
+        lay = oracle.layout(idx, E, A, cap)
+        _, rc, dst, src = gpu_layout(idx, E, A, cap, handle=h)
+        assert_layout_equal(rc, dst, src, lay)
+        assert_rank_equal(rc, idx, E)
+
+
 def test_layout_cumulative_stats():
     rng = np.random.default_rng(12)
     E = 40
