@@ -188,15 +188,16 @@ def test_layout_forms_alternate_on_one_handle():
         assert_rank_equal(rc, idx, E)
 
 
-def test_layout_cumulative_stats():
+@pytest.mark.parametrize("T,K", [(500, 4), (5000, 4), (40000, 8), (70000, 8)])   # every form
+def test_layout_cumulative_stats(T, K):
     rng = np.random.default_rng(12)
     E = 40
-    h = ep.Handle(500, 4, E, 8)
+    h = ep.Handle(T, K, E, 8)
     stats = torch.zeros(E, dtype=torch.int32, device="cuda")
     total = np.zeros(E, np.int64)
     for rep in range(3):
-        idx = rng.integers(-1, E, size=(500, 4))
-        say("layout stats", rep)
+        idx = rng.integers(-1, E, size=(T, K))
+        say("layout stats", T, K, rep)
         h.layout(torch.from_numpy(idx).cuda(), cumulative_stats=stats)
         total += oracle.layout(idx, E, 8, h.capacity).counts
     torch.cuda.synchronize()
