@@ -119,6 +119,32 @@ def test_layout_capacity_error():
     _check(idx, 3, 4, 12)
 
 
+@pytest.mark.parametrize("T", [100, 5000, 40000, 70000])     # every layout form
+def test_layout_capacity_in_every_form(T):
+    """A capacity one row short of what the routing needs is reported as
+    EP_ERR_CAPACITY and dispatch and combine then write nothing; the exact
+    capacity succeeds bit-exactly."""
+    K, E, A, H = 8, 64, 4, 64
+    idx = np.random.default_rng(T + 1).integers(-1, E, size=(T, K))
+    need = oracle.layout(idx, E, A, T * K + A * E).num_expanded
+    for cap in (need - 1, need):
+        say("layout capacity", T, cap, need)
+        lay = oracle.layout(idx, E, A, cap)
+        h, rc, dst, src = gpu_layout(idx, E, A, cap)
+        assert_layout_equal(rc, dst, src, lay)
+        out_x = poison_(torch.empty((cap, H), dtype=torch.bfloat16, device="cuda"))
+        out = poison_(torch.empty((T, H), dtype=torch.bfloat16, device="cuda"))
+        h.dispatch(torch.ones((T, H), dtype=torch.bfloat16, device="cuda"), out_x=out_x,
+                   zero_padding=True)
+        h.combine(torch.ones((cap, H), dtype=torch.bfloat16, device="cuda"), out=out)
+        torch.cuda.synchronize()
+        if cap < need:
+            assert rc["status"] == ep.EP_ERR_CAPACITY
+            assert np.all(u8(out_x) == POISON) and np.all(u8(out) == POISON)
+        else:
+            assert not np.any(u8(out) == POISON)
+
+
 @pytest.mark.parametrize("T", [64, 4096, 70000])     # one-tile, count + place, lookback forms
 def test_layout_timeout_bit_is_sticky(T):
     """Once a layout scan's bounded wait has given up, the handle stays void
