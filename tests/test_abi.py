@@ -302,3 +302,18 @@ def test_quant_validation():
     assert d(h, A16, 128, 0, None, None, A16, 1, 0, None, 0, None) == ep.EP_ERR_NULL
     assert d(h, A16, 128, 0, A16 + 2, A16, A16, 1, 0, None, 0, None) == ep.EP_ERR_MISALIGNED
 
+
+
+def test_binding_constants_match_the_header():
+    """The binding's copies of the header's enums and #defines (status codes,
+    dtypes, scale formats, error bits, scalar indices) have the header's
+    values."""
+    text = open(os.path.join(ROOT, "include", "ep.h")).read()
+    defines = dict(re.findall(r"#define (EP_(?:ERRBIT|SCALAR)_[A-Z_]+) (\d+)u?", text))
+    enums = dict(re.findall(r"\b(EP_[A-Z0-9_]+) = (\d+)", text))
+    checked = 0
+    for name, value in list(defines.items()) + list(enums.items()):
+        if hasattr(ep, name):
+            assert getattr(ep, name) == int(value), name
+            checked += 1
+    assert checked >= 25, checked
