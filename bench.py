@@ -163,6 +163,14 @@ def cpu_baseline(cfg, wl, y_host, min_seconds: float):
     return statistics.median(times), len(times), lay
 
 
+def _oracle_rank_quant(oracle, x_bits, idx, E, row, w):
+    """The quantising rank dispatch as the oracle states it: quantise (fp32
+    scales), then dispatch codes and scales into the rank layout."""
+    q, sf = oracle.quantize_fp8(x_bits, oracle.SF_F32)
+    return oracle.dispatch_rank(q, idx, E, row, idx.shape[0], sf=sf, weights=w,
+                                num_sf_packs=sf.shape[1])
+
+
 def cpu_oracle_rows(cfg, wl, tokens: int):
     """The CPU oracle (single thread, as it stands) on the first `tokens`
     tokens of the workload for every call beyond layout + dispatch +
@@ -210,6 +218,9 @@ def cpu_oracle_rows(cfg, wl, tokens: int):
                                T * 2 * H + V * (H + 4 * P["f32"]) + 4 * T * K),
         "dispatch_quant_ue8m0": (lambda: oracle.dispatch_quant(xq, lay, cap, oracle.SF_UE8M0),
                                  T * 2 * H + V * (H + 4 * P["ue8m0"]) + 4 * T * K),
+        "dispatch_rank_quant_f32": (lambda: _oracle_rank_quant(oracle, xq, idx, E, row, w),
+                                    T * 2 * H + nrecv * (H + 4 * P["f32"]) + 12 * T * K
+                                    + 12 * nrecv * K + 4 * T),
     }
     out = {}
     for name, (fn, nb) in calls.items():
@@ -451,19 +462,29 @@ def main():
                                                     ("ue8m0", ep.EP_SF_UE8M0))}
         sft = {f: torch.empty((T, P[f]), dtype=torch.float32 if f == "f32" else torch.int32,
                               device="cuda") for f in P}
+        nrq = int(rc["num_recv_tokens"])
+        rqx = torch.empty((T, H), dtype=torch.uint8, device="cuda")
+        rqsf = torch.empty((T, P["f32"]), dtype=torch.float32, device="cuda")
+        rqi = torch.empty((T, K), dtype=torch.int64, device="cuda")
+        rqw = torch.empty((T, K), dtype=torch.float32, device="cuda")
         qb = {"quantize_f32": T * 2 * H + T * H + 4 * T * P["f32"],
               "quantize_ue8m0": T * 2 * H + T * H + 4 * T * P["ue8m0"],
               "dispatch_quant_f32": T * 2 * H + V * (H + 4 * P["f32"]) + 4 * T * K,
-              "dispatch_quant_ue8m0": T * 2 * H + V * (H + 4 * P["ue8m0"]) + 4 * T * K}
+              "dispatch_quant_ue8m0": T * 2 * H + V * (H + 4 * P["ue8m0"]) + 4 * T * K,
+              "dispatch_rank_quant_f32": T * 2 * H + nrq * (H + 4 * P["f32"]) + 12 * T * K
+                                         + 12 * nrq * K + 4 * T}
         qcalls = {"quantize_f32": lambda: ep.quantize_fp8(xq, "f32", out_q=qt, out_sf=sft["f32"]),
                   "quantize_ue8m0": lambda: ep.quantize_fp8(xq, "ue8m0", out_q=qt,
                                                             out_sf=sft["ue8m0"]),
                   "dispatch_quant_f32": lambda: h.dispatch_quant(xq, "f32", out_x=qx,
                                                                  out_sf=sfs["f32"]),
                   "dispatch_quant_ue8m0": lambda: h.dispatch_quant(xq, "ue8m0", out_x=qx,
-                                                                   out_sf=sfs["ue8m0"])}
+                                                                   out_sf=sfs["ue8m0"]),
+                  "dispatch_rank_quant_f32": lambda: h.dispatch_rank_quant(
+                      xq, "f32", topk_weights=w, out_x=rqx, out_sf=rqsf, out_topk_idx=rqi,
+                      out_topk_weights=rqw)}
         quant = time_calls(qcalls, qb, args.quant_reps, big)
-        del xq, qx, qt, sfs, sft
+        del xq, qx, qt, sfs, sft, rqx, rqsf, rqi, rqw
     del big
 
     total_bytes = sum(nbytes.values())

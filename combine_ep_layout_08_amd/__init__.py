@@ -26,7 +26,8 @@ __all__ = [
     "ep_workspace_bytes", "ep_handle_init", "ep_layout", "ep_handle_read_counts",
     "ep_handle_import", "ep_dispatch", "ep_combine", "ep_status_str", "ep_handle_sizeof",
     "ep_time_next_call", "time_next_call", "ep_combine_backward", "ep_dispatch_backward",
-    "ep_dispatch_rank", "ep_combine_rank", "ep_tma_aligned_rows", "ep_sf_packs",
+    "ep_dispatch_rank", "ep_dispatch_rank_quant", "ep_combine_rank", "ep_tma_aligned_rows",
+    "ep_sf_packs",
     "ep_quantize_fp8", "ep_dispatch_quant", "EP_SF_F32", "EP_SF_UE8M0", "quantize_fp8",
 ]
 
@@ -100,6 +101,8 @@ _SIGNATURES = {
     "ep_combine": (ctypes.c_int, [_HP, _P, ctypes.c_int, _I32, _P, _P, _P, _P, _P, _P]),
     "ep_dispatch_rank": (ctypes.c_int, [_HP, _P, ctypes.c_int, _I32, _P, _I64, _I64, _I32, _P,
                                         _P, _P, _I64, _I64, _P, _P, _P]),
+    "ep_dispatch_rank_quant": (ctypes.c_int, [_HP, _P, _I32, ctypes.c_int, _P, _P, _P, _I64,
+                                              _I64, _P, _P, _P]),
     "ep_combine_rank": (ctypes.c_int, [_HP, _P, _I32, _P, _P, _P, _P]),
     "ep_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "ep_time_next_call": (ctypes.c_int, [_P, _P]),
@@ -211,6 +214,13 @@ def ep_dispatch_rank(h: ep_handle, x_ptr, x_dtype, hidden, sf_ptr, sf_ts, sf_hs,
     return lib().ep_dispatch_rank(ctypes.byref(h), x_ptr, x_dtype, hidden, sf_ptr, sf_ts, sf_hs,
                                   num_sf_packs, w_ptr, out_x_ptr, out_sf_ptr, out_ts, out_hs,
                                   out_idx_ptr, out_w_ptr, stream)
+
+
+def ep_dispatch_rank_quant(h: ep_handle, x_ptr, hidden, fmt, w_ptr, out_x_ptr, out_sf_ptr,
+                           out_ts, out_hs, out_idx_ptr, out_w_ptr, stream) -> int:
+    return lib().ep_dispatch_rank_quant(ctypes.byref(h), x_ptr, hidden, fmt, w_ptr, out_x_ptr,
+                                        out_sf_ptr, out_ts, out_hs, out_idx_ptr, out_w_ptr,
+                                        stream)
 
 
 def ep_combine_rank(h: ep_handle, x_ptr, hidden, bias0_ptr, bias1_ptr, out_ptr, stream) -> int:
@@ -681,6 +691,48 @@ class Handle:
                                 _ptr(out_sf),
                                 o_ts, o_hs, _ptr(out_topk_idx), _ptr(out_topk_weights),
                                 _stream()), "ep_dispatch_rank")
+        return out_x, out_sf, out_topk_idx, out_topk_weights
+
+    def dispatch_rank_quant(self, x: torch.Tensor, scale_format="f32",
+                            topk_weights: Optional[torch.Tensor] = None, out_x=None, out_sf=None,
+                            out_topk_idx=None, out_topk_weights=None,
+                            col_major_sf: bool = False):
+        """Quantise bf16 x [T, H] to FP8 and dispatch into the rank layout in
+        one pass.  Returns (codes uint8 [max_tokens, H], scales [max_tokens,
+        packs], out_topk_idx, out_topk_weights)."""
+        T, K = self.h.num_tokens, self.h.num_topk
+        M = self.h.max_tokens
+        _dev(x, "x")
+        _need(x.dtype == torch.bfloat16 and x.dim() == 2 and x.shape[0] == T,
+              "x must be bf16 [num_tokens, H]")
+        H = x.shape[1]
+        fmt = _sf_format(scale_format)
+        packs = ep_sf_packs(H, fmt)
+        _need(packs > 0, "hidden must be a positive multiple of 128")
+        if out_x is None:
+            out_x = torch.empty((M, H), dtype=torch.uint8, device=x.device)
+        _dev(out_x, "out_x")
+        _need(out_x.dtype in (torch.uint8, torch.float8_e4m3fn) and tuple(out_x.shape) == (M, H),
+              "out_x must be FP8 codes [max_tokens, H]")
+        out_sf = _quant_sf_out(out_sf, M, packs, fmt, col_major_sf, x.device)
+        o_ts, o_hs = out_sf.stride()
+        idx_dtype = torch.int64 if self.h.topk_idx_dtype == EP_I64 else torch.int32
+        if out_topk_idx is None:
+            out_topk_idx = torch.empty((M, K), dtype=idx_dtype, device=x.device)
+        _need(out_topk_idx.dtype == idx_dtype and tuple(out_topk_idx.shape) == (M, K),
+              "out_topk_idx must be [max_tokens, K] of the layout's id dtype")
+        if out_topk_weights is None:
+            out_topk_weights = torch.empty((M, K), dtype=torch.float32, device=x.device)
+        _need(out_topk_weights.dtype == torch.float32 and tuple(out_topk_weights.shape) == (M, K),
+              "out_topk_weights must be fp32 [max_tokens, K]")
+        if topk_weights is not None:
+            _dev(topk_weights, "topk_weights")
+            _need(topk_weights.dtype == torch.float32 and tuple(topk_weights.shape) == (T, K),
+                  "topk_weights must be fp32 [T, K]")
+        _check(ep_dispatch_rank_quant(self.h, _ptr(x), H, fmt, _ptr(topk_weights), _ptr(out_x),
+                                      _ptr(out_sf), o_ts, o_hs, _ptr(out_topk_idx),
+                                      _ptr(out_topk_weights), _stream()),
+               "ep_dispatch_rank_quant")
         return out_x, out_sf, out_topk_idx, out_topk_weights
 
     def combine_rank(self, x: torch.Tensor, bias_0=None, bias_1=None, out=None) -> torch.Tensor:

@@ -600,6 +600,58 @@ ep_status ep_dispatch_rank(const ep_handle *h, const void *x, ep_dtype x_dtype, 
     return hip_status(ep::launch_dispatch_rank(a, stream, ev));
 }
 
+ep_status ep_dispatch_rank_quant(const ep_handle *h, const void *x, int32_t hidden,
+                                 ep_sf_format fmt, const float *topk_weights, void *out_x,
+                                 void *out_sf, int64_t out_sf_token_stride,
+                                 int64_t out_sf_hidden_stride, void *out_topk_idx,
+                                 float *out_topk_weights, hipStream_t stream) {
+    const ep::CallEvents ev = take_events();
+    if (!h) return EP_ERR_NULL;
+    if (!handle_ready(h)) return EP_ERR_WORKSPACE;
+    if (!h->laid_out) return EP_ERR_NOT_LAID_OUT;
+    const bool rows = h->num_tokens > 0;
+    ep::DispatchArgs a{};
+    const ep_status st = quant_args(x, hidden, fmt, out_x, out_sf, out_sf_token_stride,
+                                    out_sf_hidden_stride, rows, rows, &a);
+    if (st != EP_OK) return st;
+    const bool meta = out_topk_idx || out_topk_weights;
+    if (meta && rows && !h->topk_idx) return EP_ERR_NULL;
+    if (!aligned(topk_weights, 4) || !aligned(out_topk_weights, 4) ||
+        !aligned(out_topk_idx, h->topk_idx_dtype == EP_I64 ? 8 : 4))
+        return EP_ERR_MISALIGNED;
+    if (!rows) return EP_OK;
+    // Codes and packs: the quantising dispatch with one destination per
+    // token, its rank row (or none); like the copying rank dispatch it stops
+    // only on a scan timeout (the rank layout does not depend on capacity).
+    a.num_tokens = h->num_tokens;
+    a.num_topk = 1;
+    a.alignment = 1;
+    a.capacity = h->num_tokens;             // rank rows lie in [0, num_tokens)
+    a.dst = h->recv_row;
+    a.scalars = h->scalars;
+    a.stop_bits = EP_ERRBIT_SCAN_TIMEOUT;
+    ep::CallEvents first = ev;
+    if (meta) first.stop = nullptr;
+    const hipError_t e = ep::launch_dispatch(a, stream, first);
+    if (e != hipSuccess || !meta) return hip_status(e);
+    // Received top-k ids and weights: the rank dispatch with empty rows.
+    ep::RankArgs r{};
+    r.row_vecs = 0;
+    r.num_tokens = h->num_tokens;
+    r.num_topk = h->num_topk;
+    r.num_experts = h->num_experts;
+    r.recv_row = h->recv_row;
+    r.scalars = h->scalars;
+    r.topk_idx = h->topk_idx;
+    r.idx_is_i64 = h->topk_idx_dtype == EP_I64;
+    r.w = topk_weights;
+    r.out_idx = out_topk_idx;
+    r.out_w = out_topk_weights;
+    ep::CallEvents second = ev;
+    second.start = nullptr;
+    return hip_status(ep::launch_dispatch_rank(r, stream, second));
+}
+
 ep_status ep_combine_rank(const ep_handle *h, const void *x, int32_t hidden, const void *bias_0,
                           const void *bias_1, void *out, hipStream_t stream) {
     const ep::CallEvents ev = take_events();

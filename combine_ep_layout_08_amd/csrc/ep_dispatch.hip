@@ -379,7 +379,7 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_kernel(DispatchArgs
                                                                    int64_t token_units,
                                                                    int64_t total_units,
                                                                    int gap_chunks, int passes) {
-    if (a.scalars && (a.scalars[EP_SCALAR_ERROR_BITS] & EP_ERRBIT_FATAL)) return;
+    if (a.scalars && (a.scalars[EP_SCALAR_ERROR_BITS] & a.stop_bits)) return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     for (int64_t u = blockIdx.x; u < total_units; u += gridDim.x) {
         if (u < token_units) {

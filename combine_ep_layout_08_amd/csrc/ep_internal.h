@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/ep.h"
+
 namespace ep {
 
 // 16-byte vector as a native clang vector (usable with the nontemporal
@@ -123,6 +125,7 @@ struct DispatchArgs {
     float *out_w;
     bool zero_padding;
     int32_t quant;               // 0: copy x; EP_SF_F32 + 1 / EP_SF_UE8M0 + 1: quantise bf16 x
+    uint32_t stop_bits = EP_ERRBIT_FATAL;  // error bits in *scalars that make it write nothing
 };
 
 struct CombineArgs {

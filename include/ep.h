@@ -21,8 +21,8 @@
  *              biases, and round to bf16.
  * and around them: the non-expanded ("rank") layout (each received token
  * once) with its dispatch and combine, the backward of combine and of
- * dispatch, and an FP8 quantiser (alone or fused into dispatch) with fp32 or
- * packed UE8M0 scales.
+ * dispatch, and an FP8 quantiser (alone, or fused into the expanded or the
+ * rank dispatch) with fp32 or packed UE8M0 scales.
  *
  * Memory ownership: the library never allocates, frees or keeps memory.  All
  * device buffers (workspace, inputs, outputs) belong to the caller and must
@@ -343,6 +343,23 @@ ep_status ep_dispatch_rank(const ep_handle *h, const void *x, ep_dtype x_dtype,
                            int64_t out_sf_token_stride, int64_t out_sf_hidden_stride,
                            void *out_topk_idx, float *out_topk_weights,
                            hipStream_t stream);
+
+/*
+ * Quantising rank dispatch: ep_quantize_fp8 of bf16 x fused with
+ * ep_dispatch_rank of the codes and packs [Ch7 §7.4 rank layout, §7.3 FP8
+ * data with scale packs and the received top-k metadata].  Row recv_row[t]
+ * of out_x ([max_tokens, hidden] E4M3FN codes, 16-byte aligned) gets token
+ * t's codes and row recv_row[t] of out_sf ([max_tokens,
+ * ep_sf_packs(hidden, fmt)] packs, any strides) its packs; out_topk_idx and
+ * out_topk_weights (NULL or as in ep_dispatch_rank) get the received top-k
+ * metadata.  hidden % 128 == 0.  Rows at or past num_recv_tokens are not
+ * written; with no tokens in the layout every buffer may be NULL.
+ */
+ep_status ep_dispatch_rank_quant(const ep_handle *h, const void *x, int32_t hidden,
+                                 ep_sf_format fmt, const float *topk_weights, void *out_x,
+                                 void *out_sf, int64_t out_sf_token_stride,
+                                 int64_t out_sf_hidden_stride, void *out_topk_idx,
+                                 float *out_topk_weights, hipStream_t stream);
 
 /*
  * Combine from the rank layout [Ch8 §8.1: reduce back to the source token,

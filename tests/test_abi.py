@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported():
     names = declared_functions()
-    assert len(names) == 19, names
+    assert len(names) == 20, names
     for n in names:
         assert hasattr(ep.lib(), n), n
         assert n in ep._SIGNATURES, f"binding lacks {n}"
@@ -301,6 +301,19 @@ def test_quant_validation():
     assert d(h, A16, 128, 2, None, A16, A16, 1, 0, None, 0, None) == ep.EP_ERR_DTYPE
     assert d(h, A16, 128, 0, None, None, A16, 1, 0, None, 0, None) == ep.EP_ERR_NULL
     assert d(h, A16, 128, 0, A16 + 2, A16, A16, 1, 0, None, 0, None) == ep.EP_ERR_MISALIGNED
+    r = ep.ep_dispatch_rank_quant
+    assert r(_fake_handle(laid_out=0), A16, 128, 0, None, A16, A16, 1, 0, None, None,
+             None) == ep.EP_ERR_NOT_LAID_OUT
+    assert r(h, A16, 120, 0, None, A16, A16, 1, 0, None, None, None) == ep.EP_ERR_MISALIGNED
+    assert r(h, A16, 128, 5, None, A16, A16, 1, 0, None, None, None) == ep.EP_ERR_DTYPE
+    assert r(h, None, 128, 0, None, A16, A16, 1, 0, None, None, None) == ep.EP_ERR_NULL
+    assert r(h, A16, 128, 0, None, A16, None, 1, 0, None, None, None) == ep.EP_ERR_NULL
+    assert r(h, A16, 128, 0, None, A16, A16, -1, 0, None, None, None) == ep.EP_ERR_SHAPE
+    assert r(h, A16, 128, 0, None, A16, A16, 1, 0, A16 + 4, None, None) == ep.EP_ERR_MISALIGNED
+    assert r(h, A16, 128, 0, A16 + 2, A16, A16, 1, 0, None, None, None) == ep.EP_ERR_MISALIGNED
+    no_ids = _fake_handle()
+    no_ids.topk_idx = None                        # ids needed for the received metadata
+    assert r(no_ids, A16, 128, 0, None, A16, A16, 1, 0, A16, None, None) == ep.EP_ERR_NULL
 
 
 

@@ -235,11 +235,13 @@ def test_empty_batch_every_call():
         gy, gw, gb = h.combine_backward(xb, y=y, want_grad_weights=True, want_grad_bias=True)
         gx, gxw = h.dispatch_backward(y, want_grad_weights=True)
         r = h.dispatch_rank(xb)
+        rq = h.dispatch_rank_quant(xb, "ue8m0")
         out_r = h.combine_rank(xb)
         q, qs = ep.quantize_fp8(xb)
         torch.cuda.synchronize()
         assert out.shape == (0, H) and gx.shape == (0, H) and out_r.shape == (0, H)
         assert gw.shape == (0, K) and gxw.shape == (0, K) and r[0].shape == (0, H)
+        assert rq[0].shape == (0, H) and rq[1].shape == (0, ep.ep_sf_packs(H, ep.EP_SF_UE8M0))
         assert q.shape == (0, H) and qs.shape == (0, H // 128)
         assert np.all(gb.cpu().numpy() == 0)
         for t in (out_x, out_w, o8, osf, oq, oqs):

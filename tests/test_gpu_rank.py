@@ -67,6 +67,59 @@ def test_dispatch_rank(fp8, H, idx32):
     assert np.all(u8(out_w)[n:] == POISON)
 
 
+@pytest.mark.parametrize("name,fmt", [("f32", oracle.SF_F32), ("ue8m0", oracle.SF_UE8M0)])
+@pytest.mark.parametrize("H,idx32,col,weights", [(1152, False, False, True),
+                                                 (7168, True, True, True),
+                                                 (2176, False, True, False)])
+def test_dispatch_rank_quant(name, fmt, H, idx32, col, weights):
+    """Quantising rank dispatch: the oracle's quantiser followed by its rank
+    dispatch of the codes and packs, bit-exact, with empty tokens, invalid
+    ids, row- or column-major scales (2176 channels: a partial UE8M0 pack),
+    and unwritten rows poison-checked."""
+    rng = np.random.default_rng(H * 3 + fmt + idx32)
+    T, K, E = 700, 6, 20
+    idx = np.where(rng.random((T, K)) < 0.55, -1, rng.integers(-2, E + 2, size=(T, K)))
+    w = rng.random((T, K), dtype=np.float32) if weights else None
+    h, rc, _, _ = gpu_layout(idx, E, 4, T * K + 4 * E,
+                             idx_dtype=torch.int32 if idx32 else torch.int64)
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    x *= (10.0 ** rng.integers(-6, 5, size=(T, H // 128, 1))).repeat(128, axis=2).reshape(T, H)
+    xb = torch.from_numpy(x).to(torch.bfloat16)
+    P = ep.ep_sf_packs(H, fmt)
+    out_x = poison_(torch.empty((T, H), dtype=torch.uint8, device="cuda"))
+    if col:
+        store = poison_(torch.empty((P, ep.ep_tma_aligned_rows(T)), dtype=torch.int32,
+                                    device="cuda"))
+        out_sf = store[:, :T].t()
+    else:
+        out_sf = poison_(torch.empty((T, P), dtype=torch.int32, device="cuda"))
+    if name == "f32":
+        out_sf = out_sf.view(torch.float32)
+    out_i = poison_(torch.empty((T, K), dtype=torch.int32 if idx32 else torch.int64,
+                                device="cuda"))
+    out_w = poison_(torch.empty((T, K), dtype=torch.float32, device="cuda"))
+    say("dispatch rank quant", name, H, idx32, col, weights)
+    h.dispatch_rank_quant(xb.cuda(), name,
+                          topk_weights=None if w is None else torch.from_numpy(w).cuda(),
+                          out_x=out_x, out_sf=out_sf, out_topk_idx=out_i, out_topk_weights=out_w)
+    torch.cuda.synchronize()
+    q, sf = oracle.quantize_fp8(u16(xb), fmt)
+    row, _, n = oracle.rank_layout(idx, E)
+    pf = np.frombuffer(bytes([POISON] * 4), np.float32)[0]
+    ox = np.full((T, H), POISON, np.uint8)
+    osf = np.full((T, P), np.uint32(0xA5A5A5A5), np.uint32)
+    oi = np.full((T, K), np.frombuffer(bytes([POISON] * 8), np.int64)[0], np.int64)
+    ow = np.full((T, K), pf, np.float32)
+    oracle.dispatch_rank(q, idx, E, row, T, sf=sf, weights=w, out_x=ox, out_sf=osf, out_idx=oi,
+                         out_w=ow, num_sf_packs=P)
+    np.testing.assert_array_equal(u8(out_x), ox)
+    np.testing.assert_array_equal(out_sf.contiguous().view(torch.int32).cpu().numpy()
+                                  .view(np.uint32), osf)
+    np.testing.assert_array_equal(out_i.cpu().numpy().astype(np.int64)[:n], oi[:n])
+    np.testing.assert_array_equal(out_w.cpu().numpy()[:n], ow[:n])
+    assert np.all(u8(out_w)[n:] == POISON)
+
+
 def test_dispatch_rank_packed_scales_column_major():
     """Rank dispatch with int32 scale packs into a column-major, 16-byte
     aligned scale buffer, bit-exact with the oracle."""
