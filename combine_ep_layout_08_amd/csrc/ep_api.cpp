@@ -620,36 +620,28 @@ ep_status ep_dispatch_rank_quant(const ep_handle *h, const void *x, int32_t hidd
         !aligned(out_topk_idx, h->topk_idx_dtype == EP_I64 ? 8 : 4))
         return EP_ERR_MISALIGNED;
     if (!rows) return EP_OK;
-    // Codes and packs: the quantising dispatch with one destination per
-    // token, its rank row (or none); like the copying rank dispatch it stops
-    // only on a scan timeout (the rank layout does not depend on capacity).
+    // The quantising dispatch with one destination per token, its rank row
+    // (or none); the wave that quantises a row's first pass also writes the
+    // row's received ids and weights.  Like the copying rank dispatch it
+    // stops only on a scan timeout (the rank layout does not depend on
+    // capacity).
     a.num_tokens = h->num_tokens;
     a.num_topk = 1;
+    a.num_experts = h->num_experts;
     a.alignment = 1;
     a.capacity = h->num_tokens;             // rank rows lie in [0, num_tokens)
     a.dst = h->recv_row;
     a.scalars = h->scalars;
     a.stop_bits = EP_ERRBIT_SCAN_TIMEOUT;
-    ep::CallEvents first = ev;
-    if (meta) first.stop = nullptr;
-    const hipError_t e = ep::launch_dispatch(a, stream, first);
-    if (e != hipSuccess || !meta) return hip_status(e);
-    // Received top-k ids and weights: the rank dispatch with empty rows.
-    ep::RankArgs r{};
-    r.row_vecs = 0;
-    r.num_tokens = h->num_tokens;
-    r.num_topk = h->num_topk;
-    r.num_experts = h->num_experts;
-    r.recv_row = h->recv_row;
-    r.scalars = h->scalars;
-    r.topk_idx = h->topk_idx;
-    r.idx_is_i64 = h->topk_idx_dtype == EP_I64;
-    r.w = topk_weights;
-    r.out_idx = out_topk_idx;
-    r.out_w = out_topk_weights;
-    ep::CallEvents second = ev;
-    second.start = nullptr;
-    return hip_status(ep::launch_dispatch_rank(r, stream, second));
+    if (meta) {
+        a.meta_idx = h->topk_idx;
+        a.meta_i64 = h->topk_idx_dtype == EP_I64;
+        a.meta_topk = h->num_topk;
+        a.meta_w = topk_weights;
+        a.out_meta_idx = out_topk_idx;
+        a.out_meta_w = out_topk_weights;
+    }
+    return hip_status(ep::launch_dispatch(a, stream, ev));
 }
 
 ep_status ep_combine_rank(const ep_handle *h, const void *x, int32_t hidden, const void *bias_0,

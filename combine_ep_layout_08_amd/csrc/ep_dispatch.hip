@@ -303,10 +303,28 @@ __device__ inline u32x4 quantise16(const u32x4 lo, const u32x4 hi, uint32_t *pac
     return u32x4{w[0], w[1], w[2], w[3]};
 }
 
+// Received top-k ids and weights of token t at its rank row r (lanes below
+// meta_topk): an id outside [0, num_experts) is written as -1 with weight 0.
+__device__ inline void rank_meta(const DispatchArgs &a, int64_t t, int64_t r, int lane) {
+    const int K = a.meta_topk;
+    if (lane >= K) return;
+    const int64_t e = a.meta_i64 ? static_cast<const int64_t *>(a.meta_idx)[t * K + lane]
+                                 : static_cast<const int32_t *>(a.meta_idx)[t * K + lane];
+    const bool valid = e >= 0 && e < a.num_experts;
+    if (a.out_meta_idx) {
+        if (a.meta_i64) static_cast<int64_t *>(a.out_meta_idx)[r * K + lane] = valid ? e : -1;
+        else static_cast<int32_t *>(a.out_meta_idx)[r * K + lane] =
+                 valid ? static_cast<int32_t>(e) : -1;
+    }
+    if (a.out_meta_w)
+        a.out_meta_w[r * K + lane] = valid ? (a.meta_w ? a.meta_w[t * K + lane] : 1.0f) : 0.0f;
+}
+
 // Quantise one pass of a token's row (one wave: code vectors [c0, c0 +
 // 64*QPL)) and store codes and scale packs to every valid slot's row; pass 0
-// also stores the weight.  Without a slot index (plain quantiser) the
-// token's own row t is the one destination.
+// also stores the weight, or for a rank row the received ids and weights.
+// Without a slot index (plain quantiser) the token's own row t is the one
+// destination.
 template <int QPL, int MODE>
 __device__ inline void quant_token(const DispatchArgs &a, int64_t t, int64_t pass, int lane) {
     const int64_t V = a.row_vecs;                 // 16-byte code vectors per row
@@ -316,6 +334,10 @@ __device__ inline void quant_token(const DispatchArgs &a, int64_t t, int64_t pas
                            : (lane == 0 ? static_cast<int32_t>(t) : -1);
     if (my_dst >= a.capacity) my_dst = -1;
     if (pass == 0 && a.out_w && my_dst >= 0) a.out_w[my_dst] = a.w ? a.w[t * K + lane] : 1.0f;
+    if (pass == 0 && (a.out_meta_idx || a.out_meta_w)) {
+        const int32_t r = __builtin_amdgcn_readlane(my_dst, 0);   // lane 0 holds the one row
+        if (r >= 0) rank_meta(a, t, r, lane);
+    }
     const u32x4 *src = static_cast<const u32x4 *>(a.x) + t * 2 * V;
     const int64_t c0 = pass * 64 * QPL;
     u32x4 v[QPL];

@@ -126,6 +126,15 @@ struct DispatchArgs {
     bool zero_padding;
     int32_t quant;               // 0: copy x; EP_SF_F32 + 1 / EP_SF_UE8M0 + 1: quantise bf16 x
     uint32_t stop_bits = EP_ERRBIT_FATAL;  // error bits in *scalars that make it write nothing
+    // Rank-row metadata (quantising rank dispatch, num_topk 1): the token's
+    // meta_topk ids (valid ones, else -1) and weights (valid ones, else 0)
+    // go to its one destination row; null outputs skip them.
+    const void *meta_idx = nullptr;
+    bool meta_i64 = false;
+    int32_t meta_topk = 0;
+    const float *meta_w = nullptr;
+    void *out_meta_idx = nullptr;
+    float *out_meta_w = nullptr;
 };
 
 struct CombineArgs {
