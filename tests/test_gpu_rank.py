@@ -120,6 +120,60 @@ def test_dispatch_rank_quant(name, fmt, H, idx32, col, weights):
     assert np.all(u8(out_w)[n:] == POISON)
 
 
+@pytest.mark.parametrize("idx32", [False, True])
+@pytest.mark.parametrize("give_ids,give_weights", [(True, True), (True, False), (False, True),
+                                                   (False, False)])
+def test_dispatch_rank_quant_limits(idx32, give_ids, give_weights):
+    """Quantising rank dispatch at the limits (E = 1024, K = 64: every lane of
+    the quantising wave writes an id and a weight) through the C ABI, with
+    either metadata output NULL: the given ones match the oracle bit for bit,
+    the codes and scales do too, and nothing else is written."""
+    rng = np.random.default_rng(641 + 2 * idx32 + give_ids + 4 * give_weights)
+    T, K, E, H = 300, 64, 1024, 512
+    idx = np.where(rng.random((T, K)) < 0.5, -1, rng.integers(-3, E + 3, size=(T, K)))
+    idx[:7] = -1                                       # tokens with no slot
+    w = rng.random((T, K), dtype=np.float32)
+    h, _, _, _ = gpu_layout(idx, E, 1, T * K, idx_dtype=torch.int32 if idx32 else torch.int64)
+    xb = _bf16((T, H), 642)
+    fmt = oracle.SF_F32
+    P = ep.ep_sf_packs(H, fmt)
+    out_x = poison_(torch.empty((T, H), dtype=torch.uint8, device="cuda"))
+    out_sf = poison_(torch.empty((T, P), dtype=torch.int32, device="cuda"))
+    out_i = poison_(torch.empty((T, K), dtype=torch.int32 if idx32 else torch.int64,
+                                device="cuda"))
+    out_w = poison_(torch.empty((T, K), dtype=torch.float32, device="cuda"))
+    x = xb.cuda()
+    wt = torch.from_numpy(w).cuda()
+    say("dispatch rank quant limits", idx32, give_ids, give_weights)
+    st = ep.ep_dispatch_rank_quant(h.h, x.data_ptr(), H, ep.EP_SF_F32, wt.data_ptr(),
+                                   out_x.data_ptr(), out_sf.data_ptr(), P, 1,
+                                   out_i.data_ptr() if give_ids else None,
+                                   out_w.data_ptr() if give_weights else None,
+                                   torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert st == ep.EP_OK
+    q, sf = oracle.quantize_fp8(u16(xb), fmt)
+    row, _, n = oracle.rank_layout(idx, E)
+    ox = np.full((T, H), POISON, np.uint8)
+    osf = np.full((T, P), np.uint32(0xA5A5A5A5), np.uint32)
+    oi = np.zeros((T, K), np.int64)
+    ow = np.zeros((T, K), np.float32)
+    oracle.dispatch_rank(q, idx, E, row, T, sf=sf, weights=w, out_x=ox, out_sf=osf, out_idx=oi,
+                         out_w=ow, num_sf_packs=P)
+    np.testing.assert_array_equal(u8(out_x), ox)
+    np.testing.assert_array_equal(out_sf.cpu().numpy().view(np.uint32), osf)
+    if give_ids:
+        np.testing.assert_array_equal(out_i.cpu().numpy().astype(np.int64)[:n], oi[:n])
+        assert np.all(u8(out_i)[n:] == POISON)
+    else:
+        assert np.all(u8(out_i) == POISON)
+    if give_weights:
+        np.testing.assert_array_equal(out_w.cpu().numpy()[:n], ow[:n])
+        assert np.all(u8(out_w)[n:] == POISON)
+    else:
+        assert np.all(u8(out_w) == POISON)
+
+
 def test_dispatch_rank_packed_scales_column_major():
     """Rank dispatch with int32 scale packs into a column-major, 16-byte
     aligned scale buffer, bit-exact with the oracle."""
