@@ -29,10 +29,17 @@ constexpr int kGapRowsPerBlock = kWavesPerBlock;
 // 16-byte vectors, to every slot; EP_DISPATCH_MAX_VPL caps VPL (a smaller
 // cap spreads a token over more waves: 1 measured equal on the FP8 prefill
 // dispatch and 9 % faster on 32768 bf16 rows of 7168 than one pass per
-// token).  EP_DISPATCH_NT_STORE streams the row stores past the caches
-// (measured 2-6 % slower).
+// token).  Cache hints of the row copy: non-temporal stores measured 2-6 %
+// slower (57 us against 47 on the FP8 prefill rows together with
+// non-temporal loads).  Non-temporal loads of the token rows with ordinary
+// stores (EP_DISPATCH_NT_LOAD) took the 4096-token FP8 prefill dispatch from
+// 47.0 to 44.4 us but were 2-3 % slower at every other size measured (FP8
+// rows of 8192-32768 tokens, bf16 rows of 2048-32768 tokens), so they are off.
 #ifndef EP_DISPATCH_MAX_VPL
 #define EP_DISPATCH_MAX_VPL 1
+#endif
+#ifndef EP_DISPATCH_NT_LOAD
+#define EP_DISPATCH_NT_LOAD 0
 #endif
 #ifndef EP_DISPATCH_NT_STORE
 #define EP_DISPATCH_NT_STORE 0
@@ -90,7 +97,7 @@ __device__ inline void dispatch_token(const DispatchArgs &a, int64_t t, int64_t 
 #pragma unroll
     for (int q = 0; q < VPL; ++q) {
         const int64_t c = c0 + q * 64 + lane;
-        if (c < V) v[q] = src[c];
+        if (c < V) v[q] = EP_DISPATCH_NT_LOAD ? __builtin_nontemporal_load(src + c) : src[c];
     }
     for (int k = 0; k < K; ++k) {
         const int32_t r = __builtin_amdgcn_readlane(my_dst, k);

@@ -7,9 +7,12 @@
 // bias_0 and bias_1.  At one rank a token is received when it has a valid
 // slot; ep_layout gives each such token its row (recv_row) in token order.
 //
-// dispatch_rank: one wave per token copies the row (16-byte vectors), its
-// FP8 scales and its top-k ids / weights (-1 / 0 on empty or invalid slots)
-// to row recv_row[t].
+// dispatch_rank: one wave per token copies the row (16-byte vectors,
+// non-temporal stores: faster at every size measured, e.g. 4096 FP8 rows of
+// 7168 11.7-12.8 -> 9.9-10.2 us, 32768 bf16 rows 199 -> 178 us, 32768 FP8
+// rows 107 -> 72 us; non-temporal loads measured slower), its FP8 scales
+// and its top-k ids / weights (-1 / 0 on empty or invalid slots) to row
+// recv_row[t].
 // combine_rank: one thread per 16-byte output vector; the token's row (or
 // +0.0), then bias_0, then bias_1, in binary32, rounded to bf16 (RNE).
 #include "ep_internal.h"
@@ -60,7 +63,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_rank_kernel(RankArgs a) {
 #pragma unroll
         for (int q = 0; q < VPL; ++q) {
             const int64_t c = c0 + q * 64 + lane;
-            if (c < V) dst[c] = v[q];
+            if (c < V) __builtin_nontemporal_store(v[q], dst + c);
         }
     }
     for (int j = lane; j < a.num_sf; j += 64)
