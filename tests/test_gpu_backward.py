@@ -14,7 +14,8 @@ import combine_ep_layout_08_amd as ep
 import ep_workloads as W
 import oracle
 from tests import bruteforce as BF
-from tests.gpu_util import POISON, assert_rows_equal, gpu_layout, needs_gpu, poison_, say, u16
+from tests.gpu_util import (POISON, assert_layout_equal, assert_rows_equal, gpu_layout, needs_gpu,
+                            poison_, say, u16)
 from tests.tolerance import check_sum
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
@@ -42,8 +43,9 @@ _check_sum = check_sum
 def _run(idx, E, A, cap, g, y, w=None, b=None, want_bias=True, want_y=True, want_w=True):
     T, K = idx.shape
     H = g.shape[1]
-    h, rc, dst, _ = gpu_layout(idx, E, A, cap)
+    h, rc, dst, src = gpu_layout(idx, E, A, cap)
     lay = oracle.layout(idx, E, A, cap)
+    assert_layout_equal(rc, dst, src, lay)      # a gradient mismatch below is then not the layout's
     gy = poison_(torch.empty((cap, H), dtype=torch.bfloat16, device="cuda")) if want_y else None
     wd = None if w is None else torch.from_numpy(w).cuda()
     bd = None if b is None else b.cuda()
@@ -127,10 +129,11 @@ def test_dispatch_backward():
     go = wl.y                                        # any bf16 [capacity, H]
     gwr = torch.randn(cap, generator=torch.Generator().manual_seed(5))
     say("dispatch backward")
-    h, rc, dst, _ = gpu_layout(wl.topk_idx, cfg.experts, cfg.alignment, cap)
+    h, rc, dst, src = gpu_layout(wl.topk_idx, cfg.experts, cfg.alignment, cap)
+    lay = oracle.layout(wl.topk_idx, cfg.experts, cfg.alignment, cap)
+    assert_layout_equal(rc, dst, src, lay)      # a grad_x mismatch below is then not the layout's
     gx, gw = h.dispatch_backward(go.cuda(), grad_out_w=gwr.cuda(), want_grad_weights=True)
     torch.cuda.synchronize()
-    lay = oracle.layout(wl.topk_idx, cfg.experts, cfg.alignment, cap)
     o_gx, o_gw = oracle.dispatch_backward(u16(go), wl.topk_idx, lay.dst, gwr.numpy())
     assert_rows_equal(u16(gx), o_gx, "grad_x")
     np.testing.assert_array_equal(gw.cpu().numpy(), o_gw)

@@ -13,7 +13,8 @@ import torch
 import combine_ep_layout_08_amd as ep
 import ep_workloads as W
 import oracle
-from tests.gpu_util import assert_rows_equal, gpu_layout, needs_gpu, POISON, poison_, say, u16, u8
+from tests.gpu_util import (assert_layout_equal, assert_rows_equal, gpu_layout, needs_gpu, POISON,
+                            poison_, say, u16, u8)
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
 
@@ -33,9 +34,10 @@ def _gpu_combine(h, y, w=None, bias=None):
 
 
 def _check(idx, E, A, cap, y, w=None, bias=None):
-    h, rc, dst, _ = gpu_layout(idx, E, A, cap)
-    got = _gpu_combine(h, y, w, bias)
+    h, rc, dst, src = gpu_layout(idx, E, A, cap)
     lay = oracle.layout(idx, E, A, cap)
+    assert_layout_equal(rc, dst, src, lay)      # a combine mismatch below is then not the layout's
+    got = _gpu_combine(h, y, w, bias)
     exp = oracle.combine(u16(y), idx, lay.dst, w, None if bias is None else u16(bias))
     assert_rows_equal(got, exp, "combine")
     return got
