@@ -314,20 +314,29 @@ def main():
         if scratch is not None:
             scratch.sum()
 
+    # The step's three calls, validated and marshalled once (bound calls:
+    # the same entry points and kernels, about 3 us of host time per call
+    # instead of 5-6, so small batches are not bound by the Python side).
+    h.layout(idx)
+    layout_call = h.bind_layout(idx)
+    dispatch_call = h.bind_dispatch(wl.x, sf=wl.sf, zero_padding=cfg.zero_padding,
+                                    out_x=out_x, out_sf=out_sf)
+    combine_call = h.bind_combine(wl.y, topk_weights=w, bias=wl.bias, out=out)
+
     def step(ev=None):
         # ev: six events; each pair is stamped on the kernels of one call.
         flush()
         if ev is not None:
             ep.time_next_call(ev[0], ev[1])
-        h.layout(idx)
+        layout_call()
         flush()
         if ev is not None:
             ep.time_next_call(ev[2], ev[3])
-        h.dispatch(wl.x, sf=wl.sf, zero_padding=cfg.zero_padding, out_x=out_x, out_sf=out_sf)
+        dispatch_call()
         flush()
         if ev is not None:
             ep.time_next_call(ev[4], ev[5])
-        h.combine(wl.y, topk_weights=w, bias=wl.bias, out=out)
+        combine_call()
 
     for _ in range(args.warmup):
         step()

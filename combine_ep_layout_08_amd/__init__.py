@@ -22,7 +22,7 @@ __all__ = [
     "EP_OK", "EP_ERR_NULL", "EP_ERR_SHAPE", "EP_ERR_DTYPE", "EP_ERR_UNSUPPORTED",
     "EP_ERR_MISALIGNED", "EP_ERR_WORKSPACE", "EP_ERR_NOT_LAID_OUT", "EP_ERR_CAPACITY",
     "EP_ERR_INVALID_ID", "EP_ERR_HIP", "EP_ERR_TIMEOUT", "EP_BF16", "EP_FP8_E4M3", "EP_F32", "EP_I32",
-    "EP_I64", "EpError", "ep_handle", "lib", "Handle", "ep_capacity_bound",
+    "EP_I64", "EpError", "ep_handle", "lib", "Handle", "BoundCall", "ep_capacity_bound",
     "ep_workspace_bytes", "ep_handle_init", "ep_layout", "ep_handle_read_counts",
     "ep_handle_import", "ep_dispatch", "ep_combine", "ep_status_str", "ep_handle_sizeof",
     "ep_time_next_call", "time_next_call", "ep_combine_backward", "ep_dispatch_backward",
@@ -292,6 +292,38 @@ def _dev_strided(t: torch.Tensor, name: str):
     _need(t.dim() == 2 and min(t.stride()) >= 0, f"{name} must be a 2-D strided view")
 
 
+class BoundCall:
+    """One entry point with its arguments validated and marshalled once.
+
+    Calling it enqueues the same call on the current stream (read at every
+    call) and returns what the direct method returns.  It keeps the tensors it
+    was bound to alive: their contents may change between calls (new routing,
+    new payloads), their storage and shapes may not.  A direct method spends
+    about 5-6 us of host time per call on validation and marshalling, a bound
+    call about 3 us (the C entry point and the launch), which lets small
+    batches run at the GPU's pace.
+
+    Dispatch and combine calls are bound for the handle's token count at bind
+    time (their tensors were checked against it) and refuse to run once a
+    later layout has changed it, as the direct methods would."""
+    __slots__ = ("_fn", "_args", "_what", "_result", "_keep", "_h", "_tokens")
+
+    def __init__(self, fn, args, what, result, keep, h=None):
+        self._fn, self._args, self._what = fn, args, what
+        self._result, self._keep = result, keep
+        self._h = h
+        self._tokens = None if h is None else h.num_tokens
+
+    def __call__(self):
+        if self._h is not None and self._h.num_tokens != self._tokens:
+            raise ValueError(f"{self._what}: bound for {self._tokens} tokens, but the handle's "
+                             f"layout now has {self._h.num_tokens}")
+        status = self._fn(*self._args, _stream())
+        if status != EP_OK:
+            raise EpError(status, self._what)
+        return self._result
+
+
 _SF_DTYPES = (torch.float32, torch.int32)
 
 
@@ -421,8 +453,7 @@ class Handle:
     def recv_src(self) -> torch.Tensor:
         return self._view(self.h.recv_src, self.h.max_tokens)
 
-    def layout(self, topk_idx: torch.Tensor,
-               cumulative_stats: Optional[torch.Tensor] = None) -> "Handle":
+    def _layout_call(self, topk_idx, cumulative_stats):
         _dev(topk_idx, "topk_idx")
         _need(topk_idx.dim() == 2 and topk_idx.shape[1] == self.h.num_topk,
               "topk_idx must be [num_tokens, num_topk]")
@@ -433,10 +464,23 @@ class Handle:
                   cumulative_stats.numel() == self.h.num_experts,
                   "cumulative_stats must be int32 [num_experts]")
         dt = EP_I64 if topk_idx.dtype == torch.int64 else EP_I32
-        _check(ep_layout(self.h, _ptr(topk_idx), dt, topk_idx.shape[0],
-                         _ptr(cumulative_stats), _stream()), "ep_layout")
+        return lib().ep_layout, (ctypes.byref(self.h), _ptr(topk_idx), dt, topk_idx.shape[0],
+                                 _ptr(cumulative_stats))
+
+    def layout(self, topk_idx: torch.Tensor,
+               cumulative_stats: Optional[torch.Tensor] = None) -> "Handle":
+        fn, args = self._layout_call(topk_idx, cumulative_stats)
+        _check(fn(*args, _stream()), "ep_layout")
         self.topk_idx = topk_idx
         return self
+
+    def bind_layout(self, topk_idx: torch.Tensor,
+                    cumulative_stats: Optional[torch.Tensor] = None) -> BoundCall:
+        """``layout`` bound to these tensors (see BoundCall); the handle
+        borrows ``topk_idx`` from now on."""
+        fn, args = self._layout_call(topk_idx, cumulative_stats)
+        self.topk_idx = topk_idx
+        return BoundCall(fn, args, "ep_layout", self, (topk_idx, cumulative_stats))
 
     def import_layout(self, topk_idx: torch.Tensor, counts, psum, dst_slot, src_meta,
                       num_recv_tokens: int) -> "Handle":
@@ -482,6 +526,24 @@ class Handle:
         Returns (out_x, out_sf, out_w); outputs are allocated with
         ``capacity`` rows unless given (out_sf column-major, TMA-aligned, when
         ``col_major_sf``)."""
+        fn, args, result, _ = self._dispatch_call(x, sf, topk_weights, zero_padding, out_x,
+                                                  out_sf, out_w, want_weights, col_major_sf)
+        _check(fn(*args, _stream()), "ep_dispatch")
+        return result
+
+    def bind_dispatch(self, x: torch.Tensor, sf: Optional[torch.Tensor] = None,
+                      topk_weights: Optional[torch.Tensor] = None, zero_padding: bool = False,
+                      out_x: Optional[torch.Tensor] = None, out_sf: Optional[torch.Tensor] = None,
+                      out_w: Optional[torch.Tensor] = None, want_weights: bool = False,
+                      col_major_sf: bool = False) -> BoundCall:
+        """``dispatch`` bound to these tensors (see BoundCall); each call
+        returns (out_x, out_sf, out_w)."""
+        fn, args, result, keep = self._dispatch_call(x, sf, topk_weights, zero_padding, out_x,
+                                                      out_sf, out_w, want_weights, col_major_sf)
+        return BoundCall(fn, args, "ep_dispatch", result, keep, self.h)
+
+    def _dispatch_call(self, x, sf, topk_weights, zero_padding, out_x, out_sf, out_w,
+                       want_weights, col_major_sf):
         T = self.h.num_tokens
         _dev(x, "x")
         _need(x.dim() == 2 and x.shape[0] == T, "x must be [num_tokens, hidden]")
@@ -509,11 +571,10 @@ class Handle:
         if out_w is not None:
             _dev(out_w, "out_w")
             _need(out_w.dtype == torch.float32 and out_w.numel() == cap, "out_w: fp32 [capacity]")
-        _check(ep_dispatch(self.h, _ptr(x), EP_FP8_E4M3 if fp8 else EP_BF16, H, _ptr(sf),
-                           sf_ts, sf_hs, packs, _ptr(topk_weights), _ptr(out_x), _ptr(out_sf),
-                           o_ts, o_hs, _ptr(out_w), 1 if zero_padding else 0, _stream()),
-               "ep_dispatch")
-        return out_x, out_sf, out_w
+        args = (ctypes.byref(self.h), _ptr(x), EP_FP8_E4M3 if fp8 else EP_BF16, H, _ptr(sf),
+                sf_ts, sf_hs, packs, _ptr(topk_weights), _ptr(out_x), _ptr(out_sf), o_ts, o_hs,
+                _ptr(out_w), 1 if zero_padding else 0)
+        return lib().ep_dispatch, args, (out_x, out_sf, out_w), (x, sf, topk_weights)
 
     def dispatch_quant(self, x: torch.Tensor, scale_format="f32",
                        topk_weights: Optional[torch.Tensor] = None, zero_padding: bool = False,
@@ -560,6 +621,20 @@ class Handle:
         """y: bf16 [capacity, H] expert outputs; returns bf16 [T, H].  bias is
         the per-expert [E, H] bias; bias_0 / bias_1 are per-token [T, H]
         biases added after the reduction."""
+        fn, args, out, _ = self._combine_call(y, topk_weights, bias, out, bias_0, bias_1)
+        _check(fn(*args, _stream()), "ep_combine")
+        return out
+
+    def bind_combine(self, y: torch.Tensor, topk_weights: Optional[torch.Tensor] = None,
+                     bias: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                     bias_0: Optional[torch.Tensor] = None,
+                     bias_1: Optional[torch.Tensor] = None) -> BoundCall:
+        """``combine`` bound to these tensors (see BoundCall); each call
+        returns ``out``."""
+        fn, args, out, keep = self._combine_call(y, topk_weights, bias, out, bias_0, bias_1)
+        return BoundCall(fn, args, "ep_combine", out, keep, self.h)
+
+    def _combine_call(self, y, topk_weights, bias, out, bias_0, bias_1):
         T = self.h.num_tokens
         _dev(y, "y")
         _need(y.dtype == torch.bfloat16, "combine input must be bf16")
@@ -583,9 +658,9 @@ class Handle:
             out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
         _dev(out, "out")
         _need(tuple(out.shape) == (T, H) and out.dtype == torch.bfloat16, "out must be bf16 [T, H]")
-        _check(ep_combine(self.h, _ptr(y), EP_BF16, H, _ptr(topk_weights), _ptr(bias),
-                          _ptr(bias_0), _ptr(bias_1), _ptr(out), _stream()), "ep_combine")
-        return out
+        args = (ctypes.byref(self.h), _ptr(y), EP_BF16, H, _ptr(topk_weights), _ptr(bias),
+                _ptr(bias_0), _ptr(bias_1), _ptr(out))
+        return lib().ep_combine, args, out, (y, topk_weights, bias, bias_0, bias_1)
 
 
     # ------------------------------------------------------------ backward

@@ -126,3 +126,63 @@ def test_error_status_raises(fake):
     fake.status = ep.EP_ERR_SHAPE
     with pytest.raises(ep.EpError, match="fake status"):
         h.combine(torch.zeros((h.capacity, 64), dtype=torch.bfloat16))
+
+
+def test_bound_calls_pass_what_the_direct_calls_pass(fake, monkeypatch):
+    """bind_layout / bind_dispatch / bind_combine marshal once; every call
+    hands the C entry point the same arguments as the direct method, with
+    the stream read at call time."""
+    h = _handle(fake)
+    T, K, H = 16, 4, 256
+    idx = torch.zeros((T, K), dtype=torch.int64)
+    x = torch.zeros((T, H), dtype=torch.bfloat16)
+    w = torch.zeros((T, K), dtype=torch.float32)
+    y = torch.zeros((h.capacity, H), dtype=torch.bfloat16)
+    out_x = torch.zeros((h.capacity, H), dtype=torch.bfloat16)
+    out = torch.zeros((T, H), dtype=torch.bfloat16)
+    direct = []
+    h.layout(idx)
+    direct.append(fake.last("ep_layout"))
+    h.dispatch(x, topk_weights=w, out_x=out_x, zero_padding=True)
+    direct.append(fake.last("ep_dispatch"))
+    h.combine(y, topk_weights=w, out=out)
+    direct.append(fake.last("ep_combine"))
+    bl = h.bind_layout(idx)
+    bd = h.bind_dispatch(x, topk_weights=w, out_x=out_x, zero_padding=True)
+    bc = h.bind_combine(y, topk_weights=w, out=out)
+    n_before = len(fake.calls)
+    assert bl() is h and h.topk_idx is idx
+    assert bd()[0] is out_x and bc() is out
+    bound = [a for _, a in fake.calls[n_before:]]
+    assert [n for n, _ in fake.calls[n_before:]] == ["ep_layout", "ep_dispatch", "ep_combine"]
+    for d, b in zip(direct, bound):
+        assert d[1:] == b[1:]
+    monkeypatch.setattr(ep, "_stream", lambda: STREAM + 1)
+    bc()
+    assert fake.last("ep_combine")[-1] == STREAM + 1
+
+
+def test_bound_call_refuses_a_changed_token_count(fake):
+    """A later layout with another token count makes a bound dispatch or
+    combine refuse to run (its tensors were checked against the old count)."""
+    h = _handle(fake)
+    x = torch.zeros((16, 128), dtype=torch.bfloat16)
+    y = torch.zeros((h.capacity, 128), dtype=torch.bfloat16)
+    bd, bc = h.bind_dispatch(x), h.bind_combine(y)
+    n_before = len(fake.calls)
+    h.h.num_tokens = 12                               # what ep_layout does for 12 tokens
+    for call in (bd, bc):
+        with pytest.raises(ValueError, match="bound for 16 tokens"):
+            call()
+    assert len(fake.calls) == n_before                # nothing reached the library
+    h.h.num_tokens = 16
+    bd()
+    assert fake.calls[-1][0] == "ep_dispatch"
+
+
+def test_bound_call_raises_on_status(fake):
+    h = _handle(fake)
+    bc = h.bind_combine(torch.zeros((h.capacity, 64), dtype=torch.bfloat16))
+    fake.status = ep.EP_ERR_NOT_LAID_OUT
+    with pytest.raises(ep.EpError):
+        bc()
