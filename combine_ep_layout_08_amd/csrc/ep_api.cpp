@@ -224,8 +224,9 @@ ep_status ep_handle_import(ep_handle *h, const void *topk_idx, ep_dtype idx_dtyp
     for (int64_t i = 0; i < slots; ++i)
         if (dst_slot[i] < -1 || dst_slot[i] >= expanded) return EP_ERR_SHAPE;
     // src_meta must be the inverse of dst_slot: every row of an expert's run
-    // names a slot that points back at it and every gap row is -1 (the
-    // dispatch and combine walk dst_slot, the bias gradient walks src_meta).
+    // names a slot that points back at it and every gap row is -1 (the row
+    // copies and combine walk dst_slot; the dispatch's scale copy and the
+    // bias gradient walk src_meta).
     int64_t routed = 0;
     for (int64_t i = 0; i < slots; ++i) routed += dst_slot[i] >= 0;
     int64_t runs = 0;
@@ -352,6 +353,7 @@ ep_status ep_dispatch(const ep_handle *h, const void *x, ep_dtype x_dtype, int32
     a.out_hs = out_sf_hidden_stride;
     a.out_w = out_w;
     a.zero_padding = zero_padding != 0;
+    a.src_meta = h->src_meta;
     return hip_status(ep::launch_dispatch(a, stream, ev));
 }
 

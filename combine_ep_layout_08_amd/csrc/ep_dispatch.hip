@@ -50,6 +50,28 @@ constexpr int kGapRowsPerBlock = kWavesPerBlock;
 #define EP_DISPATCH_BLOCKS_PER_CU 0
 #endif
 constexpr int kDispatchBlocksPerCu = EP_DISPATCH_BLOCKS_PER_CU;
+// Scale packs of a copying dispatch, when the layout's source slots are
+// given: moved by blocks of their own in expanded-row order (each wave takes
+// kSfRowsPerWave consecutive rows, so neighbouring rows' packs share cache
+// lines written together) rather than by each token's first-pass wave, whose
+// 224-byte stores (56 fp32 packs) land one row here, one there and leave
+// partly written lines.  At most kSfBlocks such blocks stride over the rows
+// below psum[E], placed first in the grid.  Measured on the FP8 prefill
+// dispatch (4096 x 7168, 56 fp32 packs per row), interleaved runs on one
+// box: 51.1 -> 48.0 us warm, 54.0 -> 51.6 us after a cache flush; 8 rows per
+// wave 54.8 us, 256 blocks 49.5 us, 4096 blocks 51.3 / 56.1 us, the blocks
+// placed last in the grid 47.8 / 53.5 us.
+#ifndef EP_DISPATCH_SF_BY_ROW
+#define EP_DISPATCH_SF_BY_ROW 1
+#endif
+#ifndef EP_DISPATCH_SF_ROWS_PER_WAVE
+#define EP_DISPATCH_SF_ROWS_PER_WAVE 4
+#endif
+#ifndef EP_DISPATCH_SF_BLOCKS
+#define EP_DISPATCH_SF_BLOCKS 1024
+#endif
+constexpr int kSfRowsPerWave = EP_DISPATCH_SF_ROWS_PER_WAVE;
+constexpr int64_t kSfBlocks = EP_DISPATCH_SF_BLOCKS;
 
 __device__ inline void store_row_vec(u32x4 *p, u32x4 v) {
     if (EP_DISPATCH_NT_STORE)
@@ -71,7 +93,7 @@ __device__ inline void dispatch_token(const DispatchArgs &a, int64_t t, int64_t 
     if (my_dst >= a.capacity) my_dst = -1;
     if (pass == 0) {
         if (a.out_w && my_dst >= 0) a.out_w[my_dst] = a.w ? a.w[t * K + lane] : 1.0f;
-        if (a.num_sf) {
+        if (a.num_sf && !a.src_meta) {
             // A token's scale packs (at most 64 * kMaxSfPerLane) go to
             // registers once and are stored for every valid slot.
             uint32_t sfv[kMaxSfPerLane];
@@ -107,6 +129,42 @@ __device__ inline void dispatch_token(const DispatchArgs &a, int64_t t, int64_t 
         for (int q = 0; q < VPL; ++q) {
             const int64_t c = c0 + q * 64 + lane;
             if (c < V) store_row_vec(d + c, v[q]);
+        }
+    }
+}
+
+// Scale packs of kSfRowsPerWave consecutive expanded rows from r0 (one wave):
+// each routed row's packs are its source token's (source slot / K); gap rows
+// (source -1, zeroed by the gap units when asked) and rows from psum[E] on
+// are not written.
+__device__ inline void dispatch_sf_rows(const DispatchArgs &a, int64_t r0, int64_t end,
+                                        int lane) {
+    const int64_t num_slots = static_cast<int64_t>(a.num_tokens) * a.num_topk;
+    int32_t slot[kSfRowsPerWave];
+#pragma unroll
+    for (int i = 0; i < kSfRowsPerWave; ++i) {
+        const int64_t r = r0 + i;
+        slot[i] = r < end ? a.src_meta[r] : -1;
+        if (slot[i] >= num_slots) slot[i] = -1;
+    }
+    uint32_t v[kSfRowsPerWave][kMaxSfPerLane];
+#pragma unroll
+    for (int i = 0; i < kSfRowsPerWave; ++i) {
+        const int64_t t = slot[i] >= 0 ? slot[i] / a.num_topk : 0;
+#pragma unroll
+        for (int q = 0; q < kMaxSfPerLane; ++q) {
+            const int j = lane + 64 * q;
+            v[i][q] = (slot[i] >= 0 && j < a.num_sf) ? a.sf[t * a.sf_ts + j * a.sf_hs] : 0u;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kSfRowsPerWave; ++i) {
+        if (slot[i] < 0) continue;
+        const int64_t r = r0 + i;
+#pragma unroll
+        for (int q = 0; q < kMaxSfPerLane; ++q) {
+            const int j = lane + 64 * q;
+            if (j < a.num_sf) a.out_sf[r * a.out_ts + j * a.out_hs] = v[i][q];
         }
     }
 }
@@ -405,12 +463,23 @@ __device__ inline void dispatch_gap_row(const DispatchArgs &a, int e, int64_t r,
 // kGapRowsPerBlock gap rows each.
 template <int VPL, int MODE>
 __global__ __launch_bounds__(kDispatchThreads) void dispatch_kernel(DispatchArgs a,
+                                                                   int64_t sf_units,
                                                                    int64_t token_units,
                                                                    int64_t total_units,
                                                                    int gap_chunks, int passes) {
     if (a.scalars && (a.scalars[EP_SCALAR_ERROR_BITS] & a.stop_bits)) return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int64_t u = blockIdx.x; u < total_units; u += gridDim.x) {
+    for (int64_t u0 = blockIdx.x; u0 < total_units; u0 += gridDim.x) {
+        if (MODE == 0 && u0 < sf_units) {
+            // Scale units come first in the grid: rows below psum[E], striding.
+            const int64_t e = a.psum[a.num_experts];
+            const int64_t end = e < a.capacity ? e : a.capacity;
+            const int64_t step = sf_units * kWavesPerBlock * kSfRowsPerWave;
+            for (int64_t r0 = (u0 * kWavesPerBlock + wave) * kSfRowsPerWave; r0 < end; r0 += step)
+                dispatch_sf_rows(a, r0, end, lane);
+            continue;
+        }
+        const int64_t u = u0 - sf_units;
         if (u < token_units) {
             const int64_t wv = u * kWavesPerBlock + wave;
             const int64_t t = wv / passes;
@@ -435,13 +504,29 @@ hipError_t launch_vpl(const DispatchArgs &a, hipStream_t stream, CallEvents ev) 
     int gap_chunks = 0;
     if (a.zero_padding && a.alignment > 1)
         gap_chunks = (a.alignment - 1 + kGapRowsPerBlock - 1) / kGapRowsPerBlock;
-    const int64_t total = token_units + static_cast<int64_t>(gap_chunks) * a.num_experts;
+    DispatchArgs b = a;
+    int64_t sf_units = 0;
+    // Only where routed rows fill a good part of the buffer: the scale units
+    // stride over every row below psum[E], gap rows included, so with sparse
+    // routing (decode: 1024 slots in 33536 rows) they would cost more than
+    // the token waves' stores they replace.
+    const int64_t slots = static_cast<int64_t>(a.num_tokens) * a.num_topk;
+    if (MODE == 0 && EP_DISPATCH_SF_BY_ROW && a.src_meta && a.num_sf > 0 && slots > 0 &&
+        slots * 4 >= a.capacity) {
+        const int64_t rows_per_unit = kWavesPerBlock * kSfRowsPerWave;
+        sf_units = (a.capacity + rows_per_unit - 1) / rows_per_unit;
+        if (sf_units > kSfBlocks) sf_units = kSfBlocks;
+    }
+    if (sf_units == 0) b.src_meta = nullptr;      // token waves copy the packs
+    const int64_t total =
+        sf_units + token_units + static_cast<int64_t>(gap_chunks) * a.num_experts;
     const int64_t blocks = persistent_grid(total, kDispatchBlocksPerCu);
     if (blocks == 0) return hipSuccess;
     if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
     return launch_kernel(dispatch_kernel<VPL, MODE>, dim3(static_cast<unsigned>(blocks)),
-                         dim3(kDispatchThreads), stream, ev.start, ev.stop, a, token_units, total,
-                         gap_chunks > 0 ? gap_chunks : 1, static_cast<int>(passes));
+                         dim3(kDispatchThreads), stream, ev.start, ev.stop, b, sf_units,
+                         token_units, total, gap_chunks > 0 ? gap_chunks : 1,
+                         static_cast<int>(passes));
 }
 
 // Most code vectors a lane holds per pass of the quantiser; each pass of a

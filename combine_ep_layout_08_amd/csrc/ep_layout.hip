@@ -149,7 +149,8 @@ __device__ bool lookback(const uint64_t *status, int NB, int tile, int b, uint32
 // lane's rank is the popcount of matching lower lanes; the group leader bumps
 // the wave's LDS counter), flags received tokens in s_tok and counts them
 // into bucket E+1, then turns the per-wave counts in s_hist into in-tile
-// offsets.  Returns each slot's bucket (-1 empty, E invalid) and rank inside
+// offsets, in place for every thread of the block on return.  Returns each
+// slot's bucket (-1 empty, E invalid) and rank inside
 // its wave, and in agg[q] the tile's count of bucket tid + q * kLayoutThreads.
 template <typename IdxT, int R>
 __device__ void rank_tile(const LayoutArgs &a, int64_t tile_base, int64_t tile_end,
@@ -227,6 +228,10 @@ __device__ void rank_tile(const LayoutArgs &a, int64_t tile_base, int64_t tile_e
             agg[q] = run;
         }
     }
+    // Each bucket's offsets were written by the thread that owns the bucket;
+    // callers read s_hist[wave][b] for their own slots' buckets, so every
+    // offset must be in place before any thread goes on.
+    __syncthreads();
 }
 
 // Aligned exclusive scan of the experts' totals (s_total, buckets 0..E+1)

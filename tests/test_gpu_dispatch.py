@@ -230,3 +230,23 @@ def test_dispatch_large_sampled():
     if gaps.size:
         pick = torch.from_numpy(rng.choice(gaps, min(64, gaps.size), replace=False)).cuda()
         assert np.all(u8(out_x[pick]) == POISON)
+
+
+@pytest.mark.parametrize("zp", [False, True])
+def test_dispatch_scale_copy_both_orders(zp):
+    """The scale packs move in expanded-row order when routed rows fill at
+    least a quarter of the buffer (slots * 4 >= capacity), else with each
+    token's rows; the same routing and inputs through a dense handle and one
+    with eight times the capacity give the oracle's bytes either way."""
+    rng = np.random.default_rng(91 + zp)
+    T, K, E, A, H = 700, 8, 48, 16, 2048
+    idx = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int64)
+    idx = np.where(rng.random((T, K)) < 0.1, -1, idx)
+    x = torch.from_numpy(rng.integers(0, 256, size=(T, H), dtype=np.uint8))
+    sf = torch.from_numpy(rng.random((T, H // 128), dtype=np.float32))
+    w = rng.random((T, K), dtype=np.float32)
+    bound = ep.ep_capacity_bound(T, K, E, A)
+    for cap in (bound, 8 * bound):                   # row order, then token order
+        say("dispatch scale copy order", zp, cap)
+        _, g, o, _ = _run_both(idx, E, A, cap, x, sf=sf, w=w, zero_padding=zp)
+        _assert_same(g, o)
