@@ -50,13 +50,15 @@ constexpr int kGapRowsPerBlock = kWavesPerBlock;
 #define EP_DISPATCH_BLOCKS_PER_CU 0
 #endif
 constexpr int kDispatchBlocksPerCu = EP_DISPATCH_BLOCKS_PER_CU;
-// Scale packs of a copying dispatch, when the layout's source slots are
-// given: moved by blocks of their own in expanded-row order (each wave takes
-// kSfRowsPerWave consecutive rows, so neighbouring rows' packs share cache
-// lines written together) rather than by each token's first-pass wave, whose
-// 224-byte stores (56 fp32 packs) land one row here, one there and leave
-// partly written lines.  At most kSfBlocks such blocks stride over the rows
-// below psum[E], placed first in the grid.  Measured on the FP8 prefill
+// Scale packs and per-row weights of a copying dispatch, when the layout's
+// source slots are given: moved by blocks of their own in expanded-row order
+// (for packs each wave takes kSfRowsPerWave consecutive rows, for weights 64,
+// one per lane, so neighbouring rows' values share cache lines written
+// together) rather than by each token's first-pass wave, whose stores (224
+// bytes of packs, 4 bytes of weight per slot) land one row here, one there
+// and leave partly written lines.  At most kSfBlocks such blocks stride over
+// the rows below psum[E], placed first in the grid.  Weights, FP8 prefill
+// dispatch: 53.6 us with them against 49.0 without, stored by the token waves.  Measured on the FP8 prefill
 // dispatch (4096 x 7168, 56 fp32 packs per row), interleaved runs on one
 // box: 51.1 -> 48.0 us warm, 54.0 -> 51.6 us after a cache flush; 8 rows per
 // wave 54.8 us, 256 blocks 49.5 us, 4096 blocks 51.3 / 56.1 us, the blocks
@@ -92,7 +94,8 @@ __device__ inline void dispatch_token(const DispatchArgs &a, int64_t t, int64_t 
     int32_t my_dst = lane < K ? a.dst[t * K + lane] : -1;
     if (my_dst >= a.capacity) my_dst = -1;
     if (pass == 0) {
-        if (a.out_w && my_dst >= 0) a.out_w[my_dst] = a.w ? a.w[t * K + lane] : 1.0f;
+        if (a.out_w && !a.src_meta && my_dst >= 0)
+            a.out_w[my_dst] = a.w ? a.w[t * K + lane] : 1.0f;
         if (a.num_sf && !a.src_meta) {
             // A token's scale packs (at most 64 * kMaxSfPerLane) go to
             // registers once and are stored for every valid slot.
@@ -471,12 +474,23 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_kernel(DispatchArgs
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     for (int64_t u0 = blockIdx.x; u0 < total_units; u0 += gridDim.x) {
         if (MODE == 0 && u0 < sf_units) {
-            // Scale units come first in the grid: rows below psum[E], striding.
+            // Row units come first in the grid: rows below psum[E], striding.
             const int64_t e = a.psum[a.num_experts];
             const int64_t end = e < a.capacity ? e : a.capacity;
             const int64_t step = sf_units * kWavesPerBlock * kSfRowsPerWave;
-            for (int64_t r0 = (u0 * kWavesPerBlock + wave) * kSfRowsPerWave; r0 < end; r0 += step)
-                dispatch_sf_rows(a, r0, end, lane);
+            if (a.num_sf)
+                for (int64_t r0 = (u0 * kWavesPerBlock + wave) * kSfRowsPerWave; r0 < end;
+                     r0 += step)
+                    dispatch_sf_rows(a, r0, end, lane);
+            if (a.out_w) {
+                // Weights: 64 consecutive rows per wave, one per lane.
+                const int64_t num_slots = static_cast<int64_t>(a.num_tokens) * a.num_topk;
+                const int64_t wstep = sf_units * kWavesPerBlock * 64;
+                for (int64_t r = (u0 * kWavesPerBlock + wave) * 64 + lane; r < end; r += wstep) {
+                    const int32_t slot = a.src_meta[r];
+                    if (slot >= 0 && slot < num_slots) a.out_w[r] = a.w ? a.w[slot] : 1.0f;
+                }
+            }
             continue;
         }
         const int64_t u = u0 - sf_units;
@@ -511,13 +525,13 @@ hipError_t launch_vpl(const DispatchArgs &a, hipStream_t stream, CallEvents ev) 
     // routing (decode: 1024 slots in 33536 rows) they would cost more than
     // the token waves' stores they replace.
     const int64_t slots = static_cast<int64_t>(a.num_tokens) * a.num_topk;
-    if (MODE == 0 && EP_DISPATCH_SF_BY_ROW && a.src_meta && a.num_sf > 0 && slots > 0 &&
-        slots * 4 >= a.capacity) {
-        const int64_t rows_per_unit = kWavesPerBlock * kSfRowsPerWave;
+    if (MODE == 0 && EP_DISPATCH_SF_BY_ROW && a.src_meta && (a.num_sf > 0 || a.out_w) &&
+        slots > 0 && slots * 4 >= a.capacity) {
+        const int64_t rows_per_unit = kWavesPerBlock * (a.num_sf > 0 ? kSfRowsPerWave : 64);
         sf_units = (a.capacity + rows_per_unit - 1) / rows_per_unit;
         if (sf_units > kSfBlocks) sf_units = kSfBlocks;
     }
-    if (sf_units == 0) b.src_meta = nullptr;      // token waves copy the packs
+    if (sf_units == 0) b.src_meta = nullptr;      // token waves copy packs and weights
     const int64_t total =
         sf_units + token_units + static_cast<int64_t>(gap_chunks) * a.num_experts;
     const int64_t blocks = persistent_grid(total, kDispatchBlocksPerCu);

@@ -126,8 +126,9 @@ struct DispatchArgs {
     bool zero_padding;
     int32_t quant;               // 0: copy x; EP_SF_F32 + 1 / EP_SF_UE8M0 + 1: quantise bf16 x
     // Source slot of every expanded row (the layout's src_meta): when set, a
-    // copying dispatch moves the scale packs in expanded-row order, each row's
-    // from its source token, instead of from the token's first-pass wave.
+    // copying dispatch moves the scale packs and weights in expanded-row
+    // order, each row's from its source slot, instead of from the token's
+    // first-pass wave.
     const int32_t *src_meta = nullptr;
     uint32_t stop_bits = EP_ERRBIT_FATAL;  // error bits in *scalars that make it write nothing
     // Rank-row metadata (quantising rank dispatch, num_topk 1): the token's
