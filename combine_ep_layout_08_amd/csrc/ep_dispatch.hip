@@ -27,14 +27,22 @@ constexpr int kGapRowsPerBlock = kWavesPerBlock;
 
 // Launch shape: each wave copies one pass of a token's row, 64 * VPL
 // 16-byte vectors, to every slot; EP_DISPATCH_MAX_VPL caps VPL (a smaller
-// cap spreads a token over more waves: 1 measured equal on the FP8 prefill
-// dispatch and 9 % faster on 32768 bf16 rows of 7168 than one pass per
-// token).  Cache hints of the row copy: non-temporal stores measured 2-6 %
-// slower (57 us against 47 on the FP8 prefill rows together with
-// non-temporal loads).  Non-temporal loads of the token rows with ordinary
-// stores (EP_DISPATCH_NT_LOAD) took the 4096-token FP8 prefill dispatch from
-// 47.0 to 44.4 us but were 2-3 % slower at every other size measured (FP8
-// rows of 8192-32768 tokens, bf16 rows of 2048-32768 tokens), so they are off.
+// cap spreads a token over more waves).  The copying kernel keeps 16 VGPRs
+// (8 waves per SIMD) and requests a wave's row loads, slot rows and the
+// error word together (one round trip to memory before its stores).
+// Against an earlier form with 105 VGPRs (4 waves per SIMD) and three
+// dependent round trips, interleaved on one box: FP8 prefill dispatch
+// (4096 x 7168) 47.9 -> 42.9 us back to back and 51.8 -> 47.0 us after a
+// cache flush, decode 34.6 -> 33.0 us after a flush; the bf16 dispatches
+// whose outputs exceed the MALL (16384 x 4096, 32768 x 7168) 0-7 % slower
+// (bound by HBM writes there).  Capping occupancy at 4 or 6 waves per SIMD
+// (EP_DISPATCH_WAVES_PER_EU) was slower at every size (prefill 48.1 / 44.3
+// us against 43.3); VPL 2 or 4 gained at 32768 x 7168 on one box and lost
+// on another, equal at prefill.  Cache hints of the row copy: non-temporal
+// stores measured 2-6 % slower (57 us against 47 on the FP8 prefill rows
+// together with non-temporal loads); non-temporal loads of the token rows
+// (EP_DISPATCH_NT_LOAD) within 0.5 us of ordinary ones on the prefill
+// dispatch and 2-3 % slower at larger sizes in the earlier form, so off.
 #ifndef EP_DISPATCH_MAX_VPL
 #define EP_DISPATCH_MAX_VPL 1
 #endif
@@ -44,8 +52,9 @@ constexpr int kGapRowsPerBlock = kWavesPerBlock;
 #ifndef EP_DISPATCH_NT_STORE
 #define EP_DISPATCH_NT_STORE 0
 #endif
-// Resident blocks per compute unit of a persistent grid (0 = one block per
-// work unit, the default: measured equal or faster on MI355X).
+// Resident blocks per compute unit of a persistent grid for the quantising
+// dispatch (0 = one block per work unit, the default: measured equal or
+// faster on MI355X).
 #ifndef EP_DISPATCH_BLOCKS_PER_CU
 #define EP_DISPATCH_BLOCKS_PER_CU 0
 #endif
@@ -57,12 +66,13 @@ constexpr int kDispatchBlocksPerCu = EP_DISPATCH_BLOCKS_PER_CU;
 // together) rather than by each token's first-pass wave, whose stores (224
 // bytes of packs, 4 bytes of weight per slot) land one row here, one there
 // and leave partly written lines.  At most kSfBlocks such blocks stride over
-// the rows below psum[E], placed first in the grid.  Weights, FP8 prefill
-// dispatch: 53.6 us with them against 49.0 without, stored by the token waves.  Measured on the FP8 prefill
-// dispatch (4096 x 7168, 56 fp32 packs per row), interleaved runs on one
-// box: 51.1 -> 48.0 us warm, 54.0 -> 51.6 us after a cache flush; 8 rows per
-// wave 54.8 us, 256 blocks 49.5 us, 4096 blocks 51.3 / 56.1 us, the blocks
-// placed last in the grid 47.8 / 53.5 us.
+// the rows below psum[E], placed first in the grid.  Measured on the FP8
+// prefill dispatch (4096 x 7168, 56 fp32 packs per row), interleaved runs on
+// one box, current kernel: 43.9 -> 42.9 us back to back, 50.1 -> 47.0 us
+// after a cache flush; 2048 / 4096 blocks 45.4 / 46.0 us (48.7 / 51.6
+// flushed), 8 rows per wave 45.0 (51.1), 2 rows per wave over 4096 blocks
+// 45.0 (49.6).  Weights in the earlier form: 53.6 us stored by the token
+// waves against 49.0 us without a weight output.
 #ifndef EP_DISPATCH_SF_BY_ROW
 #define EP_DISPATCH_SF_BY_ROW 1
 #endif
@@ -82,40 +92,20 @@ __device__ inline void store_row_vec(u32x4 *p, u32x4 v) {
         *p = v;
 }
 
+// True when the layout's error word holds a bit that voids this call.
+__device__ inline bool dispatch_stopped(const DispatchArgs &a) {
+    return a.scalars && (a.scalars[EP_SCALAR_ERROR_BITS] & a.stop_bits);
+}
+
 // Copy one pass of a token's row (one wave: vectors [64*VPL*pass, +64*VPL))
-// to every valid slot's row; pass 0 also copies the scale packs and weight.
+// to every valid slot's row; pass 0 also copies the scale packs and weight
+// when they are not moved in expanded-row order.  The row loads, the slot
+// rows and the error word are all requested before the wave waits on any
+// of them (one round trip to memory instead of three).
 template <int VPL>
 __device__ inline void dispatch_token(const DispatchArgs &a, int64_t t, int64_t pass, int lane) {
     const int64_t V = a.row_vecs;
-    u32x4 *out = static_cast<u32x4 *>(a.out_x);
     const int K = a.num_topk;
-    // Rows outside [0, capacity) are skipped, so no layout content can send a
-    // store out of the output buffers.
-    int32_t my_dst = lane < K ? a.dst[t * K + lane] : -1;
-    if (my_dst >= a.capacity) my_dst = -1;
-    if (pass == 0) {
-        if (a.out_w && !a.src_meta && my_dst >= 0)
-            a.out_w[my_dst] = a.w ? a.w[t * K + lane] : 1.0f;
-        if (a.num_sf && !a.src_meta) {
-            // A token's scale packs (at most 64 * kMaxSfPerLane) go to
-            // registers once and are stored for every valid slot.
-            uint32_t sfv[kMaxSfPerLane];
-#pragma unroll
-            for (int q = 0; q < kMaxSfPerLane; ++q) {
-                const int j = lane + 64 * q;
-                sfv[q] = j < a.num_sf ? a.sf[t * a.sf_ts + j * a.sf_hs] : 0u;
-            }
-            for (int k = 0; k < K; ++k) {
-                const int32_t r = __builtin_amdgcn_readlane(my_dst, k);
-                if (r < 0) continue;
-#pragma unroll
-                for (int q = 0; q < kMaxSfPerLane; ++q) {
-                    const int j = lane + 64 * q;
-                    if (j < a.num_sf) a.out_sf[r * a.out_ts + j * a.out_hs] = sfv[q];
-                }
-            }
-        }
-    }
     const u32x4 *src = static_cast<const u32x4 *>(a.x) + t * V;
     const int64_t c0 = pass * 64 * VPL;
     u32x4 v[VPL];
@@ -124,6 +114,24 @@ __device__ inline void dispatch_token(const DispatchArgs &a, int64_t t, int64_t 
         const int64_t c = c0 + q * 64 + lane;
         if (c < V) v[q] = EP_DISPATCH_NT_LOAD ? __builtin_nontemporal_load(src + c) : src[c];
     }
+    // Rows outside [0, capacity) are skipped, so no layout content can send a
+    // store out of the output buffers.
+    int32_t my_dst = lane < K ? a.dst[t * K + lane] : -1;
+    if (my_dst >= a.capacity) my_dst = -1;
+    if (dispatch_stopped(a)) return;
+    if (pass == 0 && !a.src_meta) {
+        if (a.out_w && my_dst >= 0) a.out_w[my_dst] = a.w ? a.w[t * K + lane] : 1.0f;
+        // A token's scale packs, 64 at a time: loaded once, stored to every
+        // valid slot's row.
+        for (int j = lane; j - lane < a.num_sf; j += 64) {
+            const uint32_t p = j < a.num_sf ? a.sf[t * a.sf_ts + j * a.sf_hs] : 0u;
+            for (int k = 0; k < K; ++k) {
+                const int32_t r = __builtin_amdgcn_readlane(my_dst, k);
+                if (r >= 0 && j < a.num_sf) a.out_sf[r * a.out_ts + j * a.out_hs] = p;
+            }
+        }
+    }
+    u32x4 *out = static_cast<u32x4 *>(a.out_x);
     for (int k = 0; k < K; ++k) {
         const int32_t r = __builtin_amdgcn_readlane(my_dst, k);
         if (r < 0) continue;
@@ -139,36 +147,26 @@ __device__ inline void dispatch_token(const DispatchArgs &a, int64_t t, int64_t 
 // Scale packs of kSfRowsPerWave consecutive expanded rows from r0 (one wave):
 // each routed row's packs are its source token's (source slot / K); gap rows
 // (source -1, zeroed by the gap units when asked) and rows from psum[E] on
-// are not written.
+// are not written.  Packs go 64 at a time (one per lane and row), so a row
+// of up to 64 packs takes one load and one store per lane.
 __device__ inline void dispatch_sf_rows(const DispatchArgs &a, int64_t r0, int64_t end,
                                         int lane) {
     const int64_t num_slots = static_cast<int64_t>(a.num_tokens) * a.num_topk;
-    int32_t slot[kSfRowsPerWave];
+    int64_t tok[kSfRowsPerWave];
 #pragma unroll
     for (int i = 0; i < kSfRowsPerWave; ++i) {
         const int64_t r = r0 + i;
-        slot[i] = r < end ? a.src_meta[r] : -1;
-        if (slot[i] >= num_slots) slot[i] = -1;
+        const int32_t slot = r < end ? a.src_meta[r] : -1;
+        tok[i] = (slot >= 0 && slot < num_slots) ? slot / a.num_topk : -1;
     }
-    uint32_t v[kSfRowsPerWave][kMaxSfPerLane];
+    for (int j = lane; j - lane < a.num_sf; j += 64) {
+        uint32_t v[kSfRowsPerWave];
 #pragma unroll
-    for (int i = 0; i < kSfRowsPerWave; ++i) {
-        const int64_t t = slot[i] >= 0 ? slot[i] / a.num_topk : 0;
+        for (int i = 0; i < kSfRowsPerWave; ++i)
+            v[i] = (tok[i] >= 0 && j < a.num_sf) ? a.sf[tok[i] * a.sf_ts + j * a.sf_hs] : 0u;
 #pragma unroll
-        for (int q = 0; q < kMaxSfPerLane; ++q) {
-            const int j = lane + 64 * q;
-            v[i][q] = (slot[i] >= 0 && j < a.num_sf) ? a.sf[t * a.sf_ts + j * a.sf_hs] : 0u;
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < kSfRowsPerWave; ++i) {
-        if (slot[i] < 0) continue;
-        const int64_t r = r0 + i;
-#pragma unroll
-        for (int q = 0; q < kMaxSfPerLane; ++q) {
-            const int j = lane + 64 * q;
-            if (j < a.num_sf) a.out_sf[r * a.out_ts + j * a.out_hs] = v[i][q];
-        }
+        for (int i = 0; i < kSfRowsPerWave; ++i)
+            if (tok[i] >= 0 && j < a.num_sf) a.out_sf[(r0 + i) * a.out_ts + j * a.out_hs] = v[i];
     }
 }
 
@@ -460,46 +458,78 @@ __device__ inline void dispatch_gap_row(const DispatchArgs &a, int e, int64_t r,
     if (a.out_w && lane == 0) a.out_w[r] = 0.0f;
 }
 
-// Grid over work units (one block per unit unless a persistent grid is
-// configured): units [0, token_units) give each wave one (token, pass) to
-// copy (MODE 0) or quantise (MODE 1, 2), `passes` per token; the rest zero
+// Copying dispatch, one work unit per block: blocks [0, sf_units) move the
+// scale packs and weights in expanded-row order (when the layout's source
+// slots are given), the next token_units blocks give each wave one (token,
+// pass) to copy, the rest zero kGapRowsPerBlock gap rows each.  No loop over
+// units: the kernel keeps few registers live (8 waves per SIMD).
+#ifndef EP_DISPATCH_WAVES_PER_EU
+#define EP_DISPATCH_WAVES_PER_EU 8
+#endif
+template <int VPL>
+__global__ __launch_bounds__(kDispatchThreads)
+__attribute__((amdgpu_waves_per_eu(1, EP_DISPATCH_WAVES_PER_EU))) void dispatch_copy_kernel(DispatchArgs a,
+                                                                        int64_t sf_units,
+                                                                        int64_t token_units,
+                                                                        int gap_chunks,
+                                                                        int passes) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t u0 = blockIdx.x;
+    if (u0 < sf_units) {
+        if (dispatch_stopped(a)) return;
+        // Rows below psum[E], striding over the sf_units blocks.
+        const int64_t e = a.psum[a.num_experts];
+        const int64_t end = e < a.capacity ? e : a.capacity;
+        if (a.num_sf) {
+            const int64_t step = sf_units * kWavesPerBlock * kSfRowsPerWave;
+            for (int64_t r0 = (u0 * kWavesPerBlock + wave) * kSfRowsPerWave; r0 < end; r0 += step)
+                dispatch_sf_rows(a, r0, end, lane);
+        }
+        if (a.out_w) {
+            // Weights: 64 consecutive rows per wave, one per lane.
+            const int64_t num_slots = static_cast<int64_t>(a.num_tokens) * a.num_topk;
+            const int64_t wstep = sf_units * kWavesPerBlock * 64;
+            for (int64_t r = (u0 * kWavesPerBlock + wave) * 64 + lane; r < end; r += wstep) {
+                const int32_t slot = a.src_meta[r];
+                if (slot >= 0 && slot < num_slots) a.out_w[r] = a.w ? a.w[slot] : 1.0f;
+            }
+        }
+        return;
+    }
+    const int64_t u = u0 - sf_units;
+    if (u < token_units) {
+        const int64_t wv = u * kWavesPerBlock + wave;
+        const int64_t t = wv / passes;
+        if (t < a.num_tokens) dispatch_token<VPL>(a, t, wv - t * passes, lane);
+        return;
+    }
+    if (dispatch_stopped(a)) return;
+    const int64_t g = u - token_units;
+    const int e = static_cast<int>(g / gap_chunks);
+    const int64_t chunk = g - static_cast<int64_t>(e) * gap_chunks;
+    const int64_t r = static_cast<int64_t>(a.psum[e]) + a.counts[e] + chunk * kGapRowsPerBlock +
+                      wave;
+    dispatch_gap_row(a, e, r, lane);
+}
+
+// Quantising dispatch over work units (one block per unit unless a
+// persistent grid is configured): units [0, token_units) give each wave one
+// (token, pass) to quantise, `passes` per token; the rest zero
 // kGapRowsPerBlock gap rows each.
 template <int VPL, int MODE>
 __global__ __launch_bounds__(kDispatchThreads) void dispatch_kernel(DispatchArgs a,
-                                                                   int64_t sf_units,
                                                                    int64_t token_units,
                                                                    int64_t total_units,
                                                                    int gap_chunks, int passes) {
-    if (a.scalars && (a.scalars[EP_SCALAR_ERROR_BITS] & a.stop_bits)) return;
+    if (dispatch_stopped(a)) return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int64_t u0 = blockIdx.x; u0 < total_units; u0 += gridDim.x) {
-        if (MODE == 0 && u0 < sf_units) {
-            // Row units come first in the grid: rows below psum[E], striding.
-            const int64_t e = a.psum[a.num_experts];
-            const int64_t end = e < a.capacity ? e : a.capacity;
-            const int64_t step = sf_units * kWavesPerBlock * kSfRowsPerWave;
-            if (a.num_sf)
-                for (int64_t r0 = (u0 * kWavesPerBlock + wave) * kSfRowsPerWave; r0 < end;
-                     r0 += step)
-                    dispatch_sf_rows(a, r0, end, lane);
-            if (a.out_w) {
-                // Weights: 64 consecutive rows per wave, one per lane.
-                const int64_t num_slots = static_cast<int64_t>(a.num_tokens) * a.num_topk;
-                const int64_t wstep = sf_units * kWavesPerBlock * 64;
-                for (int64_t r = (u0 * kWavesPerBlock + wave) * 64 + lane; r < end; r += wstep) {
-                    const int32_t slot = a.src_meta[r];
-                    if (slot >= 0 && slot < num_slots) a.out_w[r] = a.w ? a.w[slot] : 1.0f;
-                }
-            }
-            continue;
-        }
-        const int64_t u = u0 - sf_units;
+    for (int64_t u = blockIdx.x; u < total_units; u += gridDim.x) {
         if (u < token_units) {
             const int64_t wv = u * kWavesPerBlock + wave;
             const int64_t t = wv / passes;
             if (t >= a.num_tokens) continue;
-            if (MODE == 0) dispatch_token<VPL>(a, t, wv % passes, lane);
-            else quant_token<VPL, MODE>(a, t, wv % passes, lane);
+            quant_token<VPL, MODE>(a, t, wv % passes, lane);
         } else {
             const int64_t g = u - token_units;
             const int e = static_cast<int>(g / gap_chunks);
@@ -518,6 +548,16 @@ hipError_t launch_vpl(const DispatchArgs &a, hipStream_t stream, CallEvents ev) 
     int gap_chunks = 0;
     if (a.zero_padding && a.alignment > 1)
         gap_chunks = (a.alignment - 1 + kGapRowsPerBlock - 1) / kGapRowsPerBlock;
+    const int64_t gap_units = static_cast<int64_t>(gap_chunks) * a.num_experts;
+    if constexpr (MODE != 0) {
+        const int64_t total = token_units + gap_units;
+        const int64_t blocks = persistent_grid(total, kDispatchBlocksPerCu);
+        if (blocks == 0) return hipSuccess;
+        if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
+        return launch_kernel(dispatch_kernel<VPL, MODE>, dim3(static_cast<unsigned>(blocks)),
+                             dim3(kDispatchThreads), stream, ev.start, ev.stop, a, token_units,
+                             total, gap_chunks > 0 ? gap_chunks : 1, static_cast<int>(passes));
+    } else {
     DispatchArgs b = a;
     int64_t sf_units = 0;
     // Only where routed rows fill a good part of the buffer: the scale units
@@ -525,22 +565,20 @@ hipError_t launch_vpl(const DispatchArgs &a, hipStream_t stream, CallEvents ev) 
     // routing (decode: 1024 slots in 33536 rows) they would cost more than
     // the token waves' stores they replace.
     const int64_t slots = static_cast<int64_t>(a.num_tokens) * a.num_topk;
-    if (MODE == 0 && EP_DISPATCH_SF_BY_ROW && a.src_meta && (a.num_sf > 0 || a.out_w) &&
-        slots > 0 && slots * 4 >= a.capacity) {
+    if (EP_DISPATCH_SF_BY_ROW && a.src_meta && (a.num_sf > 0 || a.out_w) && slots > 0 &&
+        slots * 4 >= a.capacity) {
         const int64_t rows_per_unit = kWavesPerBlock * (a.num_sf > 0 ? kSfRowsPerWave : 64);
         sf_units = (a.capacity + rows_per_unit - 1) / rows_per_unit;
         if (sf_units > kSfBlocks) sf_units = kSfBlocks;
     }
     if (sf_units == 0) b.src_meta = nullptr;      // token waves copy packs and weights
-    const int64_t total =
-        sf_units + token_units + static_cast<int64_t>(gap_chunks) * a.num_experts;
-    const int64_t blocks = persistent_grid(total, kDispatchBlocksPerCu);
+    const int64_t blocks = sf_units + token_units + gap_units;
     if (blocks == 0) return hipSuccess;
     if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
-    return launch_kernel(dispatch_kernel<VPL, MODE>, dim3(static_cast<unsigned>(blocks)),
+    return launch_kernel(dispatch_copy_kernel<VPL>, dim3(static_cast<unsigned>(blocks)),
                          dim3(kDispatchThreads), stream, ev.start, ev.stop, b, sf_units,
-                         token_units, total, gap_chunks > 0 ? gap_chunks : 1,
-                         static_cast<int>(passes));
+                         token_units, gap_chunks > 0 ? gap_chunks : 1, static_cast<int>(passes));
+    }
 }
 
 // Most code vectors a lane holds per pass of the quantiser; each pass of a
