@@ -23,7 +23,8 @@ __all__ = [
     "EP_ERR_MISALIGNED", "EP_ERR_WORKSPACE", "EP_ERR_NOT_LAID_OUT", "EP_ERR_CAPACITY",
     "EP_ERR_INVALID_ID", "EP_ERR_HIP", "EP_ERR_TIMEOUT", "EP_BF16", "EP_FP8_E4M3", "EP_F32", "EP_I32",
     "EP_I64", "EpError", "ep_handle", "lib", "Handle", "BoundCall", "ep_capacity_bound",
-    "ep_workspace_bytes", "ep_handle_init", "ep_layout", "ep_handle_read_counts",
+    "ep_workspace_bytes", "ep_handle_init", "ep_layout", "ep_layout_noalloc",
+    "ep_handle_read_counts",
     "ep_handle_import", "ep_dispatch", "ep_combine", "ep_status_str", "ep_handle_sizeof",
     "ep_time_next_call", "time_next_call", "ep_combine_backward", "ep_dispatch_backward",
     "ep_dispatch_rank", "ep_dispatch_rank_quant", "ep_combine_rank", "ep_tma_aligned_rows",
@@ -89,6 +90,7 @@ _SIGNATURES = {
     "ep_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32, _I32, _I64]),
     "ep_handle_init": (ctypes.c_int, [_HP, _I32, _I32, _I32, _I32, _I64, _P, ctypes.c_size_t, _P]),
     "ep_layout": (ctypes.c_int, [_HP, _P, ctypes.c_int, _I32, _P, _P]),
+    "ep_layout_noalloc": (ctypes.c_int, [_HP, _P, ctypes.c_int, _I32, _P, _P]),
     "ep_handle_read_counts": (ctypes.c_int, [_HP, _P, _P, _P, _P, _P, _P, _P]),
     "ep_handle_import": (ctypes.c_int, [_HP, _P, ctypes.c_int, _I32, _P, _P, _P, _P, _I32, _P]),
     "ep_dispatch": (ctypes.c_int, [_HP, _P, ctypes.c_int, _I32, _P, _I64, _I64, _I32, _P, _P,
@@ -158,6 +160,12 @@ def ep_handle_init(h: ep_handle, max_tokens, num_topk, num_experts, expert_align
 def ep_layout(h: ep_handle, topk_idx_ptr, idx_dtype, num_tokens, stats_ptr, stream) -> int:
     return lib().ep_layout(ctypes.byref(h), topk_idx_ptr, idx_dtype, num_tokens, stats_ptr,
                            stream)
+
+
+def ep_layout_noalloc(h: ep_handle, topk_idx_ptr, idx_dtype, num_tokens, stats_ptr,
+                      stream) -> int:
+    return lib().ep_layout_noalloc(ctypes.byref(h), topk_idx_ptr, idx_dtype, num_tokens,
+                                   stats_ptr, stream)
 
 
 def ep_handle_read_counts(h: ep_handle, counts_ptr, psum_ptr, num_expanded_ptr,
@@ -453,7 +461,7 @@ class Handle:
     def recv_src(self) -> torch.Tensor:
         return self._view(self.h.recv_src, self.h.max_tokens)
 
-    def _layout_call(self, topk_idx, cumulative_stats):
+    def _layout_call(self, topk_idx, cumulative_stats, noalloc=False):
         _dev(topk_idx, "topk_idx")
         _need(topk_idx.dim() == 2 and topk_idx.shape[1] == self.h.num_topk,
               "topk_idx must be [num_tokens, num_topk]")
@@ -464,13 +472,24 @@ class Handle:
                   cumulative_stats.numel() == self.h.num_experts,
                   "cumulative_stats must be int32 [num_experts]")
         dt = EP_I64 if topk_idx.dtype == torch.int64 else EP_I32
-        return lib().ep_layout, (ctypes.byref(self.h), _ptr(topk_idx), dt, topk_idx.shape[0],
-                                 _ptr(cumulative_stats))
+        fn = lib().ep_layout_noalloc if noalloc else lib().ep_layout
+        return fn, (ctypes.byref(self.h), _ptr(topk_idx), dt, topk_idx.shape[0],
+                    _ptr(cumulative_stats))
 
     def layout(self, topk_idx: torch.Tensor,
                cumulative_stats: Optional[torch.Tensor] = None) -> "Handle":
         fn, args = self._layout_call(topk_idx, cumulative_stats)
         _check(fn(*args, _stream()), "ep_layout")
+        self.topk_idx = topk_idx
+        return self
+
+    def layout_noalloc(self, topk_idx: torch.Tensor,
+                       cumulative_stats: Optional[torch.Tensor] = None) -> "Handle":
+        """``layout`` through ep_layout_noalloc: the scans' scratch is the
+        library's static per-device array, not the handle's workspace (calls
+        that overlap on one device race)."""
+        fn, args = self._layout_call(topk_idx, cumulative_stats, noalloc=True)
+        _check(fn(*args, _stream()), "ep_layout_noalloc")
         self.topk_idx = topk_idx
         return self
 

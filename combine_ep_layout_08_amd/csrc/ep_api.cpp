@@ -136,15 +136,23 @@ ep_status ep_time_next_call(hipEvent_t start, hipEvent_t stop) {
     return EP_OK;
 }
 
-ep_status ep_layout(ep_handle *h, const void *topk_idx, ep_dtype idx_dtype, int32_t num_tokens,
-                    int32_t *cumulative_stats, hipStream_t stream) {
+// ep_layout and ep_layout_noalloc: the same checks and kernels; the scans'
+// ticket, epoch and tile status words come from the handle's workspace or
+// from the library's static scratch.
+static ep_status layout_call(ep_handle *h, const void *topk_idx, ep_dtype idx_dtype,
+                             int32_t num_tokens, int32_t *cumulative_stats, hipStream_t stream,
+                             bool static_scratch) {
     const ep::CallEvents ev = take_events();
     if (!h) return EP_ERR_NULL;
     if (!handle_ready(h)) return EP_ERR_WORKSPACE;
     if (idx_dtype != EP_I64 && idx_dtype != EP_I32) return EP_ERR_DTYPE;
     if (num_tokens < 0 || num_tokens > h->max_tokens) return EP_ERR_SHAPE;
-    if (ep::layout_status_tiles(num_tokens, h->num_topk) > h->status_tiles)
+    const int64_t tiles = ep::layout_status_tiles(num_tokens, h->num_topk);
+    if (static_scratch) {
+        if (tiles * (h->num_experts + 2) > ep::kScratchStatusWords) return EP_ERR_WORKSPACE;
+    } else if (tiles > h->status_tiles) {
         return EP_ERR_WORKSPACE;
+    }
     if (num_tokens > 0 && !topk_idx) return EP_ERR_NULL;
     if (!aligned(topk_idx, idx_dtype == EP_I64 ? 8 : 4)) return EP_ERR_MISALIGNED;
     if (!aligned(cumulative_stats, 4)) return EP_ERR_MISALIGNED;
@@ -162,6 +170,11 @@ ep_status ep_layout(ep_handle *h, const void *topk_idx, ep_dtype idx_dtype, int3
     a.src_meta = h->src_meta;
     a.scalars = h->scalars;
     a.tile_status = h->tile_status;
+    a.ticket = h->scalars + EP_SCALAR_TICKET;
+    a.epoch = h->scalars + EP_SCALAR_EPOCH;
+    if (static_scratch &&
+        ep::layout_scratch(stream, &a.tile_status, &a.ticket, &a.epoch) != hipSuccess)
+        return EP_ERR_HIP;
     a.cumulative_stats = cumulative_stats;
     a.recv_row = h->recv_row;
     a.recv_src = h->recv_src;
@@ -172,6 +185,16 @@ ep_status ep_layout(ep_handle *h, const void *topk_idx, ep_dtype idx_dtype, int3
     h->topk_idx_dtype = idx_dtype;
     h->laid_out = 1;
     return EP_OK;
+}
+
+ep_status ep_layout(ep_handle *h, const void *topk_idx, ep_dtype idx_dtype, int32_t num_tokens,
+                    int32_t *cumulative_stats, hipStream_t stream) {
+    return layout_call(h, topk_idx, idx_dtype, num_tokens, cumulative_stats, stream, false);
+}
+
+ep_status ep_layout_noalloc(ep_handle *h, const void *topk_idx, ep_dtype idx_dtype,
+                            int32_t num_tokens, int32_t *cumulative_stats, hipStream_t stream) {
+    return layout_call(h, topk_idx, idx_dtype, num_tokens, cumulative_stats, stream, true);
 }
 
 ep_status ep_handle_read_counts(const ep_handle *h, int32_t *counts, int32_t *psum,

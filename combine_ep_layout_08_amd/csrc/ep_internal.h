@@ -105,6 +105,9 @@ struct LayoutArgs {
     int64_t capacity;
     int32_t *counts, *psum, *dst, *src_meta, *scalars;
     uint64_t *tile_status;
+    // Tile ticket and call epoch of the scans over tile_status (the handle's
+    // scalars, or the header of the library's static scratch).
+    int32_t *ticket, *epoch;
     int32_t *cumulative_stats;
     int32_t *recv_row, *recv_src;
 };
@@ -201,6 +204,13 @@ struct GatherArgs {
 hipError_t launch_handle_clear(int32_t *scalars, uint64_t *tile_status,
                                int64_t status_words, hipStream_t stream);
 hipError_t launch_layout(const LayoutArgs &a, hipStream_t stream, CallEvents ev);
+// Status words of the library's static scratch (ep_layout_noalloc) on the
+// current device; set up on the first call per device.
+constexpr int64_t kScratchBytes = EP_LAYOUT_SCRATCH_BYTES;
+constexpr int64_t kScratchHeaderBytes = 256;
+constexpr int64_t kScratchStatusWords = (kScratchBytes - kScratchHeaderBytes) / 8;
+hipError_t layout_scratch(hipStream_t stream, uint64_t **status, int32_t **ticket,
+                          int32_t **epoch);
 hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t stream, CallEvents ev);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t stream, CallEvents ev);
 hipError_t launch_combine_backward(const BackwardArgs &a, hipStream_t stream, CallEvents ev);

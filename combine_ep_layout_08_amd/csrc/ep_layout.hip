@@ -47,6 +47,8 @@
 #include "ep_internal.h"
 #include "../../include/ep.h"
 
+#include <mutex>
+
 namespace ep {
 namespace {
 
@@ -323,9 +325,9 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_scan_kernel(LayoutArgs 
     const int E = a.num_experts, NB = E + 2, K = a.num_topk;
     const int B_INVALID = E, B_RECV = E + 1;
     if (tid == 0) {
-        s_tile = __hip_atomic_fetch_add(&a.scalars[EP_SCALAR_TICKET], 1, __ATOMIC_RELAXED,
+        s_tile = __hip_atomic_fetch_add(a.ticket, 1, __ATOMIC_RELAXED,
                                         __HIP_MEMORY_SCOPE_AGENT);
-        s_epoch = static_cast<uint32_t>(a.scalars[EP_SCALAR_EPOCH]);
+        s_epoch = static_cast<uint32_t>(*a.epoch);
     }
     __syncthreads();
     const int tile = s_tile;
@@ -430,10 +432,10 @@ template <typename IdxT>
 __global__ __launch_bounds__(256) void layout_finalize_kernel(LayoutArgs a, int slot_blocks) {
     const int tid = threadIdx.x;
     if (blockIdx.x == 0 && tid == 0) {
-        a.scalars[EP_SCALAR_TICKET] = 0;
-        uint32_t next = static_cast<uint32_t>(a.scalars[EP_SCALAR_EPOCH]) + 1u;
+        *a.ticket = 0;
+        uint32_t next = static_cast<uint32_t>(*a.epoch) + 1u;
         if (next >= (1u << 30)) next = 1u;
-        a.scalars[EP_SCALAR_EPOCH] = static_cast<int32_t>(next);
+        *a.epoch = static_cast<int32_t>(next);
     }
     if (a.scalars[EP_SCALAR_ERROR_BITS] & EP_ERRBIT_FATAL) return;
     const int E = a.num_experts;
@@ -563,7 +565,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_count_kernel(LayoutArgs
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int E = a.num_experts, NB = E + 2, K = a.num_topk;
     const int tile = blockIdx.x;
-    const uint32_t epoch = static_cast<uint32_t>(a.scalars[EP_SCALAR_EPOCH]);
+    const uint32_t epoch = static_cast<uint32_t>(*a.epoch);
     const int64_t num_slots = static_cast<int64_t>(a.num_tokens) * K;
     const int64_t tile_base = static_cast<int64_t>(tile) * tokens_per_tile * K;
     const int64_t tile_end_full = tile_base + static_cast<int64_t>(tokens_per_tile) * K;
@@ -723,10 +725,10 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_place_kernel(LayoutArgs
 
     // 5. Tile 0 retires this call's status words.
     if (tile == 0 && tid == 0) {
-        a.scalars[EP_SCALAR_TICKET] = 0;
-        uint32_t next = static_cast<uint32_t>(a.scalars[EP_SCALAR_EPOCH]) + 1u;
+        *a.ticket = 0;
+        uint32_t next = static_cast<uint32_t>(*a.epoch) + 1u;
         if (next >= (1u << 30)) next = 1u;
-        a.scalars[EP_SCALAR_EPOCH] = static_cast<int32_t>(next);
+        *a.epoch = static_cast<int32_t>(next);
     }
 }
 
@@ -737,7 +739,61 @@ __global__ void handle_clear_kernel(int32_t *scalars, uint64_t *status, int64_t 
     if (gid < EP_NUM_SCALARS) scalars[gid] = (gid == EP_SCALAR_EPOCH) ? 1 : 0;
 }
 
+// Header of the static scratch: int32 ticket, int32 epoch (1 after set-up).
+__global__ void scratch_clear_kernel(uint64_t *words, int64_t n) {
+    const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (int64_t i = gid; i < n; i += stride) words[i] = 0;
+    if (gid == 0) {
+        int32_t *header = reinterpret_cast<int32_t *>(words);
+        header[1] = 1;
+    }
+}
+
+// Scratch of ep_layout_noalloc: the layout scans' ticket, epoch and per-tile
+// status words in a file-scope device array, so that call needs no
+// workspace region of its own.  Each device holds its own copy (at its own
+// address, found once per device with hipGetSymbolAddress); every
+// ep_layout_noalloc call on a device shares it, so such calls that overlap
+// on one device race.
+static __device__ __align__(256) uint64_t scratch[kScratchBytes / 8];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices] = {};
+
 }  // namespace
+
+hipError_t layout_scratch(hipStream_t stream, uint64_t **status, int32_t **ticket,
+                          int32_t **epoch) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void *ptr = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(g_scratch_mutex);
+        ptr = g_scratch_ptr[dev];
+        if (!ptr) {
+            // Set-up, once per device with that device current: the array's
+            // device address, then one clear (ticket 0, epoch 1, status
+            // words 0) ordered before the first layout on this stream.
+            e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            if (!ptr) return hipErrorInvalidSymbol;
+            scratch_clear_kernel<<<dim3(256), dim3(256), 0, stream>>>(
+                static_cast<uint64_t *>(ptr), kScratchBytes / 8);
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            g_scratch_ptr[dev] = ptr;
+        }
+    }
+    char *base = static_cast<char *>(ptr);
+    *ticket = reinterpret_cast<int32_t *>(base);
+    *epoch = reinterpret_cast<int32_t *>(base) + 1;
+    *status = reinterpret_cast<uint64_t *>(base + kScratchHeaderBytes);
+    return hipSuccess;
+}
 
 hipError_t launch_handle_clear(int32_t *scalars, uint64_t *tile_status, int64_t status_words,
                                hipStream_t stream) {

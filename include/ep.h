@@ -191,6 +191,29 @@ ep_status ep_layout(ep_handle *h, const void *topk_idx, ep_dtype idx_dtype,
                     hipStream_t stream);
 
 /*
+ * ep_layout for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same arguments, checks, kernels and outputs as ep_layout; the layout
+ * scans' scratch (tile ticket, call epoch, per-tile status words) lives in
+ * a static device array of the library, EP_LAYOUT_SCRATCH_BYTES (1 MiB) per
+ * device, held until the process ends, instead of in the handle's
+ * workspace.  The first call on a device finds that array's address and
+ * enqueues one clear kernel on `stream`; no call allocates or frees.
+ * Returns EP_ERR_WORKSPACE, with nothing launched, when the batch needs
+ * more status words than the array holds: (number of tiles) * (E + 2) >
+ * (1 MiB - 256) / 8, with 128 tokens per tile at K = 8 up to 64 tiles
+ * (65536 slots) and 256 tokens per tile beyond (e.g. E = 256: up to
+ * 507 tiles, 129792 tokens at K = 8).  Every ep_layout_noalloc call on a
+ * device shares the array: calls that overlap on one device (other streams,
+ * other threads) race and may produce wrong layouts; calls ordered on one
+ * stream are safe, and the array keeps the last call's status words.
+ */
+#define EP_LAYOUT_SCRATCH_BYTES (1 << 20)
+ep_status ep_layout_noalloc(ep_handle *h, const void *topk_idx, ep_dtype idx_dtype,
+                            int32_t num_tokens, int32_t *cumulative_stats,
+                            hipStream_t stream);
+
+/*
  * The only blocking call besides import [Ch7 §7.2: with CPU sync the host
  * waits for the receive counts and then sizes outputs exactly].  Waits for
  * `stream`, then copies to any non-NULL host pointer: counts [E], psum [E+1],

@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported():
     names = declared_functions()
-    assert len(names) == 20, names
+    assert len(names) == 21, names
     for n in names:
         assert hasattr(ep.lib(), n), n
         assert n in ep._SIGNATURES, f"binding lacks {n}"
@@ -124,6 +124,25 @@ def test_layout_validation():
     small = _fake_handle()
     small.max_tokens, small.status_tiles = 1024, 1    # scratch for fewer tiles than asked
     assert ep.ep_layout(small, A16, ep.EP_I64, 1024, None, None) == ep.EP_ERR_WORKSPACE
+
+
+def test_layout_noalloc_validation_before_any_launch():
+    """ep_layout_noalloc checks what ep_layout checks, and refuses a batch
+    whose scan status words would not fit its static scratch, all before it
+    touches the device: (1 MiB - 256 B) / 8 = 131040 words hold 127 long
+    tiles of E + 2 = 1026 words (32512 tokens at K = 8); 32513 need 128."""
+    h = _fake_handle()
+    assert ep.lib().ep_layout_noalloc(None, A16, ep.EP_I64, 8, None, None) == ep.EP_ERR_NULL
+    assert ep.ep_layout_noalloc(h, A16, ep.EP_F32, 8, None, None) == ep.EP_ERR_DTYPE
+    assert ep.ep_layout_noalloc(h, A16, ep.EP_I64, 9, None, None) == ep.EP_ERR_SHAPE
+    assert ep.ep_layout_noalloc(h, None, ep.EP_I64, 8, None, None) == ep.EP_ERR_NULL
+    assert ep.ep_layout_noalloc(h, A16 + 4, ep.EP_I64, 8, None, None) == ep.EP_ERR_MISALIGNED
+    assert ep.ep_layout_noalloc(ep.ep_handle(), A16, ep.EP_I64, 0, None, None) == \
+        ep.EP_ERR_WORKSPACE
+    big = _fake_handle()
+    big.max_tokens, big.num_topk, big.num_experts = 40000, 8, 1024
+    assert ep.ep_layout_noalloc(big, A16, ep.EP_I64, 32513, None, None) == ep.EP_ERR_WORKSPACE
+    assert ep.ep_layout_noalloc(big, A16, ep.EP_I64, 40000, None, None) == ep.EP_ERR_WORKSPACE
 
 
 def test_dispatch_validation():
