@@ -2,7 +2,9 @@
 
 TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
 benchmark's CPU-baseline leg, never by the product path.  It wraps the plain C
-definitions in ``ep_oracle.c`` (built with gcc, single-threaded) and shares no
+definitions in ``ep_oracle.c`` (built with gcc; single-threaded unless
+``set_threads`` asks for more on the token loops of dispatch and combine, for
+the benchmark's all-cores leg) and shares no
 code with the HIP library.  Arrays are numpy, on the host.
 """
 from __future__ import annotations
@@ -18,7 +20,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "ep_oracle.c")
 _LIB = os.path.join(_HERE, "libep_oracle.so")
 
-CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
+CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
           "-fPIC", "-shared", "-Wall", "-Wextra"]
 
 ERR_CAPACITY = 1
@@ -38,6 +40,8 @@ _I = ctypes.c_int64
 
 
 def _bind(lib):
+    lib.oracle_set_threads.restype = None
+    lib.oracle_set_threads.argtypes = [ctypes.c_int]
     lib.oracle_capacity_bound.restype = _I
     lib.oracle_capacity_bound.argtypes = [_I, _I, _I, _I]
     lib.oracle_layout.restype = ctypes.c_int
@@ -88,6 +92,12 @@ def load(path: Optional[str] = None):
             build()
         _lib = _bind(ctypes.CDLL(_LIB))
     return _lib
+
+
+def set_threads(threads: int, lib=None) -> None:
+    """Threads of the token loops of dispatch and the combines (1 = the plain
+    sequential loops; results are identical for any count)."""
+    (lib or load()).oracle_set_threads(int(threads))
 
 
 def _ptr(a: Optional[np.ndarray]):

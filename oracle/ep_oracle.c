@@ -6,7 +6,7 @@
  * check and the benchmark's CPU-baseline leg load it; the product path never
  * does.  It shares no code, header, table or helper with the HIP library.
  *
- * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -shared -fPIC
+ * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -fopenmp -shared -fPIC
  * (x86-64 SSE arithmetic: every float operation below is one IEEE-754
  * binary32 operation rounded to nearest even; nothing is fused or reassociated).
  *
@@ -52,6 +52,19 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+
+/*
+ * Threads of the token loops of oracle_dispatch and of the combines (the
+ * benchmark's all-cores leg; 1 by default).  Tokens are independent: each
+ * writes only its own slot rows or output row, so any thread count gives
+ * the same bytes as one thread.  Every other function is single-threaded.
+ */
+static int g_threads = 1;
+
+void oracle_set_threads(int threads)
+{
+    g_threads = threads > 1 ? threads : 1;
+}
 
 /* Error codes returned by oracle_layout. */
 #define ORACLE_OK 0
@@ -181,6 +194,7 @@ void oracle_dispatch(int64_t T, int64_t K, int64_t E, int64_t row_bytes,
                      const int32_t *dst, uint8_t *out_x, uint32_t *out_sf,
                      int64_t o_ts, int64_t o_hs, float *out_w, int zero_padding)
 {
+#pragma omp parallel for num_threads(g_threads) if (g_threads > 1) schedule(static)
     for (int64_t t = 0; t < T; ++t) {
         for (int64_t k = 0; k < K; ++k) {
             int64_t r = dst[t * K + k];
@@ -195,6 +209,7 @@ void oracle_dispatch(int64_t T, int64_t K, int64_t E, int64_t row_bytes,
     }
     if (!zero_padding)
         return;
+#pragma omp parallel for num_threads(g_threads) if (g_threads > 1) schedule(static)
     for (int64_t e = 0; e < E; ++e) {
         for (int64_t r = (int64_t)psum[e] + counts[e]; r < psum[e + 1]; ++r) {
             memset(out_x + r * row_bytes, 0, (size_t)row_bytes);
@@ -244,6 +259,7 @@ static void combine_tokens(int64_t T, int64_t K, int64_t H, const uint16_t *y,
                            const int64_t *topk_idx, const int32_t *dst,
                            const uint16_t *b0, const uint16_t *b1, uint16_t *out)
 {
+#pragma omp parallel for num_threads(g_threads) if (g_threads > 1) schedule(static)
     for (int64_t t = 0; t < T; ++t) {
         for (int64_t h = 0; h < H; ++h) {
             float acc = 0.0f;
