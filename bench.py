@@ -8,16 +8,22 @@ with fp32 weights.  Default workload: prefill, 4096 tokens x hidden 7168,
 expert_alignment 128, buffers sized at the worst-case bound (65280 rows).
 Inputs are seeded synthetic data, resident in HBM before timing starts.
 
-Prints one JSON line.  ``value`` is whole-step algorithmic HBM throughput
-(GB/s); per-kernel microseconds, GB/s and fractions of the 8 TB/s HBM peak
-are reported beside it, with the roofline of the dominant kernel (combine)
-and the CPU oracle's throughput on the host as a baseline.  Per-call times
-come from HIP events that the library attaches to the calls' own kernel
-dispatches (ep_time_next_call), on the stream the kernels run on.
+Prints one JSON line.  ``value`` is the whole step's algorithmic HBM
+throughput (GB/s) over back-to-back steps.  Per-call figures (``kernels``)
+follow the cache-cold protocol: every timed call runs right after a 1 GiB
+read that leaves L2 and the 256 MB MALL full of unrelated clean lines, and
+is timed by HIP events attached to its own kernel dispatches
+(ep_time_next_call); median, p10, p90 and mean over the calls.  Back-to-back
+per-call figures are the secondary ones (``kernels_back_to_back``).  Beside
+them: the calls' time including the write-back of what they leave dirty in
+the MALL, bandwidth ceilings measured with plain kernels of the same access
+patterns (libep_ceilings.so), the roofline of dispatch and combine, and the
+CPU oracle's throughput on the host's cores as a baseline.
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -29,41 +35,50 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, AMD published peak
-PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "prefill_hbm_counters.json")
+MALL_BYTES = 256 << 20          # MI355X last-level cache (Infinity Cache)
+FLUSH_BYTES = 1 << 30           # the cache flush: a 1 GiB read
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "hbm_counters.json")
 CSRC = os.path.join(ROOT, "combine_ep_layout_08_amd", "csrc")
-KERNEL_SOURCES = {"combine": ["ep_combine.hip", "ep_internal.h"],
-                  "dispatch": ["ep_dispatch.hip", "ep_internal.h"]}
+CEILINGS_LIB = os.path.join(ROOT, "combine_ep_layout_08_amd", "libep_ceilings.so")
+# Sources whose change makes a kernel's committed HBM counters stale: the
+# kernel's file, the shared header, and the C ABI that chooses its launch
+# (grid, which work units run, which outputs are written).
+KERNEL_SOURCES = {"combine": ["ep_combine.hip", "ep_internal.h", "ep_api.cpp"],
+                  "dispatch": ["ep_dispatch.hip", "ep_internal.h", "ep_api.cpp"],
+                  "layout": ["ep_layout.hip", "ep_internal.h", "ep_api.cpp"]}
+PHASES = ("steps", "cold", "writeback", "ceilings", "graph", "backward", "rank", "quant")
 
 
-def parse():
+def parse(argv=None):
     p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--config", default="prefill", help="workload name (default prefill)")
+    p.add_argument("--calls", type=int, default=50,
+                   help="timed calls per entry point in the cache-cold protocol "
+                        "(after 5 untimed ones)")
+    p.add_argument("--phases", default=",".join(PHASES),
+                   help="comma-separated phases to run, of: " + ", ".join(PHASES))
     p.add_argument("--no-cpu-baseline", action="store_true",
                    help="skip the oracle timing (for profiler runs)")
-    p.add_argument("--cpu-seconds", type=float, default=10.0,
-                   help="minimum oracle time for the CPU baseline")
-    p.add_argument("--cold-reps", type=int, default=30,
-                   help="calls per kernel in the cold-cache phase after the timed steps (0 = skip)")
-    p.add_argument("--backward-reps", type=int, default=30,
-                   help="calls of each backward entry point after the timed steps (0 = skip)")
-    p.add_argument("--rank-reps", type=int, default=30,
-                   help="calls of the rank-layout and per-token-bias entry points (0 = skip)")
+    p.add_argument("--cpu-seconds", type=float, default=6.0,
+                   help="minimum oracle time per CPU-baseline leg (1 thread, all cores)")
     p.add_argument("--cpu-row-tokens", type=int, default=512,
                    help="tokens of the CPU-oracle sample for the calls beyond the step")
-    p.add_argument("--quant-reps", type=int, default=30,
-                   help="calls timed for the FP8 quantiser phase (0 skips it)")
+    p.add_argument("--reps", type=int, default=30,
+                   help="cache-cold calls per entry point in the backward, rank and "
+                        "quantiser phases")
     p.add_argument("--graph-steps", type=int, default=200,
-                   help="replays of one step captured in a HIP graph, timed after the "
-                        "eager steps (0 = skip)")
-    p.add_argument("--flush", action="store_true",
-                   help="read a 1 GiB scratch buffer before every call (outside the per-call "
-                        "events) so each kernel starts with cold L2 and MALL")
+                   help="replays of one step captured in a HIP graph")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device copy (profiler calibration)")
-    return p.parse_args()
+    a = p.parse_args(argv)
+    a.phases = [x for x in a.phases.split(",") if x]
+    bad = [x for x in a.phases if x not in PHASES]
+    if bad:
+        p.error(f"unknown phases {bad}")
+    return a
 
 
 def algorithmic_bytes(cfg, V: int, G: int, expanded: int, idx_bytes: int = 8) -> dict:
@@ -82,6 +97,14 @@ def algorithmic_bytes(cfg, V: int, G: int, expanded: int, idx_bytes: int = 8) ->
     return {"layout": layout, "dispatch": dispatch, "combine": combine}
 
 
+def written_bytes(cfg, V: int, G: int) -> dict:
+    """Bytes each call writes (the part that can sit dirty in the MALL)."""
+    T, H = cfg.tokens, cfg.hidden
+    R = H if cfg.fp8 else 2 * H
+    S = 4 * (H // 128) if cfg.fp8 else 0
+    return {"dispatch": (V + (G if cfg.zero_padding else 0)) * (R + S), "combine": T * 2 * H}
+
+
 def kernel_source_hash(kernel: str) -> str:
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[kernel]:
@@ -90,59 +113,232 @@ def kernel_source_hash(kernel: str) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counters
-    (FETCH_SIZE + WRITE_SIZE, calibrated on a plain copy), if they were taken
-    on the kernel's current source; else None."""
+def counter_record(kernel: str, workload: str):
+    """The committed rocprofv3 record of `kernel` at `workload`, or None."""
     if not os.path.exists(PROFILE_COUNTERS):
         return None
     with open(PROFILE_COUNTERS) as f:
-        k = json.load(f).get("kernels", {}).get(kernel)
-    if not k or k.get("source_sha256_16") != kernel_source_hash(kernel):
-        return None
-    return k.get("hbm_bytes_per_launch")
+        return json.load(f).get("workloads", {}).get(workload, {}).get(kernel)
 
 
-def copy_calibration():
-    import torch
-    n = 1 << 30
-    a = torch.empty(n, dtype=torch.uint8, device="cuda")
-    b = torch.empty(n, dtype=torch.uint8, device="cuda")
-    a.fill_(1)
+def measured_traffic(kernel: str, workload: str = "prefill"):
+    """(HBM bytes per launch from the committed FETCH_SIZE + WRITE_SIZE
+    counters, calibrated on a plain copy; stale flag).  The bytes are None
+    when no record exists or when the record was taken on another version of
+    the kernel's sources (stale = True then, and bench.py warns)."""
+    rec = counter_record(kernel, workload)
+    if not rec:
+        return None, False
+    if rec.get("source_sha256_16") != kernel_source_hash(kernel):
+        return None, True
+    return rec.get("hbm_bytes_per_launch"), False
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_threads() -> int:
+    """Host cores this process may use: its affinity mask, capped by
+    OMP_NUM_THREADS when that is set (the GPU machine's share of the host)."""
+    n = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, n)
+
+
+# ---------------------------------------------------------------- ceilings library
+
+class Ceilings:
+    """ctypes binding of libep_ceilings.so (bandwidth-ceiling kernels)."""
+
+    def __init__(self, torch):
+        if not os.path.exists(CEILINGS_LIB):
+            raise RuntimeError(f"{CEILINGS_LIB} is missing: build it with "
+                               "`python -m combine_ep_layout_08_amd.build`")
+        self.torch = torch
+        lib = ctypes.CDLL(CEILINGS_LIB)
+        P, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+        sig = {"epc_read_sink_words": (I64, [SZ, I32, I32]),
+               "epc_read": (ctypes.c_int, [P, SZ, P, I32, I32, I32, P, P, P]),
+               "epc_write": (ctypes.c_int, [P, SZ, ctypes.c_uint32, I32, I32, I32, P, P, P]),
+               "epc_copy": (ctypes.c_int, [P, P, SZ, I32, I32, I32, P, P, P]),
+               "epc_row_store": (ctypes.c_int, [P, I64, I64, P, I64, I32, P, P, P]),
+               "epc_gather": (ctypes.c_int, [P, P, I64, I64, P, I64, I32, P, P, P])}
+        for name, (res, args) in sig.items():
+            fn = getattr(lib, name)
+            fn.restype, fn.argtypes = res, args
+        self.lib = lib
+        self.sink = torch.empty(int(lib.epc_read_sink_words(FLUSH_BYTES, 1, 0)) + 64,
+                                dtype=torch.int32, device="cuda")
+        self.flush_buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda")
+
+    @staticmethod
+    def _stream():
+        import combine_ep_layout_08_amd as ep
+        return ep._stream()
+
+    @staticmethod
+    def _ev(e):
+        if e is None:
+            return None
+        if e.cuda_event == 0:
+            e.record()
+        return e.cuda_event
+
+    def _ok(self, rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} failed ({rc})")
+
+    # Tunables of the sequential kernels: (vectors per thread, blocks,
+    # non-temporal); FLUSH_TUNE reads with the most requests in flight.
+    FLUSH_TUNE = (4, 0, 0)
+
+    def read(self, t, nbytes=None, start=None, stop=None, tune=FLUSH_TUNE):
+        n = t.numel() * t.element_size() if nbytes is None else nbytes
+        self._ok(self.lib.epc_read(t.data_ptr(), n, self.sink.data_ptr(), *tune, self._stream(),
+                                   self._ev(start), self._ev(stop)), "epc_read")
+
+    def flush(self):
+        """Leave L2 and the MALL full of clean lines of an unrelated buffer."""
+        self.read(self.flush_buf)
+
+    def write(self, t, nbytes, start=None, stop=None, tune=FLUSH_TUNE):
+        self._ok(self.lib.epc_write(t.data_ptr(), nbytes, 7, *tune, self._stream(),
+                                    self._ev(start), self._ev(stop)), "epc_write")
+
+    def copy(self, dst, src, nbytes, start=None, stop=None, tune=FLUSH_TUNE):
+        self._ok(self.lib.epc_copy(dst.data_ptr(), src.data_ptr(), nbytes, *tune, self._stream(),
+                                   self._ev(start), self._ev(stop)), "epc_copy")
+
+    def row_store(self, dst, rows, row_bytes, slot_row, tokens, K, start=None, stop=None):
+        self._ok(self.lib.epc_row_store(dst.data_ptr(), rows, row_bytes, slot_row.data_ptr(),
+                                        tokens, K, self._stream(), self._ev(start),
+                                        self._ev(stop)), "epc_row_store")
+
+    def gather(self, out, inp, rows, row_bytes, slot_row, tokens, K, start=None, stop=None):
+        self._ok(self.lib.epc_gather(out.data_ptr(), inp.data_ptr(), rows, row_bytes,
+                                     slot_row.data_ptr(), tokens, K, self._stream(),
+                                     self._ev(start), self._ev(stop)), "epc_gather")
+
+
+# ---------------------------------------------------------------- timing protocols
+
+def _stats(us):
+    import numpy as np
+    return {"us_median": round(statistics.median(us), 2),
+            "us_p10": round(float(np.percentile(us, 10)), 2),
+            "us_p90": round(float(np.percentile(us, 90)), 2),
+            "us_mean": round(statistics.mean(us), 2), "calls": len(us)}
+
+
+def _rate(nbytes, us):
+    gbps = nbytes / (us * 1e-6) / 1e9
+    return {"GBps": round(gbps, 1), "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+
+
+def events(torch, n):
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    for a, b in ev:                 # created (first record) outside any timed region
+        a.record()
+        b.record()
     torch.cuda.synchronize()
-    for _ in range(3):
-        b.copy_(a)
-    torch.cuda.synchronize()
-    print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
+    return ev
 
 
-def ceilings(torch, nbytes=1 << 30, reps=5):
-    """Measured device ceilings: 1 GiB device-to-device copy and fill (torch
-    kernels)."""
-    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
-    b = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
-    a.fill_(3)
-    b.copy_(a)
+def time_cold(torch, ep, ceil, fn, calls, warm=5):
+    """Cache-cold per-call protocol: `warm` untimed calls, then `calls` calls,
+    each right after the 1 GiB flush (outside its events), each timed by
+    events attached to its own kernels.  Returns the list of µs."""
+    for _ in range(warm):
+        ceil.flush()
+        fn()
+    ev = events(torch, calls)
+    for e0, e1 in ev:
+        ceil.flush()
+        ep.time_next_call(e0, e1)
+        fn()
     torch.cuda.synchronize()
+    return [e0.elapsed_time(e1) * 1e3 for e0, e1 in ev]
+
+
+def time_back_to_back(torch, ep, fn, calls):
+    """The same call repeated with nothing between: µs per call."""
+    fn()
+    ev = events(torch, calls)
+    for e0, e1 in ev:
+        ep.time_next_call(e0, e1)
+        fn()
+    torch.cuda.synchronize()
+    return [e0.elapsed_time(e1) * 1e3 for e0, e1 in ev]
+
+
+def time_with_writeback(torch, ep, ceil, fn, calls, probe):
+    """The call's time including the write-back of the lines it leaves dirty
+    in the MALL: after a flush, the interval from the call's first kernel to
+    the end of a fixed 1 GiB read (`probe`, which evicts those lines), minus
+    the same read timed alone after a flush; medians over `calls` pairs taken
+    in turn."""
+    with_call, alone = [], []
+    ev = events(torch, 2 * calls)
+    for i in range(calls):
+        e0, e1 = ev[2 * i]
+        ceil.flush()
+        ep.ep_time_next_call(e0.cuda_event, None)     # stamps the call's first kernel
+        fn()
+        ceil.read(probe, stop=e1)
+        f0, f1 = ev[2 * i + 1]
+        ceil.flush()
+        ceil.read(probe, start=f0, stop=f1)
+    torch.cuda.synchronize()
+    for i in range(calls):
+        e0, e1 = ev[2 * i]
+        f0, f1 = ev[2 * i + 1]
+        with_call.append(e0.elapsed_time(e1) * 1e3)
+        alone.append(f0.elapsed_time(f1) * 1e3)
+    a, b = statistics.median(with_call), statistics.median(alone)
+    return {"call_plus_read_us_median": round(a, 2), "read_alone_us_median": round(b, 2),
+            "us_with_writeback": round(a - b, 2)}
+
+
+def time_ceiling(torch, ceil, fn, calls):
+    """A ceiling kernel under the cache-cold protocol (fn takes start, stop)."""
+    fn(None, None)
+    ev = events(torch, calls)
+    for e0, e1 in ev:
+        ceil.flush()
+        fn(e0, e1)
+    torch.cuda.synchronize()
+    return statistics.median(e0.elapsed_time(e1) * 1e3 for e0, e1 in ev)
+
+
+def time_calls(torch, ep, ceil, calls, nbytes, reps):
+    """Cache-cold median/p10/p90 per call, and the back-to-back mean."""
     out = {}
-    for name, fn, moved in (("copy", lambda: b.copy_(a), 2 * nbytes),
-                            ("fill", lambda: b.fill_(7), nbytes)):
-        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s.record()
-        for _ in range(reps):
-            fn()
-        e.record()
-        torch.cuda.synchronize()
-        ms = s.elapsed_time(e) / reps
-        out[name + "_GBps"] = round(moved / ms / 1e6, 1)
-    del a, b
+    for name, fn in calls.items():
+        cold = _stats(time_cold(torch, ep, ceil, fn, reps))
+        warm = statistics.mean(time_back_to_back(torch, ep, fn, reps))
+        out[name] = {**cold, "bytes": nbytes[name], **_rate(nbytes[name], cold["us_median"]),
+                     "back_to_back_us_mean": round(warm, 2),
+                     "back_to_back_GBps": _rate(nbytes[name], warm)["GBps"]}
     return out
 
 
-def cpu_baseline(cfg, wl, y_host, min_seconds: float):
-    """Time the CPU oracle (single thread, as it stands) on the same workload:
-    full layout + dispatch + combine of the whole batch, repeated until
-    ``min_seconds`` have passed; median step time."""
+# ---------------------------------------------------------------- CPU oracle
+
+def cpu_baseline(cfg, wl, y_host, min_seconds: float, threads: int):
+    """The CPU oracle as it stands on the same workload: layout (single
+    threaded) + dispatch + combine (OpenMP over tokens with `threads`) of the
+    whole batch, repeated until ``min_seconds`` have passed; median step."""
     import numpy as np
     import oracle
     import torch
@@ -152,18 +348,21 @@ def cpu_baseline(cfg, wl, y_host, min_seconds: float):
     out_x = np.empty((cap, x_bytes.shape[1]), np.uint8)
     out_sf = np.empty((cap, sf.shape[1]), np.float32) if sf is not None else None
     times = []
-    lay = None
-    t_end = time.perf_counter() + min_seconds
-    while True:
-        t0 = time.perf_counter()
-        lay = oracle.layout(wl.topk_idx, cfg.experts, cfg.alignment, cap)
-        oracle.dispatch(x_bytes, lay, cap, sf=sf, zero_padding=cfg.zero_padding,
-                        out_x=out_x, out_sf=out_sf)
-        oracle.combine(y_host, wl.topk_idx, lay.dst, wl.topk_weights)
-        times.append(time.perf_counter() - t0)
-        if time.perf_counter() >= t_end and len(times) >= 1:
-            break
-    return statistics.median(times), len(times), lay
+    oracle.set_threads(threads)
+    try:
+        t_end = time.perf_counter() + min_seconds
+        while True:
+            t0 = time.perf_counter()
+            lay = oracle.layout(wl.topk_idx, cfg.experts, cfg.alignment, cap)
+            oracle.dispatch(x_bytes, lay, cap, sf=sf, zero_padding=cfg.zero_padding,
+                            out_x=out_x, out_sf=out_sf)
+            oracle.combine(y_host, wl.topk_idx, lay.dst, wl.topk_weights)
+            times.append(time.perf_counter() - t0)
+            if time.perf_counter() >= t_end and len(times) >= 3:
+                break
+    finally:
+        oracle.set_threads(1)
+    return statistics.median(times), len(times)
 
 
 def _oracle_rank_quant(oracle, x_bits, idx, E, row, w):
@@ -183,6 +382,7 @@ def cpu_oracle_rows(cfg, wl, tokens: int):
     the quantiser's search does its real work (timing only)."""
     import numpy as np
     import oracle
+    import torch
     import ep_workloads as W
     T, K, E, A, H = min(tokens, cfg.tokens), cfg.topk, cfg.experts, cfg.alignment, cfg.hidden
     idx = np.ascontiguousarray(wl.topk_idx[:T])
@@ -192,9 +392,10 @@ def cpu_oracle_rows(cfg, wl, tokens: int):
     V = int((lay.dst >= 0).sum())
     row, _, nrecv = oracle.rank_layout(idx, E)
     y = np.zeros((cap, H), np.uint16)
+
     def bits(t):
         return t.view(torch.int16).numpy().view(np.uint16)
-    import torch
+
     g = bits(W.payload_bf16(T, H, cfg.seed + 1, 3, "cpu"))
     b = np.zeros((T, H), np.uint16)
     gwr = np.zeros(cap, np.float32)
@@ -239,44 +440,20 @@ def cpu_oracle_rows(cfg, wl, tokens: int):
     return out
 
 
-def time_calls(calls, nbytes, reps, flush=None):
-    """Each call once untimed, then `reps` calls whose kernel intervals are
-    stamped by ep_time_next_call; mean µs, GB/s of the algorithmic bytes.
-    With `flush` (a 1 GiB device tensor), `reps` more calls each run right
-    after a full read of it (outside the stamped interval), so inputs that
-    would fit the 256 MB MALL between repeated calls come from HBM: the
-    cold_* figures."""
+def copy_calibration():
     import torch
-    import combine_ep_layout_08_amd as ep
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
 
-    def run(fn, cold):
-        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                 for _ in range(reps)]
-        for e0, e1 in pairs:
-            e0.record()
-            e1.record()
-        for e0, e1 in pairs:
-            if cold:
-                flush.sum()
-            ep.time_next_call(e0, e1)
-            fn()
-        torch.cuda.synchronize()
-        return statistics.mean(e0.elapsed_time(e1) * 1e3 for e0, e1 in pairs)
 
-    out = {}
-    for name, fn in calls.items():
-        fn()
-        us = run(fn, False)
-        gbps = nbytes[name] / (us * 1e-6) / 1e9
-        out[name] = {"us_mean": round(us, 2), "bytes": nbytes[name], "GBps": round(gbps, 1),
-                     "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
-        if flush is not None:
-            cus = run(fn, True)
-            cg = nbytes[name] / (cus * 1e-6) / 1e9
-            out[name].update({"cold_us_mean": round(cus, 2), "cold_GBps": round(cg, 1),
-                              "cold_frac_hbm_peak": round(cg / HBM_PEAK_GBPS, 4)})
-    return out
-
+# ---------------------------------------------------------------- main
 
 def main():
     args = parse()
@@ -295,7 +472,8 @@ def main():
     import combine_ep_layout_08_amd as ep
     import ep_workloads as W
 
-    cfg = W.CONFIGS[args.config]
+    phases = set(args.phases)
+    cfg = W.config(args.config)
     cap = ep.ep_capacity_bound(cfg.tokens, cfg.topk, cfg.experts, cfg.alignment)
     wl = W.make(cfg, device="cuda", y_rows=cap)
     idx = torch.from_numpy(wl.topk_idx).cuda()
@@ -305,14 +483,7 @@ def main():
     out_sf = (torch.empty((cap, cfg.hidden // 128), dtype=torch.float32, device="cuda")
               if cfg.fp8 else None)
     out = torch.empty((cfg.tokens, cfg.hidden), dtype=torch.bfloat16, device="cuda")
-
-    # Cache flush by reading 1 GiB (four times the 256 MB MALL): the caches
-    # end up full of clean lines, so the next kernel pays no write-back.
-    scratch = (torch.ones(1 << 28, dtype=torch.int32, device="cuda") if args.flush else None)
-
-    def flush():
-        if scratch is not None:
-            scratch.sum()
+    ceil = Ceilings(torch)
 
     # The step's three calls, validated and marshalled once (bound calls:
     # the same entry points and kernels, about 3 us of host time per call
@@ -322,20 +493,11 @@ def main():
     dispatch_call = h.bind_dispatch(wl.x, sf=wl.sf, zero_padding=cfg.zero_padding,
                                     out_x=out_x, out_sf=out_sf)
     combine_call = h.bind_combine(wl.y, topk_weights=w, bias=wl.bias, out=out)
+    calls = {"layout": layout_call, "dispatch": dispatch_call, "combine": combine_call}
 
-    def step(ev=None):
-        # ev: six events; each pair is stamped on the kernels of one call.
-        flush()
-        if ev is not None:
-            ep.time_next_call(ev[0], ev[1])
+    def step():
         layout_call()
-        flush()
-        if ev is not None:
-            ep.time_next_call(ev[2], ev[3])
         dispatch_call()
-        flush()
-        if ev is not None:
-            ep.time_next_call(ev[4], ev[5])
         combine_call()
 
     for _ in range(args.warmup):
@@ -345,56 +507,144 @@ def main():
     V = int((wl.topk_idx >= 0).sum())
     G = int(rc["num_expanded"]) - V
     nbytes = algorithmic_bytes(cfg, V, G, int(rc["num_expanded"]))
+    total_bytes = sum(nbytes.values())
 
-    # Timed region: exactly `steps` steps, synchronised on both sides, with
-    # nothing but the calls themselves on the stream.
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
+    # Timed region: exactly `steps` steps back to back, synchronised on both
+    # sides, nothing but the calls on the stream.
+    ms_per_step = None
+    kernels_b2b = None
+    if "steps" in phases:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+        # Back-to-back per-call figures: `steps` more steps with each call's
+        # kernels stamped by events attached to their dispatches (the stamps
+        # cost GPU time of their own, ≈ 5 µs per call, so they stay out of
+        # the timed region above).
+        evs = [events(torch, 3) for _ in range(args.steps)]
+        per = {k: [] for k in calls}
+        for e3 in evs:
+            for (e0, e1), (name, fn) in zip(e3, calls.items()):
+                ep.time_next_call(e0, e1)
+                fn()
+        torch.cuda.synchronize()
+        for e3 in evs:
+            for (e0, e1), name in zip(e3, calls):
+                per[name].append(e0.elapsed_time(e1) * 1e3)
+        kernels_b2b = {k: {**_stats(v), **_rate(nbytes[k], statistics.mean(v))}
+                       for k, v in per.items()}
 
-    # Kernel durations: `steps` more steps, each call's kernels stamped by
-    # events attached to their dispatches (ep_time_next_call).  The stamps
-    # cost GPU time of their own (measured ≈ 5 µs per call), so they stay out
-    # of the timed region above; the events are created (first record)
-    # before this region starts.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
-    for e6 in evs:
-        for e in e6:
-            e.record()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    ms_per_step_stamped = (time.perf_counter() - t1) * 1e3 / args.steps
-    per = {"layout": [], "dispatch": [], "combine": []}
-    for e in evs:
-        per["layout"].append(e[0].elapsed_time(e[1]) * 1e3)
-        per["dispatch"].append(e[2].elapsed_time(e[3]) * 1e3)
-        per["combine"].append(e[4].elapsed_time(e[5]) * 1e3)
-    step_gpu_ms = sum(e[0].elapsed_time(e[5]) for e in evs) / args.steps
-    kernels = {}
-    for k, v in per.items():
-        us = statistics.mean(v)
-        gbps = nbytes[k] / (us * 1e-6) / 1e9
-        kernels[k] = {"us_mean": round(us, 2), "us_median": round(statistics.median(v), 2),
-                      "us_p10": round(float(np.percentile(v, 10)), 2),
-                      "us_p90": round(float(np.percentile(v, 90)), 2),
-                      "bytes": nbytes[k], "GBps": round(gbps, 1),
-                      "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
-        if k in KERNEL_SOURCES:
-            kernels[k]["traffic"] = measured_traffic(k)
-    # Graph replay (after the timed region): the step's three calls captured
-    # once in a HIP graph (torch.cuda.CUDAGraph; the library launches on the
-    # capturing stream and allocates nothing) and replayed back to back, so
-    # the host's per-call launch cost drops out; the replayed output must equal
-    # the eager one bit for bit.
+    # Headline per-call figures: the cache-cold protocol.
+    kernels = None
+    if "cold" in phases:
+        kernels = {}
+        for name, fn in calls.items():
+            st = _stats(time_cold(torch, ep, ceil, fn, args.calls))
+            kernels[name] = {**st, "bytes": nbytes[name], **_rate(nbytes[name], st["us_median"]),
+                             "mean_GBps": _rate(nbytes[name], st["us_mean"])["GBps"]}
+            if name in ("dispatch", "combine"):
+                traffic, stale = measured_traffic(name, cfg.name)
+                kernels[name]["traffic"] = traffic
+                if stale:
+                    kernels[name]["traffic_stale"] = True
+                    print(f"bench.py: committed HBM counters of {name} at {cfg.name} were taken "
+                          "on other kernel sources; traffic reported as null", file=sys.stderr)
+        h.read_counts()
+
+    # Write-back: what the call leaves dirty in the MALL, evicted by a fixed
+    # 1 GiB read; the difference to the read alone is the call's time with
+    # its write-back.
+    writeback = None
+    if "writeback" in phases:
+        probe = torch.ones(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda")
+        wbytes = written_bytes(cfg, V, G)
+        writeback = {"protocol": "flush; call + 1 GiB read, minus the 1 GiB read alone; "
+                                 "medians", "mall_bytes": MALL_BYTES}
+        for name in ("dispatch", "combine"):
+            r = time_with_writeback(torch, ep, ceil, calls[name], max(10, args.calls // 2), probe)
+            r.update(_rate(nbytes[name], r["us_with_writeback"]))
+            r["written_bytes"] = wbytes[name]
+            r["writes_fit_mall"] = wbytes[name] < MALL_BYTES
+            writeback[name] = r
+        del probe
+        h.read_counts()
+
+    # Ceilings: plain kernels of the same access patterns, cache-cold.
+    ceilings = None
+    if "ceilings" in phases:
+        # Sizes: the sequential write and copy move 4 GiB and 2 + 2 GiB, so
+        # the 256 MB MALL, which can keep the last written lines dirty past
+        # the kernel's end, absorbs at most ~6 % of their writes; the write
+        # of the dispatch's own output bytes fits the MALL and shows what
+        # absorption alone gives.
+        n = 20
+        big = 4 * FLUSH_BYTES
+        a = torch.empty(big // 4, dtype=torch.int32, device="cuda")
+        b = torch.empty(big // 8, dtype=torch.int32, device="cuda")
+        a.fill_(3)
+        K, H = cfg.topk, cfg.hidden
+        R = H if cfg.fp8 else 2 * H
+        wd = written_bytes(cfg, V, G)["dispatch"]
+        wd16 = min(FLUSH_BYTES, (wd + 15) // 16 * 16)
+        contig = torch.arange(cfg.tokens * K, dtype=torch.int32, device="cuda")
+        y_rows = wl.y.shape[0]
+        # The sequential ceilings keep the fastest of a few launch settings
+        # (vectors per thread, grid, non-temporal).
+        tunes = [(1, 0, 0), (2, 0, 0), (4, 0, 0), (8, 0, 0), (16, 0, 0), (4, 2048, 0),
+                 (4, 8192, 0), (8, 4096, 0), (1, 0, 1), (4, 0, 1), (16, 0, 1)]
+        seq = {"read_1GiB": lambda t: (lambda s, e: ceil.read(a, FLUSH_BYTES, s, e, tune=t)),
+               "write_4GiB": lambda t: (lambda s, e: ceil.write(a, big, s, e, tune=t)),
+               "copy_2GiB": lambda t: (lambda s, e: ceil.copy(b, a, big // 2, s, e, tune=t)),
+               "write_dispatch_bytes": lambda t: (lambda s, e: ceil.write(a, wd16, s, e, tune=t))}
+        ceil_us, ceil_tune = {}, {}
+        for name, mk in seq.items():
+            best = min(((time_ceiling(torch, ceil, mk(t), n), t) for t in tunes))
+            ceil_us[name], ceil_tune[name] = best
+        ceil_us.update({
+            "row_store_dispatch_rows": time_ceiling(
+                torch, ceil, lambda s, e: ceil.row_store(out_x, cap, R, h.dst_slot, cfg.tokens, K,
+                                                         s, e), n),
+            "gather_combine_rows": time_ceiling(
+                torch, ceil, lambda s, e: ceil.gather(out, wl.y, y_rows, 2 * H, h.dst_slot,
+                                                      cfg.tokens, K, s, e), n),
+        })
+        if y_rows >= cfg.tokens * K:
+            ceil_us["gather_contiguous_rows"] = time_ceiling(
+                torch, ceil, lambda s, e: ceil.gather(out, wl.y, y_rows, 2 * H, contig,
+                                                      cfg.tokens, K, s, e), n)
+        moved = {"read_1GiB": FLUSH_BYTES, "write_4GiB": big, "copy_2GiB": big,
+                 "write_dispatch_bytes": wd16,
+                 "row_store_dispatch_rows": V * R,
+                 "gather_combine_rows": V * 2 * H + cfg.tokens * 2 * H,
+                 "gather_contiguous_rows": cfg.tokens * K * 2 * H + cfg.tokens * 2 * H}
+        ceilings = {k: {"us_median": round(v, 2), "bytes": moved[k], **_rate(moved[k], v)}
+                    for k, v in ceil_us.items()}
+        for k, t in ceil_tune.items():
+            ceilings[k]["tune"] = {"vec_per_thread": t[0], "blocks": t[1], "nontemporal": t[2]}
+        ceilings["note"] = ("cache-cold medians of plain kernels (libep_ceilings.so): sequential "
+                            "read, sequential write, 1:1 copy (best of 11 launch settings each), "
+                            "a sequential write of the dispatch's output bytes (fits the MALL), "
+                            "the dispatch's row stores alone (same rows, no loads), the "
+                            "combine's row loads and output stores alone (same rows, XOR "
+                            "instead of arithmetic), and the same with contiguous rows")
+        del a, b, contig
+        h.read_counts()
+        if kernels:
+            for name, ck in (("dispatch", "row_store_dispatch_rows"),
+                             ("combine", "gather_combine_rows")):
+                cu = ceilings[ck]["us_median"]
+                kernels[name]["ceiling"] = {"kernel": ck, "us": cu,
+                                            "frac_of_ceiling": round(cu / kernels[name]["us_median"], 4)}
+
+    # Graph replay: the step captured once in a HIP graph and replayed back
+    # to back; the replayed output must equal the eager one bit for bit.
     graph = None
-    if args.graph_steps > 0 and not args.flush:
+    if "graph" in phases and args.graph_steps > 0:
+        step()
+        torch.cuda.synchronize()
         out_eager = out.clone()
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
@@ -412,47 +662,17 @@ def main():
             cg.replay()
         torch.cuda.synchronize()
         g_ms = (time.perf_counter() - t2) * 1e3 / args.graph_steps
-        h.read_counts()                         # raises on any device error
+        h.read_counts()
         if not torch.equal(out.view(torch.int16), out_eager.view(torch.int16)):
             raise RuntimeError("graph replay gave a different combine output")
         graph = {"steps": args.graph_steps, "ms_per_step": round(g_ms, 4),
-                 "GBps": round(sum(nbytes.values()) / (g_ms * 1e-3) / 1e9, 1)}
+                 "GBps": round(total_bytes / (g_ms * 1e-3) / 1e9, 1)}
         del cg
 
-    # Cold-cache phase (after the timed region): each call runs right after a
-    # 1 GiB read that leaves L2 and the MALL full of unrelated clean lines, so
-    # its inputs come from HBM; timed by the events on its own kernels.
-    kernels_cold = None
-    big = None
-    if args.cold_reps > 0:
-        big = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
-        calls = {"layout": lambda: h.layout(idx),
-                 "dispatch": lambda: h.dispatch(wl.x, sf=wl.sf, zero_padding=cfg.zero_padding,
-                                                out_x=out_x, out_sf=out_sf),
-                 "combine": lambda: h.combine(wl.y, topk_weights=w, bias=wl.bias, out=out)}
-        kernels_cold = {}
-        for name, fn in calls.items():
-            pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                     for _ in range(args.cold_reps)]
-            for e0, e1 in pairs:
-                e0.record()
-                e1.record()
-            for e0, e1 in pairs:
-                big.sum()
-                ep.time_next_call(e0, e1)
-                fn()
-            torch.cuda.synchronize()
-            us = statistics.mean(e0.elapsed_time(e1) * 1e3 for e0, e1 in pairs)
-            gbps = nbytes[name] / (us * 1e-6) / 1e9
-            kernels_cold[name] = {"us_mean": round(us, 2), "GBps": round(gbps, 1),
-                                  "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
-
-    # Backward pair on the same layout (a separate phase after the timed
-    # steps): combine backward with row and weight gradients, dispatch
-    # backward with the row combine and the weight gather.
+    T, K, H = cfg.tokens, cfg.topk, cfg.hidden
+    # Backward pair on the same layout.
     backward = None
-    if args.backward_reps > 0:
-        T, K, H = cfg.tokens, cfg.topk, cfg.hidden
+    if "backward" in phases:
         g = W.payload_bf16(T, H, cfg.seed + 1, 3, "cuda")
         grad_y = torch.empty((cap, H), dtype=torch.bfloat16, device="cuda")
         gw_rows = torch.randn(cap, device="cuda")
@@ -462,12 +682,12 @@ def main():
                       g, topk_weights=w, y=wl.y, grad_y=grad_y, want_grad_weights=True),
                   "dispatch_backward": lambda: h.dispatch_backward(
                       wl.y, grad_out_w=gw_rows, want_grad_weights=True)}
-        backward = time_calls(bcalls, bb, args.backward_reps, big)
+        backward = time_calls(torch, ep, ceil, bcalls, bb, args.reps)
+        del g, grad_y, gw_rows
 
     # Rank (non-expanded) layout and per-token biases, on the same layout.
     rank = None
-    if args.rank_reps > 0:
-        T, K, H = cfg.tokens, cfg.topk, cfg.hidden
+    if "rank" in phases:
         nrecv = int(rc["num_recv_tokens"])
         R = H if cfg.fp8 else 2 * H
         S = 4 * (H // 128) if cfg.fp8 else 0
@@ -487,22 +707,20 @@ def main():
                   "combine_rank": lambda: h.combine_rank(xr, bias_0=b0, bias_1=b1, out=out),
                   "combine_token_biases": lambda: h.combine(wl.y, topk_weights=w, bias=wl.bias,
                                                             out=out, bias_0=b0, bias_1=b1)}
-        rank = time_calls(rcalls, rb, args.rank_reps, big)
+        rank = time_calls(torch, ep, ceil, rcalls, rb, args.reps)
         del rx, rsf, ri, rw, xr, b0, b1
 
     # FP8 quantiser on its own and fused with dispatch: bf16 rows of the
     # same workload, on the same layout, fp32 and packed UE8M0 scales.
     quant = None
-    if args.quant_reps > 0 and cfg.hidden % 128 == 0:
-        T, K, H = cfg.tokens, cfg.topk, cfg.hidden
+    if "quant" in phases and H % 128 == 0:
         xq = W.payload_bf16(T, H, cfg.seed + 5, 3, "cuda")
         qx = torch.empty((cap, H), dtype=torch.uint8, device="cuda")
         qt = torch.empty((T, H), dtype=torch.uint8, device="cuda")
-        sfs = {f: torch.empty((cap, ep.ep_sf_packs(H, c)),
-                              dtype=torch.float32 if f == "f32" else torch.int32, device="cuda")
-               for f, c in (("f32", ep.EP_SF_F32), ("ue8m0", ep.EP_SF_UE8M0))}
         P = {f: ep.ep_sf_packs(H, c) for f, c in (("f32", ep.EP_SF_F32),
                                                     ("ue8m0", ep.EP_SF_UE8M0))}
+        sfs = {f: torch.empty((cap, P[f]), dtype=torch.float32 if f == "f32" else torch.int32,
+                              device="cuda") for f in P}
         sft = {f: torch.empty((T, P[f]), dtype=torch.float32 if f == "f32" else torch.int32,
                               device="cuda") for f in P}
         nrq = int(rc["num_recv_tokens"])
@@ -526,25 +744,33 @@ def main():
                   "dispatch_rank_quant_f32": lambda: h.dispatch_rank_quant(
                       xq, "f32", topk_weights=w, out_x=rqx, out_sf=rqsf, out_topk_idx=rqi,
                       out_topk_weights=rqw)}
-        quant = time_calls(qcalls, qb, args.quant_reps, big)
+        quant = time_calls(torch, ep, ceil, qcalls, qb, args.reps)
         del xq, qx, qt, sfs, sft, rqx, rqsf, rqi, rqw
-    del big
+    h.read_counts()
 
-    total_bytes = sum(nbytes.values())
-    if args.flush:
-        # The wall time also holds the cache flushes; use the calls' own time.
-        ms_per_step = sum(kernels[k]["us_mean"] for k in kernels) / 1e3
-    value = total_bytes / (ms_per_step * 1e-3) / 1e9
-    dc_us = kernels["dispatch"]["us_mean"] + kernels["combine"]["us_mean"]
-    comb = kernels["combine"]
-    roofline = {"bound": "hbm", "achieved": comb["GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(comb["GBps"] / HBM_PEAK_GBPS, 4),
-                "traffic": measured_traffic("combine"), "kernel": "combine",
-                "bytes_per_launch": nbytes["combine"]}
-    if kernels_cold:
-        roofline["achieved_cold_cache"] = kernels_cold["combine"]["GBps"]
-        roofline["frac_cold_cache"] = kernels_cold["combine"]["frac_hbm_peak"]
-    ceil = ceilings(torch)
+    # Roofline of dispatch and combine (combine is the dominant kernel: the
+    # most bytes per step): algorithmic bytes over the cache-cold mean
+    # duration (rocprofv3's average over the same launches, with
+    # `--phases cold`, must agree), with the back-to-back figures beside.
+    roofline = None
+    if kernels:
+        def roof(name):
+            k = kernels[name]
+            ach = nbytes[name] / (k["us_mean"] * 1e-6) / 1e9
+            r = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
+                 "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
+                 "traffic": k.get("traffic"), "kernel": name,
+                 "bytes_per_launch": nbytes[name], "timing": "cache-cold mean",
+                 "frac_median": k["frac_hbm_peak"]}
+            if kernels_b2b:
+                r["frac_back_to_back"] = kernels_b2b[name]["frac_hbm_peak"]
+            if writeback and name in writeback:
+                r["frac_with_writeback"] = writeback[name]["frac_hbm_peak"]
+            if "ceiling" in k:
+                r["frac_of_ceiling"] = k["ceiling"]["frac_of_ceiling"]
+            return r
+        roofline = roof("combine")
+        roofline["per_kernel"] = {"dispatch": roof("dispatch"), "combine": roof("combine")}
 
     cpu = None
     cpu_rows = None
@@ -552,23 +778,31 @@ def main():
         y_host = wl.y.view(torch.int16).cpu().numpy().view(np.uint16)
         wl_host = W.Workload(cfg, wl.topk_idx, wl.topk_weights, wl.x.cpu(),
                              None if wl.sf is None else wl.sf.cpu(), None, None)
-        med, reps, _ = cpu_baseline(cfg, wl_host, y_host, args.cpu_seconds)
-        cpu = {"value": round(total_bytes / med / 1e9, 3), "unit": "GB/s", "cores": 1,
+        n_thr = cpu_threads()
+        med1, reps1 = cpu_baseline(cfg, wl_host, y_host, args.cpu_seconds, 1)
+        medn, repsn = cpu_baseline(cfg, wl_host, y_host, args.cpu_seconds, n_thr)
+        cpu = {"value": round(total_bytes / medn / 1e9, 3), "unit": "GB/s", "cores": n_thr,
                "kind": "oracle",
-               "sample": f"whole {cfg.name} batch ({cfg.tokens} tokens): layout + dispatch + "
-                         f"combine, {reps} repetitions, median {med:.3f} s per step, "
-                         "single-threaded C oracle",
-               "ms_per_step": round(med * 1e3, 1)}
+               "sample": f"whole {cfg.name} batch ({cfg.tokens} tokens): layout (1 thread) + "
+                         f"dispatch + combine (OpenMP over tokens, {n_thr} threads), {repsn} "
+                         f"repetitions, median {medn:.3f} s per step",
+               "ms_per_step": round(medn * 1e3, 1),
+               "single_thread": {"value": round(total_bytes / med1 / 1e9, 3), "cores": 1,
+                                 "ms_per_step": round(med1 * 1e3, 1), "repetitions": reps1},
+               "cpu_model": cpu_model()}
         cpu_rows = cpu_oracle_rows(cfg, wl_host, args.cpu_row_tokens)
 
+    value = (total_bytes / (ms_per_step * 1e-3) / 1e9) if ms_per_step else None
+    head = kernels or kernels_b2b or {}
+    dc_us = (head["dispatch"]["us_median"] + head["combine"]["us_median"]) if head else None
     line = {
         "metric": "dispatch+combine µs/call and HBM GB/s (% of peak) at 4096×7168 top-8",
-        "value": round(value, 1),
+        "value": round(value, 1) if value else None,
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": round(ms_per_step, 4) if ms_per_step else None,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -582,20 +816,24 @@ def main():
                    "topk": cfg.topk, "expert_alignment": cfg.alignment, "capacity": cap,
                    "zero_padding": cfg.zero_padding, "routed_slots": V, "gap_rows": G,
                    "seed": cfg.seed},
-        "dispatch_plus_combine_us": round(dc_us, 2),
-        "dispatch_plus_combine_GBps": round((nbytes["dispatch"] + nbytes["combine"]) /
-                                            (dc_us * 1e-6) / 1e9, 1),
-        "step_gpu_ms_stamped": round(step_gpu_ms, 4),
-        "ms_per_step_stamped": round(ms_per_step_stamped, 4),
-        "graph_replay": graph,
-        "cache_flush_between_calls": bool(args.flush),
+        "timing": {"value": "back-to-back steps, wall clock",
+                   "kernels": "cache-cold: 1 GiB read before every call, outside its events; "
+                              f"{args.calls} calls after 5 untimed; events on the call's kernels",
+                   "kernels_back_to_back": "steps back to back, events on each call's kernels"},
+        "dispatch_plus_combine_us": round(dc_us, 2) if dc_us else None,
+        "dispatch_plus_combine_GBps": (round((nbytes["dispatch"] + nbytes["combine"]) /
+                                             (dc_us * 1e-6) / 1e9, 1) if dc_us else None),
+        "uncached_dispatch_us": (round(head["layout"]["us_median"] + head["dispatch"]["us_median"],
+                                       2) if head else None),
         "kernels": kernels,
-        "kernels_cold_cache": kernels_cold,
+        "kernels_back_to_back": kernels_b2b,
+        "writeback": writeback,
+        "ceilings": ceilings,
+        "graph_replay": graph,
         "backward": backward,
         "rank_and_token_bias": rank,
         "quantize": quant,
         "roofline": roofline,
-        "ceilings": ceil,
         "cpu_baseline": cpu,
         "cpu_oracle_other_calls": cpu_rows,
     }

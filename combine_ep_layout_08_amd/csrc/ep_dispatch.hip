@@ -37,7 +37,10 @@ constexpr int kGapRowsPerBlock = kWavesPerBlock;
 // whose outputs exceed the MALL (16384 x 4096, 32768 x 7168) 0-7 % slower
 // (bound by HBM writes there).  Capping occupancy at 4 or 6 waves per SIMD
 // (EP_DISPATCH_WAVES_PER_EU) was slower at every size (prefill 48.1 / 44.3
-// us against 43.3); VPL 2 or 4 gained at 32768 x 7168 on one box and lost
+// us against 43.3).  A persistent grid of 2-8 blocks per CU whose waves
+// walk several passes, each requesting the next pass's loads before storing
+// the current one, measured 56-68 us after a flush against 46.4 at prefill
+// and 10-12 % slower at 16384 x 4096 and 32768 x 7168.  VPL 2 or 4 gained at 32768 x 7168 on one box and lost
 // on another, equal at prefill.  Cache hints of the row copy: non-temporal
 // stores measured 2-6 % slower (57 us against 47 on the FP8 prefill rows
 // together with non-temporal loads); non-temporal loads of the token rows
@@ -59,6 +62,7 @@ constexpr int kGapRowsPerBlock = kWavesPerBlock;
 #define EP_DISPATCH_BLOCKS_PER_CU 0
 #endif
 constexpr int kDispatchBlocksPerCu = EP_DISPATCH_BLOCKS_PER_CU;
+
 // Scale packs and per-row weights of a copying dispatch, when the layout's
 // source slots are given: moved by blocks of their own in expanded-row order
 // (for packs each wave takes kSfRowsPerWave consecutive rows, for weights 64,
@@ -71,7 +75,9 @@ constexpr int kDispatchBlocksPerCu = EP_DISPATCH_BLOCKS_PER_CU;
 // one box, current kernel: 43.9 -> 42.9 us back to back, 50.1 -> 47.0 us
 // after a cache flush; 2048 / 4096 blocks 45.4 / 46.0 us (48.7 / 51.6
 // flushed), 8 rows per wave 45.0 (51.1), 2 rows per wave over 4096 blocks
-// 45.0 (49.6).  Weights in the earlier form: 53.6 us stored by the token
+// 45.0 (49.6); a wave taking its 2 or 3 strided row groups at once (every
+// source slot, then every pack load requested before any is used) 44.7 /
+// 45.2 us (49.5 / 50.5 flushed).  Weights in the earlier form: 53.6 us stored by the token
 // waves against 49.0 us without a weight output.
 #ifndef EP_DISPATCH_SF_BY_ROW
 #define EP_DISPATCH_SF_BY_ROW 1
@@ -97,28 +103,15 @@ __device__ inline bool dispatch_stopped(const DispatchArgs &a) {
     return a.scalars && (a.scalars[EP_SCALAR_ERROR_BITS] & a.stop_bits);
 }
 
-// Copy one pass of a token's row (one wave: vectors [64*VPL*pass, +64*VPL))
-// to every valid slot's row; pass 0 also copies the scale packs and weight
-// when they are not moved in expanded-row order.  The row loads, the slot
-// rows and the error word are all requested before the wave waits on any
-// of them (one round trip to memory instead of three).
+// Stores of one pass of token t's row (one wave), held in v, to every valid
+// slot row in my_dst (lane k holds slot k's row, -1 if none); pass 0 also
+// stores the scale packs and weight when they are not moved in expanded-row
+// order.
 template <int VPL>
-__device__ inline void dispatch_token(const DispatchArgs &a, int64_t t, int64_t pass, int lane) {
+__device__ inline void store_token_pass(const DispatchArgs &a, int64_t t, int64_t pass, int lane,
+                                        const u32x4 (&v)[VPL], int32_t my_dst) {
     const int64_t V = a.row_vecs;
     const int K = a.num_topk;
-    const u32x4 *src = static_cast<const u32x4 *>(a.x) + t * V;
-    const int64_t c0 = pass * 64 * VPL;
-    u32x4 v[VPL];
-#pragma unroll
-    for (int q = 0; q < VPL; ++q) {
-        const int64_t c = c0 + q * 64 + lane;
-        if (c < V) v[q] = EP_DISPATCH_NT_LOAD ? __builtin_nontemporal_load(src + c) : src[c];
-    }
-    // Rows outside [0, capacity) are skipped, so no layout content can send a
-    // store out of the output buffers.
-    int32_t my_dst = lane < K ? a.dst[t * K + lane] : -1;
-    if (my_dst >= a.capacity) my_dst = -1;
-    if (dispatch_stopped(a)) return;
     if (pass == 0 && !a.src_meta) {
         if (a.out_w && my_dst >= 0) a.out_w[my_dst] = a.w ? a.w[t * K + lane] : 1.0f;
         // A token's scale packs, 64 at a time: loaded once, stored to every
@@ -132,6 +125,7 @@ __device__ inline void dispatch_token(const DispatchArgs &a, int64_t t, int64_t 
         }
     }
     u32x4 *out = static_cast<u32x4 *>(a.out_x);
+    const int64_t c0 = pass * 64 * VPL;
     for (int k = 0; k < K; ++k) {
         const int32_t r = __builtin_amdgcn_readlane(my_dst, k);
         if (r < 0) continue;
@@ -144,11 +138,43 @@ __device__ inline void dispatch_token(const DispatchArgs &a, int64_t t, int64_t 
     }
 }
 
+// Loads of one pass of token t's row and of its slot rows (rows outside
+// [0, capacity) become -1, so no layout content can send a store out of
+// the output buffers).
+template <int VPL>
+__device__ inline void load_token_pass(const DispatchArgs &a, int64_t t, int64_t pass, int lane,
+                                       u32x4 (&v)[VPL], int32_t &my_dst) {
+    const int64_t V = a.row_vecs;
+    const int K = a.num_topk;
+    const u32x4 *src = static_cast<const u32x4 *>(a.x) + t * V;
+    const int64_t c0 = pass * 64 * VPL;
+#pragma unroll
+    for (int q = 0; q < VPL; ++q) {
+        const int64_t c = c0 + q * 64 + lane;
+        if (c < V) v[q] = EP_DISPATCH_NT_LOAD ? __builtin_nontemporal_load(src + c) : src[c];
+    }
+    my_dst = lane < K ? a.dst[t * K + lane] : -1;
+    if (my_dst >= a.capacity) my_dst = -1;
+}
+
+// Copy one pass of a token's row (one wave: vectors [64*VPL*pass, +64*VPL))
+// to every valid slot's row.  The row loads, the slot rows and the error
+// word are all requested before the wave waits on any of them (one round
+// trip to memory instead of three).
+template <int VPL>
+__device__ inline void dispatch_token(const DispatchArgs &a, int64_t t, int64_t pass, int lane) {
+    u32x4 v[VPL];
+    int32_t my_dst;
+    load_token_pass<VPL>(a, t, pass, lane, v, my_dst);
+    if (dispatch_stopped(a)) return;
+    store_token_pass<VPL>(a, t, pass, lane, v, my_dst);
+}
+
 // Scale packs of kSfRowsPerWave consecutive expanded rows from r0 (one wave):
 // each routed row's packs are its source token's (source slot / K); gap rows
-// (source -1, zeroed by the gap units when asked) and rows from psum[E] on
-// are not written.  Packs go 64 at a time (one per lane and row), so a row
-// of up to 64 packs takes one load and one store per lane.
+// (source -1, zeroed by the gap units when asked) and rows from `end`
+// (psum[E]) on are not written.  Packs go 64 at a time (one per lane and
+// row), so a row of up to 64 packs takes one load and one store per lane.
 __device__ inline void dispatch_sf_rows(const DispatchArgs &a, int64_t r0, int64_t end,
                                         int lane) {
     const int64_t num_slots = static_cast<int64_t>(a.num_tokens) * a.num_topk;

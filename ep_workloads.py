@@ -75,6 +75,21 @@ CONFIGS = {
 }
 
 
+# Benchmark-only shape (not a parity configuration of its own: the layout
+# tests cover its form at 65537-70000 tokens): prefill routing at 70000
+# tokens, 560000 slots, more than 256 layout tiles of 2048 slots, the size
+# at which the layout takes its single-pass decoupled-lookback form.
+BENCH_CONFIGS = {
+    "prefill_70k": Config("prefill_70k", 70000, 7168, 256, 8, 128, "fp8", False,
+                          "grouped", 0.0, "sigmoid_norm", False, "bound", 1006),
+}
+
+
+def config(name: str) -> Config:
+    """A parity configuration or a benchmark-only shape, by name."""
+    return CONFIGS[name] if name in CONFIGS else BENCH_CONFIGS[name]
+
+
 def _children(seed: int):
     return np.random.SeedSequence(seed).spawn(6)
 
@@ -231,7 +246,7 @@ def make(name_or_cfg, seed: Optional[int] = None, device="cpu",
     ``device``.  Expert outputs y are drawn only when ``y_rows`` is given (the
     caller sizes them to its expanded-buffer capacity); a row of y is only read
     where the layout placed a routed slot."""
-    cfg = CONFIGS[name_or_cfg] if isinstance(name_or_cfg, str) else name_or_cfg
+    cfg = config(name_or_cfg) if isinstance(name_or_cfg, str) else name_or_cfg
     seed = cfg.seed if seed is None else seed
     idx, w = routing(cfg, seed)
     x = sf = y = b = None
