@@ -172,7 +172,8 @@ class Ceilings:
                "epc_write": (ctypes.c_int, [P, SZ, ctypes.c_uint32, I32, I32, I32, P, P, P]),
                "epc_copy": (ctypes.c_int, [P, P, SZ, I32, I32, I32, P, P, P]),
                "epc_row_store": (ctypes.c_int, [P, I64, I64, P, I64, I32, P, P, P]),
-               "epc_gather": (ctypes.c_int, [P, P, I64, I64, P, I64, I32, P, P, P])}
+               "epc_gather": (ctypes.c_int, [P, P, I64, I64, P, I64, I32, P, P, P]),
+               "epc_empty": (ctypes.c_int, [I32, I32, P, P, P])}
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
             fn.restype, fn.argtypes = res, args
@@ -223,6 +224,10 @@ class Ceilings:
         self._ok(self.lib.epc_row_store(dst.data_ptr(), rows, row_bytes, slot_row.data_ptr(),
                                         tokens, K, self._stream(), self._ev(start),
                                         self._ev(stop)), "epc_row_store")
+
+    def empty(self, blocks, threads, start=None, stop=None):
+        self._ok(self.lib.epc_empty(blocks, threads, self._stream(), self._ev(start),
+                                    self._ev(stop)), "epc_empty")
 
     def gather(self, out, inp, rows, row_bytes, slot_row, tokens, K, start=None, stop=None):
         self._ok(self.lib.epc_gather(out.data_ptr(), inp.data_ptr(), rows, row_bytes,
@@ -611,6 +616,13 @@ def main():
                 torch, ceil, lambda s, e: ceil.gather(out, wl.y, y_rows, 2 * H, h.dst_slot,
                                                       cfg.tokens, K, s, e), n),
         })
+        # The floor of a timed launch: an empty grid of one block and one of
+        # the combine's grid size (one 256-thread block per 4 KB of output).
+        comb_blocks = max(1, (cfg.tokens * (2 * H // 16) + 255) // 256)
+        ceil_us["empty_1_block"] = time_ceiling(torch, ceil,
+                                                lambda s, e: ceil.empty(1, 256, s, e), n)
+        ceil_us["empty_combine_grid"] = time_ceiling(
+            torch, ceil, lambda s, e: ceil.empty(comb_blocks, 256, s, e), n)
         if y_rows >= cfg.tokens * K:
             ceil_us["gather_contiguous_rows"] = time_ceiling(
                 torch, ceil, lambda s, e: ceil.gather(out, wl.y, y_rows, 2 * H, contig,
@@ -619,9 +631,12 @@ def main():
                  "write_dispatch_bytes": wd16,
                  "row_store_dispatch_rows": V * R,
                  "gather_combine_rows": V * 2 * H + cfg.tokens * 2 * H,
-                 "gather_contiguous_rows": cfg.tokens * K * 2 * H + cfg.tokens * 2 * H}
-        ceilings = {k: {"us_median": round(v, 2), "bytes": moved[k], **_rate(moved[k], v)}
+                 "gather_contiguous_rows": cfg.tokens * K * 2 * H + cfg.tokens * 2 * H,
+                 "empty_1_block": 0, "empty_combine_grid": 0}
+        ceilings = {k: {"us_median": round(v, 2), "bytes": moved[k],
+                        **(_rate(moved[k], v) if moved[k] else {})}
                     for k, v in ceil_us.items()}
+        ceilings["empty_combine_grid"]["blocks"] = comb_blocks
         for k, t in ceil_tune.items():
             ceilings[k]["tune"] = {"vec_per_thread": t[0], "blocks": t[1], "nontemporal": t[2]}
         ceilings["note"] = ("cache-cold medians of plain kernels (libep_ceilings.so): sequential "

@@ -235,6 +235,7 @@ ep_status ep_handle_import(ep_handle *h, const void *topk_idx, ep_dtype idx_dtyp
     if (num_tokens < 0 || num_tokens > h->max_tokens) return EP_ERR_SHAPE;
     if (num_tokens > 0 && (!topk_idx || !dst_slot)) return EP_ERR_NULL;
     const int32_t E = h->num_experts;
+    if (num_tokens == 0 && num_recv_tokens != 0) return EP_ERR_SHAPE;
     const int64_t expanded = psum[E];
     if (expanded < 0 || expanded > h->capacity) return EP_ERR_CAPACITY;
     if (expanded > 0 && !src_meta) return EP_ERR_NULL;
@@ -276,26 +277,25 @@ ep_status ep_handle_import(ep_handle *h, const void *topk_idx, ep_dtype idx_dtyp
         e = hipMemcpy(h->dst_slot, dst_slot, sizeof(int32_t) * slots, hipMemcpyHostToDevice);
     if (e == hipSuccess && expanded)
         e = hipMemcpy(h->src_meta, src_meta, sizeof(int32_t) * expanded, hipMemcpyHostToDevice);
-    if (e == hipSuccess && num_tokens > 0) {
-        // Rank layout from the slots: tokens with a routed slot, in order.
-        std::vector<int32_t> row(num_tokens), src(num_tokens);
-        int32_t n = 0;
-        for (int32_t t = 0; t < num_tokens; ++t) {
-            bool any = false;
-            for (int32_t k = 0; k < h->num_topk; ++k)
-                any = any || dst_slot[static_cast<int64_t>(t) * h->num_topk + k] >= 0;
-            row[t] = any ? n : -1;
-            if (any) src[n++] = t;
-        }
-        e = hipMemcpy(h->recv_row, row.data(), sizeof(int32_t) * num_tokens,
-                      hipMemcpyHostToDevice);
-        if (e == hipSuccess && n > 0)
-            e = hipMemcpy(h->recv_src, src.data(), sizeof(int32_t) * n, hipMemcpyHostToDevice);
-    }
     if (e == hipSuccess) e = hipMemcpy(h->scalars, sc, sizeof(sc), hipMemcpyHostToDevice);
     if (e == hipSuccess)
         e = hipMemcpy(h->scalars + EP_SCALAR_NUM_EXPANDED, &exp32, sizeof(exp32),
                       hipMemcpyHostToDevice);
+    // The rank layout comes from the device's numbering of the slot rows
+    // (tokens with a routed slot, in token order), which also recounts the
+    // received tokens into the scalars.
+    int32_t recv = 0;
+    if (e == hipSuccess && num_tokens > 0)
+        e = ep::launch_rank_rows(h->dst_slot, num_tokens, h->num_topk, h->recv_row, h->recv_src,
+                                 h->scalars + EP_SCALAR_NUM_RECV_TOKENS, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e == hipSuccess)
+        e = hipMemcpy(&recv, h->scalars + EP_SCALAR_NUM_RECV_TOKENS, sizeof(recv),
+                      hipMemcpyDeviceToHost);
+    if (e == hipSuccess && recv != num_recv_tokens) {
+        h->laid_out = 0;
+        return EP_ERR_SHAPE;
+    }
     if (e != hipSuccess) return EP_ERR_HIP;
     h->num_tokens = num_tokens;
     h->topk_idx = topk_idx;

@@ -17,6 +17,7 @@
 //               (token, 16-byte column) loads that column of each of the
 //               token's K slot rows, XORs them and stores one vector (K reads
 //               per write: 8:1 at top-8)
+//   empty       a grid that does nothing (the floor of a timed launch)
 // Page: DeepEP notes ch.7 "V2: how dispatch builds expert inputs", s7.4 (the
 // copy / permute the expanded layout costs) names the traffic being bounded.
 #include <hip/hip_ext.h>
@@ -193,6 +194,9 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(u32x4 *out, const u32x
     __builtin_nontemporal_store(acc, out + t * row_vecs + c);
 }
 
+// Does nothing: the floor of a launch timed by events on its dispatch.
+__global__ void empty_kernel() {}
+
 int status(hipError_t e) { return e == hipSuccess ? 0 : static_cast<int>(e); }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -272,6 +276,13 @@ int epc_gather(void *out, const void *in, int64_t rows, int64_t row_bytes,
                          stream, start, stop, static_cast<u32x4 *>(out),
                          static_cast<const u32x4 *>(in), slot_row, tokens, static_cast<int>(K),
                          row_vecs, rows));
+}
+
+int epc_empty(int32_t blocks, int32_t threads, hipStream_t stream, hipEvent_t start,
+              hipEvent_t stop) {
+    if (blocks < 1 || threads < 1 || threads > 1024) return -1;
+    return status(launch(empty_kernel, dim3(static_cast<unsigned>(blocks)),
+                         dim3(static_cast<unsigned>(threads)), stream, start, stop));
 }
 
 }  // extern "C"

@@ -216,6 +216,11 @@ hipError_t launch_combine(const CombineArgs &a, hipStream_t stream, CallEvents e
 hipError_t launch_combine_backward(const BackwardArgs &a, hipStream_t stream, CallEvents ev);
 hipError_t launch_gather_rows(const GatherArgs &a, hipStream_t stream, CallEvents ev);
 hipError_t launch_dispatch_rank(const RankArgs &a, hipStream_t stream, CallEvents ev);
+// Rank rows (recv_row, recv_src) and the received count from a layout's slot
+// rows: the tokens with a slot row >= 0, numbered in token order.
+hipError_t launch_rank_rows(const int32_t *dst, int64_t num_tokens, int num_topk,
+                            int32_t *recv_row, int32_t *recv_src, int32_t *num_recv,
+                            hipStream_t stream);
 hipError_t launch_combine_rank(const RankArgs &a, hipStream_t stream, CallEvents ev);
 
 }  // namespace ep

@@ -124,7 +124,66 @@ hipError_t launch_drank(const RankArgs &a, hipStream_t s, CallEvents ev) {
                          ev.stop, a);
 }
 
+// Rank rows of a layout given as slot rows (ep_handle_import): token t is
+// received when one of its K slots has a row (dst >= 0); received tokens get
+// rows 0, 1, ... in token order.  One block of kRowsThreads threads, each
+// taking a run of consecutive tokens: count its received tokens, exclusive
+// scan over the block, then number them.  Writes recv_row [T], recv_src
+// [received] and the received count.
+constexpr int kRowsThreads = 1024;
+
+__global__ __launch_bounds__(kRowsThreads) void rank_rows_kernel(const int32_t *dst, int64_t T,
+                                                                 int K, int32_t *recv_row,
+                                                                 int32_t *recv_src,
+                                                                 int32_t *num_recv) {
+    __shared__ int64_t s_wave[kRowsThreads / 64];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t per = (T + kRowsThreads - 1) / kRowsThreads;
+    const int64_t t0 = tid * per;
+    const int64_t t1 = t0 + per < T ? t0 + per : T;
+    int64_t cnt = 0;
+    for (int64_t t = t0; t < t1; ++t) {
+        bool any = false;
+        for (int k = 0; k < K; ++k) any = any || dst[t * K + k] >= 0;
+        cnt += any;
+    }
+    int64_t x = cnt;                                   // inclusive scan in the wave
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int64_t y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    if (lane == 63) s_wave[wave] = x;
+    __syncthreads();
+    int64_t base = 0, total = 0;
+    for (int w = 0; w < kRowsThreads / 64; ++w) {
+        if (w < wave) base += s_wave[w];
+        total += s_wave[w];
+    }
+    int64_t row = base + x - cnt;
+    for (int64_t t = t0; t < t1; ++t) {
+        bool any = false;
+        for (int k = 0; k < K; ++k) any = any || dst[t * K + k] >= 0;
+        if (any) {
+            recv_row[t] = static_cast<int32_t>(row);
+            recv_src[row] = static_cast<int32_t>(t);
+            ++row;
+        } else {
+            recv_row[t] = -1;
+        }
+    }
+    if (tid == 0) *num_recv = static_cast<int32_t>(total);
+}
+
 }  // namespace
+
+hipError_t launch_rank_rows(const int32_t *dst, int64_t num_tokens, int num_topk,
+                            int32_t *recv_row, int32_t *recv_src, int32_t *num_recv,
+                            hipStream_t stream) {
+    rank_rows_kernel<<<dim3(1), dim3(kRowsThreads), 0, stream>>>(dst, num_tokens, num_topk,
+                                                                 recv_row, recv_src, num_recv);
+    return hipGetLastError();
+}
 
 hipError_t launch_dispatch_rank(const RankArgs &a, hipStream_t stream, CallEvents ev) {
     if (a.num_tokens == 0) return hipSuccess;

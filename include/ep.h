@@ -236,7 +236,11 @@ ep_status ep_handle_read_counts(const ep_handle *h, int32_t *counts,
  * expert's run fits its segment, every dst_slot lies in [-1, psum[E]), and
  * src_meta is the inverse of dst_slot (every run row names a slot that
  * points back at it, every gap row is -1) - else EP_ERR_SHAPE; psum[E] >
- * capacity gives EP_ERR_CAPACITY.  The rank rows are derived on the host.
+ * capacity gives EP_ERR_CAPACITY.  After the copy, one kernel on `stream`
+ * numbers the rank rows from dst_slot (tokens with a slot row >= 0, in token
+ * order [Ch7 §7.4]) and counts them; if that count differs from
+ * num_recv_tokens the call returns EP_ERR_SHAPE and leaves the handle not
+ * laid out.
  */
 ep_status ep_handle_import(ep_handle *h, const void *topk_idx, ep_dtype idx_dtype,
                            int32_t num_tokens, const int32_t *counts,

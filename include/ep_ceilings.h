@@ -75,6 +75,11 @@ int epc_gather(void *out, const void *in, int64_t rows, int64_t row_bytes,
                const int32_t *slot_row, int64_t tokens, int32_t K,
                hipStream_t stream, hipEvent_t start, hipEvent_t stop);
 
+/* A grid of `blocks` x `threads` that does nothing: the floor of a launch
+ * timed by events on its dispatch (small calls are bound by it). */
+int epc_empty(int32_t blocks, int32_t threads, hipStream_t stream, hipEvent_t start,
+              hipEvent_t stop);
+
 #ifdef __cplusplus
 }
 #endif

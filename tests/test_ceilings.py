@@ -31,7 +31,7 @@ def declared():
 
 def test_every_declared_function_is_exported(ceil):
     names = declared()
-    assert names == ["epc_copy", "epc_gather", "epc_read", "epc_read_sink_words",
+    assert names == ["epc_copy", "epc_empty", "epc_gather", "epc_read", "epc_read_sink_words",
                      "epc_row_store", "epc_write"]
     for n in names:
         assert hasattr(ceil, n), n
@@ -46,6 +46,9 @@ def test_invalid_arguments_launch_nothing(ceil):
     ceil.epc_gather.argtypes = [P, P, I64, I64, P, I64, I32, P, P, P]
     ceil.epc_read_sink_words.restype = I64
     ceil.epc_read_sink_words.argtypes = [SZ, I32, I32]
+    ceil.epc_empty.argtypes = [I32, I32, P, P, P]
+    assert ceil.epc_empty(0, 64, None, None, None) == -1
+    assert ceil.epc_empty(1, 2048, None, None, None) == -1
     A = 0x300000
     assert ceil.epc_read(A, 17, A, 4, 0, 0, None, None, None) == -1     # not a multiple of 16
     assert ceil.epc_read(A + 4, 32, A, 4, 0, 0, None, None, None) == -1  # misaligned

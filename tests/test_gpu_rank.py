@@ -282,3 +282,60 @@ def test_imported_layout_has_rank_rows():
     row, src, n = oracle.rank_layout(idx, E)
     np.testing.assert_array_equal(h.recv_row.cpu().numpy(), row)
     np.testing.assert_array_equal(h.recv_src.cpu().numpy()[:n], src)
+
+
+@pytest.mark.parametrize("name", ["prefill", "skewed"])
+def test_rank_dispatch_after_import_equals_after_layout(name):
+    """The imported layout's rank rows come from the device's numbering of
+    its slot rows: a rank dispatch after ep_handle_import of the oracle's
+    layout writes the same bytes (rows, scales, received ids and weights) as
+    one after ep_layout on the same ids."""
+    cfg = W.CONFIGS[name]
+    wl = W.make(cfg, device="cuda")
+    idx = torch.from_numpy(wl.topk_idx).cuda()
+    w = torch.from_numpy(wl.topk_weights).cuda()
+    cap = ep.ep_capacity_bound(cfg.tokens, cfg.topk, cfg.experts, cfg.alignment)
+    lay = oracle.layout(wl.topk_idx, cfg.experts, cfg.alignment, cap)
+    outs = []
+    for how in ("layout", "import"):
+        h = ep.Handle(cfg.tokens, cfg.topk, cfg.experts, cfg.alignment, cap)
+        say("rank dispatch after", how, name)
+        if how == "layout":
+            h.layout(idx)
+        else:
+            h.import_layout(idx, lay.counts, lay.psum, lay.dst, lay.src_meta[:lay.num_expanded],
+                            lay.num_recv_tokens)
+        rx = poison_(torch.empty((cfg.tokens, cfg.hidden), dtype=wl.x.dtype, device="cuda"))
+        rsf = (poison_(torch.empty((cfg.tokens, cfg.hidden // 128), dtype=torch.float32,
+                                   device="cuda")) if cfg.fp8 else None)
+        ri = poison_(torch.empty((cfg.tokens, cfg.topk), dtype=torch.int64, device="cuda"))
+        rw = poison_(torch.empty((cfg.tokens, cfg.topk), dtype=torch.float32, device="cuda"))
+        h.dispatch_rank(wl.x, sf=wl.sf, topk_weights=w, out_x=rx, out_sf=rsf, out_topk_idx=ri,
+                        out_topk_weights=rw)
+        torch.cuda.synchronize()
+        assert h.read_counts(check=False)["num_recv_tokens"] == lay.num_recv_tokens
+        outs.append([u8(t) for t in (rx, rsf, ri, rw) if t is not None] +
+                    [h.recv_row.cpu().numpy().copy()])
+    for a, b in zip(*outs):
+        np.testing.assert_array_equal(a, b)
+
+
+def test_import_with_wrong_received_count_is_refused():
+    rng = np.random.default_rng(11)
+    T, K, E = 300, 4, 9
+    idx = np.where(rng.random((T, K)) < 0.5, -1, rng.integers(0, E, size=(T, K)))
+    lay = oracle.layout(idx, E, 2, T * K + 2 * E)
+    h = ep.Handle(T, K, E, 2, T * K + 2 * E)
+    say("import wrong received count")
+    with pytest.raises(ep.EpError) as err:
+        h.import_layout(torch.from_numpy(idx).cuda(), lay.counts, lay.psum, lay.dst,
+                        lay.src_meta[:lay.num_expanded], lay.num_recv_tokens + 1)
+    assert err.value.status == ep.EP_ERR_SHAPE
+    assert h.h.laid_out == 0
+    with pytest.raises(ep.EpError) as err:
+        h.read_counts()
+    assert err.value.status == ep.EP_ERR_NOT_LAID_OUT
+    # the right count is taken
+    h.import_layout(torch.from_numpy(idx).cuda(), lay.counts, lay.psum, lay.dst,
+                    lay.src_meta[:lay.num_expanded], lay.num_recv_tokens)
+    assert h.read_counts(check=False)["num_recv_tokens"] == lay.num_recv_tokens
