@@ -23,7 +23,7 @@ __all__ = [
     "EP_ERR_MISALIGNED", "EP_ERR_WORKSPACE", "EP_ERR_NOT_LAID_OUT", "EP_ERR_CAPACITY",
     "EP_ERR_INVALID_ID", "EP_ERR_HIP", "EP_ERR_TIMEOUT", "EP_BF16", "EP_FP8_E4M3", "EP_F32", "EP_I32",
     "EP_I64", "EpError", "ep_handle", "lib", "Handle", "BoundCall", "ep_capacity_bound",
-    "ep_workspace_bytes", "ep_handle_init", "ep_layout", "ep_layout_noalloc",
+    "ep_workspace_bytes", "ep_handle_init", "ep_layout", "ep_layout_noalloc", "ep_layout_dispatch",
     "ep_handle_read_counts",
     "ep_handle_import", "ep_dispatch", "ep_combine", "ep_status_str", "ep_handle_sizeof",
     "ep_time_next_call", "time_next_call", "ep_combine_backward", "ep_dispatch_backward",
@@ -95,6 +95,9 @@ _SIGNATURES = {
     "ep_handle_import": (ctypes.c_int, [_HP, _P, ctypes.c_int, _I32, _P, _P, _P, _P, _I32, _P]),
     "ep_dispatch": (ctypes.c_int, [_HP, _P, ctypes.c_int, _I32, _P, _I64, _I64, _I32, _P, _P,
                                    _P, _I64, _I64, _P, _I32, _P]),
+    "ep_layout_dispatch": (ctypes.c_int, [_HP, _P, ctypes.c_int, _I32, _P,
+                                          _P, ctypes.c_int, _I32, _P, _I64, _I64, _I32, _P, _P,
+                                          _P, _I64, _I64, _P, _I32, _P]),
     "ep_tma_aligned_rows": (_I64, [_I64]),
     "ep_sf_packs": (_I32, [_I32, ctypes.c_int]),
     "ep_quantize_fp8": (ctypes.c_int, [_P, _I32, _I32, ctypes.c_int, _P, _P, _I64, _I64, _P]),
@@ -501,6 +504,50 @@ class Handle:
         self.topk_idx = topk_idx
         return BoundCall(fn, args, "ep_layout", self, (topk_idx, cumulative_stats))
 
+    def _layout_dispatch_call(self, topk_idx, x, sf, topk_weights, zero_padding, out_x, out_sf,
+                              out_w, want_weights, col_major_sf, cumulative_stats):
+        lfn, largs = self._layout_call(topk_idx, cumulative_stats)
+        _, dargs, result, keep = self._dispatch_call(
+            x, sf, topk_weights, zero_padding, out_x, out_sf, out_w, want_weights, col_major_sf,
+            num_tokens=topk_idx.shape[0])
+        # ep_layout_dispatch takes the layout's arguments, then the dispatch's
+        # (the handle appears once)
+        args = largs + dargs[1:]
+        return lib().ep_layout_dispatch, args, result, keep + (topk_idx, cumulative_stats)
+
+    def layout_dispatch(self, topk_idx: torch.Tensor, x: torch.Tensor,
+                        sf: Optional[torch.Tensor] = None,
+                        topk_weights: Optional[torch.Tensor] = None, zero_padding: bool = False,
+                        out_x: Optional[torch.Tensor] = None, out_sf: Optional[torch.Tensor] = None,
+                        out_w: Optional[torch.Tensor] = None, want_weights: bool = False,
+                        col_major_sf: bool = False,
+                        cumulative_stats: Optional[torch.Tensor] = None):
+        """``layout`` then ``dispatch`` in one call (ep_layout_dispatch: the
+        same outputs, one host-side check of both argument sets).  Returns
+        (out_x, out_sf, out_w)."""
+        fn, args, result, _ = self._layout_dispatch_call(
+            topk_idx, x, sf, topk_weights, zero_padding, out_x, out_sf, out_w, want_weights,
+            col_major_sf, cumulative_stats)
+        _check(fn(*args, _stream()), "ep_layout_dispatch")
+        self.topk_idx = topk_idx
+        return result
+
+    def bind_layout_dispatch(self, topk_idx: torch.Tensor, x: torch.Tensor,
+                             sf: Optional[torch.Tensor] = None,
+                             topk_weights: Optional[torch.Tensor] = None,
+                             zero_padding: bool = False, out_x: Optional[torch.Tensor] = None,
+                             out_sf: Optional[torch.Tensor] = None,
+                             out_w: Optional[torch.Tensor] = None, want_weights: bool = False,
+                             col_major_sf: bool = False,
+                             cumulative_stats: Optional[torch.Tensor] = None) -> "BoundCall":
+        """``layout_dispatch`` bound to these tensors (see BoundCall)."""
+        fn, args, result, keep = self._layout_dispatch_call(
+            topk_idx, x, sf, topk_weights, zero_padding, out_x, out_sf, out_w, want_weights,
+            col_major_sf, cumulative_stats)
+        self.topk_idx = topk_idx
+        # no token-count check: the call lays the batch out itself
+        return BoundCall(fn, args, "ep_layout_dispatch", result, keep)
+
     def import_layout(self, topk_idx: torch.Tensor, counts, psum, dst_slot, src_meta,
                       num_recv_tokens: int) -> "Handle":
         """Install a host-computed layout (numpy int32 arrays)."""
@@ -562,8 +609,8 @@ class Handle:
         return BoundCall(fn, args, "ep_dispatch", result, keep, self.h)
 
     def _dispatch_call(self, x, sf, topk_weights, zero_padding, out_x, out_sf, out_w,
-                       want_weights, col_major_sf):
-        T = self.h.num_tokens
+                       want_weights, col_major_sf, num_tokens=None):
+        T = self.h.num_tokens if num_tokens is None else num_tokens
         _dev(x, "x")
         _need(x.dim() == 2 and x.shape[0] == T, "x must be [num_tokens, hidden]")
         H = x.shape[1]

@@ -136,13 +136,12 @@ ep_status ep_time_next_call(hipEvent_t start, hipEvent_t stop) {
     return EP_OK;
 }
 
-// ep_layout and ep_layout_noalloc: the same checks and kernels; the scans'
-// ticket, epoch and tile status words come from the handle's workspace or
-// from the library's static scratch.
-static ep_status layout_call(ep_handle *h, const void *topk_idx, ep_dtype idx_dtype,
-                             int32_t num_tokens, int32_t *cumulative_stats, hipStream_t stream,
-                             bool static_scratch) {
-    const ep::CallEvents ev = take_events();
+// Checks of a layout call and its kernel arguments (nothing launched).  The
+// scans' ticket, epoch and tile status words come from the handle's
+// workspace or, for ep_layout_noalloc, from the library's static scratch.
+static ep_status layout_prepare(const ep_handle *h, const void *topk_idx, ep_dtype idx_dtype,
+                                int32_t num_tokens, int32_t *cumulative_stats,
+                                bool static_scratch, ep::LayoutArgs *a) {
     if (!h) return EP_ERR_NULL;
     if (!handle_ready(h)) return EP_ERR_WORKSPACE;
     if (idx_dtype != EP_I64 && idx_dtype != EP_I32) return EP_ERR_DTYPE;
@@ -156,34 +155,49 @@ static ep_status layout_call(ep_handle *h, const void *topk_idx, ep_dtype idx_dt
     if (num_tokens > 0 && !topk_idx) return EP_ERR_NULL;
     if (!aligned(topk_idx, idx_dtype == EP_I64 ? 8 : 4)) return EP_ERR_MISALIGNED;
     if (!aligned(cumulative_stats, 4)) return EP_ERR_MISALIGNED;
-    ep::LayoutArgs a{};
-    a.topk_idx = topk_idx;
-    a.idx_is_i64 = idx_dtype == EP_I64;
-    a.num_tokens = num_tokens;
-    a.num_topk = h->num_topk;
-    a.num_experts = h->num_experts;
-    a.alignment = h->expert_alignment;
-    a.capacity = h->capacity;
-    a.counts = h->counts;
-    a.psum = h->psum;
-    a.dst = h->dst_slot;
-    a.src_meta = h->src_meta;
-    a.scalars = h->scalars;
-    a.tile_status = h->tile_status;
-    a.ticket = h->scalars + EP_SCALAR_TICKET;
-    a.epoch = h->scalars + EP_SCALAR_EPOCH;
-    if (static_scratch &&
-        ep::layout_scratch(stream, &a.tile_status, &a.ticket, &a.epoch) != hipSuccess)
-        return EP_ERR_HIP;
-    a.cumulative_stats = cumulative_stats;
-    a.recv_row = h->recv_row;
-    a.recv_src = h->recv_src;
-    const hipError_t e = ep::launch_layout(a, stream, ev);
-    if (e != hipSuccess) return EP_ERR_HIP;
+    *a = ep::LayoutArgs{};
+    a->topk_idx = topk_idx;
+    a->idx_is_i64 = idx_dtype == EP_I64;
+    a->num_tokens = num_tokens;
+    a->num_topk = h->num_topk;
+    a->num_experts = h->num_experts;
+    a->alignment = h->expert_alignment;
+    a->capacity = h->capacity;
+    a->counts = h->counts;
+    a->psum = h->psum;
+    a->dst = h->dst_slot;
+    a->src_meta = h->src_meta;
+    a->scalars = h->scalars;
+    a->tile_status = h->tile_status;
+    a->ticket = h->scalars + EP_SCALAR_TICKET;
+    a->epoch = h->scalars + EP_SCALAR_EPOCH;
+    a->cumulative_stats = cumulative_stats;
+    a->recv_row = h->recv_row;
+    a->recv_src = h->recv_src;
+    return EP_OK;
+}
+
+static void layout_done(ep_handle *h, const void *topk_idx, ep_dtype idx_dtype,
+                        int32_t num_tokens) {
     h->num_tokens = num_tokens;
     h->topk_idx = topk_idx;
     h->topk_idx_dtype = idx_dtype;
     h->laid_out = 1;
+}
+
+static ep_status layout_call(ep_handle *h, const void *topk_idx, ep_dtype idx_dtype,
+                             int32_t num_tokens, int32_t *cumulative_stats, hipStream_t stream,
+                             bool static_scratch) {
+    const ep::CallEvents ev = take_events();
+    ep::LayoutArgs a;
+    const ep_status st =
+        layout_prepare(h, topk_idx, idx_dtype, num_tokens, cumulative_stats, static_scratch, &a);
+    if (st != EP_OK) return st;
+    if (static_scratch &&
+        ep::layout_scratch(stream, &a.tile_status, &a.ticket, &a.epoch) != hipSuccess)
+        return EP_ERR_HIP;
+    if (ep::launch_layout(a, stream, ev) != hipSuccess) return EP_ERR_HIP;
+    layout_done(h, topk_idx, idx_dtype, num_tokens);
     return EP_OK;
 }
 
@@ -327,22 +341,22 @@ int64_t ep_tma_aligned_rows(int64_t rows) {
     return (rows + 3) / 4 * 4;
 }
 
-ep_status ep_dispatch(const ep_handle *h, const void *x, ep_dtype x_dtype, int32_t hidden,
-                      const void *sf, int64_t sf_token_stride, int64_t sf_hidden_stride,
-                      int32_t num_sf_packs, const float *topk_weights, void *out_x, void *out_sf,
-                      int64_t out_sf_token_stride, int64_t out_sf_hidden_stride, float *out_w,
-                      int32_t zero_padding, hipStream_t stream) {
-    const ep::CallEvents ev = take_events();
-    if (!h) return EP_ERR_NULL;
-    if (!handle_ready(h)) return EP_ERR_WORKSPACE;
-    if (!h->laid_out) return EP_ERR_NOT_LAID_OUT;
+// Checks of a copying dispatch over `num_tokens` tokens of handle h and its
+// kernel arguments (nothing launched).
+static ep_status dispatch_prepare(const ep_handle *h, int32_t num_tokens, const void *x,
+                                  ep_dtype x_dtype, int32_t hidden, const void *sf,
+                                  int64_t sf_token_stride, int64_t sf_hidden_stride,
+                                  int32_t num_sf_packs, const float *topk_weights, void *out_x,
+                                  void *out_sf, int64_t out_sf_token_stride,
+                                  int64_t out_sf_hidden_stride, float *out_w,
+                                  int32_t zero_padding, ep::DispatchArgs *a) {
     if (x_dtype != EP_BF16 && x_dtype != EP_FP8_E4M3) return EP_ERR_DTYPE;
     if (hidden <= 0) return EP_ERR_SHAPE;
     const bool fp8 = x_dtype == EP_FP8_E4M3;
     if (fp8 ? (hidden % 128) != 0 : (hidden % 8) != 0) return EP_ERR_MISALIGNED;
     // With no tokens nothing is read, and only zero padding can write (the
     // gap rows of an imported layout, inside the capacity).
-    const bool reads = h->num_tokens > 0;
+    const bool reads = num_tokens > 0;
     const bool writes = reads || (zero_padding != 0 && h->capacity > 0);
     int32_t packs = 0;
     const ep_status st = check_sf(fp8, hidden, sf, out_sf, num_sf_packs, reads, writes,
@@ -353,31 +367,74 @@ ep_status ep_dispatch(const ep_handle *h, const void *x, ep_dtype x_dtype, int32
     if (!aligned(x, 16) || !aligned(out_x, 16)) return EP_ERR_MISALIGNED;
     if (!aligned(topk_weights, 4) || !aligned(out_w, 4)) return EP_ERR_MISALIGNED;
     const int64_t row_bytes = fp8 ? hidden : 2 * static_cast<int64_t>(hidden);
-    ep::DispatchArgs a{};
-    a.x = x;
-    a.row_vecs = row_bytes / 16;
-    a.num_tokens = h->num_tokens;
-    a.num_topk = h->num_topk;
-    a.num_experts = h->num_experts;
-    a.alignment = h->expert_alignment;
-    a.capacity = h->capacity;
-    a.dst = h->dst_slot;
-    a.counts = h->counts;
-    a.psum = h->psum;
-    a.scalars = h->scalars;
-    a.w = topk_weights;
-    a.out_x = out_x;
-    a.sf = static_cast<const uint32_t *>(sf);
-    a.sf_ts = sf_token_stride;
-    a.sf_hs = sf_hidden_stride;
-    a.num_sf = packs;
-    a.out_sf = static_cast<uint32_t *>(out_sf);
-    a.out_ts = out_sf_token_stride;
-    a.out_hs = out_sf_hidden_stride;
-    a.out_w = out_w;
-    a.zero_padding = zero_padding != 0;
-    a.src_meta = h->src_meta;
+    *a = ep::DispatchArgs{};
+    a->x = x;
+    a->row_vecs = row_bytes / 16;
+    a->num_tokens = num_tokens;
+    a->num_topk = h->num_topk;
+    a->num_experts = h->num_experts;
+    a->alignment = h->expert_alignment;
+    a->capacity = h->capacity;
+    a->dst = h->dst_slot;
+    a->counts = h->counts;
+    a->psum = h->psum;
+    a->scalars = h->scalars;
+    a->w = topk_weights;
+    a->out_x = out_x;
+    a->sf = static_cast<const uint32_t *>(sf);
+    a->sf_ts = sf_token_stride;
+    a->sf_hs = sf_hidden_stride;
+    a->num_sf = packs;
+    a->out_sf = static_cast<uint32_t *>(out_sf);
+    a->out_ts = out_sf_token_stride;
+    a->out_hs = out_sf_hidden_stride;
+    a->out_w = out_w;
+    a->zero_padding = zero_padding != 0;
+    a->src_meta = h->src_meta;
+    return EP_OK;
+}
+
+ep_status ep_dispatch(const ep_handle *h, const void *x, ep_dtype x_dtype, int32_t hidden,
+                      const void *sf, int64_t sf_token_stride, int64_t sf_hidden_stride,
+                      int32_t num_sf_packs, const float *topk_weights, void *out_x, void *out_sf,
+                      int64_t out_sf_token_stride, int64_t out_sf_hidden_stride, float *out_w,
+                      int32_t zero_padding, hipStream_t stream) {
+    const ep::CallEvents ev = take_events();
+    if (!h) return EP_ERR_NULL;
+    if (!handle_ready(h)) return EP_ERR_WORKSPACE;
+    if (!h->laid_out) return EP_ERR_NOT_LAID_OUT;
+    ep::DispatchArgs a;
+    const ep_status st = dispatch_prepare(h, h->num_tokens, x, x_dtype, hidden, sf,
+                                          sf_token_stride, sf_hidden_stride, num_sf_packs,
+                                          topk_weights, out_x, out_sf, out_sf_token_stride,
+                                          out_sf_hidden_stride, out_w, zero_padding, &a);
+    if (st != EP_OK) return st;
     return hip_status(ep::launch_dispatch(a, stream, ev));
+}
+
+ep_status ep_layout_dispatch(ep_handle *h, const void *topk_idx, ep_dtype idx_dtype,
+                             int32_t num_tokens, int32_t *cumulative_stats, const void *x,
+                             ep_dtype x_dtype, int32_t hidden, const void *sf,
+                             int64_t sf_token_stride, int64_t sf_hidden_stride,
+                             int32_t num_sf_packs, const float *topk_weights, void *out_x,
+                             void *out_sf, int64_t out_sf_token_stride,
+                             int64_t out_sf_hidden_stride, float *out_w, int32_t zero_padding,
+                             hipStream_t stream) {
+    const ep::CallEvents ev = take_events();
+    ep::LayoutArgs la;
+    ep_status st = layout_prepare(h, topk_idx, idx_dtype, num_tokens, cumulative_stats, false, &la);
+    if (st != EP_OK) return st;
+    ep::DispatchArgs da;
+    st = dispatch_prepare(h, num_tokens, x, x_dtype, hidden, sf, sf_token_stride,
+                          sf_hidden_stride, num_sf_packs, topk_weights, out_x, out_sf,
+                          out_sf_token_stride, out_sf_hidden_stride, out_w, zero_padding, &da);
+    if (st != EP_OK) return st;
+    ep::CallEvents first, last;
+    first.start = ev.start;
+    last.stop = ev.stop;
+    if (ep::launch_layout(la, stream, first) != hipSuccess) return EP_ERR_HIP;
+    layout_done(h, topk_idx, idx_dtype, num_tokens);
+    return hip_status(ep::launch_dispatch(da, stream, last));
 }
 
 int32_t ep_sf_packs(int32_t hidden, ep_sf_format fmt) {

@@ -286,6 +286,24 @@ ep_status ep_dispatch(const ep_handle *h, const void *x, ep_dtype x_dtype,
                       float *out_w, int32_t zero_padding, hipStream_t stream);
 
 /*
+ * Uncached dispatch: ep_layout on topk_idx, then ep_dispatch of x, in one
+ * call with the same arguments and the same outputs as those two calls [Ch7
+ * §7.2: the dispatch kernel also produces the counts, the source metadata
+ * and the slot index].  The layout's kernels and the copy are enqueued
+ * back to back on `stream` after one host-side check of both argument sets:
+ * errors are those of the two calls, and nothing is launched unless both
+ * argument sets are valid.
+ */
+ep_status ep_layout_dispatch(ep_handle *h, const void *topk_idx, ep_dtype idx_dtype,
+                             int32_t num_tokens, int32_t *cumulative_stats,
+                             const void *x, ep_dtype x_dtype, int32_t hidden,
+                             const void *sf, int64_t sf_token_stride,
+                             int64_t sf_hidden_stride, int32_t num_sf_packs,
+                             const float *topk_weights, void *out_x, void *out_sf,
+                             int64_t out_sf_token_stride, int64_t out_sf_hidden_stride,
+                             float *out_w, int32_t zero_padding, hipStream_t stream);
+
+/*
  * Rows of a column-major scale buffer aligned for the tensor-memory loads of
  * a grouped GEMM [Ch7 §7.3: the FP8 scales may use a column-major stride
  * aligned for TMA]: `rows` rounded up to a whole 16 bytes of 4-byte packs,

@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported():
     names = declared_functions()
-    assert len(names) == 21, names
+    assert len(names) == 22, names
     for n in names:
         assert hasattr(ep.lib(), n), n
         assert n in ep._SIGNATURES, f"binding lacks {n}"

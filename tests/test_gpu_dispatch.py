@@ -250,3 +250,43 @@ def test_dispatch_scale_copy_both_orders(zp):
         say("dispatch scale copy order", zp, cap)
         _, g, o, _ = _run_both(idx, E, A, cap, x, sf=sf, w=w, zero_padding=zp)
         _assert_same(g, o)
+
+
+@pytest.mark.parametrize("name", list(W.CONFIGS))
+def test_layout_dispatch_equals_layout_then_dispatch(name):
+    """ep_layout_dispatch (the uncached dispatch: layout, then the copy, in one
+    call) writes exactly what ep_layout followed by ep_dispatch writes: the
+    whole layout, every output row, scale pack and weight (poison-filled
+    buffers on both sides, compared on the device)."""
+    cfg = W.CONFIGS[name]
+    cap = ep.ep_capacity_bound(cfg.tokens, cfg.topk, cfg.experts, cfg.alignment)
+    wl = W.make(cfg, device="cuda")
+    idx = torch.from_numpy(wl.topk_idx).cuda()
+    w = torch.from_numpy(wl.topk_weights).cuda()
+    outs = []
+    for fused in (False, True):
+        h = ep.Handle(cfg.tokens, cfg.topk, cfg.experts, cfg.alignment, cap)
+        ox = poison_(torch.empty((cap, cfg.hidden), dtype=wl.x.dtype, device="cuda"))
+        osf = (poison_(torch.empty((cap, cfg.hidden // 128), dtype=torch.float32, device="cuda"))
+               if cfg.fp8 else None)
+        ow = poison_(torch.empty(cap, dtype=torch.float32, device="cuda"))
+        say("layout_dispatch", name, "fused" if fused else "two calls")
+        if fused:
+            h.layout_dispatch(idx, wl.x, sf=wl.sf, topk_weights=w, zero_padding=cfg.zero_padding,
+                              out_x=ox, out_sf=osf, out_w=ow)
+        else:
+            h.layout(idx)
+            h.dispatch(wl.x, sf=wl.sf, topk_weights=w, zero_padding=cfg.zero_padding, out_x=ox,
+                       out_sf=osf, out_w=ow)
+        rc = h.read_counts(check=False)
+        n = rc["num_expanded"]
+        outs.append((rc, h.dst_slot.clone(), h.src_meta[:n].clone(), h.recv_row.clone(),
+                     ox, osf, ow))
+    (rc1, d1, s1, r1, x1, sf1, w1), (rc2, d2, s2, r2, x2, sf2, w2) = outs
+    for k in ("num_expanded", "num_recv_tokens", "error_bits", "invalid_count"):
+        assert rc1[k] == rc2[k], k
+    np.testing.assert_array_equal(rc1["counts"], rc2["counts"])
+    np.testing.assert_array_equal(rc1["psum"], rc2["psum"])
+    for a, b in ((d1, d2), (s1, s2), (r1, r2), (x1, x2), (sf1, sf2), (w1, w2)):
+        if a is not None:
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
