@@ -71,12 +71,6 @@ __device__ inline uint64_t load_status(const uint64_t *p) {
                              __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// The count half (low 32 bits) of a status word.
-__device__ inline uint32_t load_count(const uint64_t *p) {
-    return __hip_atomic_load(reinterpret_cast<uint32_t *>(const_cast<uint64_t *>(p)),
-                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 __device__ inline int64_t align_up(int64_t c, int64_t a) { return (c + a - 1) / a * a; }
 
 // Exclusive scan of one int64 per thread over a 256-thread block.
@@ -238,12 +232,13 @@ __device__ void rank_tile(const LayoutArgs &a, int64_t tile_base, int64_t tile_e
 
 // Aligned exclusive scan of the experts' totals (s_total, buckets 0..E+1)
 // into s_psum, and the call's error verdict in *s_fatal (nonzero: capacity
-// exceeded or an earlier timeout; the layout is void).  Every block that
+// exceeded or an earlier timeout, passed in as the error word `sticky`; the
+// layout is void).  Every block that
 // calls it on the same totals gets the same result; with `publish` the block
 // also writes the scalars, counts, psum and cumulative stats.  Ends after a
 // block barrier.
 __device__ void scan_experts(const LayoutArgs &a, const int32_t *s_total, int32_t *s_psum,
-                             int64_t *s_wave, int32_t *s_fatal, bool publish) {
+                             int64_t *s_wave, int32_t *s_fatal, bool publish, uint32_t sticky) {
     const int tid = threadIdx.x, E = a.num_experts;
     const int per = (E + kLayoutThreads - 1) / kLayoutThreads;
     const int b0 = tid * per;
@@ -259,10 +254,9 @@ __device__ void scan_experts(const LayoutArgs &a, const int32_t *s_total, int32_
     if (tid == 0) {
         s_psum[E] = static_cast<int32_t>(min(total, static_cast<int64_t>(INT32_MAX)));
         // Every block reaches the same verdict: the capacity test uses the
-        // same totals, and the sticky timeout bit is the same before and
-        // after the publishing block rewrites the word.
-        uint32_t err = static_cast<uint32_t>(a.scalars[EP_SCALAR_ERROR_BITS]) &
-                       EP_ERRBIT_SCAN_TIMEOUT;
+        // same totals, and the sticky timeout bit (`sticky`, read when the
+        // caller's kernel started) is the same in every block.
+        uint32_t err = sticky & EP_ERRBIT_SCAN_TIMEOUT;
         if (total > a.capacity) err |= EP_ERRBIT_CAPACITY;
         if (s_total[E] > 0) err |= EP_ERRBIT_INVALID_ID;
         *s_fatal = (err & EP_ERRBIT_FATAL) != 0;
@@ -481,6 +475,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_single_kernel(LayoutArg
     const int E = a.num_experts, NB = E + 2;
     const int64_t num_slots = static_cast<int64_t>(a.num_tokens) * a.num_topk;
     const int64_t wave_base = static_cast<int64_t>(wave) * (R * 64);
+    const uint32_t sticky = static_cast<uint32_t>(a.scalars[EP_SCALAR_ERROR_BITS]);
     if (blockIdx.x > 0) {
         const IdxT *idx = static_cast<const IdxT *>(a.topk_idx);
         for (int b = tid; b < NB; b += kLayoutThreads) s_total[b] = 0;
@@ -491,7 +486,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_single_kernel(LayoutArg
             else if (e != -1) atomicAdd(&s_total[E], 1);
         }
         __syncthreads();
-        scan_experts(a, s_total, s_psum, s_wave, &s_fatal, false);
+        scan_experts(a, s_total, s_psum, s_wave, &s_fatal, false, sticky);
         if (s_fatal) return;
         for (int e = blockIdx.x - 1; e < E; e += gridDim.x - 1) {
             const int64_t end = s_psum[e + 1] < a.capacity ? s_psum[e + 1] : a.capacity;
@@ -511,7 +506,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_single_kernel(LayoutArg
         if (b < NB) s_total[b] = agg[q];
     }
     __syncthreads();
-    scan_experts(a, s_total, s_psum, s_wave, &s_fatal, true);
+    scan_experts(a, s_total, s_psum, s_wave, &s_fatal, true, sticky);
     const bool fatal = s_fatal != 0;
     if (!fatal) {
 #pragma unroll
@@ -593,6 +588,53 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_count_kernel(LayoutArgs
     }
 }
 
+// Counts of buckets tid + q * kLayoutThreads (q < kBucketsPerThread) over
+// every tile: the sum over tiles before `tile` into s_excl[b], over all
+// tiles into s_total[b].  The words were written by an earlier kernel, so
+// ordinary loads (which may hit in L2) see them; kCountWindow tiles of two
+// buckets per round trip, all in flight together.  At 256 experts (258
+// buckets: threads 0 and 1 hold two) 32 short tiles take one round trip
+// instead of two and 128 long tiles four instead of eight; measured
+// cache-cold, interleaved on one box: prefill 4096 x 8 layout 15.2 ->
+// 14.3 us, 32768 x 8 25.0 -> 24.0 us.
+constexpr int kCountWindow = 32;
+
+__device__ void sum_tile_counts(const uint64_t *status, int NB, int num_tiles, int tile,
+                                int32_t *s_excl, int32_t *s_total) {
+    const int tid = threadIdx.x;
+    for (int q = 0; q < kBucketsPerThread; q += 2) {
+        const int b0 = tid + q * kLayoutThreads, b1 = b0 + kLayoutThreads;
+        if (b0 >= NB) break;
+        const bool two = b1 < NB;
+        uint32_t ex0 = 0, tot0 = 0, ex1 = 0, tot1 = 0;
+        for (int t0 = 0; t0 < num_tiles; t0 += kCountWindow) {
+            uint32_t c0[kCountWindow], c1[kCountWindow];
+#pragma unroll
+            for (int w = 0; w < kCountWindow; ++w) {
+                const uint32_t *row =
+                    reinterpret_cast<const uint32_t *>(status + static_cast<int64_t>(t0 + w) * NB);
+                c0[w] = t0 + w < num_tiles ? row[2 * b0] : 0u;
+                c1[w] = t0 + w < num_tiles && two ? row[2 * b1] : 0u;
+            }
+#pragma unroll
+            for (int w = 0; w < kCountWindow; ++w) {
+                if (t0 + w < tile) {
+                    ex0 += c0[w];
+                    ex1 += c1[w];
+                }
+                tot0 += c0[w];
+                tot1 += c1[w];
+            }
+        }
+        s_excl[b0] = static_cast<int32_t>(ex0);
+        s_total[b0] = static_cast<int32_t>(tot0);
+        if (two) {
+            s_excl[b1] = static_cast<int32_t>(ex1);
+            s_total[b1] = static_cast<int32_t>(tot1);
+        }
+    }
+}
+
 template <typename IdxT, int R>
 __global__ __launch_bounds__(kLayoutThreads) void layout_place_kernel(LayoutArgs a,
                                                                      int tokens_per_tile,
@@ -603,9 +645,6 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_place_kernel(LayoutArgs
     __shared__ uint8_t s_tok[kTileSlots];
     __shared__ int64_t s_wave[kLayoutWaves];
     __shared__ int32_t s_fatal;
-    // Tiles' counts a thread has in flight at once (per bucket): all of them
-    // for short tiles (at most kSmallTilesMax, 32 per round trip).
-    constexpr int W = R == kRoundsSmall ? 32 : 16;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int E = a.num_experts, NB = E + 2, K = a.num_topk;
     const bool gap_block = static_cast<int>(blockIdx.x) >= num_tiles;
@@ -615,6 +654,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_place_kernel(LayoutArgs
     const int64_t tile_end_full = tile_base + static_cast<int64_t>(tokens_per_tile) * K;
     const int64_t tile_end = gap_block ? 0 : (tile_end_full < num_slots ? tile_end_full : num_slots);
     const int64_t wave_base = tile_base + static_cast<int64_t>(wave) * (R * 64);
+    const uint32_t sticky = static_cast<uint32_t>(a.scalars[EP_SCALAR_ERROR_BITS]);
 
     // The tile's parked slots (independent of the counts: loads issued first).
     uint32_t parked[R];
@@ -626,65 +666,11 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_place_kernel(LayoutArgs
     for (int i = tid; i < tokens_per_tile; i += kLayoutThreads) s_tok[i] = 0;
 
     // 1. Every tile's counts: this tile's exclusive offsets and the totals.
-    if (R == kRoundsLarge && NB > kLayoutThreads && NB <= 2 * kLayoutThreads) {
-        // Long tiles: threads with a second bucket keep both buckets' loads in
-        // flight together instead of a second series of round trips (the
-        // counts only: the kernel boundary already makes every word of this
-        // call visible).  Measured: 32768 x 8 slots over 128 tiles 26.9 ->
-        // 24.1-24.6 us; with one bucket per thread, or with short tiles'
-        // 32-word windows, the single-bucket loop is as fast or faster.
-        const int b0 = tid, b1 = tid + kLayoutThreads;
-        uint32_t ex0 = 0, tot0 = 0, ex1 = 0, tot1 = 0;
-        for (int t0 = 0; t0 < num_tiles; t0 += W) {
-            uint32_t c0[W], c1[W];
-#pragma unroll
-            for (int w = 0; w < W; ++w) {
-                const int64_t row = static_cast<int64_t>(t0 + w) * NB;
-                c0[w] = t0 + w < num_tiles && b0 < NB ? load_count(&a.tile_status[row + b0]) : 0u;
-                c1[w] = t0 + w < num_tiles && b1 < NB ? load_count(&a.tile_status[row + b1]) : 0u;
-            }
-#pragma unroll
-            for (int w = 0; w < W; ++w) {
-                if (t0 + w < tile) {
-                    ex0 += c0[w];
-                    ex1 += c1[w];
-                }
-                tot0 += c0[w];
-                tot1 += c1[w];
-            }
-        }
-        if (b0 < NB) {
-            s_excl[b0] = static_cast<int32_t>(ex0);
-            s_total[b0] = static_cast<int32_t>(tot0);
-        }
-        if (b1 < NB) {
-            s_excl[b1] = static_cast<int32_t>(ex1);
-            s_total[b1] = static_cast<int32_t>(tot1);
-        }
-    } else
-    for (int b = tid; b < NB; b += kLayoutThreads) {
-        uint32_t ex = 0, tot = 0;
-        for (int t0 = 0; t0 < num_tiles; t0 += W) {
-            uint32_t c[W];
-#pragma unroll
-            for (int w = 0; w < W; ++w)
-                c[w] = t0 + w < num_tiles
-                           ? static_cast<uint32_t>(load_status(
-                                 &a.tile_status[static_cast<int64_t>(t0 + w) * NB + b]))
-                           : 0u;
-#pragma unroll
-            for (int w = 0; w < W; ++w) {
-                if (t0 + w < tile) ex += c[w];
-                tot += c[w];
-            }
-        }
-        s_excl[b] = static_cast<int32_t>(ex);
-        s_total[b] = static_cast<int32_t>(tot);
-    }
+    sum_tile_counts(a.tile_status, NB, num_tiles, tile, s_excl, s_total);
     __syncthreads();
 
     // 2. Aligned exclusive scan over experts (identical in every block).
-    scan_experts(a, s_total, s_psum, s_wave, &s_fatal, tile == 0);
+    scan_experts(a, s_total, s_psum, s_wave, &s_fatal, tile == 0, sticky);
     const bool fatal = s_fatal != 0;
     if (gap_block) {
         // Gap markers of expert blockIdx.x - num_tiles.
