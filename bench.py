@@ -171,7 +171,7 @@ class Ceilings:
                "epc_read": (ctypes.c_int, [P, SZ, P, I32, I32, I32, P, P, P]),
                "epc_write": (ctypes.c_int, [P, SZ, ctypes.c_uint32, I32, I32, I32, P, P, P]),
                "epc_copy": (ctypes.c_int, [P, P, SZ, I32, I32, I32, P, P, P]),
-               "epc_row_store": (ctypes.c_int, [P, I64, I64, P, I64, I32, P, P, P]),
+               "epc_row_store": (ctypes.c_int, [P, I64, I64, P, I64, I32, I32, P, P, P]),
                "epc_gather": (ctypes.c_int, [P, P, I64, I64, P, I64, I32, P, P, P]),
                "epc_empty": (ctypes.c_int, [I32, I32, P, P, P])}
         for name, (res, args) in sig.items():
@@ -220,10 +220,11 @@ class Ceilings:
         self._ok(self.lib.epc_copy(dst.data_ptr(), src.data_ptr(), nbytes, *tune, self._stream(),
                                    self._ev(start), self._ev(stop)), "epc_copy")
 
-    def row_store(self, dst, rows, row_bytes, slot_row, tokens, K, start=None, stop=None):
+    def row_store(self, dst, rows, row_bytes, slot_row, tokens, K, start=None, stop=None,
+                  nontemporal=False):
         self._ok(self.lib.epc_row_store(dst.data_ptr(), rows, row_bytes, slot_row.data_ptr(),
-                                        tokens, K, self._stream(), self._ev(start),
-                                        self._ev(stop)), "epc_row_store")
+                                        tokens, K, 1 if nontemporal else 0, self._stream(),
+                                        self._ev(start), self._ev(stop)), "epc_row_store")
 
     def empty(self, blocks, threads, start=None, stop=None):
         self._ok(self.lib.epc_empty(blocks, threads, self._stream(), self._ev(start),
@@ -326,8 +327,10 @@ def time_ceiling(torch, ceil, fn, calls):
     return statistics.median(e0.elapsed_time(e1) * 1e3 for e0, e1 in ev)
 
 
-def time_calls(torch, ep, ceil, calls, nbytes, reps):
-    """Cache-cold median/p10/p90 per call, and the back-to-back mean."""
+def time_calls(torch, ep, ceil, calls, nbytes, reps, probe=None):
+    """Cache-cold median/p10/p90 per call, the back-to-back mean and, with a
+    1 GiB `probe`, the time including the write-back of what the call leaves
+    dirty in the MALL (time_with_writeback)."""
     out = {}
     for name, fn in calls.items():
         cold = _stats(time_cold(torch, ep, ceil, fn, reps))
@@ -335,6 +338,10 @@ def time_calls(torch, ep, ceil, calls, nbytes, reps):
         out[name] = {**cold, "bytes": nbytes[name], **_rate(nbytes[name], cold["us_median"]),
                      "back_to_back_us_mean": round(warm, 2),
                      "back_to_back_GBps": _rate(nbytes[name], warm)["GBps"]}
+        if probe is not None:
+            wb = time_with_writeback(torch, ep, ceil, fn, max(10, reps // 2), probe)
+            out[name]["with_writeback_us"] = wb["us_with_writeback"]
+            out[name]["with_writeback_GBps"] = _rate(nbytes[name], wb["us_with_writeback"])["GBps"]
     return out
 
 
@@ -503,6 +510,14 @@ def main():
     # timed beside the step's calls in the cache-cold protocol.
     fused_call = h.bind_layout_dispatch(idx, wl.x, sf=wl.sf, zero_padding=cfg.zero_padding,
                                         out_x=out_x, out_sf=out_sf)
+    # Both with streaming (non-temporal) row stores: the rows go on to HBM
+    # during the call instead of staying dirty in the MALL.
+    streaming_calls = {
+        "dispatch_streaming": h.bind_dispatch(wl.x, sf=wl.sf, zero_padding=cfg.zero_padding,
+                                              out_x=out_x, out_sf=out_sf, streaming=True),
+        "layout_dispatch_streaming": h.bind_layout_dispatch(
+            idx, wl.x, sf=wl.sf, zero_padding=cfg.zero_padding, out_x=out_x, out_sf=out_sf,
+            streaming=True)}
 
     def step():
         layout_call()
@@ -550,8 +565,10 @@ def main():
     kernels = None
     if "cold" in phases:
         kernels = {}
-        nbytes_all = dict(nbytes, layout_dispatch=nbytes["layout"] + nbytes["dispatch"])
-        for name, fn in {**calls, "layout_dispatch": fused_call}.items():
+        nbytes_all = dict(nbytes, layout_dispatch=nbytes["layout"] + nbytes["dispatch"],
+                          dispatch_streaming=nbytes["dispatch"],
+                          layout_dispatch_streaming=nbytes["layout"] + nbytes["dispatch"])
+        for name, fn in {**calls, "layout_dispatch": fused_call, **streaming_calls}.items():
             st = _stats(time_cold(torch, ep, ceil, fn, args.calls))
             nb = nbytes_all[name]
             kernels[name] = {**st, "bytes": nb, **_rate(nb, st["us_median"]),
@@ -574,11 +591,14 @@ def main():
         wbytes = written_bytes(cfg, V, G)
         writeback = {"protocol": "flush; call + 1 GiB read, minus the 1 GiB read alone; "
                                  "medians", "mall_bytes": MALL_BYTES}
-        for name in ("dispatch", "combine"):
-            r = time_with_writeback(torch, ep, ceil, calls[name], max(10, args.calls // 2), probe)
-            r.update(_rate(nbytes[name], r["us_with_writeback"]))
-            r["written_bytes"] = wbytes[name]
-            r["writes_fit_mall"] = wbytes[name] < MALL_BYTES
+        wcalls = {**calls, "dispatch_streaming": streaming_calls["dispatch_streaming"]}
+        for name in ("dispatch", "dispatch_streaming", "combine"):
+            base = "dispatch" if name == "dispatch_streaming" else name
+            r = time_with_writeback(torch, ep, ceil, wcalls[name], max(10, args.calls // 2),
+                                    probe)
+            r.update(_rate(nbytes[base], r["us_with_writeback"]))
+            r["written_bytes"] = wbytes[base]
+            r["writes_fit_mall"] = wbytes[base] < MALL_BYTES
             writeback[name] = r
         del probe
         h.read_counts()
@@ -615,6 +635,9 @@ def main():
             best = min(((time_ceiling(torch, ceil, mk(t), n), t) for t in tunes))
             ceil_us[name], ceil_tune[name] = best
         ceil_us.update({
+            "row_store_dispatch_rows_streaming": time_ceiling(
+                torch, ceil, lambda s, e: ceil.row_store(out_x, cap, R, h.dst_slot, cfg.tokens, K,
+                                                         s, e, nontemporal=True), n),
             "row_store_dispatch_rows": time_ceiling(
                 torch, ceil, lambda s, e: ceil.row_store(out_x, cap, R, h.dst_slot, cfg.tokens, K,
                                                          s, e), n),
@@ -636,6 +659,7 @@ def main():
         moved = {"read_1GiB": FLUSH_BYTES, "write_4GiB": big, "copy_2GiB": big,
                  "write_dispatch_bytes": wd16,
                  "row_store_dispatch_rows": V * R,
+                 "row_store_dispatch_rows_streaming": V * R,
                  "gather_combine_rows": V * 2 * H + cfg.tokens * 2 * H,
                  "gather_contiguous_rows": cfg.tokens * K * 2 * H + cfg.tokens * 2 * H,
                  "empty_1_block": 0, "empty_combine_grid": 0}
@@ -648,14 +672,18 @@ def main():
         ceilings["note"] = ("cache-cold medians of plain kernels (libep_ceilings.so): sequential "
                             "read, sequential write, 1:1 copy (best of 11 launch settings each), "
                             "a sequential write of the dispatch's output bytes (fits the MALL), "
-                            "the dispatch's row stores alone (same rows, no loads), the "
+                            "the dispatch's row stores alone (same rows, no loads; ordinary "
+                            "and non-temporal stores), the "
                             "combine's row loads and output stores alone (same rows, XOR "
                             "instead of arithmetic), and the same with contiguous rows")
         del a, b, contig
         h.read_counts()
         if kernels:
             for name, ck in (("dispatch", "row_store_dispatch_rows"),
+                             ("dispatch_streaming", "row_store_dispatch_rows_streaming"),
                              ("combine", "gather_combine_rows")):
+                if name not in kernels:
+                    continue
                 cu = ceilings[ck]["us_median"]
                 kernels[name]["ceiling"] = {"kernel": ck, "us": cu,
                                             "frac_of_ceiling": round(cu / kernels[name]["us_median"], 4)}
@@ -691,6 +719,10 @@ def main():
         del cg
 
     T, K, H = cfg.tokens, cfg.topk, cfg.hidden
+    # The 1 GiB read that evicts what a call leaves dirty, for the with-write-
+    # back figures of the other calls.
+    probe = (torch.ones(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda")
+             if {"backward", "rank", "quant"} & set(phases) else None)
     # Backward pair on the same layout.
     backward = None
     if "backward" in phases:
@@ -703,7 +735,7 @@ def main():
                       g, topk_weights=w, y=wl.y, grad_y=grad_y, want_grad_weights=True),
                   "dispatch_backward": lambda: h.dispatch_backward(
                       wl.y, grad_out_w=gw_rows, want_grad_weights=True)}
-        backward = time_calls(torch, ep, ceil, bcalls, bb, args.reps)
+        backward = time_calls(torch, ep, ceil, bcalls, bb, args.reps, probe)
         del g, grad_y, gw_rows
 
     # Rank (non-expanded) layout and per-token biases, on the same layout.
@@ -728,7 +760,7 @@ def main():
                   "combine_rank": lambda: h.combine_rank(xr, bias_0=b0, bias_1=b1, out=out),
                   "combine_token_biases": lambda: h.combine(wl.y, topk_weights=w, bias=wl.bias,
                                                             out=out, bias_0=b0, bias_1=b1)}
-        rank = time_calls(torch, ep, ceil, rcalls, rb, args.reps)
+        rank = time_calls(torch, ep, ceil, rcalls, rb, args.reps, probe)
         del rx, rsf, ri, rw, xr, b0, b1
 
     # FP8 quantiser on its own and fused with dispatch: bf16 rows of the
@@ -765,8 +797,9 @@ def main():
                   "dispatch_rank_quant_f32": lambda: h.dispatch_rank_quant(
                       xq, "f32", topk_weights=w, out_x=rqx, out_sf=rqsf, out_topk_idx=rqi,
                       out_topk_weights=rqw)}
-        quant = time_calls(torch, ep, ceil, qcalls, qb, args.reps)
+        quant = time_calls(torch, ep, ceil, qcalls, qb, args.reps, probe)
         del xq, qx, qt, sfs, sft, rqx, rqsf, rqi, rqw
+    del probe
     h.read_counts()
 
     # Roofline of dispatch and combine (combine is the dominant kernel: the
@@ -792,6 +825,15 @@ def main():
             return r
         roofline = roof("combine")
         roofline["per_kernel"] = {"dispatch": roof("dispatch"), "combine": roof("combine")}
+        if "dispatch_streaming" in kernels:
+            k = kernels["dispatch_streaming"]
+            st = {"frac": round(k["mean_GBps"] / HBM_PEAK_GBPS, 4),
+                  "frac_median": k["frac_hbm_peak"], "timing": "cache-cold mean"}
+            if writeback and "dispatch_streaming" in writeback:
+                st["frac_with_writeback"] = writeback["dispatch_streaming"]["frac_hbm_peak"]
+            if "ceiling" in k:
+                st["frac_of_ceiling"] = k["ceiling"]["frac_of_ceiling"]
+            roofline["per_kernel"]["dispatch"]["streaming_stores"] = st
 
     cpu = None
     cpu_rows = None

@@ -39,6 +39,7 @@ LIB_PATH = os.environ.get("EP_LIBRARY") or os.path.join(
  EP_ERR_WORKSPACE, EP_ERR_NOT_LAID_OUT, EP_ERR_CAPACITY, EP_ERR_INVALID_ID,
  EP_ERR_HIP, EP_ERR_TIMEOUT) = range(12)
 EP_BF16, EP_FP8_E4M3, EP_F32, EP_I32, EP_I64 = range(5)
+EP_DISPATCH_ZERO_PADDING, EP_DISPATCH_STREAMING = 1, 2
 EP_SF_F32, EP_SF_UE8M0 = 0, 1
 _SF_FORMATS = {"f32": EP_SF_F32, "ue8m0": EP_SF_UE8M0}
 EP_ERRBIT_CAPACITY = 1
@@ -186,11 +187,11 @@ def ep_handle_import(h: ep_handle, topk_idx_ptr, idx_dtype, num_tokens, counts_p
 
 
 def ep_dispatch(h: ep_handle, x_ptr, x_dtype, hidden, sf_ptr, sf_ts, sf_hs, num_sf_packs,
-                w_ptr, out_x_ptr, out_sf_ptr, out_ts, out_hs, out_w_ptr, zero_padding,
+                w_ptr, out_x_ptr, out_sf_ptr, out_ts, out_hs, out_w_ptr, flags,
                 stream) -> int:
     return lib().ep_dispatch(ctypes.byref(h), x_ptr, x_dtype, hidden, sf_ptr, sf_ts, sf_hs,
                              num_sf_packs, w_ptr, out_x_ptr, out_sf_ptr, out_ts, out_hs,
-                             out_w_ptr, zero_padding, stream)
+                             out_w_ptr, flags, stream)
 
 
 def ep_tma_aligned_rows(rows: int) -> int:
@@ -505,11 +506,11 @@ class Handle:
         return BoundCall(fn, args, "ep_layout", self, (topk_idx, cumulative_stats))
 
     def _layout_dispatch_call(self, topk_idx, x, sf, topk_weights, zero_padding, out_x, out_sf,
-                              out_w, want_weights, col_major_sf, cumulative_stats):
+                              out_w, want_weights, col_major_sf, cumulative_stats, streaming):
         lfn, largs = self._layout_call(topk_idx, cumulative_stats)
         _, dargs, result, keep = self._dispatch_call(
             x, sf, topk_weights, zero_padding, out_x, out_sf, out_w, want_weights, col_major_sf,
-            num_tokens=topk_idx.shape[0])
+            num_tokens=topk_idx.shape[0], streaming=streaming)
         # ep_layout_dispatch takes the layout's arguments, then the dispatch's
         # (the handle appears once)
         args = largs + dargs[1:]
@@ -521,13 +522,14 @@ class Handle:
                         out_x: Optional[torch.Tensor] = None, out_sf: Optional[torch.Tensor] = None,
                         out_w: Optional[torch.Tensor] = None, want_weights: bool = False,
                         col_major_sf: bool = False,
-                        cumulative_stats: Optional[torch.Tensor] = None):
+                        cumulative_stats: Optional[torch.Tensor] = None,
+                        streaming: bool = False):
         """``layout`` then ``dispatch`` in one call (ep_layout_dispatch: the
         same outputs, one host-side check of both argument sets).  Returns
         (out_x, out_sf, out_w)."""
         fn, args, result, _ = self._layout_dispatch_call(
             topk_idx, x, sf, topk_weights, zero_padding, out_x, out_sf, out_w, want_weights,
-            col_major_sf, cumulative_stats)
+            col_major_sf, cumulative_stats, streaming)
         _check(fn(*args, _stream()), "ep_layout_dispatch")
         self.topk_idx = topk_idx
         return result
@@ -539,11 +541,12 @@ class Handle:
                              out_sf: Optional[torch.Tensor] = None,
                              out_w: Optional[torch.Tensor] = None, want_weights: bool = False,
                              col_major_sf: bool = False,
-                             cumulative_stats: Optional[torch.Tensor] = None) -> "BoundCall":
+                             cumulative_stats: Optional[torch.Tensor] = None,
+                             streaming: bool = False) -> "BoundCall":
         """``layout_dispatch`` bound to these tensors (see BoundCall)."""
         fn, args, result, keep = self._layout_dispatch_call(
             topk_idx, x, sf, topk_weights, zero_padding, out_x, out_sf, out_w, want_weights,
-            col_major_sf, cumulative_stats)
+            col_major_sf, cumulative_stats, streaming)
         self.topk_idx = topk_idx
         # no token-count check: the call lays the batch out itself
         return BoundCall(fn, args, "ep_layout_dispatch", result, keep)
@@ -586,14 +589,16 @@ class Handle:
                  topk_weights: Optional[torch.Tensor] = None, zero_padding: bool = False,
                  out_x: Optional[torch.Tensor] = None, out_sf: Optional[torch.Tensor] = None,
                  out_w: Optional[torch.Tensor] = None, want_weights: bool = False,
-                 col_major_sf: bool = False):
+                 col_major_sf: bool = False, streaming: bool = False):
         """x: bf16 [T, H], or FP8 (float8_e4m3fn or uint8 codes) [T, H] with
         scales ``sf``: fp32 [T, H/128] or int32 packs [T, P] (any strides).
         Returns (out_x, out_sf, out_w); outputs are allocated with
         ``capacity`` rows unless given (out_sf column-major, TMA-aligned, when
-        ``col_major_sf``)."""
+        ``col_major_sf``).  ``streaming``: non-temporal stores of the rows
+        (EP_DISPATCH_STREAMING)."""
         fn, args, result, _ = self._dispatch_call(x, sf, topk_weights, zero_padding, out_x,
-                                                  out_sf, out_w, want_weights, col_major_sf)
+                                                  out_sf, out_w, want_weights, col_major_sf,
+                                                  streaming=streaming)
         _check(fn(*args, _stream()), "ep_dispatch")
         return result
 
@@ -601,15 +606,16 @@ class Handle:
                       topk_weights: Optional[torch.Tensor] = None, zero_padding: bool = False,
                       out_x: Optional[torch.Tensor] = None, out_sf: Optional[torch.Tensor] = None,
                       out_w: Optional[torch.Tensor] = None, want_weights: bool = False,
-                      col_major_sf: bool = False) -> BoundCall:
+                      col_major_sf: bool = False, streaming: bool = False) -> BoundCall:
         """``dispatch`` bound to these tensors (see BoundCall); each call
         returns (out_x, out_sf, out_w)."""
         fn, args, result, keep = self._dispatch_call(x, sf, topk_weights, zero_padding, out_x,
-                                                      out_sf, out_w, want_weights, col_major_sf)
+                                                      out_sf, out_w, want_weights, col_major_sf,
+                                                      streaming=streaming)
         return BoundCall(fn, args, "ep_dispatch", result, keep, self.h)
 
     def _dispatch_call(self, x, sf, topk_weights, zero_padding, out_x, out_sf, out_w,
-                       want_weights, col_major_sf, num_tokens=None):
+                       want_weights, col_major_sf, num_tokens=None, streaming=False):
         T = self.h.num_tokens if num_tokens is None else num_tokens
         _dev(x, "x")
         _need(x.dim() == 2 and x.shape[0] == T, "x must be [num_tokens, hidden]")
@@ -639,7 +645,8 @@ class Handle:
             _need(out_w.dtype == torch.float32 and out_w.numel() == cap, "out_w: fp32 [capacity]")
         args = (ctypes.byref(self.h), _ptr(x), EP_FP8_E4M3 if fp8 else EP_BF16, H, _ptr(sf),
                 sf_ts, sf_hs, packs, _ptr(topk_weights), _ptr(out_x), _ptr(out_sf), o_ts, o_hs,
-                _ptr(out_w), 1 if zero_padding else 0)
+                _ptr(out_w), (EP_DISPATCH_ZERO_PADDING if zero_padding else 0) |
+                (EP_DISPATCH_STREAMING if streaming else 0))
         return lib().ep_dispatch, args, (out_x, out_sf, out_w), (x, sf, topk_weights)
 
     def dispatch_quant(self, x: torch.Tensor, scale_format="f32",

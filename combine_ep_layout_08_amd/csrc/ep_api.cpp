@@ -349,7 +349,9 @@ static ep_status dispatch_prepare(const ep_handle *h, int32_t num_tokens, const 
                                   int32_t num_sf_packs, const float *topk_weights, void *out_x,
                                   void *out_sf, int64_t out_sf_token_stride,
                                   int64_t out_sf_hidden_stride, float *out_w,
-                                  int32_t zero_padding, ep::DispatchArgs *a) {
+                                  int32_t flags, ep::DispatchArgs *a) {
+    if (flags & ~(EP_DISPATCH_ZERO_PADDING | EP_DISPATCH_STREAMING)) return EP_ERR_UNSUPPORTED;
+    const bool zero_padding = (flags & EP_DISPATCH_ZERO_PADDING) != 0;
     if (x_dtype != EP_BF16 && x_dtype != EP_FP8_E4M3) return EP_ERR_DTYPE;
     if (hidden <= 0) return EP_ERR_SHAPE;
     const bool fp8 = x_dtype == EP_FP8_E4M3;
@@ -357,7 +359,7 @@ static ep_status dispatch_prepare(const ep_handle *h, int32_t num_tokens, const 
     // With no tokens nothing is read, and only zero padding can write (the
     // gap rows of an imported layout, inside the capacity).
     const bool reads = num_tokens > 0;
-    const bool writes = reads || (zero_padding != 0 && h->capacity > 0);
+    const bool writes = reads || (zero_padding && h->capacity > 0);
     int32_t packs = 0;
     const ep_status st = check_sf(fp8, hidden, sf, out_sf, num_sf_packs, reads, writes,
                                   sf_token_stride, sf_hidden_stride, out_sf_token_stride,
@@ -389,7 +391,8 @@ static ep_status dispatch_prepare(const ep_handle *h, int32_t num_tokens, const 
     a->out_ts = out_sf_token_stride;
     a->out_hs = out_sf_hidden_stride;
     a->out_w = out_w;
-    a->zero_padding = zero_padding != 0;
+    a->zero_padding = zero_padding;
+    a->streaming = (flags & EP_DISPATCH_STREAMING) != 0;
     a->src_meta = h->src_meta;
     return EP_OK;
 }
@@ -398,7 +401,7 @@ ep_status ep_dispatch(const ep_handle *h, const void *x, ep_dtype x_dtype, int32
                       const void *sf, int64_t sf_token_stride, int64_t sf_hidden_stride,
                       int32_t num_sf_packs, const float *topk_weights, void *out_x, void *out_sf,
                       int64_t out_sf_token_stride, int64_t out_sf_hidden_stride, float *out_w,
-                      int32_t zero_padding, hipStream_t stream) {
+                      int32_t flags, hipStream_t stream) {
     const ep::CallEvents ev = take_events();
     if (!h) return EP_ERR_NULL;
     if (!handle_ready(h)) return EP_ERR_WORKSPACE;
@@ -407,7 +410,7 @@ ep_status ep_dispatch(const ep_handle *h, const void *x, ep_dtype x_dtype, int32
     const ep_status st = dispatch_prepare(h, h->num_tokens, x, x_dtype, hidden, sf,
                                           sf_token_stride, sf_hidden_stride, num_sf_packs,
                                           topk_weights, out_x, out_sf, out_sf_token_stride,
-                                          out_sf_hidden_stride, out_w, zero_padding, &a);
+                                          out_sf_hidden_stride, out_w, flags, &a);
     if (st != EP_OK) return st;
     return hip_status(ep::launch_dispatch(a, stream, ev));
 }
@@ -418,7 +421,7 @@ ep_status ep_layout_dispatch(ep_handle *h, const void *topk_idx, ep_dtype idx_dt
                              int64_t sf_token_stride, int64_t sf_hidden_stride,
                              int32_t num_sf_packs, const float *topk_weights, void *out_x,
                              void *out_sf, int64_t out_sf_token_stride,
-                             int64_t out_sf_hidden_stride, float *out_w, int32_t zero_padding,
+                             int64_t out_sf_hidden_stride, float *out_w, int32_t flags,
                              hipStream_t stream) {
     const ep::CallEvents ev = take_events();
     ep::LayoutArgs la;
@@ -427,7 +430,7 @@ ep_status ep_layout_dispatch(ep_handle *h, const void *topk_idx, ep_dtype idx_dt
     ep::DispatchArgs da;
     st = dispatch_prepare(h, num_tokens, x, x_dtype, hidden, sf, sf_token_stride,
                           sf_hidden_stride, num_sf_packs, topk_weights, out_x, out_sf,
-                          out_sf_token_stride, out_sf_hidden_stride, out_w, zero_padding, &da);
+                          out_sf_token_stride, out_sf_hidden_stride, out_w, flags, &da);
     if (st != EP_OK) return st;
     ep::CallEvents first, last;
     first.start = ev.start;

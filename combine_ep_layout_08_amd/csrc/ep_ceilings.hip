@@ -12,7 +12,8 @@
 //   row_store   the dispatch's store pattern without its loads: one wave per
 //               (token, 1 KB pass of a row) stores a constant to each of the
 //               token's slot rows given by a slot -> row table (rows of the
-//               expanded layout in the order the dispatch writes them)
+//               expanded layout in the order the dispatch writes them), with
+//               ordinary or non-temporal stores as the dispatch can
 //   gather      the combine's pattern without its arithmetic: one thread per
 //               (token, 16-byte column) loads that column of each of the
 //               token's K slot rows, XORs them and stores one vector (K reads
@@ -149,6 +150,7 @@ bool valid_vpt(int32_t v) { return v == 1 || v == 2 || v == 4 || v == 8 || v == 
 
 // One wave per (token, pass of 64 vectors): the token's K slot rows (-1 or
 // rows outside [0, rows) skipped) each get the pass stored.
+template <bool NT>
 __global__ __launch_bounds__(kThreads) void row_store_kernel(u32x4 *dst, const int32_t *slot_row,
                                                              int64_t tokens, int K,
                                                              int64_t row_vecs, int64_t rows,
@@ -164,7 +166,12 @@ __global__ __launch_bounds__(kThreads) void row_store_kernel(u32x4 *dst, const i
     for (int k = 0; k < K; ++k) {
         const int32_t r = __builtin_amdgcn_readlane(my_row, k);
         if (r < 0) continue;
-        if (c < row_vecs) dst[static_cast<int64_t>(r) * row_vecs + c] = v;
+        if (c >= row_vecs) continue;
+        u32x4 *p = dst + static_cast<int64_t>(r) * row_vecs + c;
+        if constexpr (NT)
+            __builtin_nontemporal_store(v, p);
+        else
+            *p = v;
     }
 }
 
@@ -249,8 +256,8 @@ int epc_copy(void *dst, const void *src, size_t bytes, int32_t vec_per_thread, i
 }
 
 int epc_row_store(void *dst, int64_t rows, int64_t row_bytes, const int32_t *slot_row,
-                  int64_t tokens, int32_t K, hipStream_t stream, hipEvent_t start,
-                  hipEvent_t stop) {
+                  int64_t tokens, int32_t K, int32_t nontemporal, hipStream_t stream,
+                  hipEvent_t start, hipEvent_t stop) {
     if (rows < 0 || tokens < 0 || K < 1 || K > 64 || row_bytes <= 0 || (row_bytes & 15) ||
         !aligned16(dst) || (tokens && (!dst || !slot_row)))
         return -1;
@@ -258,8 +265,9 @@ int epc_row_store(void *dst, int64_t rows, int64_t row_bytes, const int32_t *slo
     const int64_t passes = (row_vecs + 63) / 64;
     const int64_t blocks = (tokens * passes + kThreads / 64 - 1) / (kThreads / 64);
     if (blocks == 0 || blocks > INT32_MAX) return blocks == 0 ? 0 : -1;
-    return status(launch(row_store_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads),
-                         stream, start, stop, static_cast<u32x4 *>(dst), slot_row, tokens,
+    auto kernel = nontemporal ? row_store_kernel<true> : row_store_kernel<false>;
+    return status(launch(kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), stream,
+                         start, stop, static_cast<u32x4 *>(dst), slot_row, tokens,
                          static_cast<int>(K), row_vecs, rows, static_cast<int>(passes)));
 }
 

@@ -41,19 +41,22 @@ constexpr int kGapRowsPerBlock = kWavesPerBlock;
 // walk several passes, each requesting the next pass's loads before storing
 // the current one, measured 56-68 us after a flush against 46.4 at prefill
 // and 10-12 % slower at 16384 x 4096 and 32768 x 7168.  VPL 2 or 4 gained at 32768 x 7168 on one box and lost
-// on another, equal at prefill.  Cache hints of the row copy: non-temporal
-// stores measured 2-6 % slower (57 us against 47 on the FP8 prefill rows
-// together with non-temporal loads); non-temporal loads of the token rows
+// on another, equal at prefill.  Non-temporal loads of the token rows
 // (EP_DISPATCH_NT_LOAD) within 0.5 us of ordinary ones on the prefill
 // dispatch and 2-3 % slower at larger sizes in the earlier form, so off.
+//
+// Stores of the rows: the caller chooses (EP_DISPATCH_STREAMING).  Ordinary
+// stores leave the rows in the MALL, dirty, for a consumer that reads them
+// next (a grouped GEMM) and for the write-back later; non-temporal
+// (streaming) stores send them on to HBM during the call.  FP8 prefill
+// (4096 x 7168), interleaved on one box: ordinary 46.1 us after a cache
+// flush, 43.3 back to back, 79.0-79.4 us with the write-back of what it
+// leaves dirty; streaming 53.0 / 45.8 / 56.6-57.0 us.
 #ifndef EP_DISPATCH_MAX_VPL
 #define EP_DISPATCH_MAX_VPL 1
 #endif
 #ifndef EP_DISPATCH_NT_LOAD
 #define EP_DISPATCH_NT_LOAD 0
-#endif
-#ifndef EP_DISPATCH_NT_STORE
-#define EP_DISPATCH_NT_STORE 0
 #endif
 // Resident blocks per compute unit of a persistent grid for the quantising
 // dispatch (0 = one block per work unit, the default: measured equal or
@@ -91,8 +94,9 @@ constexpr int kDispatchBlocksPerCu = EP_DISPATCH_BLOCKS_PER_CU;
 constexpr int kSfRowsPerWave = EP_DISPATCH_SF_ROWS_PER_WAVE;
 constexpr int64_t kSfBlocks = EP_DISPATCH_SF_BLOCKS;
 
+template <bool NT>
 __device__ inline void store_row_vec(u32x4 *p, u32x4 v) {
-    if (EP_DISPATCH_NT_STORE)
+    if constexpr (NT)
         __builtin_nontemporal_store(v, p);
     else
         *p = v;
@@ -107,7 +111,7 @@ __device__ inline bool dispatch_stopped(const DispatchArgs &a) {
 // slot row in my_dst (lane k holds slot k's row, -1 if none); pass 0 also
 // stores the scale packs and weight when they are not moved in expanded-row
 // order.
-template <int VPL>
+template <int VPL, bool NT>
 __device__ inline void store_token_pass(const DispatchArgs &a, int64_t t, int64_t pass, int lane,
                                         const u32x4 (&v)[VPL], int32_t my_dst) {
     const int64_t V = a.row_vecs;
@@ -133,7 +137,7 @@ __device__ inline void store_token_pass(const DispatchArgs &a, int64_t t, int64_
 #pragma unroll
         for (int q = 0; q < VPL; ++q) {
             const int64_t c = c0 + q * 64 + lane;
-            if (c < V) store_row_vec(d + c, v[q]);
+            if (c < V) store_row_vec<NT>(d + c, v[q]);
         }
     }
 }
@@ -161,13 +165,13 @@ __device__ inline void load_token_pass(const DispatchArgs &a, int64_t t, int64_t
 // to every valid slot's row.  The row loads, the slot rows and the error
 // word are all requested before the wave waits on any of them (one round
 // trip to memory instead of three).
-template <int VPL>
+template <int VPL, bool NT>
 __device__ inline void dispatch_token(const DispatchArgs &a, int64_t t, int64_t pass, int lane) {
     u32x4 v[VPL];
     int32_t my_dst;
     load_token_pass<VPL>(a, t, pass, lane, v, my_dst);
     if (dispatch_stopped(a)) return;
-    store_token_pass<VPL>(a, t, pass, lane, v, my_dst);
+    store_token_pass<VPL, NT>(a, t, pass, lane, v, my_dst);
 }
 
 // Scale packs of kSfRowsPerWave consecutive expanded rows from r0 (one wave):
@@ -474,12 +478,13 @@ __device__ inline void quant_token(const DispatchArgs &a, int64_t t, int64_t pas
 }
 
 // Zero one alignment-gap row (one wave): rows [psum[e] + counts[e], psum[e+1]).
+template <bool NT>
 __device__ inline void dispatch_gap_row(const DispatchArgs &a, int e, int64_t r, int lane) {
     if (r >= a.psum[e + 1] || r >= a.capacity) return;
     const int64_t V = a.row_vecs;
     const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
     u32x4 *d = static_cast<u32x4 *>(a.out_x) + r * V;
-    for (int64_t c = lane; c < V; c += 64) store_row_vec(d + c, zero);
+    for (int64_t c = lane; c < V; c += 64) store_row_vec<NT>(d + c, zero);
     for (int j = lane; j < a.num_sf; j += 64) a.out_sf[r * a.out_ts + j * a.out_hs] = 0u;
     if (a.out_w && lane == 0) a.out_w[r] = 0.0f;
 }
@@ -492,7 +497,7 @@ __device__ inline void dispatch_gap_row(const DispatchArgs &a, int e, int64_t r,
 #ifndef EP_DISPATCH_WAVES_PER_EU
 #define EP_DISPATCH_WAVES_PER_EU 8
 #endif
-template <int VPL>
+template <int VPL, bool NT>
 __global__ __launch_bounds__(kDispatchThreads)
 __attribute__((amdgpu_waves_per_eu(1, EP_DISPATCH_WAVES_PER_EU))) void dispatch_copy_kernel(DispatchArgs a,
                                                                         int64_t sf_units,
@@ -527,7 +532,7 @@ __attribute__((amdgpu_waves_per_eu(1, EP_DISPATCH_WAVES_PER_EU))) void dispatch_
     if (u < token_units) {
         const int64_t wv = u * kWavesPerBlock + wave;
         const int64_t t = wv / passes;
-        if (t < a.num_tokens) dispatch_token<VPL>(a, t, wv - t * passes, lane);
+        if (t < a.num_tokens) dispatch_token<VPL, NT>(a, t, wv - t * passes, lane);
         return;
     }
     if (dispatch_stopped(a)) return;
@@ -536,7 +541,7 @@ __attribute__((amdgpu_waves_per_eu(1, EP_DISPATCH_WAVES_PER_EU))) void dispatch_
     const int64_t chunk = g - static_cast<int64_t>(e) * gap_chunks;
     const int64_t r = static_cast<int64_t>(a.psum[e]) + a.counts[e] + chunk * kGapRowsPerBlock +
                       wave;
-    dispatch_gap_row(a, e, r, lane);
+    dispatch_gap_row<NT>(a, e, r, lane);
 }
 
 // Quantising dispatch over work units (one block per unit unless a
@@ -562,7 +567,7 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_kernel(DispatchArgs
             const int64_t chunk = g % gap_chunks;
             const int64_t r = static_cast<int64_t>(a.psum[e]) + a.counts[e] +
                               chunk * kGapRowsPerBlock + wave;
-            dispatch_gap_row(a, e, r, lane);
+            dispatch_gap_row<false>(a, e, r, lane);
         }
     }
 }
@@ -601,9 +606,15 @@ hipError_t launch_vpl(const DispatchArgs &a, hipStream_t stream, CallEvents ev) 
     const int64_t blocks = sf_units + token_units + gap_units;
     if (blocks == 0) return hipSuccess;
     if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
-    return launch_kernel(dispatch_copy_kernel<VPL>, dim3(static_cast<unsigned>(blocks)),
+    const int gc = gap_chunks > 0 ? gap_chunks : 1;
+    const int np = static_cast<int>(passes);
+    if (a.streaming)
+        return launch_kernel(dispatch_copy_kernel<VPL, true>, dim3(static_cast<unsigned>(blocks)),
+                             dim3(kDispatchThreads), stream, ev.start, ev.stop, b, sf_units,
+                             token_units, gc, np);
+    return launch_kernel(dispatch_copy_kernel<VPL, false>, dim3(static_cast<unsigned>(blocks)),
                          dim3(kDispatchThreads), stream, ev.start, ev.stop, b, sf_units,
-                         token_units, gap_chunks > 0 ? gap_chunks : 1, static_cast<int>(passes));
+                         token_units, gc, np);
     }
 }
 

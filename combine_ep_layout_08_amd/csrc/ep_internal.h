@@ -127,6 +127,7 @@ struct DispatchArgs {
     int64_t out_ts, out_hs;
     float *out_w;
     bool zero_padding;
+    bool streaming;              // non-temporal stores of the copied rows (copying form)
     int32_t quant;               // 0: copy x; EP_SF_F32 + 1 / EP_SF_UE8M0 + 1: quantise bf16 x
     // Source slot of every expanded row (the layout's src_meta): when set, a
     // copying dispatch moves the scale packs and weights in expanded-row

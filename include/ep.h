@@ -271,19 +271,29 @@ ep_status ep_handle_import(ep_handle *h, const void *topk_idx, ep_dtype idx_dtyp
  *            is the grouped-GEMM scale layout.
  *   out_w    NULL or device fp32 [capacity]: weight of the row's slot
  *            (1.0 when topk_weights is NULL).
- *   zero_padding  nonzero: gap rows get zero bytes, zero scales, weight 0.
+ *   flags    0, or EP_DISPATCH_ZERO_PADDING and/or EP_DISPATCH_STREAMING
+ *            (other bits: EP_ERR_UNSUPPORTED).  EP_DISPATCH_ZERO_PADDING
+ *            [Ch7 §7.3, do_zero_padding]: gap rows get zero bytes, zero
+ *            scales, weight 0.  EP_DISPATCH_STREAMING: the rows of out_x
+ *            are written with non-temporal stores, which go on to HBM
+ *            during the call; without it they are written through the
+ *            caches and may stay dirty in the last-level cache (MALL) for
+ *            a consumer that reads them next, and reach HBM later.  The
+ *            bytes written are the same either way.
  * With no tokens in the layout, x and sf may be NULL, and so may out_x and
- * out_sf unless zero_padding is set and capacity > 0 (an imported layout
- * can have gap rows and no tokens).
+ * out_sf unless zero padding is asked for and capacity > 0 (an imported
+ * layout can have gap rows and no tokens).
  * Rows at or past psum[E], and gap rows without zero padding, are not
  * written.  Reuses the handle, so a cached re-dispatch is just another call.
  */
+#define EP_DISPATCH_ZERO_PADDING 1
+#define EP_DISPATCH_STREAMING 2
 ep_status ep_dispatch(const ep_handle *h, const void *x, ep_dtype x_dtype,
                       int32_t hidden, const void *sf, int64_t sf_token_stride,
                       int64_t sf_hidden_stride, int32_t num_sf_packs,
                       const float *topk_weights, void *out_x, void *out_sf,
                       int64_t out_sf_token_stride, int64_t out_sf_hidden_stride,
-                      float *out_w, int32_t zero_padding, hipStream_t stream);
+                      float *out_w, int32_t flags, hipStream_t stream);
 
 /*
  * Uncached dispatch: ep_layout on topk_idx, then ep_dispatch of x, in one
@@ -301,7 +311,7 @@ ep_status ep_layout_dispatch(ep_handle *h, const void *topk_idx, ep_dtype idx_dt
                              int64_t sf_hidden_stride, int32_t num_sf_packs,
                              const float *topk_weights, void *out_x, void *out_sf,
                              int64_t out_sf_token_stride, int64_t out_sf_hidden_stride,
-                             float *out_w, int32_t zero_padding, hipStream_t stream);
+                             float *out_w, int32_t flags, hipStream_t stream);
 
 /*
  * Rows of a column-major scale buffer aligned for the tensor-memory loads of

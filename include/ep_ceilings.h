@@ -62,9 +62,11 @@ int epc_copy(void *dst, const void *src, size_t bytes, int32_t vec_per_thread,
 /* The dispatch's store pattern alone: for each token t < tokens and each
  * 1 KB pass of a row (one wave), a constant is stored to that pass of row
  * slot_row[t*K + k] of dst [rows, row_bytes] for every k with
- * 0 <= slot_row[t*K + k] < rows (others skipped).  1 <= K <= 64. */
+ * 0 <= slot_row[t*K + k] < rows (others skipped).  1 <= K <= 64.
+ * nontemporal: nonzero for streaming stores (the dispatch's
+ * EP_DISPATCH_STREAMING). */
 int epc_row_store(void *dst, int64_t rows, int64_t row_bytes,
-                  const int32_t *slot_row, int64_t tokens, int32_t K,
+                  const int32_t *slot_row, int64_t tokens, int32_t K, int32_t nontemporal,
                   hipStream_t stream, hipEvent_t start, hipEvent_t stop);
 
 /* The combine's traffic alone: out[t] (row_bytes, out holds tokens rows) =

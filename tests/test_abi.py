@@ -149,12 +149,20 @@ def test_dispatch_validation():
     h = _fake_handle()
     args = dict(x=A16, dt=ep.EP_BF16, H=64, sf=None, w=None, out=A16, osf=None, ow=None, np=0)
 
-    def call(hh=h, **kw):
+    def call(hh=h, flags=0, **kw):
         a = dict(args, **kw)
         return ep.ep_dispatch(hh, a["x"], a["dt"], a["H"], a["sf"], 0, 0, a["np"], a["w"],
-                              a["out"], a["osf"], 0, 0, a["ow"], 0, None)
+                              a["out"], a["osf"], 0, 0, a["ow"], flags, None)
 
     assert call(hh=_fake_handle(laid_out=0)) == ep.EP_ERR_NOT_LAID_OUT
+    for bad in (4, 8, 1 << 30, -1):                       # flag bits beyond the two defined
+        assert call(flags=bad) == ep.EP_ERR_UNSUPPORTED
+        fused = ep.lib().ep_layout_dispatch(ctypes.byref(h), A16, ep.EP_I64, 4, None, A16,
+                                            ep.EP_BF16, 64, None, 0, 0, 0, None, A16, None, 0,
+                                            0, None, bad, None)
+        assert fused == ep.EP_ERR_UNSUPPORTED
+    assert call(flags=ep.EP_DISPATCH_STREAMING | ep.EP_DISPATCH_ZERO_PADDING, x=None) == \
+        ep.EP_ERR_NULL                                    # the defined bits pass the flag check
     assert call(dt=ep.EP_F32) == ep.EP_ERR_DTYPE
     assert call(H=0) == ep.EP_ERR_SHAPE
     assert call(H=60) == ep.EP_ERR_MISALIGNED                # bf16 rows of 120 bytes

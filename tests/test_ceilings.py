@@ -42,7 +42,7 @@ def test_invalid_arguments_launch_nothing(ceil):
     ceil.epc_read.argtypes = [P, SZ, P, I32, I32, I32, P, P, P]
     ceil.epc_write.argtypes = [P, SZ, ctypes.c_uint32, I32, I32, I32, P, P, P]
     ceil.epc_copy.argtypes = [P, P, SZ, I32, I32, I32, P, P, P]
-    ceil.epc_row_store.argtypes = [P, I64, I64, P, I64, I32, P, P, P]
+    ceil.epc_row_store.argtypes = [P, I64, I64, P, I64, I32, I32, P, P, P]
     ceil.epc_gather.argtypes = [P, P, I64, I64, P, I64, I32, P, P, P]
     ceil.epc_read_sink_words.restype = I64
     ceil.epc_read_sink_words.argtypes = [SZ, I32, I32]
@@ -57,9 +57,9 @@ def test_invalid_arguments_launch_nothing(ceil):
     assert ceil.epc_read(A, 0, A, 4, 0, 0, None, None, None) == 0       # nothing to do
     assert ceil.epc_write(None, 32, 0, 4, 0, 0, None, None, None) == -1
     assert ceil.epc_copy(A, A + 8, 32, 4, 0, 0, None, None, None) == -1
-    assert ceil.epc_row_store(A, 10, 100, A, 4, 8, None, None, None) == -1   # row bytes % 16
-    assert ceil.epc_row_store(A, 10, 128, A, 4, 0, None, None, None) == -1   # K < 1
-    assert ceil.epc_row_store(A, 10, 128, A, 4, 65, None, None, None) == -1  # K > 64
+    assert ceil.epc_row_store(A, 10, 100, A, 4, 8, 0, None, None, None) == -1   # row bytes % 16
+    assert ceil.epc_row_store(A, 10, 128, A, 4, 0, 1, None, None, None) == -1   # K < 1
+    assert ceil.epc_row_store(A, 10, 128, A, 4, 65, 0, None, None, None) == -1  # K > 64
     assert ceil.epc_gather(A, A, 10, 128, None, 4, 8, None, None, None) == -1
     assert ceil.epc_gather(A, A, -1, 128, A, 4, 8, None, None, None) == -1
     # a block covers 4096 * vec_per_thread bytes per round; one word per wave
@@ -96,16 +96,17 @@ def test_ceiling_kernels_move_what_they_claim():
     T, K, rows, rb = 5, 3, 12, 2064
     slot_row = torch.tensor([0, 4, -1, 7, 1, 11, 12, 2, 3, -1, -1, 5, 6, 9, 8], dtype=torch.int32,
                             device="cuda")
-    out = torch.full((rows, rb // 4), -5, dtype=torch.int32, device="cuda")
-    c.row_store(out, rows, rb, slot_row, T, K)
-    torch.cuda.synchronize()
-    o = out.cpu().numpy().reshape(rows, rb // 16, 4)
-    for t in range(T):
-        for k in range(K):
-            r = int(slot_row[t * K + k])
-            if 0 <= r < rows:
-                assert (o[r] == np.array([t, 1, 2, 3])).all()
-    assert (o[10] == -5).all()                      # no slot maps to row 10
+    for nt in (False, True):
+        out = torch.full((rows, rb // 4), -5, dtype=torch.int32, device="cuda")
+        c.row_store(out, rows, rb, slot_row, T, K, nontemporal=nt)
+        torch.cuda.synchronize()
+        o = out.cpu().numpy().reshape(rows, rb // 16, 4)
+        for t in range(T):
+            for k in range(K):
+                r = int(slot_row[t * K + k])
+                if 0 <= r < rows:
+                    assert (o[r] == np.array([t, 1, 2, 3])).all()
+        assert (o[10] == -5).all()                  # no slot maps to row 10
     # combine-pattern gather: out[t] = XOR of its slot rows
     inp = torch.randint(0, 2**31 - 1, (rows, rb // 4), dtype=torch.int32, device="cuda")
     g = torch.empty((T, rb // 4), dtype=torch.int32, device="cuda")

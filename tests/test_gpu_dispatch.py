@@ -17,7 +17,7 @@ pytestmark = [pytest.mark.gpu, needs_gpu]
 
 
 def _run_both(idx, E, A, cap, x, sf=None, w=None, zero_padding=False, want_w=True,
-              sf_cols=False, handle=None):
+              sf_cols=False, handle=None, streaming=False):
     """GPU layout + dispatch, and the oracle on the same inputs."""
     T, K = idx.shape
     h, rc, dst, _ = gpu_layout(idx, E, A, cap, handle=handle)
@@ -33,7 +33,7 @@ def _run_both(idx, E, A, cap, x, sf=None, w=None, zero_padding=False, want_w=Tru
     out_w = poison_(torch.empty(cap, dtype=torch.float32, device="cuda")) if want_w else None
     w_dev = None if w is None else torch.from_numpy(w).cuda()
     h.dispatch(x.cuda(), sf=sf_dev, topk_weights=w_dev, zero_padding=zero_padding,
-               out_x=out_x, out_sf=out_sf, out_w=out_w)
+               out_x=out_x, out_sf=out_sf, out_w=out_w, streaming=streaming)
     torch.cuda.synchronize()
     lay = oracle.layout(idx, E, A, cap)
     o_x = np.full((cap, u8(x[:1]).shape[1]), POISON, np.uint8)
@@ -64,6 +64,20 @@ def test_dispatch_configs_full(name):
     say("dispatch", name, cap)
     _, g, o, _ = _run_both(wl.topk_idx, cfg.experts, cfg.alignment, cap, wl.x, sf=wl.sf,
                            w=wl.topk_weights, zero_padding=cfg.zero_padding)
+    _assert_same(g, o)
+
+
+@pytest.mark.parametrize("name,zp", [("decode", True), ("prefill", False), ("prefill", True),
+                                     ("skewed", True)])
+def test_dispatch_streaming_stores(name, zp):
+    """EP_DISPATCH_STREAMING changes only how the rows are stored: the same
+    bytes as the oracle over the whole poisoned buffers."""
+    cfg = W.CONFIGS[name]
+    wl = W.make(cfg)
+    cap = ep.ep_capacity_bound(cfg.tokens, cfg.topk, cfg.experts, cfg.alignment)
+    say("dispatch streaming", name, zp)
+    _, g, o, _ = _run_both(wl.topk_idx, cfg.experts, cfg.alignment, cap, wl.x, sf=wl.sf,
+                           w=wl.topk_weights, zero_padding=zp, streaming=True)
     _assert_same(g, o)
 
 
@@ -257,7 +271,8 @@ def test_layout_dispatch_equals_layout_then_dispatch(name):
     """ep_layout_dispatch (the uncached dispatch: layout, then the copy, in one
     call) writes exactly what ep_layout followed by ep_dispatch writes: the
     whole layout, every output row, scale pack and weight (poison-filled
-    buffers on both sides, compared on the device)."""
+    buffers on both sides, compared on the device).  At decode and prefill
+    the one-call form stores its rows with streaming stores."""
     cfg = W.CONFIGS[name]
     cap = ep.ep_capacity_bound(cfg.tokens, cfg.topk, cfg.experts, cfg.alignment)
     wl = W.make(cfg, device="cuda")
@@ -273,7 +288,8 @@ def test_layout_dispatch_equals_layout_then_dispatch(name):
         say("layout_dispatch", name, "fused" if fused else "two calls")
         if fused:
             h.layout_dispatch(idx, wl.x, sf=wl.sf, topk_weights=w, zero_padding=cfg.zero_padding,
-                              out_x=ox, out_sf=osf, out_w=ow)
+                              out_x=ox, out_sf=osf, out_w=ow,
+                              streaming=name in ("decode", "prefill"))
         else:
             h.layout(idx)
             h.dispatch(wl.x, sf=wl.sf, topk_weights=w, zero_padding=cfg.zero_padding, out_x=ox,
