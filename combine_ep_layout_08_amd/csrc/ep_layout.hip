@@ -539,8 +539,8 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_single_kernel(LayoutArg
 // count is visible): one block per tile sums the counts of the tiles before it
 // and of all tiles, scans the aligned totals into psum (every block the same
 // way), writes its slots' final rows and source metadata and its tokens' rank
-// rows; one more block per expert (same totals and scan) marks that expert's
-// alignment gap; tile 0 writes counts, psum and the scalars and finally moves
+// rows; place_gap_blocks more blocks (same totals and scan) mark the experts'
+// alignment gaps; tile 0 writes counts, psum and the scalars and finally moves
 // the epoch on, so no later call can mistake these status words for its own.
 // Nothing waits on another block.
 #ifndef EP_LAYOUT_COUNT_PLACE_MAX_TILES
@@ -638,7 +638,8 @@ __device__ void sum_tile_counts(const uint64_t *status, int NB, int num_tiles, i
 template <typename IdxT, int R>
 __global__ __launch_bounds__(kLayoutThreads) void layout_place_kernel(LayoutArgs a,
                                                                      int tokens_per_tile,
-                                                                     int num_tiles) {
+                                                                     int num_tiles,
+                                                                     int gap_blocks) {
     __shared__ int32_t s_excl[kMaxBuckets];
     __shared__ int32_t s_total[kMaxBuckets];
     __shared__ int32_t s_psum[kMaxExperts + 1];
@@ -672,14 +673,21 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_place_kernel(LayoutArgs
     // 2. Aligned exclusive scan over experts (identical in every block).
     scan_experts(a, s_total, s_psum, s_wave, &s_fatal, tile == 0, sticky);
     const bool fatal = s_fatal != 0;
+    // Gap markers: of every gap_blocks-th expert from blockIdx.x - num_tiles
+    // in the gap blocks, or, without gap blocks, of every num_tiles-th expert
+    // from the tile's own index in the tile blocks (at the end).
+    const int gap_first = gap_block ? static_cast<int>(blockIdx.x) - num_tiles : tile;
+    const int gap_step = gap_block ? gap_blocks : num_tiles;
+    auto mark_gaps = [&]() {
+        for (int e = gap_first; e < E; e += gap_step) {
+            const int64_t end = s_psum[e + 1] < a.capacity ? s_psum[e + 1] : a.capacity;
+            for (int64_t r = static_cast<int64_t>(s_psum[e]) + s_total[e] + tid; r < end;
+                 r += kLayoutThreads)
+                a.src_meta[r] = -1;
+        }
+    };
     if (gap_block) {
-        // Gap markers of expert blockIdx.x - num_tiles.
-        const int e = static_cast<int>(blockIdx.x) - num_tiles;
-        if (fatal) return;
-        const int64_t end = s_psum[e + 1] < a.capacity ? s_psum[e + 1] : a.capacity;
-        for (int64_t r = static_cast<int64_t>(s_psum[e]) + s_total[e] + tid; r < end;
-             r += kLayoutThreads)
-            a.src_meta[r] = -1;
+        if (!fatal) mark_gaps();
         return;
     }
 
@@ -708,6 +716,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_place_kernel(LayoutArgs
     // 4. Rank layout: the tile's received tokens after those of earlier tiles.
     number_rank_rows(a, static_cast<int64_t>(tile) * tokens_per_tile, tokens_per_tile, s_tok,
                      s_excl[E + 1], s_wave);
+    if (gap_blocks == 0 && !fatal) mark_gaps();
 
     // 5. Tile 0 retires this call's status words.
     if (tile == 0 && tid == 0) {
@@ -793,6 +802,23 @@ hipError_t launch_handle_clear(int32_t *scalars, uint64_t *tile_status, int64_t 
 
 namespace {
 
+// Extra blocks of layout_place that mark the alignment gaps, each taking
+// every EP_LAYOUT_PLACE_GAP_BLOCKS-th expert (0: the tile blocks mark them
+// after their rank rows).  Every such block reads all tiles' counts again,
+// so fewer of them cost less; cache-cold, interleaved on one box, layout at
+// prefill 4096 x 8 / 32768 x 8: one block per expert (256) 14.4 / 24.0 us,
+// 64 blocks 13.9 / 23.2, 16 blocks 14.5 / 23.2, none 15.0 / 23.5.  (One
+// block scan for both the expert totals and the rank rows instead of two:
+// 14.0 / 23.5 us, not kept.)
+#ifndef EP_LAYOUT_PLACE_GAP_BLOCKS
+#define EP_LAYOUT_PLACE_GAP_BLOCKS 64
+#endif
+int place_gap_blocks(const LayoutArgs &a) {
+    const int g = EP_LAYOUT_PLACE_GAP_BLOCKS;
+    if (g < 0 || g > a.num_experts) return a.num_experts;
+    return g;
+}
+
 template <typename IdxT, int R>
 hipError_t launch_count_place(const LayoutArgs &a, hipStream_t stream, CallEvents ev) {
     const int tpt = layout_tokens_per_tile(a.num_topk, R);
@@ -800,8 +826,9 @@ hipError_t launch_count_place(const LayoutArgs &a, hipStream_t stream, CallEvent
     hipError_t e = launch_kernel(layout_count_kernel<IdxT, R>, dim3(tiles), dim3(kLayoutThreads),
                                  stream, ev.start, nullptr, a, tpt);
     if (e == hipSuccess)
-        e = launch_kernel(layout_place_kernel<IdxT, R>, dim3(tiles + a.num_experts),
-                          dim3(kLayoutThreads), stream, nullptr, ev.stop, a, tpt, tiles);
+        e = launch_kernel(layout_place_kernel<IdxT, R>, dim3(tiles + place_gap_blocks(a)),
+                          dim3(kLayoutThreads), stream, nullptr, ev.stop, a, tpt, tiles,
+                          place_gap_blocks(a));
     return e;
 }
 
