@@ -10,7 +10,7 @@
 // Three forms.  A batch that fits in one tile (at most 2048 slots) is laid
 // out in one launch (layout_single, below; tiny 64 x 4 and decode 128 x 8:
 // 11-13 -> 6 us).  Larger batches take two kernels over tiles of whole
-// tokens.  Up to kCountPlaceMaxTiles long tiles (524288 slots):
+// tokens.  Up to kCountPlaceMaxTiles long tiles (819200 slots):
 // layout_count + layout_place (below), which exchange the tiles' counts
 // through the kernel boundary and never wait on another block; measured
 // 1-2 us faster than the lookback form at every size from 64 x 4 to
@@ -18,8 +18,12 @@
 // (4 rounds, 1024 slots) use those: twice the blocks share the ranking, and
 // every place thread still reads all tiles' counts in one or two round trips
 // (prefill 4096 x 8: 16.3 -> 14.5 us).  Beyond kCountPlaceMaxTiles long
-// tiles, where every place block would read too many tiles' counts, the
-// single-pass lookback:
+// tiles, where every place block reads too many tiles' counts, the
+// single-pass lookback.  Cache-cold, K 8, E 256, one box, count + place
+// against lookback: 257 tiles 35.6 / 40.6 us, 274 tiles 38.6 / 42.0, 391
+// tiles 48.3 / 55.7, 512 tiles 85.6 / 69.8, 768 tiles 132.8 / 95.9, 1024
+// tiles 224.9 / 124.7 (a lookback window of 32 or 64 predecessors instead
+// of 16: 47.5 / 57.0 us at 274 tiles).  The lookback form:
 //  1. layout_scan: one 256-thread block per long tile of whole tokens (at
 //     most kTileSlots slots).  The block first loads all of its ids (every load in
 //     flight at once), then each wave takes 64 slots per round: lanes holding
@@ -55,7 +59,10 @@ namespace {
 constexpr uint64_t kFlagAggregate = 1;
 constexpr uint64_t kFlagPrefix = 2;
 constexpr uint32_t kMaxSpins = 1u << 21;
-constexpr int kLookbackWindow = 16;
+#ifndef EP_LAYOUT_LOOKBACK_WINDOW
+#define EP_LAYOUT_LOOKBACK_WINDOW 16
+#endif
+constexpr int kLookbackWindow = EP_LAYOUT_LOOKBACK_WINDOW;
 constexpr int kBucketsPerThread = (kMaxBuckets + kLayoutThreads - 1) / kLayoutThreads;
 
 __device__ inline uint64_t pack_status(uint32_t epoch, uint64_t flag, uint32_t value) {
@@ -544,7 +551,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_single_kernel(LayoutArg
 // the epoch on, so no later call can mistake these status words for its own.
 // Nothing waits on another block.
 #ifndef EP_LAYOUT_COUNT_PLACE_MAX_TILES
-#define EP_LAYOUT_COUNT_PLACE_MAX_TILES 256
+#define EP_LAYOUT_COUNT_PLACE_MAX_TILES 400
 #endif
 constexpr int kCountPlaceMaxTiles = EP_LAYOUT_COUNT_PLACE_MAX_TILES;
 

@@ -76,12 +76,12 @@ CONFIGS = {
 
 
 # Benchmark-only shape (not a parity configuration of its own: the layout
-# tests cover its form at 65537-70000 tokens): prefill routing at 70000
-# tokens, 560000 slots, more than 256 layout tiles of 2048 slots, the size
+# tests cover its form at 102401-110000 tokens): prefill routing at 110000
+# tokens, 880000 slots, more than 400 layout tiles of 2048 slots, the size
 # at which the layout takes its single-pass decoupled-lookback form.
 BENCH_CONFIGS = {
-    "prefill_70k": Config("prefill_70k", 70000, 7168, 256, 8, 128, "fp8", False,
-                          "grouped", 0.0, "sigmoid_norm", False, "bound", 1006),
+    "prefill_110k": Config("prefill_110k", 110000, 7168, 256, 8, 128, "fp8", False,
+                           "grouped", 0.0, "sigmoid_norm", False, "bound", 1006),
 }
 
 

@@ -55,12 +55,12 @@ def test_layout_tile_boundaries(slots, K, E):
 
 @pytest.mark.parametrize("T,K,E", [(128, 8, 256), (129, 8, 256), (256, 8, 256), (257, 8, 256),
                                    (8192, 8, 256), (8193, 8, 256), (10880, 6, 64),
-                                   (10881, 6, 64), (65536, 8, 256), (65537, 8, 256),
+                                   (10881, 6, 64), (102400, 8, 256), (102401, 8, 256),
                                    (8229, 64, 1024)])
 def test_layout_forms_meet(T, K, E):
     """A batch within one tile (up to 2048 slots) is laid out by one block in
     one launch; up to 64 short tiles (1024 slots) by count + place over short
-    tiles, up to 256 tiles of 2048 slots over long ones; beyond that by the
+    tiles, up to 400 tiles of 2048 slots over long ones; beyond that by the
     single-pass lookback.  Both sides of each switch, bit-exact, with empty
     and invalid ids."""
     rng = np.random.default_rng(T + K)
@@ -119,7 +119,7 @@ def test_layout_capacity_error():
     _check(idx, 3, 4, 12)
 
 
-@pytest.mark.parametrize("T", [100, 5000, 40000, 70000])     # every layout form
+@pytest.mark.parametrize("T", [100, 5000, 40000, 110000])     # every layout form
 def test_layout_capacity_in_every_form(T):
     """A capacity one row short of what the routing needs is reported as
     EP_ERR_CAPACITY and dispatch and combine then write nothing; the exact
@@ -145,7 +145,7 @@ def test_layout_capacity_in_every_form(T):
             assert not np.any(u8(out) == POISON)
 
 
-@pytest.mark.parametrize("T", [64, 4096, 70000])     # one-tile, count + place, lookback forms
+@pytest.mark.parametrize("T", [64, 4096, 110000])     # one-tile, count + place, lookback forms
 def test_layout_timeout_bit_is_sticky(T):
     """Once a layout scan's bounded wait has given up, the handle stays void
     until it is set up again.  The timeout bit is set here from the host in the
@@ -194,16 +194,16 @@ def test_layout_handle_reuse_and_determinism():
 
 
 def test_layout_forms_alternate_on_one_handle():
-    """One handle sized for 70000 tokens lays out batches that take every form
-    in turn - lookback (70000 x 8), count + place over long tiles (40000) and
+    """One handle sized for 110000 tokens lays out batches that take every form
+    in turn - lookback (110000 x 8), count + place over long tiles (40000) and
     short tiles (8192, 5000), one launch (256, 100) and the empty batch - in
     an order that switches form on every call, so each form starts from the
     call tags, counters and status words another form left behind."""
-    K, E, A, Tmax = 8, 64, 4, 70000
+    K, E, A, Tmax = 8, 64, 4, 110000
     cap = ep.ep_capacity_bound(Tmax, K, E, A)
     h = ep.Handle(Tmax, K, E, A, cap)
     rng = np.random.default_rng(77)
-    for n, T in enumerate([70000, 256, 40000, 100, 8192, 0, 70000, 5000, 256, 40000, 70000]):
+    for n, T in enumerate([110000, 256, 40000, 100, 8192, 0, 110000, 5000, 256, 40000, 110000]):
         idx = rng.integers(-1, E, size=(T, K))
         if T:
             idx[rng.integers(0, T, size=3), 0] = E + 1          # a few invalid ids
@@ -214,7 +214,7 @@ def test_layout_forms_alternate_on_one_handle():
         assert_rank_equal(rc, idx, E)
 
 
-@pytest.mark.parametrize("T,K", [(500, 4), (5000, 4), (40000, 8), (70000, 8)])   # every form
+@pytest.mark.parametrize("T,K", [(500, 4), (5000, 4), (40000, 8), (110000, 8)])   # every form
 def test_layout_cumulative_stats(T, K):
     rng = np.random.default_rng(12)
     E = 40

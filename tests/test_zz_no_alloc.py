@@ -51,7 +51,7 @@ def _assert_same(got, want, what):
 
 def test_noalloc_layout_matches_layout_on_shrinking_batches():
     K, E, A = 8, 256, 128
-    T_max = 70000                     # 560000 slots: more than 256 long tiles
+    T_max = 110000                    # 880000 slots: more than 400 long tiles
     cap = ep.ep_capacity_bound(T_max, K, E, A)
     ref = ep.Handle(T_max, K, E, A, cap)
     h = ep.Handle(T_max, K, E, A, cap)
@@ -76,13 +76,13 @@ def test_noalloc_layout_two_handles_alternate():
     """Two handles take turns on the shared array (ordered on one stream):
     each call must see only its own status words."""
     K, E, A = 8, 64, 16
-    T_max = 70000
+    T_max = 110000
     cap = T_max * K + (A - 1) * E
     hs = [ep.Handle(T_max, K, E, A, cap) for _ in range(2)]
     refs = [ep.Handle(T_max, K, E, A, cap) for _ in range(2)]
     stats = torch.zeros(E, dtype=torch.int32, device="cuda")
     # lookback, lookback, count + place, count + place
-    for n, T in enumerate([T_max, 66000, 9000, 8000]):
+    for n, T in enumerate([T_max, 104000, 9000, 8000]):
         i = n % 2
         idx = torch.from_numpy(_ids(T, K, E, seed=700 + n)).cuda()
         say("noalloc alternate", i, T, K, E, A)
