@@ -200,14 +200,15 @@ def test_dispatch_with_imported_oracle_layout():
     np.testing.assert_array_equal(u8(out_x), o_x)
 
 
-def test_dispatch_after_capacity_error_writes_nothing():
+@pytest.mark.parametrize("streaming", [False, True])
+def test_dispatch_after_capacity_error_writes_nothing(streaming):
     idx = np.array([[0, 1], [1, 2], [2, 0]])
     x = torch.arange(3 * 64, dtype=torch.float32).reshape(3, 64).to(torch.bfloat16)
     h, rc, _, _ = gpu_layout(idx, 3, 4, 11)
     assert rc["status"] == ep.EP_ERR_CAPACITY
     out = poison_(torch.empty((11, 64), dtype=torch.bfloat16, device="cuda"))
-    say("dispatch after capacity error")
-    h.dispatch(x.cuda(), zero_padding=True, out_x=out)
+    say("dispatch after capacity error", streaming)
+    h.dispatch(x.cuda(), zero_padding=True, out_x=out, streaming=streaming)
     torch.cuda.synchronize()
     assert np.all(u8(out) == POISON)
 
