@@ -68,7 +68,8 @@ typedef enum ep_status {
     EP_ERR_DTYPE = 3,         /* element type not accepted by this call        */
     EP_ERR_UNSUPPORTED = 4,   /* valid for the method, beyond this library's   */
                               /* limits (K > 64, E > 1024, capacity >= 2^31, */
-                              /* more than 256 scale packs per token)          */
+                              /* more than 256 scale packs per token), or a   */
+                              /* dispatch flag bit this library does not know */
     EP_ERR_MISALIGNED = 5,    /* pointer or row size not 16-byte aligned       */
     EP_ERR_WORKSPACE = 6,     /* workspace NULL or smaller than required       */
     EP_ERR_NOT_LAID_OUT = 7,  /* dispatch / combine before a layout            */
