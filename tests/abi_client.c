@@ -1,8 +1,9 @@
 /*
  * A plain C client of libep.so: no torch and no Python in the path.  It reads
  * a routing and payloads from binary files, runs ep_layout, ep_dispatch (bf16
- * rows, top-k weights, zero padding) and ep_combine (weights and an expert
- * bias) through the C ABI on a stream of its own, with buffers from
+ * rows, top-k weights, zero padding, streaming stores) and ep_combine
+ * (weights and an expert bias) through the C ABI on a stream of its own,
+ * with buffers from
  * hipMalloc, and writes the layout and every output back to files.
  *
  * ep_client_run(DIR, T, K, E, A, H)
@@ -130,8 +131,9 @@ int ep_client_run(const char *dir, int32_t T, int32_t K, int32_t E, int32_t A, i
 
     EP_TRY(ep_handle_init(&h, T, K, E, A, cap, ws, ws_bytes, stream));
     EP_TRY(ep_layout(&h, idx, EP_I64, T, NULL, stream));
-    EP_TRY(ep_dispatch(&h, x, EP_BF16, H, NULL, 0, 0, 0, w, out_x, NULL, 0, 0, out_w, 1,
-                       stream));
+    /* zero padding, rows stored with streaming (non-temporal) stores */
+    EP_TRY(ep_dispatch(&h, x, EP_BF16, H, NULL, 0, 0, 0, w, out_x, NULL, 0, 0, out_w,
+                       EP_DISPATCH_ZERO_PADDING | EP_DISPATCH_STREAMING, stream));
     EP_TRY(ep_combine(&h, y, EP_BF16, H, w, bias, NULL, NULL, out, stream));
     EP_TRY(ep_handle_read_counts(&h, NULL, NULL, &num_expanded, &num_recv, &bits, &invalid,
                                  stream));
