@@ -3,8 +3,8 @@
  * a routing and payloads from binary files, runs ep_layout, ep_dispatch (bf16
  * rows, top-k weights, zero padding, streaming stores) and ep_combine
  * (weights and an expert bias) through the C ABI on a stream of its own,
- * with buffers from
- * hipMalloc, and writes the layout and every output back to files.
+ * with buffers from hipMalloc, and writes the layout and every output back
+ * to files.
  *
  * ep_client_run(DIR, T, K, E, A, H)
  *   reads  DIR/topk_idx.bin (int64 [T,K]), x.bin (bf16 bits [T,H]),
